@@ -1,0 +1,154 @@
+"""Python binding of the anchor-attention C ABI (include/anchor_attn.h).
+
+Argument marshalling only: torch tensors supply device memory and the current HIP
+stream; every step of the computation runs in the HIP kernels of
+``libanchor_attn.so``.  There is no CPU fallback -- if the library is missing or
+cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libanchor_attn.so")
+
+FP32, BF16 = 0, 1
+PLAN_AUTO, PLAN_FUSED, PLAN_SPLIT = 0, 1, 2
+_PLANS = {"auto": PLAN_AUTO, "fused": PLAN_FUSED, "split": PLAN_SPLIT}
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Loads libanchor_attn.so (once).  Raises RuntimeError if it is not built."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"anchor attention HIP library not found at {_LIB_PATH}; build it with "
+                "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int
+        lib.anchor_attn_create.argtypes = [ctypes.POINTER(vp)]
+        lib.anchor_attn_destroy.argtypes = [vp]
+        lib.anchor_attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        lib.anchor_attn_set_plan.argtypes = [vp, i32]
+        lib.anchor_attn_describe_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32,
+                                                  ctypes.c_char_p, i32]
+        lib.anchor_attn_status_string.argtypes = [i32]
+        lib.anchor_attn_status_string.restype = ctypes.c_char_p
+        for f in (lib.anchor_attn_create, lib.anchor_attn_destroy, lib.anchor_attn_forward,
+                  lib.anchor_attn_set_plan, lib.anchor_attn_describe_plan):
+            f.restype = i32
+        _lib = lib
+        return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().anchor_attn_status_string(int(code)).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise RuntimeError(f"{what}: {status_string(code)} (status {code})")
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return FP32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"anchor attention supports float32 and bfloat16, got {t.dtype}")
+
+
+class AnchorAttention:
+    """Owns one library context (and its workspace) on one device."""
+
+    def __init__(self, device=None, plan: str = "auto"):
+        import torch
+        self.device = torch.device("cuda", torch.cuda.current_device() if device is None
+                                   else torch.device(device).index or 0)
+        lib = load_library()
+        handle = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check(lib.anchor_attn_create(ctypes.byref(handle)), "anchor_attn_create")
+        self._h = handle
+        self._lib = lib
+        if plan != "auto":
+            self.set_plan(plan)
+
+    def set_plan(self, plan: str) -> None:
+        _check(self._lib.anchor_attn_set_plan(self._h, _PLANS[plan]), "anchor_attn_set_plan")
+
+    def describe(self, B, h, n, m, d, dtype: str = "bf16") -> str:
+        buf = ctypes.create_string_buffer(512)
+        code = FP32 if dtype == "fp32" else BF16
+        _check(self._lib.anchor_attn_describe_plan(self._h, B, h, n, m, d, code, buf, 512),
+               "anchor_attn_describe_plan")
+        return buf.value.decode()
+
+    def forward(self, Q, U, V, out=None, stream=None):
+        """Q, V: [B, h, n, d]; U: [h, m, d]; same dtype, contiguous, on this device.
+        Returns H [B, h, n, d] (``out`` if given).  Enqueued on ``stream`` (default: the
+        current torch stream); no synchronisation."""
+        import torch
+        if Q.dim() != 4 or V.shape != Q.shape or U.dim() != 3:
+            raise ValueError(f"bad shapes Q{tuple(Q.shape)} U{tuple(U.shape)} V{tuple(V.shape)}")
+        B, h, n, d = Q.shape
+        if U.shape[0] != h or U.shape[2] != d:
+            raise ValueError(f"U must be [h={h}, m, d={d}], got {tuple(U.shape)}")
+        m = U.shape[1]
+        for name, t in (("Q", Q), ("U", U), ("V", V)):
+            if not t.is_cuda or t.device != self.device:
+                raise ValueError(f"{name} must live on {self.device}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            if t.dtype != Q.dtype:
+                raise TypeError("Q, U and V must share one dtype")
+        if out is None:
+            out = torch.empty_like(V)
+        elif out.shape != Q.shape or out.dtype != Q.dtype or not out.is_contiguous() \
+                or out.device != self.device:
+            raise ValueError("out must be a contiguous tensor like V")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        _check(self._lib.anchor_attn_forward(
+            self._h, Q.data_ptr(), U.data_ptr(), V.data_ptr(), out.data_ptr(),
+            B, h, n, m, d, _dtype_code(Q), ctypes.c_void_p(stream.cuda_stream)),
+            "anchor_attn_forward")
+        return out
+
+    __call__ = forward
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.anchor_attn_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_default: dict = {}
+
+
+def forward(Q, U, V, out=None, stream=None):
+    """H = A (Delta^-1 (A^T V)) with A = rowsoftmax(Q U^T / sqrt(d)), on Q's device."""
+    key = Q.device.index
+    ctx = _default.get(key)
+    if ctx is None:
+        ctx = _default[key] = AnchorAttention(Q.device)
+    return ctx.forward(Q, U, V, out=out, stream=stream)

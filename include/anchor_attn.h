@@ -1,0 +1,106 @@
+/*
+ * anchor_attn.h -- C ABI of the MI355X (gfx950) AnchorFormer anchor-attention library.
+ *
+ * What it computes (AnchorFormer, arXiv 2505.16463; Pith verdict page: referee report
+ * summary for Eq. (11) and the Eq. (12) multiplication order, desk-editor letter for A
+ * row-stochastic and Delta the diagonal of its column sums; paper abstract for the
+ * anchors as neurons of a layer and the O(mn) cost):
+ *
+ *   for every batch b and head j, with q = Q[b,j] (n x d), v = V[b,j] (n x d) and the
+ *   head's anchors u = U[j] (m x d):
+ *       A     = rowsoftmax(q u^T / sqrt(d))          n x m, softmax over the m anchors
+ *       Delta = diag(1^T A)                          column sums (anchor degrees)
+ *       H[b,j] = A (Delta^-1 (A^T v))                n x d, never forming an n x n matrix
+ *   An anchor whose column sum is exactly 0 contributes nothing (its row of
+ *   Delta^-1 A^T v is taken as 0).
+ *
+ * Layouts: Q, V and H are [B, h, n, d] and U is [h, m, d], all contiguous row-major
+ * (d fastest).  U is shared by every batch element (anchors are per-head parameters).
+ * Q, U, V and H have one element type (fp32 or bf16); accumulation is fp32 and the
+ * output is rounded to nearest-even.
+ *
+ * Memory and ownership: all four pointers are device pointers on the context's device,
+ * owned by the caller, 16-byte aligned; H must not overlap Q, U or V.  The context owns
+ * a grow-only device workspace used by long sequences: the first call that needs a
+ * larger workspace allocates it (hipMalloc, which may synchronize); later calls of the
+ * same or smaller size allocate nothing.  A context must not be used by two host
+ * threads at once.
+ *
+ * Errors: every function returns a status; nothing is thrown, printed or aborted across
+ * this boundary.  All arguments are validated before any work is enqueued, so on an
+ * error return nothing ran and H is untouched.  A failed launch returns
+ * ANCHOR_ATTN_ERROR_HIP; faults during execution surface at the caller's next
+ * synchronisation.
+ */
+#ifndef ANCHOR_ATTN_H
+#define ANCHOR_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct anchor_attn_ctx anchor_attn_ctx;   /* opaque */
+
+typedef enum {
+    ANCHOR_ATTN_FP32 = 0,
+    ANCHOR_ATTN_BF16 = 1
+} anchor_attn_dtype_t;
+
+typedef enum {
+    ANCHOR_ATTN_SUCCESS = 0,
+    ANCHOR_ATTN_ERROR_INVALID_VALUE = 1,   /* null pointer, negative size, m or d == 0, overlap, misalignment */
+    ANCHOR_ATTN_ERROR_NOT_SUPPORTED = 2,   /* d not 32 or 64, m > 256, unknown dtype, plan not applicable */
+    ANCHOR_ATTN_ERROR_OUT_OF_MEMORY = 3,   /* workspace allocation failed; the context stays usable */
+    ANCHOR_ATTN_ERROR_HIP = 4              /* HIP runtime error (no device, launch failure) */
+} anchor_attn_status_t;
+
+/* Plans: how a call is mapped onto kernels.  AUTO picks per shape.  FUSED keeps a whole
+ * (batch, head) slice in one workgroup (short sequences, m <= 64, bf16 only).  SPLIT
+ * splits the tokens of a slice over workgroups: pass 1 writes per-chunk partial column
+ * sums and A^T V, a finalize kernel reduces them in a fixed order into
+ * Delta^-1 A^T V, and pass 2 recomputes A and writes H. */
+typedef enum {
+    ANCHOR_ATTN_PLAN_AUTO = 0,
+    ANCHOR_ATTN_PLAN_FUSED = 1,
+    ANCHOR_ATTN_PLAN_SPLIT = 2
+} anchor_attn_plan_t;
+
+/* Creates a context bound to the calling thread's current HIP device.
+ * out: receives the handle (NULL -> INVALID_VALUE).  No device -> ERROR_HIP. */
+anchor_attn_status_t anchor_attn_create(anchor_attn_ctx** out);
+
+/* Releases the context and its workspace (hipFree synchronizes the device).
+ * ctx == NULL is a no-op returning SUCCESS. */
+anchor_attn_status_t anchor_attn_destroy(anchor_attn_ctx* ctx);
+
+/* Enqueues H = A (Delta^-1 (A^T V)) on `stream` (a hipStream_t; NULL = default stream)
+ * and returns without waiting.
+ *   Q, V, H : [B, h, n, d]  device, element type `dtype`
+ *   U       : [h, m, d]     device, element type `dtype`
+ * Domain: B, h, n >= 0 (B*h*n == 0 is a successful no-op); 1 <= m <= 256; d in {32, 64}.
+ * m >= n is accepted (the result is still defined; the O(mn) saving needs m < n). */
+anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx,
+                                         const void* Q, const void* U, const void* V, void* H,
+                                         int B, int h, int n, int m, int d,
+                                         anchor_attn_dtype_t dtype, void* stream);
+
+/* Forces a plan for later forward calls on this context (tests and tuning); AUTO
+ * restores the default choice.  A forced plan that cannot run a given shape makes that
+ * forward call return NOT_SUPPORTED. */
+anchor_attn_status_t anchor_attn_set_plan(anchor_attn_ctx* ctx, anchor_attn_plan_t plan);
+
+/* Writes a one-line, NUL-terminated description of the plan a forward call with these
+ * arguments would use (kernels, grids, chunking, workspace bytes) into buf[0..len).
+ * Validates like anchor_attn_forward but enqueues nothing and allocates nothing. */
+anchor_attn_status_t anchor_attn_describe_plan(anchor_attn_ctx* ctx, int B, int h, int n,
+                                               int m, int d, anchor_attn_dtype_t dtype,
+                                               char* buf, int len);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* anchor_attn_status_string(anchor_attn_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ANCHOR_ATTN_H */

@@ -1,0 +1,128 @@
+"""fp64 CPU oracle for AnchorFormer anchor attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and its
+Python binding) never imports, links or calls it, and it imports nothing from the
+product package.
+
+The arithmetic lives in ``anchor_oracle.c`` (plain C, fp64, libm ``exp``), built with
+gcc into ``libanchor_oracle.so`` next to this file.  This module only marshals numpy
+arrays (upcast exactly to float64) into that library.
+
+Functions
+---------
+anchor_attn(Q, U, V, nthreads)      -- H for [B,h,n,d] tensors, U [h,m,d]; Eq. (12) order
+anchor_slice(q, u, v)               -- one slice, returns (A, delta, W, H)
+anchor_bruteforce(q, u, v)          -- one slice via the bipartite chain F = D^-1 G, F^2;
+                                       returns (S_t, H)
+full_attention_slice(q, k, v, rows) -- report-only softmax(QK^T/sqrt(d))V for chosen rows
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "anchor_oracle.c")
+_LIB = os.path.join(_HERE, "libanchor_oracle.so")
+_lib = None
+
+_DBL = ctypes.POINTER(ctypes.c_double)
+_LONGP = ctypes.POINTER(ctypes.c_long)
+_L = ctypes.c_long
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (fp64, no fused contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+               "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_anchor_slice_f64.argtypes = [_DBL, _DBL, _DBL, _L, _L, _L, _DBL, _DBL, _DBL, _DBL]
+        lib.oracle_anchor_attn_f64.argtypes = [_DBL, _DBL, _DBL, _DBL, _L, _L, _L, _L, _L, ctypes.c_int]
+        lib.oracle_anchor_bruteforce_f64.argtypes = [_DBL, _DBL, _DBL, _L, _L, _L, _DBL, _DBL]
+        lib.oracle_full_attn_slice_f64.argtypes = [_DBL, _DBL, _DBL, _L, _L, _LONGP, _L, _DBL]
+        for f in (lib.oracle_anchor_slice_f64, lib.oracle_anchor_attn_f64,
+                  lib.oracle_anchor_bruteforce_f64, lib.oracle_full_attn_slice_f64):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _p(x: np.ndarray):
+    return x.ctypes.data_as(_DBL)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError(f"oracle {what} failed with code {rc}")
+
+
+def anchor_slice(q, u, v):
+    """One slice: q [n,d], u [m,d], v [n,d] -> (A [n,m], delta [m], W [m,d], H [n,d])."""
+    q, u, v = _f64(q), _f64(u), _f64(v)
+    n, d = q.shape
+    m = u.shape[0]
+    assert u.shape == (m, d) and v.shape == (n, d)
+    A = np.zeros((n, m)); delta = np.zeros(m); W = np.zeros((m, d)); H = np.zeros((n, d))
+    _check(_load().oracle_anchor_slice_f64(_p(q), _p(u), _p(v), n, m, d, _p(A), _p(delta),
+                                          _p(W), _p(H)), "anchor_slice")
+    return A, delta, W, H
+
+
+def anchor_attn(Q, U, V, nthreads: int | None = None) -> np.ndarray:
+    """Q, V [B,h,n,d]; U [h,m,d] -> H [B,h,n,d] in fp64."""
+    Q, U, V = _f64(Q), _f64(U), _f64(V)
+    B, h, n, d = Q.shape
+    m = U.shape[1]
+    assert U.shape == (h, m, d) and V.shape == Q.shape
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    H = np.zeros_like(Q)
+    _check(_load().oracle_anchor_attn_f64(_p(Q), _p(U), _p(V), _p(H), B, h, n, m, d,
+                                         int(nthreads)), "anchor_attn")
+    return H
+
+
+def anchor_bruteforce(q, u, v):
+    """One slice through F = D^-1 G and F^2 -> (S_t [n,n], H [n,d])."""
+    q, u, v = _f64(q), _f64(u), _f64(v)
+    n, d = q.shape
+    m = u.shape[0]
+    S = np.zeros((n, n)); H = np.zeros((n, d))
+    _check(_load().oracle_anchor_bruteforce_f64(_p(q), _p(u), _p(v), n, m, d, _p(S), _p(H)),
+           "anchor_bruteforce")
+    return S, H
+
+
+def full_attention_slice(q, k, v, rows=None) -> np.ndarray:
+    """Report-only: softmax(q k^T / sqrt(d)) v for the given rows (all rows if None)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n, d = q.shape
+    if rows is None:
+        rows_arr, nrows, rp = None, n, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows, rp = rows_arr.size, rows_arr.ctypes.data_as(_LONGP)
+    out = np.zeros((nrows, d))
+    _check(_load().oracle_full_attn_slice_f64(_p(q), _p(k), _p(v), n, d, rp, nrows, _p(out)),
+           "full_attention_slice")
+    return out
