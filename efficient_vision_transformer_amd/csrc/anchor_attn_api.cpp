@@ -1,0 +1,271 @@
+// anchor_attn_api.cpp -- the C ABI declared in include/anchor_attn.h.
+//
+// Validation, plan selection, the grow-only workspace and kernel launches.  Nothing here
+// computes any part of the method on the host: every step runs in the HIP kernels.
+#include "anchor_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "kernels.h"
+
+struct anchor_attn_ctx {
+  int device = 0;
+  int num_cus = 256;
+  void* workspace = nullptr;
+  size_t workspace_bytes = 0;
+  anchor_attn_plan_t plan = ANCHOR_ATTN_PLAN_AUTO;
+};
+
+namespace {
+
+using aa::FusedPlan;
+using aa::Geometry;
+using aa::SplitPlan;
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+// Argument checks shared by forward and describe.  Returns SUCCESS and fills *g, or the
+// error.  *empty is set when there is no work (B*h*n == 0).
+anchor_attn_status_t check_shape(int B, int h, int n, int m, int d, anchor_attn_dtype_t dtype,
+                                 Geometry* g, bool* empty) {
+  if (B < 0 || h < 0 || n < 0 || m < 0 || d < 0) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+  if (m == 0 || d == 0) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+  if (dtype != ANCHOR_ATTN_FP32 && dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  if (d != 32 && d != 64) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  if (m > 256) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  const long long slices = (long long)B * (long long)h;
+  *empty = (slices == 0 || n == 0);
+  // Index limits: per-slice offsets are 64-bit, but grids and token indices are 32-bit.
+  if (slices > (1LL << 24) || (long long)n > (1LL << 28)) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  g->B = B; g->h = h; g->n = n; g->m = m; g->d = d;
+  g->m_pad = (m + 31) / 32 * 32;
+  g->at = g->m_pad / 16;
+  g->slices = slices;
+  g->c2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  return ANCHOR_ATTN_SUCCESS;
+}
+
+SplitPlan make_split_plan(const Geometry& g, anchor_attn_dtype_t dtype, int num_cus) {
+  SplitPlan p{};
+  const int n = g.n;
+  // Pass 1: aim for ~2 workgroups per CU, chunks a multiple of the 128-token block.
+  const long long want1 = 2LL * num_cus;
+  int max_chunks1 = (n + aa::kPass1Block - 1) / aa::kPass1Block;
+  int c1 = (int)std::min<long long>(max_chunks1, std::max<long long>(1, (want1 + g.slices - 1) / g.slices));
+  int len1 = (n + c1 - 1) / c1;
+  len1 = (len1 + aa::kPass1Block - 1) / aa::kPass1Block * aa::kPass1Block;
+  p.chunk_len1 = len1;
+  p.chunks1 = (n + len1 - 1) / len1;
+  // Pass 2: ~4 workgroups per CU, chunks a multiple of the 64-token block.
+  const long long want2 = 4LL * num_cus;
+  int max_chunks2 = (n + aa::kPass2Block - 1) / aa::kPass2Block;
+  int c2 = (int)std::min<long long>(max_chunks2, std::max<long long>(1, (want2 + g.slices - 1) / g.slices));
+  int len2 = (n + c2 - 1) / c2;
+  len2 = (len2 + aa::kPass2Block - 1) / aa::kPass2Block * aa::kPass2Block;
+  p.chunk_len2 = len2;
+  p.chunks2 = (n + len2 - 1) / len2;
+  const size_t es = (dtype == ANCHOR_ATTN_BF16) ? 2 : 4;
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  p.part_bytes = al((size_t)g.slices * p.chunks1 * g.m_pad * g.d * sizeof(float));
+  p.dpart_bytes = al((size_t)g.slices * p.chunks1 * g.m_pad * sizeof(float));
+  p.w_bytes = al((size_t)g.slices * g.m_pad * g.d * es);
+  return p;
+}
+
+enum class Chosen { Fused, Split, Unsupported };
+
+Chosen choose(const anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t dtype,
+              FusedPlan* fp) {
+  const bool fused_ok = (dtype == ANCHOR_ATTN_BF16) && aa::fused_supported(g, fp);
+  switch (ctx->plan) {
+    case ANCHOR_ATTN_PLAN_FUSED: return fused_ok ? Chosen::Fused : Chosen::Unsupported;
+    case ANCHOR_ATTN_PLAN_SPLIT: return Chosen::Split;
+    default: return fused_ok ? Chosen::Fused : Chosen::Split;
+  }
+}
+
+anchor_attn_status_t ensure_workspace(anchor_attn_ctx* ctx, size_t bytes) {
+  if (bytes <= ctx->workspace_bytes) return ANCHOR_ATTN_SUCCESS;
+  if (ctx->workspace) {
+    if (hipFree(ctx->workspace) != hipSuccess) return ANCHOR_ATTN_ERROR_HIP;
+    ctx->workspace = nullptr;
+    ctx->workspace_bytes = 0;
+  }
+  void* p = nullptr;
+  const hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky-free error state of this thread
+    return ANCHOR_ATTN_ERROR_OUT_OF_MEMORY;
+  }
+  ctx->workspace = p;
+  ctx->workspace_bytes = bytes;
+  return ANCHOR_ATTN_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* anchor_attn_status_string(anchor_attn_status_t s) {
+  switch (s) {
+    case ANCHOR_ATTN_SUCCESS: return "ANCHOR_ATTN_SUCCESS";
+    case ANCHOR_ATTN_ERROR_INVALID_VALUE: return "ANCHOR_ATTN_ERROR_INVALID_VALUE";
+    case ANCHOR_ATTN_ERROR_NOT_SUPPORTED: return "ANCHOR_ATTN_ERROR_NOT_SUPPORTED";
+    case ANCHOR_ATTN_ERROR_OUT_OF_MEMORY: return "ANCHOR_ATTN_ERROR_OUT_OF_MEMORY";
+    case ANCHOR_ATTN_ERROR_HIP: return "ANCHOR_ATTN_ERROR_HIP";
+  }
+  return "ANCHOR_ATTN_ERROR_UNKNOWN_STATUS";
+}
+
+anchor_attn_status_t anchor_attn_create(anchor_attn_ctx** out) {
+  if (!out) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+  *out = nullptr;
+  try {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+      (void)hipGetLastError();
+      return ANCHOR_ATTN_ERROR_HIP;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ANCHOR_ATTN_ERROR_HIP;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return ANCHOR_ATTN_ERROR_HIP;
+    anchor_attn_ctx* ctx = new (std::nothrow) anchor_attn_ctx;
+    if (!ctx) return ANCHOR_ATTN_ERROR_OUT_OF_MEMORY;
+    ctx->device = dev;
+    ctx->num_cus = cus > 0 ? cus : 256;
+    *out = ctx;
+    return ANCHOR_ATTN_SUCCESS;
+  } catch (...) {
+    return ANCHOR_ATTN_ERROR_HIP;
+  }
+}
+
+anchor_attn_status_t anchor_attn_destroy(anchor_attn_ctx* ctx) {
+  if (!ctx) return ANCHOR_ATTN_SUCCESS;
+  anchor_attn_status_t st = ANCHOR_ATTN_SUCCESS;
+  if (ctx->workspace) {
+    DeviceGuard guard(ctx->device);
+    if (hipFree(ctx->workspace) != hipSuccess) st = ANCHOR_ATTN_ERROR_HIP;
+  }
+  delete ctx;
+  return st;
+}
+
+anchor_attn_status_t anchor_attn_set_plan(anchor_attn_ctx* ctx, anchor_attn_plan_t plan) {
+  if (!ctx) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+  if (plan != ANCHOR_ATTN_PLAN_AUTO && plan != ANCHOR_ATTN_PLAN_FUSED &&
+      plan != ANCHOR_ATTN_PLAN_SPLIT)
+    return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+  ctx->plan = plan;
+  return ANCHOR_ATTN_SUCCESS;
+}
+
+anchor_attn_status_t anchor_attn_describe_plan(anchor_attn_ctx* ctx, int B, int h, int n, int m,
+                                               int d, anchor_attn_dtype_t dtype, char* buf,
+                                               int len) {
+  if (!ctx || !buf || len <= 0) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+  try {
+    Geometry g{};
+    bool empty = false;
+    anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype, &g, &empty);
+    if (st != ANCHOR_ATTN_SUCCESS) return st;
+    if (empty) {
+      std::snprintf(buf, (size_t)len, "empty: no work");
+      return ANCHOR_ATTN_SUCCESS;
+    }
+    FusedPlan fp{};
+    const Chosen c = choose(ctx, g, dtype, &fp);
+    if (c == Chosen::Unsupported) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+    if (c == Chosen::Fused) {
+      std::snprintf(buf, (size_t)len,
+                    "fused: grid=%lld wg=%d waves pairs_per_wave=%d m_pad=%d workspace=0",
+                    (long long)g.slices, fp.waves, fp.pairs_per_wave, g.m_pad);
+    } else {
+      const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
+      std::snprintf(buf, (size_t)len,
+                    "split: pass1 grid=%lld chunk=%d x%d | finalize grid=%lld | pass2 grid=%lld "
+                    "chunk=%d x%d | m_pad=%d workspace=%zu",
+                    (long long)(g.slices * p.chunks1), p.chunk_len1, p.chunks1,
+                    (long long)(g.slices * g.at), (long long)(g.slices * p.chunks2), p.chunk_len2,
+                    p.chunks2, g.m_pad, p.workspace_bytes());
+    }
+    return ANCHOR_ATTN_SUCCESS;
+  } catch (...) {
+    return ANCHOR_ATTN_ERROR_HIP;
+  }
+}
+
+anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx, const void* Q, const void* U,
+                                         const void* V, void* H, int B, int h, int n, int m,
+                                         int d, anchor_attn_dtype_t dtype, void* stream) {
+  if (!ctx) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+  try {
+    Geometry g{};
+    bool empty = false;
+    anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype, &g, &empty);
+    if (st != ANCHOR_ATTN_SUCCESS) return st;
+    if (empty) return ANCHOR_ATTN_SUCCESS;
+    if (!Q || !U || !V || !H) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    const uintptr_t mis = ((uintptr_t)Q | (uintptr_t)U | (uintptr_t)V | (uintptr_t)H) & 15u;
+    if (mis) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    const size_t es = (dtype == ANCHOR_ATTN_BF16) ? 2 : 4;
+    const size_t act = (size_t)g.slices * (size_t)n * (size_t)d * es;
+    const size_t ub = (size_t)h * (size_t)m * (size_t)d * es;
+    if (overlaps(H, act, Q, act) || overlaps(H, act, V, act) || overlaps(H, act, U, ub))
+      return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+
+    FusedPlan fp{};
+    const Chosen c = choose(ctx, g, dtype, &fp);
+    if (c == Chosen::Unsupported) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok) return ANCHOR_ATTN_ERROR_HIP;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (c == Chosen::Fused) {
+      e = aa::launch_fused_bf16(g, fp, Q, U, V, H, s);
+    } else {
+      const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
+      st = ensure_workspace(ctx, p.workspace_bytes());
+      if (st != ANCHOR_ATTN_SUCCESS) return st;
+      e = (dtype == ANCHOR_ATTN_BF16)
+              ? aa::launch_split_bf16(g, p, Q, U, V, H, ctx->workspace, s)
+              : aa::launch_split_fp32(g, p, Q, U, V, H, ctx->workspace, s);
+    }
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return ANCHOR_ATTN_ERROR_HIP;
+    }
+    return ANCHOR_ATTN_SUCCESS;
+  } catch (...) {
+    return ANCHOR_ATTN_ERROR_HIP;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+// device_common.h -- CDNA4 (gfx950) building blocks shared by the anchor-attention kernels.
+//
+// MFMA lane layouts used throughout (wave64, lane = 16*g + c, c in [0,16), g in [0,4)):
+//   v_mfma_f32_16x16x32_bf16:  X operand (A-matrix, M x K): lane holds X[M=c][K=8g+s], s<8
+//                              Y operand (B-matrix, K x N): lane holds Y[K=8g+s][N=c]
+//                              accumulator:                 lane holds D[M=4g+r][N=c], r<4
+//   v_mfma_f32_16x16x4_f32:    X: X[M=c][K=g]; Y: Y[K=g][N=c]; accumulator as above.
+// Because K is a contraction index, any fixed relabelling of K that both operands share
+// leaves the product unchanged; the kernels use that freedom to keep contiguous memory
+// per lane.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace aa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 x, bf16x8 y, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float x, float y, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(x, y, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+
+// Round-to-nearest-even conversion of two accumulators into one 8 x bf16 operand.
+__device__ __forceinline__ bf16x8 pack_bf16(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+  r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
+  r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 splat_bf16(float v) {
+  const __bf16 b = (__bf16)v;
+  return bf16x8{b, b, b, b, b, b, b, b};
+}
+
+// ---- cross-lane reductions ------------------------------------------------------------
+// Over the 16 lanes of one DPP row (lanes with the same g): butterfly with quad
+// permutations and the two row mirrors; every lane of the row ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f<0x140>(x));  // row_mirror
+  return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
+  return x;
+}
+
+// Across the four lane groups g (lanes c, c+16, c+32, c+48) with the gfx950 permlane
+// swaps: permlane16_swap(v, v) hands each lane {v[l], v[l^16]}, permlane32_swap
+// {v[l], v[l^32]} (in some order), so a commutative op of the pair is symmetric.
+__device__ __forceinline__ float xor16_max(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- bf16 operand selectors -----------------------------------------------------------
+// Multiplying by a 0/1 selection matrix moves data between the lane axis and the
+// register axis exactly (each output is one bf16 input times 1, summed with zeros).
+//
+// V tile transpose.  Input X: lane (c,g) holds token c, dims 8*KS*g + 8*kk + s.  Output
+// column c of dim tile dt = 2*kk + p holds dim 8*KS*(2p + (c>>3)) + 8*kk + (c&7):
+// Y[K = 8g+s][N = c] = 1 iff g == 2p + (c>>3) and s == (c&7).
+__device__ __forceinline__ bf16x8 vsel_operand(int p, int c, int g) {
+  bf16x8 r;
+  const bool grp = (g == 2 * p + (c >> 3));
+#pragma unroll
+  for (int s = 0; s < 8; ++s) r[s] = (__bf16)((grp && s == (c & 7)) ? 1.f : 0.f);
+  return r;
+}
+// Dim of column c of V-transpose dim tile dt (matches vsel_operand).
+template <int D>
+__device__ __forceinline__ int vt_dim(int dt, int c) {
+  constexpr int KS = D / 32;
+  return 8 * KS * (2 * (dt & 1) + (c >> 3)) + 8 * (dt >> 1) + (c & 7);
+}
+__host__ __device__ constexpr int vt_dim_h(int D, int dt, int c) {
+  return 8 * (D / 32) * (2 * (dt & 1) + (c >> 3)) + 8 * (dt >> 1) + (c & 7);
+}
+
+// A transpose.  Input X: lane (c,g) holds token c, anchors {32jj + 4g + s (s<4),
+// 32jj + 16 + 4g + s - 4 (s>=4)}.  Output anchor tile half (0: anchors 32jj..+15,
+// 1: 32jj+16..+31): Y[K = 8g+s][N = c] = 1 iff that input anchor is column c.
+__device__ __forceinline__ bf16x8 asel_operand(int half, int c, int g) {
+  bf16x8 r;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const bool hit = (half == 0) ? (s < 4 && c == 4 * g + s) : (s >= 4 && c == 4 * g + s - 4);
+    r[s] = (__bf16)(hit ? 1.f : 0.f);
+  }
+  return r;
+}
+
+// Output dim of accumulator row i (= 4g + r) of a5 dim tile dt2: lane group g owns the
+// contiguous dims 4*DT*g .. 4*DT*g + 4*DT - 1, so each lane stores one run per token.
+__host__ __device__ constexpr int out_dim(int D, int dt2, int i) {
+  return (D / 4) * (i >> 2) + 4 * dt2 + (i & 3);
+}
+
+}  // namespace aa

@@ -1,0 +1,47 @@
+// kernels.h -- internal launch interface between the C ABI and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace aa {
+
+// Problem geometry of one forward call.  Q, V, H: [B, h, n, d]; U: [h, m, d].
+struct Geometry {
+  int B, h, n, m, d;
+  int m_pad;          // m rounded up to a multiple of 32
+  int at;             // anchor tiles of 16: m_pad / 16
+  long long slices;   // B * h
+  float c2;           // log2(e) / sqrt(d): logits are kept in base-2 units
+};
+
+// Split plan: pass 1 over chunks1 chunks of chunk_len1 tokens per slice writes
+// partials; finalize reduces them; pass 2 over chunks2 chunks writes H.
+struct SplitPlan {
+  int chunks1, chunk_len1;
+  int chunks2, chunk_len2;
+  size_t part_bytes, dpart_bytes, w_bytes;   // workspace sections
+  size_t workspace_bytes() const { return part_bytes + dpart_bytes + w_bytes; }
+};
+
+// Fused plan: one workgroup per slice, everything on chip.
+struct FusedPlan {
+  int waves;          // waves per workgroup
+  int pairs_per_wave; // 32-token pairs each wave keeps in registers
+};
+
+constexpr int kPass1Waves = 4;    // pass 1 block = 4 pairs = 128 tokens
+constexpr int kPass1Block = 128;
+constexpr int kPass2Waves = 4;    // pass 2 block = 4 tiles = 64 tokens
+constexpr int kPass2Block = 64;
+
+hipError_t launch_split_bf16(const Geometry& g, const SplitPlan& p, const void* Q,
+                             const void* U, const void* V, void* H, void* workspace,
+                             hipStream_t stream);
+hipError_t launch_split_fp32(const Geometry& g, const SplitPlan& p, const void* Q,
+                             const void* U, const void* V, void* H, void* workspace,
+                             hipStream_t stream);
+bool fused_supported(const Geometry& g, FusedPlan* plan);
+hipError_t launch_fused_bf16(const Geometry& g, const FusedPlan& p, const void* Q,
+                             const void* U, const void* V, void* H, hipStream_t stream);
+
+}  // namespace aa

@@ -63,6 +63,12 @@ def _load():
     return _lib
 
 
+def default_threads() -> int:
+    """Host threads for the batched oracle: the cores this process may use, at most 16
+    (the CPU share of one GPU on a shared box)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def _f64(x) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
 
@@ -95,7 +101,7 @@ def anchor_attn(Q, U, V, nthreads: int | None = None) -> np.ndarray:
     m = U.shape[1]
     assert U.shape == (h, m, d) and V.shape == Q.shape
     if nthreads is None:
-        nthreads = len(os.sched_getaffinity(0))
+        nthreads = default_threads()
     H = np.zeros_like(Q)
     _check(_load().oracle_anchor_attn_f64(_p(Q), _p(U), _p(V), _p(H), B, h, n, m, d,
                                          int(nthreads)), "anchor_attn")
