@@ -104,7 +104,9 @@ Chosen choose(const anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t
   switch (ctx->plan) {
     case ANCHOR_ATTN_PLAN_FUSED: return fused_ok ? Chosen::Fused : Chosen::Unsupported;
     case ANCHOR_ATTN_PLAN_SPLIT: return Chosen::Split;
-    default: return fused_ok ? Chosen::Fused : Chosen::Split;
+    default:
+      // one workgroup per slice pays off once the slices alone fill half of the CUs
+      return (fused_ok && g.slices * 2 >= ctx->num_cus) ? Chosen::Fused : Chosen::Split;
   }
 }
 
@@ -204,8 +206,9 @@ anchor_attn_status_t anchor_attn_describe_plan(anchor_attn_ctx* ctx, int B, int 
     if (c == Chosen::Unsupported) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
     if (c == Chosen::Fused) {
       std::snprintf(buf, (size_t)len,
-                    "fused: grid=%lld wg=%d waves pairs_per_wave=%d m_pad=%d workspace=0",
-                    (long long)g.slices, fp.waves, fp.pairs_per_wave, g.m_pad);
+                    "fused: grid=%lld wg=%d waves pairs_per_wave=%d %s m_pad=%d workspace=0",
+                    (long long)g.slices, fp.waves, fp.pairs_per_wave,
+                    fp.keep_a ? "A kept" : "A recomputed", g.m_pad);
     } else {
       const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
       std::snprintf(buf, (size_t)len,

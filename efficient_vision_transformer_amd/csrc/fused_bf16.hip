@@ -1,13 +1,342 @@
-// fused_bf16.hip -- one workgroup per (batch, head) slice for short sequences.
+// fused_bf16.hip -- one workgroup per (batch, head) slice for short token sequences.
+//
+// Computes, per slice (AnchorFormer, Pith verdict page: referee summary, Eq. (11) in the
+// Eq. (12) order; desk-editor letter: A row-stochastic, Delta its column sums):
+//   A = rowsoftmax(Q U^T / sqrt(d)),  W = Delta^-1 (A^T V),  H = A W
+// with Q and V read from HBM once and H written once.
+//
+// The slice's tokens are taken in rounds of one 32-token pair per wave.
+//   Phase A (per wave, its pair): S^T = U Q^T on the MFMA (lanes = tokens, registers =
+//     anchors), softmax over anchors in registers plus two permlane swaps, A rounded to
+//     bf16.  Selection MFMAs move A and V into the token-in-register layout; the
+//     resulting operand chunks go to LDS.
+//   Phase B (after one barrier): every wave owns distinct (16-anchor, 16-dim) tiles of
+//     A^T V and accumulates them, and the matching column sums Delta (A times ones),
+//     over all pairs of the round from LDS.  No partial sums are ever added across
+//     waves, so the result does not depend on scheduling.
+// After the last round each wave turns its tiles into W = P / Delta (0 where Delta == 0)
+// and stores them as bf16 MFMA operands in LDS; then every wave writes H^T = W^T A^T for
+// its tokens, with A kept in registers (KEEP_A) or recomputed from Q.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace aa {
 
-bool fused_supported(const Geometry&, FusedPlan*) { return false; }
+// bf16 0/1 selection operands, per lane (4 dwords = 8 bf16 slots each):
+//   0, 1: A transpose, output anchor half 0 / 1  (as asel_operand)
+//   2, 3: V transpose, output dim group p = 0 / 1 (as vsel_operand)
+struct SelTable {
+  unsigned v[4][64][4];
+};
+constexpr SelTable make_sel_table() {
+  SelTable t{};
+  for (int lane = 0; lane < 64; ++lane) {
+    const int c = lane & 15, g = lane >> 4;
+    for (int s = 0; s < 8; ++s) {
+      const bool hit[4] = {s < 4 && c == 4 * g + s, s >= 4 && c == 4 * g + s - 4,
+                           g == 0 + (c >> 3) && s == (c & 7), g == 2 + (c >> 3) && s == (c & 7)};
+      for (int k = 0; k < 4; ++k)
+        if (hit[k]) t.v[k][lane][s >> 1] |= (s & 1) ? 0x3F800000u : 0x00003F80u;
+    }
+  }
+  return t;
+}
+__constant__ SelTable kSel = make_sel_table();
 
-hipError_t launch_fused_bf16(const Geometry&, const FusedPlan&, const void*, const void*,
-                             const void*, void*, hipStream_t) {
+__device__ __forceinline__ bf16x8 sel_operand(int k, int lane) {
+  return as_bf16x8(*(const u32x4*)&kSel.v[k][lane][0]);
+}
+
+// Logits and softmax for one 16-token tile, transposed: returns A as the right operand
+// of H^T = W^T A^T, ab[jj] = anchors {32jj + 4g + s, 32jj + 16 + 4g + s - 4} of token c.
+template <int D, int MP>
+__device__ __forceinline__ void tile_softmax(const u32x4 (*u_lds)[D / 32][kWave], const u32x4* q,
+                                             int lane, int g, int m, bool token_ok, float c2,
+                                             bf16x8* ab) {
+  constexpr int KS = D / 32, AT = 2 * MP;
+  f32x4 s[AT];
+#pragma unroll
+  for (int j = 0; j < AT; ++j) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(q[kk]), acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (16 * j + 4 * g + r >= m) acc[r] = -INFINITY;
+    s[j] = acc;
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int j = 0; j < AT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[j][r]);
+  mx = xor32_max(xor16_max(mx));
+  const float mneg = -mx * c2;
+  float z = 0.f;
+#pragma unroll
+  for (int j = 0; j < AT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = exp2_fast(fmaf(s[j][r], c2, mneg));
+      s[j][r] = e;
+      z += e;
+    }
+  z = xor32_sum(xor16_sum(z));
+  const float inv = token_ok ? 1.f / z : 0.f;
+#pragma unroll
+  for (int jj = 0; jj < MP; ++jj) ab[jj] = pack_bf16(s[2 * jj] * inv, s[2 * jj + 1] * inv);
+}
+
+template <int D>
+__device__ __forceinline__ void load_rows(const __bf16* __restrict__ X, size_t base, int row, int n,
+                                          int g, u32x4* out) {
+  constexpr int KS = D / 32;
+  const bool ok = row < n;
+  const size_t off = base + (size_t)(ok ? row : 0) * D + 8 * KS * g;
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) out[kk] = ok ? *(const u32x4*)(X + off + 8 * kk) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// NW waves per workgroup, ROUNDS rounds of NW pairs (compile-time bound; the loop stops
+// at the slice's last pair).  MINW: waves per SIMD the registers must allow (two
+// workgroups per CU).
+template <int D, int MP, int NW, int ROUNDS, bool KEEP_A, int MINW>
+__global__ __launch_bounds__(NW * kWave, MINW)
+void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
+                const __bf16* __restrict__ V, __bf16* __restrict__ H, int h, int n, int m,
+                float c2) {
+  constexpr int KS = D / 32, DT = D / 16, AT = 2 * MP;
+  constexpr int TILES = AT * DT, TPW = (TILES + NW - 1) / NW;
+  const int slice = blockIdx.x;
+  const int head = slice % h;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)slice * (size_t)n * D;
+  const int npairs = (n + 31) >> 5;
+
+  __shared__ u32x4 u_lds[AT][KS][kWave];
+  __shared__ u32x4 ax_lds[AT][NW][kWave];   // A^T left operands, one chunk per pair
+  __shared__ u32x4 vy_lds[DT][NW][kWave];   // V^T right operands, one chunk per pair
+  __shared__ u32x4 w_lds[DT][MP][kWave];    // W^T left operands
+
+  // This wave's first pair goes out to memory before anything else.
+  u32x4 qc[2][KS], vc[2][KS];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    load_rows<D>(Q, base, 32 * w + 16 * tt + c, n, g, qc[tt]);
+    load_rows<D>(V, base, 32 * w + 16 * tt + c, n, g, vc[tt]);
+  }
+  // U as left operands of S^T = U Q^T: lane (c,g) of tile j holds anchor 16j + c.
+  const __bf16* Uh = U + (size_t)head * m * D;
+  for (int idx = threadIdx.x; idx < AT * KS * kWave; idx += NW * kWave) {
+    const int j = idx / (KS * kWave), kk = (idx / kWave) % KS, l = idx & 63;
+    const int a = 16 * j + (l & 15);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + 8 * KS * (l >> 4) + 8 * kk);
+    u_lds[j][kk][l] = v;
+  }
+  const bf16x8 asel0 = sel_operand(0, lane), asel1 = sel_operand(1, lane);
+  const bf16x8 vsel0 = sel_operand(2, lane), vsel1 = sel_operand(3, lane);
+  const bf16x8 ones = splat_bf16(1.f);
+  __syncthreads();
+
+  f32x4 pacc[TPW], dacc[TPW];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) { pacc[k] = zero4(); dacc[k] = zero4(); }
+  bf16x8 keep[KEEP_A ? ROUNDS : 1][2][MP];
+
+#pragma unroll (KEEP_A ? ROUNDS : 1)
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int pairs_here = min(NW, npairs - r * NW);  // uniform over the workgroup
+    if (pairs_here <= 0) break;
+    const int p = r * NW + w;
+    const bool more = (r + 1 < ROUNDS) && (p + NW < npairs);
+    u32x4 qn[2][KS], vn[2][KS];
+    if (more) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        load_rows<D>(Q, base, 32 * (p + NW) + 16 * tt + c, n, g, qn[tt]);
+        load_rows<D>(V, base, 32 * (p + NW) + 16 * tt + c, n, g, vn[tt]);
+      }
+    }
+    // Phase A.
+    if (p < npairs) {
+      f32x4 at[2][AT], vt[2][DT];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        bf16x8 ab[MP];
+        tile_softmax<D, MP>(u_lds, qc[tt], lane, g, m, 32 * p + 16 * tt + c < n, c2, ab);
+        if constexpr (KEEP_A) {
+#pragma unroll
+          for (int jj = 0; jj < MP; ++jj) keep[r][tt][jj] = ab[jj];
+        }
+        // A^T: lane (c,g) -> anchor 16ja + c, tokens 4g + r' of this tile.
+#pragma unroll
+        for (int ja = 0; ja < AT; ++ja) at[tt][ja] = mfma_bf16(ab[ja >> 1], (ja & 1) ? asel1 : asel0, zero4());
+        // V^T: lane (c,g) -> dim vt_dim(dt, c), tokens 4g + r' of this tile.
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vt[tt][dt] = mfma_bf16(as_bf16x8(vc[tt][dt >> 1]), (dt & 1) ? vsel1 : vsel0, zero4());
+      }
+      // Token order inside a chunk: {4g + s of tile 0, 4g + s - 4 of tile 1}.
+#pragma unroll
+      for (int ja = 0; ja < AT; ++ja) ax_lds[ja][w][lane] = as_u32x4(pack_bf16(at[0][ja], at[1][ja]));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vy_lds[dt][w][lane] = as_u32x4(pack_bf16(vt[0][dt], vt[1][dt]));
+    }
+    __syncthreads();
+    // Phase B: tiles t = w, w + NW, ...: anchor tile t / DT, dim tile t % DT.
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int t = w + NW * k;
+      if (t < TILES) {
+        const int ja = t / DT, dt = t - (t / DT) * DT;
+        f32x4 pa = pacc[k], da = dacc[k];
+        for (int ps = 0; ps < pairs_here; ++ps) {
+          const bf16x8 x = as_bf16x8(ax_lds[ja][ps][lane]);
+          pa = mfma_bf16(x, as_bf16x8(vy_lds[dt][ps][lane]), pa);
+          da = mfma_bf16(x, ones, da);
+        }
+        pacc[k] = pa;
+        dacc[k] = da;
+      }
+    }
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) { qc[tt][kk] = qn[tt][kk]; vc[tt][kk] = vn[tt][kk]; }
+    }
+  }
+
+  // W = P / Delta for this wave's tiles, stored as bf16 left operands of H^T = W^T A^T:
+  // [dt2][jj][lane'][slot] with lane' (c', g') holding dim out_dim(dt2, c') and anchors
+  // {32jj + 4g' + s, 32jj + 16 + 4g' + s - 4}.
+  {
+    __bf16* wl = (__bf16*)&w_lds[0][0][0];
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int t = w + NW * k;
+      if (t < TILES) {
+        const int ja = t / DT, dt = t - (t / DT) * DT;
+        const int dim = vt_dim<D>(dt, c);
+        const int rem = dim % (D / 4);
+        const int dt2 = rem >> 2, cc = 4 * (dim / (D / 4)) + (rem & 3);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int anchor = 16 * ja + 4 * g + r;
+          const float delta = dacc[k][r];
+          const float wv = (delta > 0.f) ? pacc[k][r] / delta : 0.f;
+          const int jj = anchor >> 5, hf = (anchor >> 4) & 1, gg = (anchor >> 2) & 3;
+          wl[(((dt2 * MP + jj) * 64) + 16 * gg + cc) * 8 + 4 * hf + (anchor & 3)] = (__bf16)wv;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  bf16x8 wop[DT][MP];
+#pragma unroll
+  for (int dt2 = 0; dt2 < DT; ++dt2)
+#pragma unroll
+    for (int jj = 0; jj < MP; ++jj) wop[dt2][jj] = as_bf16x8(w_lds[dt2][jj][lane]);
+
+#pragma unroll (KEEP_A ? ROUNDS : 1)
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int p = r * NW + w;
+    if (p < npairs) {
+      u32x4 qr[2][KS];
+      if constexpr (!KEEP_A) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) load_rows<D>(Q, base, 32 * p + 16 * tt + c, n, g, qr[tt]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int row = 32 * p + 16 * tt + c;
+        bf16x8 ab[MP];
+        if constexpr (KEEP_A) {
+#pragma unroll
+          for (int jj = 0; jj < MP; ++jj) ab[jj] = keep[r][tt][jj];
+        } else {
+          tile_softmax<D, MP>(u_lds, qr[tt], lane, g, m, row < n, c2, ab);
+        }
+        f32x4 hacc[DT];
+#pragma unroll
+        for (int dt2 = 0; dt2 < DT; ++dt2) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int jj = 0; jj < MP; ++jj) acc = mfma_bf16(wop[dt2][jj], ab[jj], acc);
+          hacc[dt2] = acc;
+        }
+        if (row < n) {
+          __bf16* dst = H + base + (size_t)row * D + (D / 4) * g;
+#pragma unroll
+          for (int hh = 0; hh < DT / 2; ++hh)
+            *(u32x4*)(dst + 8 * hh) = as_u32x4(pack_bf16(hacc[2 * hh], hacc[2 * hh + 1]));
+        }
+      }
+    }
+  }
+}
+
+// Plans (n <= 1024, m <= 64):
+//   m <= 32: eight waves, A kept for up to two rounds (n <= 512), else recomputed;
+//   m <= 64: four waves, A kept for up to five rounds (n <= 640), else recomputed.
+// Both keep two workgroups per CU within the register and LDS budgets.
+static bool fused_choose(const Geometry& g, FusedPlan* plan) {
+  if (g.d != 32 && g.d != 64) return false;
+  const int npairs = (g.n + 31) / 32;
+  FusedPlan p{};
+  if (g.m_pad == 32 && npairs <= 32) {
+    p.waves = 8;
+    p.pairs_per_wave = (npairs + 7) / 8;
+    p.keep_a = p.pairs_per_wave <= 2;
+  } else if (g.m_pad == 64 && npairs <= 32) {
+    p.waves = 4;
+    p.pairs_per_wave = (npairs + 3) / 4;
+    p.keep_a = p.pairs_per_wave <= 5;
+  } else {
+    return false;
+  }
+  if (plan) *plan = p;
+  return true;
+}
+
+bool fused_supported(const Geometry& g, FusedPlan* plan) { return fused_choose(g, plan); }
+
+template <int D, int MP, int NW, int ROUNDS, bool KEEP, int MINW>
+static hipError_t go(const Geometry& g, const void* Q, const void* U, const void* V, void* H,
+                     hipStream_t s) {
+  fused_bf16<D, MP, NW, ROUNDS, KEEP, MINW><<<dim3((unsigned)g.slices), dim3(NW * kWave), 0, s>>>(
+      (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (__bf16*)H, g.h, g.n, g.m, g.c2);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t dispatch(const Geometry& g, const FusedPlan& p, const void* Q, const void* U,
+                           const void* V, void* H, hipStream_t s) {
+  const int r = p.pairs_per_wave;
+  if (g.m_pad == 32) {
+    if (r == 1) return go<D, 1, 8, 1, true, 4>(g, Q, U, V, H, s);
+    if (r == 2) return go<D, 1, 8, 2, true, 2>(g, Q, U, V, H, s);
+    if (r <= 4) return go<D, 1, 8, 4, false, 2>(g, Q, U, V, H, s);
+    return hipErrorInvalidValue;
+  }
+  if (r <= 2) return go<D, 2, 4, 2, true, 2>(g, Q, U, V, H, s);
+  if (r <= 3) return go<D, 2, 4, 3, true, 2>(g, Q, U, V, H, s);
+  if (r <= 5) return go<D, 2, 4, 5, true, 2>(g, Q, U, V, H, s);
+  if (r <= 8) return go<D, 2, 4, 8, false, 2>(g, Q, U, V, H, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_bf16(const Geometry& g, const FusedPlan& p, const void* Q, const void* U,
+                             const void* V, void* H, hipStream_t s) {
+  FusedPlan chk{};
+  if (!fused_choose(g, &chk) || chk.waves != p.waves || chk.pairs_per_wave != p.pairs_per_wave ||
+      chk.keep_a != p.keep_a)
+    return hipErrorInvalidValue;
+  if (g.d == 64) return dispatch<64>(g, p, Q, U, V, H, s);
+  if (g.d == 32) return dispatch<32>(g, p, Q, U, V, H, s);
   return hipErrorInvalidValue;
 }
 

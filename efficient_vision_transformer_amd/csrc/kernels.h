@@ -26,7 +26,8 @@ struct SplitPlan {
 // Fused plan: one workgroup per slice, everything on chip.
 struct FusedPlan {
   int waves;          // waves per workgroup
-  int pairs_per_wave; // 32-token pairs each wave keeps in registers
+  int pairs_per_wave; // 32-token pairs handled by each wave
+  bool keep_a;        // A kept in registers (else recomputed from Q for the output)
 };
 
 constexpr int kPass1Waves = 4;    // pass 1 block = 4 pairs = 128 tokens

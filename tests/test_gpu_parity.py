@@ -26,7 +26,7 @@ def dev():
 @pytest.fixture(scope="module")
 def ctxs(dev):
     from efficient_vision_transformer_amd import AnchorAttention
-    out = {p: AnchorAttention(dev, plan=p) for p in ("auto", "split")}
+    out = {p: AnchorAttention(dev, plan=p) for p in ("auto", "split", "fused")}
     yield out
     for c in out.values():
         c.close()
@@ -102,11 +102,18 @@ EDGE = [
 ]
 
 
+def _fused_applies(shape, dtype):
+    B, h, n, m, d = shape
+    return dtype == "bf16" and m <= 64 and n <= 1024
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 @pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(map(str, s)))
-@pytest.mark.parametrize("plan", ["auto", "split"])
+@pytest.mark.parametrize("plan", ["auto", "split", "fused"])
 def test_edge_shapes(ctxs, dev, shape, dtype, plan):
     B, h, n, m, d = shape
+    if plan == "fused" and not _fused_applies(shape, dtype):
+        pytest.skip("the fused plan covers bf16, m <= 64, n <= 1024")
     x = random_case(7 + n + m, B, h, n, m, d, dtype=dtype, q_scale=1.5)
     got = _run(ctxs[plan], x, dev)
     ref = oracle.anchor_attn(x.Q, x.U, x.V)
@@ -123,6 +130,40 @@ def test_empty_inputs_are_noops(ctxs, dev):
         H = ctx.forward(Q, U, Q.clone())
         torch.cuda.synchronize()
         assert H.shape == Q.shape
+
+
+FUSED_EXTRA = [(3, 2, 32, 32, 64), (1, 1, 33, 64, 64), (2, 1, 512, 32, 64), (1, 2, 513, 31, 64),
+               (1, 1, 1024, 64, 64), (2, 2, 700, 50, 32), (1, 1, 96, 2, 32)]
+
+
+@pytest.mark.parametrize("shape", FUSED_EXTRA, ids=lambda s: "x".join(map(str, s)))
+def test_fused_plan_shapes(ctxs, dev, shape):
+    """Pair counts on both sides of the kept-A / recompute switch, ragged tails."""
+    B, h, n, m, d = shape
+    x = random_case(100 + n, B, h, n, m, d, dtype="bf16", q_scale=2.0)
+    got = _run(ctxs["fused"], x, dev)
+    ref = oracle.anchor_attn(x.Q, x.U, x.V)
+    assert err_for("bf16", got, ref) <= 1e-2
+
+
+def test_fused_plan_rejects_what_it_cannot_run(ctxs, dev):
+    import torch
+    Q = torch.zeros((1, 1, 64, 64), device=dev, dtype=torch.float32)
+    U = torch.zeros((1, 8, 64), device=dev, dtype=torch.float32)
+    with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
+        ctxs["fused"].forward(Q, U, Q.clone())
+    Qb = torch.zeros((1, 1, 64, 64), device=dev, dtype=torch.bfloat16)
+    Ub = torch.zeros((1, 100, 64), device=dev, dtype=torch.bfloat16)
+    with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
+        ctxs["fused"].forward(Qb, Ub, Qb.clone())
+
+
+def test_headline_plans_agree(ctxs, dev):
+    """Fused and split plans on the ViT-S/16 workload both meet the gate."""
+    x = make_inputs("vit_s16_224", with_k=False)
+    ref = oracle.anchor_attn(x.Q, x.U, x.V)
+    for plan in ("fused", "split"):
+        assert err_for("bf16", _run(ctxs[plan], x, dev), ref) <= 1e-2, plan
 
 
 # --- properties that hold at any size --------------------------------------------------
