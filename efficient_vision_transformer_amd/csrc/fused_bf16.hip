@@ -22,29 +22,24 @@
 
 namespace aa {
 
-// bf16 0/1 selection operands, per lane (4 dwords = 8 bf16 slots each):
-//   0, 1: A transpose, output anchor half 0 / 1  (as asel_operand)
-//   2, 3: V transpose, output dim group p = 0 / 1 (as vsel_operand)
-struct SelTable {
-  unsigned v[4][64][4];
-};
-constexpr SelTable make_sel_table() {
-  SelTable t{};
-  for (int lane = 0; lane < 64; ++lane) {
-    const int c = lane & 15, g = lane >> 4;
-    for (int s = 0; s < 8; ++s) {
-      const bool hit[4] = {s < 4 && c == 4 * g + s, s >= 4 && c == 4 * g + s - 4,
-                           g == 0 + (c >> 3) && s == (c & 7), g == 2 + (c >> 3) && s == (c & 7)};
-      for (int k = 0; k < 4; ++k)
-        if (hit[k]) t.v[k][lane][s >> 1] |= (s & 1) ? 0x3F800000u : 0x00003F80u;
-    }
-  }
-  return t;
+// bf16 0/1 selection operands (8 slots, two per dword; bf16 1.0 = 0x3F80), built in
+// registers.  A transpose, output anchor half `half`: slot s is 1 iff it holds anchor c,
+// i.e. s - 4*half == c - 4g.  V transpose, output dim group p: slot c&7 is 1 iff
+// g == 2p + (c >> 3).  (Same matrices as asel_operand / vsel_operand.)
+__device__ __forceinline__ bf16x8 sel_slot(bool hit, int slot) {
+  const unsigned val = (slot & 1) ? 0x3F800000u : 0x00003F80u;
+  const int dw = slot >> 1;
+  u32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r[k] = (hit && dw == k) ? val : 0u;
+  return as_bf16x8(r);
 }
-__constant__ SelTable kSel = make_sel_table();
-
-__device__ __forceinline__ bf16x8 sel_operand(int k, int lane) {
-  return as_bf16x8(*(const u32x4*)&kSel.v[k][lane][0]);
+__device__ __forceinline__ bf16x8 sel_a(int half, int c, int g) {
+  const int idx = c - 4 * g;
+  return sel_slot((unsigned)idx < 4u, 4 * half + (idx & 3));
+}
+__device__ __forceinline__ bf16x8 sel_v(int p, int c, int g) {
+  return sel_slot(g == 2 * p + (c >> 3), c & 7);
 }
 
 // Logits and softmax for one 16-token tile, transposed: returns A as the right operand
@@ -87,14 +82,17 @@ __device__ __forceinline__ void tile_softmax(const u32x4 (*u_lds)[D / 32][kWave]
   for (int jj = 0; jj < MP; ++jj) ab[jj] = pack_bf16(s[2 * jj] * inv, s[2 * jj + 1] * inv);
 }
 
+// Loads rows of Q or V in operand layout (lane (c,g): dims 8*KS*g ..), streaming (each
+// byte is read once, so the loads are marked non-temporal).  Rows past the
+// slice's end read its last row instead; their softmax weights are zeroed, so they add
+// nothing (and a non-finite value there belongs to the same slice anyway).
 template <int D>
 __device__ __forceinline__ void load_rows(const __bf16* __restrict__ X, size_t base, int row, int n,
                                           int g, u32x4* out) {
   constexpr int KS = D / 32;
-  const bool ok = row < n;
-  const size_t off = base + (size_t)(ok ? row : 0) * D + 8 * KS * g;
+  const size_t off = base + (size_t)min(row, n - 1) * D + 8 * KS * g;
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) out[kk] = ok ? *(const u32x4*)(X + off + 8 * kk) : u32x4{0u, 0u, 0u, 0u};
+  for (int kk = 0; kk < KS; ++kk) out[kk] = __builtin_nontemporal_load((const u32x4*)(X + off + 8 * kk));
 }
 
 // NW waves per workgroup, ROUNDS rounds of NW pairs (compile-time bound; the loop stops
@@ -135,8 +133,8 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + 8 * KS * (l >> 4) + 8 * kk);
     u_lds[j][kk][l] = v;
   }
-  const bf16x8 asel0 = sel_operand(0, lane), asel1 = sel_operand(1, lane);
-  const bf16x8 vsel0 = sel_operand(2, lane), vsel1 = sel_operand(3, lane);
+  const bf16x8 asel0 = sel_a(0, c, g), asel1 = sel_a(1, c, g);
+  const bf16x8 vsel0 = sel_v(0, c, g), vsel1 = sel_v(1, c, g);
   const bf16x8 ones = splat_bf16(1.f);
   __syncthreads();
 
@@ -191,10 +189,13 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       if (t < TILES) {
         const int ja = t / DT, dt = t - (t / DT) * DT;
         f32x4 pa = pacc[k], da = dacc[k];
-        for (int ps = 0; ps < pairs_here; ++ps) {
-          const bf16x8 x = as_bf16x8(ax_lds[ja][ps][lane]);
-          pa = mfma_bf16(x, as_bf16x8(vy_lds[dt][ps][lane]), pa);
-          da = mfma_bf16(x, ones, da);
+#pragma unroll
+        for (int ps = 0; ps < NW; ++ps) {
+          if (ps < pairs_here) {
+            const bf16x8 x = as_bf16x8(ax_lds[ja][ps][lane]);
+            pa = mfma_bf16(x, as_bf16x8(vy_lds[dt][ps][lane]), pa);
+            da = mfma_bf16(x, ones, da);
+          }
         }
         pacc[k] = pa;
         dacc[k] = da;
@@ -226,7 +227,7 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         for (int r = 0; r < 4; ++r) {
           const int anchor = 16 * ja + 4 * g + r;
           const float delta = dacc[k][r];
-          const float wv = (delta > 0.f) ? pacc[k][r] / delta : 0.f;
+          const float wv = (delta > 0.f) ? pacc[k][r] * __builtin_amdgcn_rcpf(delta) : 0.f;
           const int jj = anchor >> 5, hf = (anchor >> 4) & 1, gg = (anchor >> 2) & 3;
           wl[(((dt2 * MP + jj) * 64) + 16 * gg + cc) * 8 + 4 * hf + (anchor & 3)] = (__bf16)wv;
         }
@@ -272,7 +273,8 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
           __bf16* dst = H + base + (size_t)row * D + (D / 4) * g;
 #pragma unroll
           for (int hh = 0; hh < DT / 2; ++hh)
-            *(u32x4*)(dst + 8 * hh) = as_u32x4(pack_bf16(hacc[2 * hh], hacc[2 * hh + 1]));
+            __builtin_nontemporal_store(as_u32x4(pack_bf16(hacc[2 * hh], hacc[2 * hh + 1])),
+                                        (u32x4*)(dst + 8 * hh));
         }
       }
     }
