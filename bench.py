@@ -25,6 +25,30 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA bf16, published
 FP32_PEAK_TFLOPS = 157.3       # fp32 matrix, published
 ROTATE_BYTES = 1 << 30
 
+# HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE (each scaled by the
+# reading of a plain copy kernel of known size; see profiles/).  Valid only while the
+# kernel's sources hash to the recorded fingerprint; otherwise traffic is reported null.
+MEASURED_TRAFFIC = {
+    ("vit_s16_224", "fused"): {"sources": ["efficient_vision_transformer_amd/csrc/fused_bf16.hip",
+                                           "efficient_vision_transformer_amd/csrc/device_common.h"],
+                               "sha": "378766b86428f504", "read_bytes": 19435260,
+                               "write_bytes": 10028916},
+}
+
+
+def measured_traffic(workload: str, plan: str):
+    import hashlib
+    rec = MEASURED_TRAFFIC.get((workload, plan))
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    if h.hexdigest()[:16] != rec["sha"]:
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -35,7 +59,23 @@ def parse():
     ap.add_argument("--plan", default="auto", choices=["auto", "fused", "split"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="instead of the benchmark, run a plain device copy of this many MiB "
+                         "(reference reading for the HBM byte counters)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int, reps: int = 5) -> None:
+    """A plain copy kernel of known size: reads and writes `mib` MiB per launch."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_launch": mib << 20,
+                      "bytes_written_per_launch": mib << 20, "launches": reps}), flush=True)
 
 
 def cpu_baseline(x, seconds: float) -> dict:
@@ -80,6 +120,9 @@ def full_attention_gap(x, H, slices=4) -> dict:
 
 def main():
     args = parse()
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
         sys.exit(2)
@@ -137,7 +180,10 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": round(tflops / peak_tf, 4), "traffic": None}
-    roof["kernel"] = "whole forward (" + plan_desc.split(":")[0] + " plan)"
+    plan_kind = plan_desc.split(":")[0]
+    roof["traffic"] = measured_traffic(name, plan_kind)
+    roof["kernel"] = ("fused_bf16 (the whole forward is this one kernel)" if plan_kind == "fused"
+                      else f"whole forward ({plan_kind} plan: pass1 + finalize + pass2)")
     roof["per_launch"] = {"algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
                           "avg_duration_us": round(ms * 1e3, 3)}
 
