@@ -14,26 +14,28 @@
 // All products run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
 #include "device_common.h"
 #include "kernels.h"
+#include "tile_ops.h"
 
 namespace aa {
 
 // ---------------------------------------------------------------------------------------
 // Pass 1.  Four waves split the anchors (NA groups) and, when there are few anchor tiles,
-// the dims of A^T V (4/NA groups).  Each block of 128 tokens is staged through LDS: every
+// the dims of A^T V (4/NA groups).  Blocks of 128 tokens are staged through LDS: every
 // wave loads one 32-token pair of Q (kept in its MFMA operand layout) and of V (moved to
-// the token-in-register layout by a selection MFMA).  Logits are formed as S = Q U^T
+// the token-in-register layout by a selection MFMA); the next block's rows are already
+// in flight while the current block is computed.  Logits are formed as S = Q U^T
 // (lanes = anchors, registers = tokens), so the softmax over anchors is a 16-lane DPP
-// reduction plus an exchange of per-token maxima and sums between anchor groups, and the
-// normalised A is directly the left operand of A^T V.
-template <int D, int AT, int NA>
-__global__ __launch_bounds__(kPass1Waves * kWave)
+// reduction plus one exchange of per-token maxima and one of sums between the anchor
+// groups for every PX pairs, and the normalised A is directly the left operand of A^T V.
+template <int D, int AT, int NA, int PX>
+__global__ __launch_bounds__(kPass1Waves * kWave, 2)
 void pass1_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                 const __bf16* __restrict__ V, float* __restrict__ part,
                 float* __restrict__ dpart, int h, int n, int m, int chunks, int chunk_len,
                 float c2) {
   constexpr int NW = kPass1Waves, ND = NW / NA, KS = D / 32, DT = D / 16;
   constexpr int J = AT / NA, DTW = DT / ND;
-  static_assert(AT % NA == 0 && DT % ND == 0, "wave split must tile the anchors and dims");
+  static_assert(AT % NA == 0 && DT % ND == 0 && NW % PX == 0, "wave split must tile the work");
   const int slice = blockIdx.x / chunks;
   const int chunk = blockIdx.x - slice * chunks;
   const int head = slice % h;
@@ -46,22 +48,34 @@ void pass1_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 
   __shared__ u32x4 q_lds[NW][2][KS][kWave];
   __shared__ u32x4 v_lds[NW][DT][kWave];
-  __shared__ float st_max[NA][32];
-  __shared__ float st_sum[NA][32];
+  __shared__ float st_max[NA][32 * PX];
+  __shared__ float st_sum[NA][32 * PX];
+
+  // Rows of this wave's pair of the block starting at blk (clamped to the slice; rows
+  // past the chunk get zero softmax weight below).
+  auto load_pair = [&](int blk, u32x4 (*qv)[KS], u32x4 (*vv)[KS]) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const size_t off = base + (size_t)min(blk + 32 * w + 16 * tt + c, n - 1) * D + 8 * KS * g;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        qv[tt][kk] = *(const u32x4*)(Q + off + 8 * kk);   // read again by pass 2
+        vv[tt][kk] = __builtin_nontemporal_load((const u32x4*)(V + off + 8 * kk));
+      }
+    }
+  };
+  u32x4 qv[2][KS], vv[2][KS];
+  load_pair(t_begin, qv, vv);
 
   // This wave's anchors as right operands of S = Q U^T: lane (c,g) holds anchor 16j + c,
-  // dims 8*KS*g + 8*kk + s.  Padded anchors (>= m) are zero and masked below.
+  // dims 8*KS*g + 8*kk + s.  Padded anchors (>= m) are masked below.
   bf16x8 uop[J][KS];
   const __bf16* Uh = U + (size_t)head * m * D;
 #pragma unroll
   for (int jl = 0; jl < J; ++jl) {
-    const int a = 16 * (ag * J + jl) + c;
+    const int a = min(16 * (ag * J + jl) + c, m - 1);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + 8 * KS * g + 8 * kk);
-      uop[jl][kk] = as_bf16x8(v);
-    }
+    for (int kk = 0; kk < KS; ++kk) uop[jl][kk] = as_bf16x8(*(const u32x4*)(Uh + (size_t)a * D + 8 * KS * g + 8 * kk));
   }
   const bf16x8 vsel0 = vsel_operand(0, c, g), vsel1 = vsel_operand(1, c, g);
   const bf16x8 ones = splat_bf16(1.f);
@@ -75,114 +89,103 @@ void pass1_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   }
 
   for (int blk = t_begin; blk < t_end; blk += 32 * NW) {
-    {  // stage pair w of this block
-      const int p0 = blk + 32 * w;
+    {  // stage pair w of this block, then request the next block's rows
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) q_lds[w][tt][kk][lane] = qv[tt][kk];
       f32x4 vt[2][DT];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int row = p0 + 16 * tt + c;
-        const bool ok = row < t_end;
-        const size_t off = base + (size_t)(ok ? row : 0) * D + 8 * KS * g;
-        u32x4 qv[KS], vv[KS];
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          qv[kk] = ok ? *(const u32x4*)(Q + off + 8 * kk) : u32x4{0u, 0u, 0u, 0u};
-          vv[kk] = ok ? *(const u32x4*)(V + off + 8 * kk) : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) q_lds[w][tt][kk][lane] = qv[kk];
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          vt[tt][dt] = mfma_bf16(as_bf16x8(vv[dt >> 1]), (dt & 1) ? vsel1 : vsel0, zero4());
-      }
+          vt[tt][dt] = mfma_bf16(as_bf16x8(vv[tt][dt >> 1]), (dt & 1) ? vsel1 : vsel0, zero4());
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) v_lds[w][dt][lane] = as_u32x4(pack_bf16(vt[0][dt], vt[1][dt]));
+      if (blk + 32 * NW < t_end) load_pair(blk + 32 * NW, qv, vv);
     }
     __syncthreads();
 
-    for (int ps = 0; ps < NW; ++ps) {
-      const int p0 = blk + 32 * ps;
-      if (p0 >= t_end) break;  // uniform over the workgroup
-      // a1: logits in base-2 units later; s[tt][jl] lane (c,g): anchor 16j+c, token 4g+r.
-      f32x4 s[2][J];
+    for (int px = 0; px < NW; px += PX) {
+      if (blk + 32 * px >= t_end) break;  // uniform over the workgroup
+      // a1: s[pp][tt][jl] lane (c,g): anchor 16(ag*J + jl) + c, token 4g + r of tile tt of
+      // pair px + pp.
+      f32x4 s[PX][2][J];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int jl = 0; jl < J; ++jl) {
-          f32x4 acc = zero4();
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk)
-            acc = mfma_bf16(as_bf16x8(q_lds[ps][tt][kk][lane]), uop[jl][kk], acc);
-          if (16 * (ag * J + jl) + c >= m) acc = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-          s[tt][jl] = acc;
-        }
-      // a2: softmax over the anchors of each token.
-      float mx[2][4];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = s[tt][0][r];
-#pragma unroll
-          for (int jl = 1; jl < J; ++jl) v = fmaxf(v, s[tt][jl][r]);
-          mx[tt][r] = row16_max(v);
-        }
-      if (c == 0) {
+      for (int pp = 0; pp < PX; ++pp)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) st_max[ag][16 * tt + 4 * g + r] = mx[tt][r];
-      }
-      __syncthreads();
-      float z[2][4];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tok = 16 * tt + 4 * g + r;
-          float M = st_max[0][tok];
-#pragma unroll
-          for (int a2 = 1; a2 < NA; ++a2) M = fmaxf(M, st_max[a2][tok]);
-          const float mneg = -M * c2;
-          float zz = 0.f;
 #pragma unroll
           for (int jl = 0; jl < J; ++jl) {
-            const float e = exp2_fast(fmaf(s[tt][jl][r], c2, mneg));
-            s[tt][jl][r] = e;
-            zz += e;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk)
+              acc = mfma_bf16(as_bf16x8(q_lds[px + pp][tt][kk][lane]), uop[jl][kk], acc);
+            if (16 * (ag * J + jl) + c >= m) acc = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            s[pp][tt][jl] = acc;
           }
-          z[tt][r] = row16_sum(zz);
-        }
-      if (c == 0) {
+      // a2: per-token maxima and sums over anchors, combined across anchor groups.
+#pragma unroll
+      for (int pp = 0; pp < PX; ++pp)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) st_sum[ag][16 * tt + 4 * g + r] = z[tt][r];
-      }
+          for (int r = 0; r < 4; ++r) {
+            float v = s[pp][tt][0][r];
+#pragma unroll
+            for (int jl = 1; jl < J; ++jl) v = fmaxf(v, s[pp][tt][jl][r]);
+            v = row16_max(v);
+            if (c == 0) st_max[ag][32 * pp + 16 * tt + 4 * g + r] = v;
+          }
       __syncthreads();
-      f32x4 inv[2];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int pp = 0; pp < PX; ++pp)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int tok = 16 * tt + 4 * g + r;
-          float Z = st_sum[0][tok];
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-          for (int a2 = 1; a2 < NA; ++a2) Z += st_sum[a2][tok];
-          inv[tt][r] = (p0 + tok < t_end) ? 1.f / Z : 0.f;
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int tok = 32 * pp + 16 * tt + 4 * g + r;
+            float M = st_max[0][tok];
+#pragma unroll
+            for (int a2 = 1; a2 < NA; ++a2) M = fmaxf(M, st_max[a2][tok]);
+            const float mneg = -M * c2;
+            float zz = 0.f;
+#pragma unroll
+            for (int jl = 0; jl < J; ++jl) {
+              const float e = exp2_fast(fmaf(s[pp][tt][jl][r], c2, mneg));
+              s[pp][tt][jl][r] = e;
+              zz += e;
+            }
+            zz = row16_sum(zz);
+            if (c == 0) st_sum[ag][tok] = zz;
+          }
+      __syncthreads();
       // a3: Delta and A^T V.  The left operand holds anchor c and tokens
       // {4g+s of tile 0, 4g+s-4 of tile 1}; the staged V^T uses the same token order.
 #pragma unroll
-      for (int jl = 0; jl < J; ++jl) {
-        const bf16x8 ax = pack_bf16(s[0][jl] * inv[0], s[1][jl] * inv[1]);
+      for (int pp = 0; pp < PX; ++pp) {
+        f32x4 inv[2];
 #pragma unroll
-        for (int dl = 0; dl < DTW; ++dl)
-          pacc[jl][dl] = mfma_bf16(ax, as_bf16x8(v_lds[ps][dg * DTW + dl][lane]), pacc[jl][dl]);
-        if (dg == 0) dacc[jl] = mfma_bf16(ax, ones, dacc[jl]);
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tok = 32 * pp + 16 * tt + 4 * g + r;
+            float Z = st_sum[0][tok];
+#pragma unroll
+            for (int a2 = 1; a2 < NA; ++a2) Z += st_sum[a2][tok];
+            inv[tt][r] = (blk + 32 * px + tok < t_end) ? 1.f / Z : 0.f;
+          }
+#pragma unroll
+        for (int jl = 0; jl < J; ++jl) {
+          const bf16x8 ax = pack_bf16(s[pp][0][jl] * inv[0], s[pp][1][jl] * inv[1]);
+#pragma unroll
+          for (int dl = 0; dl < DTW; ++dl)
+            pacc[jl][dl] = mfma_bf16(ax, as_bf16x8(v_lds[px + pp][dg * DTW + dl][lane]), pacc[jl][dl]);
+          if (dg == 0) dacc[jl] = mfma_bf16(ax, ones, dacc[jl]);
+        }
       }
+      __syncthreads();   // st_max / st_sum are reused by the next group
     }
-    __syncthreads();
   }
 
   // Partials in accumulator layout: [slice][chunk][jt][dt][r][lane] holds
@@ -206,6 +209,154 @@ void pass1_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 }
 
 // ---------------------------------------------------------------------------------------
+// Pass 1 for up to 128 anchors.  The waves split the chunk's tokens in rounds of one
+// 32-token pair per wave.  Phase A (per wave, its pair): S^T = U Q^T (lanes = tokens), the
+// softmax over all anchors in registers plus two permlane swaps, then A and V moved to
+// the token-in-register layout by selection MFMAs and their operand chunks written to
+// LDS.  Phase B (after one barrier): each wave owns distinct (16-anchor, 16-dim) tiles
+// of A^T V and of Delta and accumulates them over the round's pairs.  Partials leave in
+// the same accumulator layout as the anchor-split pass 1.
+template <int D, int MP, int NW>
+__global__ __launch_bounds__(NW * kWave, 2)
+void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
+                 const __bf16* __restrict__ V, float* __restrict__ part,
+                 float* __restrict__ dpart, int h, int n, int m, int chunks, int chunk_len,
+                 float c2) {
+  constexpr int KS = D / 32, DT = D / 16, AT = 2 * MP;
+  constexpr int TILES = AT * DT, TPW = (TILES + NW - 1) / NW;
+  constexpr int NDA = (TPW + DT - 1) / DT;   // anchor tiles per wave needing a Delta
+  static_assert(TILES % NW == 0, "tiles split evenly over the waves");
+  const int slice = blockIdx.x / chunks;
+  const int chunk = blockIdx.x - slice * chunks;
+  const int head = slice % h;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)slice * (size_t)n * D;
+  const int t_begin = chunk * chunk_len;
+  const int t_end = min(n, t_begin + chunk_len);
+  const int npairs = (t_end - t_begin + 31) >> 5;
+
+  __shared__ u32x4 u_lds[AT][KS][kWave];
+  __shared__ u32x4 ax_lds[AT][NW][kWave];   // A^T left operands, one chunk per pair
+  __shared__ u32x4 vy_lds[DT][NW][kWave];   // V^T right operands, one chunk per pair
+
+  // U first (L2-resident after the first workgroups), then this wave's first pair.
+  constexpr int UCH = AT * KS * kWave;
+  constexpr int UPT = (UCH + NW * kWave - 1) / (NW * kWave);
+  u32x4 ust[UPT];
+  const __bf16* Uh = U + (size_t)head * m * D;
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int idx = threadIdx.x + i * NW * kWave;
+    if (idx < UCH) {
+      const int j = idx / (KS * kWave), kk = (idx / kWave) % KS, l = idx & 63;
+      const int a = min(16 * j + (l & 15), m - 1);   // padded anchors are masked
+      ust[i] = *(const u32x4*)(Uh + (size_t)a * D + 8 * KS * (l >> 4) + 8 * kk);
+    }
+  }
+  u32x4 qc[2][KS], vc[2][KS];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    load_rows<D>(Q, base, t_begin + 32 * w + 16 * tt + c, n, g, qc[tt]);
+    load_rows<D>(V, base, t_begin + 32 * w + 16 * tt + c, n, g, vc[tt]);
+  }
+#pragma unroll
+  for (int i = 0; i < UPT; ++i) {
+    const int idx = threadIdx.x + i * NW * kWave;
+    if (idx < UCH) (&u_lds[0][0][0])[idx] = ust[i];
+  }
+  const bf16x8 asel0 = sel_a(0, c, g), asel1 = sel_a(1, c, g);
+  const bf16x8 vsel0 = sel_v(0, c, g), vsel1 = sel_v(1, c, g);
+  const bf16x8 ones = splat_bf16(1.f);
+  __syncthreads();
+
+  // Wave w owns the contiguous tiles w*TPW .. w*TPW + TPW - 1 (tile t: anchor tile t / DT,
+  // dim tile t % DT); the Delta of anchor tile ja is accumulated with its dim tile 0.
+  f32x4 pacc[TPW], dacc[NDA];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) pacc[k] = zero4();
+#pragma unroll
+  for (int k = 0; k < NDA; ++k) dacc[k] = zero4();
+
+  const int rounds = (npairs + NW - 1) / NW;
+  for (int r = 0; r < rounds; ++r) {
+    const int pairs_here = min(NW, npairs - r * NW);  // uniform over the workgroup
+    const int p = r * NW + w;
+    const bool more = p + NW < npairs;
+    u32x4 qn[2][KS], vn[2][KS];
+    if (more) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        load_rows<D>(Q, base, t_begin + 32 * (p + NW) + 16 * tt + c, n, g, qn[tt]);
+        load_rows<D>(V, base, t_begin + 32 * (p + NW) + 16 * tt + c, n, g, vn[tt]);
+      }
+    }
+    if (p < npairs) {
+      bf16x8 ab[2][MP];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        tile_softmax<D, MP>(u_lds, qc[tt], lane, g, m, t_begin + 32 * p + 16 * tt + c < t_end, c2, ab[tt]);
+      // A^T: lane (c,g) -> anchor 16ja + c, tokens {4g+s of tile 0, 4g+s-4 of tile 1}.
+#pragma unroll
+      for (int ja = 0; ja < AT; ++ja) {
+        const bf16x8 sel = (ja & 1) ? asel1 : asel0;
+        const f32x4 a0 = mfma_bf16(ab[0][ja >> 1], sel, zero4());
+        const f32x4 a1 = mfma_bf16(ab[1][ja >> 1], sel, zero4());
+        ax_lds[ja][w][lane] = as_u32x4(pack_bf16(a0, a1));
+      }
+      // V^T: lane (c,g) -> dim vt_dim(dt, c), same token order.
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 sel = (dt & 1) ? vsel1 : vsel0;
+        const f32x4 v0 = mfma_bf16(as_bf16x8(vc[0][dt >> 1]), sel, zero4());
+        const f32x4 v1 = mfma_bf16(as_bf16x8(vc[1][dt >> 1]), sel, zero4());
+        vy_lds[dt][w][lane] = as_u32x4(pack_bf16(v0, v1));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int t = w * TPW + k;
+      const int ja = t / DT, dt = t - (t / DT) * DT;
+      f32x4 pa = pacc[k], da = dacc[k / DT];
+#pragma unroll
+      for (int ps = 0; ps < NW; ++ps) {
+        if (ps < pairs_here) {
+          const bf16x8 x = as_bf16x8(ax_lds[ja][ps][lane]);
+          pa = mfma_bf16(x, as_bf16x8(vy_lds[dt][ps][lane]), pa);
+          if (dt == 0) da = mfma_bf16(x, ones, da);
+        }
+      }
+      pacc[k] = pa;
+      if (dt == 0) dacc[k / DT] = da;
+    }
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) { qc[tt][kk] = qn[tt][kk]; vc[tt][kk] = vn[tt][kk]; }
+    }
+  }
+
+  // Partials: [slice][chunk][jt][dt][r][lane] holds P[16jt + 4g + r][vt_dim(dt, c)];
+  // Delta as [slice][chunk][anchor] (from the dt == 0 tile of each anchor tile).
+  const size_t sc = (size_t)slice * chunks + chunk;
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int t = w * TPW + k;
+    const int ja = t / DT, dt = t - (t / DT) * DT;
+    float* dst = part + ((sc * AT + ja) * DT + dt) * 256;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[r * 64 + lane] = pacc[k][r];
+    if (dt == 0 && c == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dpart[sc * (16 * AT) + 16 * ja + 4 * g + r] = dacc[k / DT][r];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Finalize: W = Delta^-1 (sum over chunks of P), chunk order fixed.  One workgroup per
 // (slice, 16-anchor tile).  Output layout = the left operand of pass 2's H^T = W^T A^T:
 // [slice][dt2][jj][lane'][slot] with lane' (c',g') holding dim out_dim(dt2, c') and
@@ -214,27 +365,47 @@ template <int D>
 __global__ __launch_bounds__(256)
 void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpart,
                    __bf16* __restrict__ Wop, int chunks, int AT) {
-  constexpr int DT = D / 16;
+  constexpr int DT = D / 16, U = 8;
   const int MP = AT / 2;
   const int slice = blockIdx.x / AT;
   const int jt = blockIdx.x - slice * AT;
-  for (int e = threadIdx.x; e < DT * 256; e += 256) {
-    const int dt = e >> 8, r = (e >> 6) & 3, lane = e & 63;
-    const int c = lane & 15, g = lane >> 4;
-    const int anchor = 16 * jt + 4 * g + r;
-    const int dim = vt_dim<D>(dt, c);
-    float p = 0.f, delta = 0.f;
-    for (int ch = 0; ch < chunks; ++ch) {
+  // Thread t owns accumulator slot (r, lane) of every dim tile: element dt*256 + t.
+  const int r = (threadIdx.x >> 6) & 3, lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int anchor = 16 * jt + 4 * g + r;
+  float p[DT], delta = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) p[dt] = 0.f;
+  for (int ch0 = 0; ch0 < chunks; ch0 += U) {
+    // all loads of U chunks first, then the adds in chunk order
+    float pv[U][DT], dv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ch = min(ch0 + u, chunks - 1);
       const size_t sc = (size_t)slice * chunks + ch;
-      p += part[((sc * AT + jt) * DT + dt) * 256 + r * 64 + lane];
-      delta += dpart[sc * (16 * AT) + anchor];
+      dv[u] = dpart[sc * (16 * AT) + anchor];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) pv[u][dt] = part[((sc * AT + jt) * DT + dt) * 256 + r * 64 + lane];
     }
-    const float wv = (delta > 0.f) ? p / delta : 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ch0 + u < chunks) {
+        delta += dv[u];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) p[dt] += pv[u][dt];
+      }
+    }
+  }
+  const float rinv = (delta > 0.f) ? 1.f / delta : 0.f;
+  const int jj = anchor >> 5, half = (anchor >> 4) & 1, gg = (anchor >> 2) & 3;
+  const int slot = 4 * half + (anchor & 3);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const float wv = (delta > 0.f) ? p[dt] * rinv : 0.f;
+    const int dim = vt_dim<D>(dt, c);
     const int rem = dim % (D / 4);
     const int dt2 = rem >> 2;
     const int cc = 4 * (dim / (D / 4)) + (rem & 3);
-    const int jj = anchor >> 5, half = (anchor >> 4) & 1, gg = (anchor >> 2) & 3;
-    const int slot = 4 * half + (anchor & 3);
     Wop[((((size_t)slice * DT + dt2) * MP + jj) * 64 + 16 * gg + cc) * 8 + slot] = (__bf16)wv;
   }
 }
@@ -245,7 +416,7 @@ void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpa
 // two permlane swaps and the normalised A is directly the right operand of
 // H^T = W^T A^T.  U and W stay in LDS for the whole chunk.
 template <int D, int AT>
-__global__ __launch_bounds__(kPass2Waves * kWave)
+__global__ __launch_bounds__(kPass2Waves * kWave, (AT >= 16) ? 1 : 2)
 void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                 const u32x4* __restrict__ Wop, __bf16* __restrict__ H, int h, int n, int m,
                 int chunks, int chunk_len, float c2) {
@@ -274,13 +445,21 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     (&w_lds[0][0][0])[idx] = Ws[idx];
   __syncthreads();
 
+  // Software pipeline: the next tile's Q rows are requested before this tile is computed.
+  // Rows past the chunk read the slice's last row (clamped) and are not stored.
+  auto load_q = [&](int t0, u32x4* q) {
+    const size_t off = base + (size_t)min(t0 + c, n - 1) * D + 8 * KS * g;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) q[kk] = __builtin_nontemporal_load((const u32x4*)(Q + off + 8 * kk));
+  };
+  u32x4 q[KS];
+  if (t_begin + 16 * w < t_end) load_q(t_begin + 16 * w, q);
   for (int t0 = t_begin + 16 * w; t0 < t_end; t0 += 16 * NW) {
     const int row = t0 + c;
     const bool ok = row < t_end;
-    const size_t off = base + (size_t)(ok ? row : 0) * D + 8 * KS * g;
-    u32x4 q[KS];
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) q[kk] = ok ? *(const u32x4*)(Q + off + 8 * kk) : u32x4{0u, 0u, 0u, 0u};
+    u32x4 qn[KS];
+    const bool more = t0 + 16 * NW < t_end;
+    if (more) load_q(t0 + 16 * NW, qn);
     // a1 (transposed): s[j] lane (c,g): token c, anchors 16j + 4g + r.
     f32x4 s[AT];
 #pragma unroll
@@ -328,7 +507,12 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       __bf16* dst = H + base + (size_t)row * D + (D / 4) * g;
 #pragma unroll
       for (int half = 0; half < DT / 2; ++half)
-        *(u32x4*)(dst + 8 * half) = as_u32x4(pack_bf16(hacc[2 * half], hacc[2 * half + 1]));
+        __builtin_nontemporal_store(as_u32x4(pack_bf16(hacc[2 * half], hacc[2 * half + 1])),
+                                    (u32x4*)(dst + 8 * half));
+    }
+    if (more) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) q[kk] = qn[kk];
     }
   }
 }
@@ -339,14 +523,21 @@ static hipError_t launch_split_bf16_t(const Geometry& geo, const SplitPlan& p, c
                                       const void* U, const void* V, void* H, void* ws,
                                       hipStream_t stream) {
   constexpr int NA = (AT % 4 == 0) ? 4 : 2;
+  constexpr int PX = (AT >= 16) ? 2 : 4;   // pairs per softmax exchange (register budget)
   char* wsb = (char*)ws;
   float* part = (float*)wsb;
   float* dpart = (float*)(wsb + p.part_bytes);
   void* Wop = (void*)(wsb + p.part_bytes + p.dpart_bytes);
   const long long g1 = geo.slices * p.chunks1;
-  pass1_bf16<D, AT, NA><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, stream>>>(
-      (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, part, dpart, geo.h, geo.n, geo.m,
-      p.chunks1, p.chunk_len1, geo.c2);
+  if constexpr (AT <= 8) {
+    pass1x_bf16<D, AT / 2, kPass1Waves><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, stream>>>(
+        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, part, dpart, geo.h, geo.n, geo.m,
+        p.chunks1, p.chunk_len1, geo.c2);
+  } else {
+    pass1_bf16<D, AT, NA, PX><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, stream>>>(
+        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, part, dpart, geo.h, geo.n, geo.m,
+        p.chunks1, p.chunk_len1, geo.c2);
+  }
   finalize_bf16<D><<<dim3((unsigned)(geo.slices * AT)), dim3(256), 0, stream>>>(
       part, dpart, (__bf16*)Wop, p.chunks1, AT);
   const long long g2 = geo.slices * p.chunks2;
