@@ -33,6 +33,8 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                 float c2) {
   constexpr int KS = D / 32, DT = D / 16, AT = 2 * MP;
   constexpr int TILES = AT * DT, TPW = (TILES + NW - 1) / NW;
+  constexpr int NDA = (TPW + DT - 1) / DT;   // anchor tiles per wave that need a Delta
+  static_assert(TILES % NW == 0 || NW % TILES == 0, "tiles split evenly over the waves");
   const int slice = blockIdx.x;
   const int head = slice % h;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -66,9 +68,13 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   const bf16x8 ones = splat_bf16(1.f);
   __syncthreads();
 
-  f32x4 pacc[TPW], dacc[TPW];
+  // Wave w owns the contiguous tiles w*TPW .. w*TPW + TPW - 1 (tile t: anchor tile t / DT,
+  // dim tile t % DT); the Delta of an anchor tile is accumulated with its dim tile 0.
+  f32x4 pacc[TPW], dacc[NDA];
 #pragma unroll
-  for (int k = 0; k < TPW; ++k) { pacc[k] = zero4(); dacc[k] = zero4(); }
+  for (int k = 0; k < TPW; ++k) pacc[k] = zero4();
+#pragma unroll
+  for (int k = 0; k < NDA; ++k) dacc[k] = zero4();
   bf16x8 keep[KEEP_A ? ROUNDS : 1][2][MP];
 
 #pragma unroll (KEEP_A ? ROUNDS : 1)
@@ -110,24 +116,23 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       for (int dt = 0; dt < DT; ++dt) vy_lds[dt][w][lane] = as_u32x4(pack_bf16(vt[0][dt], vt[1][dt]));
     }
     __syncthreads();
-    // Phase B: tiles t = w, w + NW, ...: anchor tile t / DT, dim tile t % DT.
+    // Phase B: this wave's tiles, accumulated over the round's pairs.
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
-      const int t = w + NW * k;
-      if (t < TILES) {
-        const int ja = t / DT, dt = t - (t / DT) * DT;
-        f32x4 pa = pacc[k], da = dacc[k];
+      const int t = w * TPW + k;
+      if (t >= TILES) break;   // uniform per wave
+      const int ja = t / DT, dt = t - (t / DT) * DT;
+      f32x4 pa = pacc[k], da = dacc[k / DT];
 #pragma unroll
-        for (int ps = 0; ps < NW; ++ps) {
-          if (ps < pairs_here) {
-            const bf16x8 x = as_bf16x8(ax_lds[ja][ps][lane]);
-            pa = mfma_bf16(x, as_bf16x8(vy_lds[dt][ps][lane]), pa);
-            da = mfma_bf16(x, ones, da);
-          }
+      for (int ps = 0; ps < NW; ++ps) {
+        if (ps < pairs_here) {
+          const bf16x8 x = as_bf16x8(ax_lds[ja][ps][lane]);
+          pa = mfma_bf16(x, as_bf16x8(vy_lds[dt][ps][lane]), pa);
+          if (dt == 0) da = mfma_bf16(x, ones, da);
         }
-        pacc[k] = pa;
-        dacc[k] = da;
       }
+      pacc[k] = pa;
+      if (dt == 0) dacc[k / DT] = da;
     }
     __syncthreads();
     if (more) {
@@ -140,25 +145,36 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 
   // W = P / Delta for this wave's tiles, stored as bf16 left operands of H^T = W^T A^T:
   // [dt2][jj][lane'][slot] with lane' (c', g') holding dim out_dim(dt2, c') and anchors
-  // {32jj + 4g' + s, 32jj + 16 + 4g' + s - 4}.
+  // {32jj + 4g' + s, 32jj + 16 + 4g' + s - 4}.  The Delta of each anchor tile goes
+  // through LDS from the wave that accumulated it.
+  __shared__ float dl_lds[AT][16];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int t = w * TPW + k;
+    const int ja = t / DT, dt = t - (t / DT) * DT;
+    if (t < TILES && dt == 0 && c == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dl_lds[ja][4 * g + r] = dacc[k / DT][r];
+    }
+  }
+  __syncthreads();
   {
     __bf16* wl = (__bf16*)&w_lds[0][0][0];
 #pragma unroll
     for (int k = 0; k < TPW; ++k) {
-      const int t = w + NW * k;
-      if (t < TILES) {
-        const int ja = t / DT, dt = t - (t / DT) * DT;
-        const int dim = vt_dim<D>(dt, c);
-        const int rem = dim % (D / 4);
-        const int dt2 = rem >> 2, cc = 4 * (dim / (D / 4)) + (rem & 3);
+      const int t = w * TPW + k;
+      if (t >= TILES) break;
+      const int ja = t / DT, dt = t - (t / DT) * DT;
+      const int dim = vt_dim<D>(dt, c);
+      const int rem = dim % (D / 4);
+      const int dt2 = rem >> 2, cc = 4 * (dim / (D / 4)) + (rem & 3);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int anchor = 16 * ja + 4 * g + r;
-          const float delta = dacc[k][r];
-          const float wv = (delta > 0.f) ? pacc[k][r] * __builtin_amdgcn_rcpf(delta) : 0.f;
-          const int jj = anchor >> 5, hf = (anchor >> 4) & 1, gg = (anchor >> 2) & 3;
-          wl[(((dt2 * MP + jj) * 64) + 16 * gg + cc) * 8 + 4 * hf + (anchor & 3)] = (__bf16)wv;
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int anchor = 16 * ja + 4 * g + r;
+        const float delta = dl_lds[ja][4 * g + r];
+        const float wv = (delta > 0.f) ? pacc[k][r] * __builtin_amdgcn_rcpf(delta) : 0.f;
+        const int jj = anchor >> 5, hf = (anchor >> 4) & 1, gg = (anchor >> 2) & 3;
+        wl[(((dt2 * MP + jj) * 64) + 16 * gg + cc) * 8 + 4 * hf + (anchor & 3)] = (__bf16)wv;
       }
     }
   }

@@ -39,9 +39,12 @@ __device__ __forceinline__ void tile_softmax(const u32x4 (*u_lds)[D / 32][kWave]
     f32x4 acc = zero4();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(q[kk]), acc);
+    // padded anchors (>= m) exist only in the last 32 when m is not a multiple of 32
+    if (j >= AT - 2 && m < 32 * MP) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (16 * j + 4 * g + r >= m) acc[r] = -INFINITY;
+      for (int r = 0; r < 4; ++r)
+        if (16 * j + 4 * g + r >= m) acc[r] = -INFINITY;
+    }
     s[j] = acc;
   }
   float mx = s[0][0];
