@@ -202,25 +202,44 @@ template <int D>
 __global__ __launch_bounds__(256)
 void finalize_fp32(const float* __restrict__ part, const float* __restrict__ dpart,
                    float* __restrict__ Wop, int chunks, int AT) {
-  constexpr int DT = D / 16;
+  constexpr int DT = D / 16, U = 8;
   const int slice = blockIdx.x / AT;
   const int jt = blockIdx.x - slice * AT;
-  for (int e = threadIdx.x; e < DT * 256; e += 256) {
-    const int dt = e >> 8, r = (e >> 6) & 3, lane = e & 63;
-    const int c = lane & 15, g = lane >> 4;
-    const int anchor = 16 * jt + 4 * g + r;
-    const int dim = 16 * dt + c;
-    float p = 0.f, delta = 0.f;
-    for (int ch = 0; ch < chunks; ++ch) {
+  // Thread t owns accumulator slot (r, lane) of every dim tile: element dt*256 + t.
+  const int r = (threadIdx.x >> 6) & 3, lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int anchor = 16 * jt + 4 * g + r;
+  float p[DT], delta = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) p[dt] = 0.f;
+  for (int ch0 = 0; ch0 < chunks; ch0 += U) {
+    // all loads of U chunks first, then the adds in chunk order
+    float pv[U][DT], dv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ch = min(ch0 + u, chunks - 1);
       const size_t sc = (size_t)slice * chunks + ch;
-      p += part[((sc * AT + jt) * DT + dt) * 256 + r * 64 + lane];
-      delta += dpart[sc * (16 * AT) + anchor];
+      dv[u] = dpart[sc * (16 * AT) + anchor];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) pv[u][dt] = part[((sc * AT + jt) * DT + dt) * 256 + r * 64 + lane];
     }
-    const float wv = (delta > 0.f) ? p / delta : 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ch0 + u < chunks) {
+        delta += dv[u];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) p[dt] += pv[u][dt];
+      }
+    }
+  }
+  const int j = anchor >> 4, gg = (anchor >> 2) & 3, rr = anchor & 3;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const float wv = (delta > 0.f) ? p[dt] / delta : 0.f;
+    const int dim = 16 * dt + c;
     const int rem = dim % (D / 4);
     const int dt2 = rem >> 2;
     const int cc = 4 * (dim / (D / 4)) + (rem & 3);
-    const int j = anchor >> 4, gg = (anchor >> 2) & 3, rr = anchor & 3;
     Wop[((((size_t)slice * DT + dt2) * AT + j) * 4 + rr) * 64 + 16 * gg + cc] = wv;
   }
 }
@@ -256,16 +275,26 @@ void pass2_fp32(const float* __restrict__ Q, const float* __restrict__ U,
     (&w_lds[0][0][0][0])[idx] = Ws[idx];
   __syncthreads();
 
+  // Software pipeline: the next tile's Q rows are requested before this tile is computed.
+  // Rows past the chunk read the slice's last row (clamped) and are not stored.
+  auto load_q = [&](int t0, f32x4* q) {
+    const size_t off = base + (size_t)min(t0 + c, n - 1) * D + (D / 4) * g;
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) q[kq] = __builtin_nontemporal_load((const f32x4*)(Q + off + 4 * kq));
+  };
+  f32x4 q[KQ];
+  if (t_begin + 16 * w < t_end) load_q(t_begin + 16 * w, q);
   for (int t0 = t_begin + 16 * w; t0 < t_end; t0 += 16 * NW) {
     const int row = t0 + c;
     const bool ok = row < t_end;
-    const size_t off = base + (size_t)(ok ? row : 0) * D + (D / 4) * g;
-    f32x4 q[KQ];
-#pragma unroll
-    for (int kq = 0; kq < KQ; ++kq) q[kq] = ok ? *(const f32x4*)(Q + off + 4 * kq) : zero4();
+    f32x4 qn[KQ];
+    const bool more = t0 + 16 * NW < t_end;
+    if (more) load_q(t0 + 16 * NW, qn);
     f32x4 s[AT];
 #pragma unroll
     for (int j = 0; j < AT; ++j) {
+      // keeps the LDS operand loads of later tiles from being hoisted (register budget)
+      if (j % 4 == 0) asm volatile("" ::: "memory");
       f32x4 acc = zero4();
 #pragma unroll
       for (int kq = 0; kq < KQ; ++kq) {
@@ -300,17 +329,23 @@ void pass2_fp32(const float* __restrict__ Q, const float* __restrict__ U,
 #pragma unroll
     for (int dt2 = 0; dt2 < DT; ++dt2) hacc[dt2] = zero4();
 #pragma unroll
-    for (int j = 0; j < AT; ++j)
+    for (int j = 0; j < AT; ++j) {
+      if (j % 2 == 0) asm volatile("" ::: "memory");
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float a = s[j][r] * inv;
 #pragma unroll
         for (int dt2 = 0; dt2 < DT; ++dt2) hacc[dt2] = mfma_f32(w_lds[dt2][j][r][lane], a, hacc[dt2]);
       }
+    }
     if (ok) {
       float* dst = H + base + (size_t)row * D + (D / 4) * g;
 #pragma unroll
-      for (int dt2 = 0; dt2 < DT; ++dt2) *(f32x4*)(dst + 4 * dt2) = hacc[dt2];
+      for (int dt2 = 0; dt2 < DT; ++dt2) __builtin_nontemporal_store(hacc[dt2], (f32x4*)(dst + 4 * dt2));
+    }
+    if (more) {
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) q[kq] = qn[kq];
     }
   }
 }
