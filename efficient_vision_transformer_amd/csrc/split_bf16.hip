@@ -416,7 +416,7 @@ void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpa
 // two permlane swaps and the normalised A is directly the right operand of
 // H^T = W^T A^T.  U and W stay in LDS for the whole chunk.
 template <int D, int AT>
-__global__ __launch_bounds__(kPass2Waves * kWave, (AT >= 16) ? 1 : 2)
+__global__ __launch_bounds__(kPass2Waves * kWave, 2)
 void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                 const u32x4* __restrict__ Wop, __bf16* __restrict__ H, int h, int n, int m,
                 int chunks, int chunk_len, float c2) {
@@ -464,6 +464,8 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     f32x4 s[AT];
 #pragma unroll
     for (int j = 0; j < AT; ++j) {
+      // keeps the LDS operand loads of later tiles from being hoisted (register budget)
+      if (AT >= 8 && j % 4 == 0) asm volatile("" ::: "memory");
       f32x4 acc = zero4();
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(q[kk]), acc);
@@ -498,6 +500,7 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     f32x4 hacc[DT];
 #pragma unroll
     for (int dt2 = 0; dt2 < DT; ++dt2) {
+      if (AT >= 8) asm volatile("" ::: "memory");
       f32x4 acc = zero4();
 #pragma unroll
       for (int jj = 0; jj < MP; ++jj) acc = mfma_bf16(as_bf16x8(w_lds[dt2][jj][lane]), abf[jj], acc);
