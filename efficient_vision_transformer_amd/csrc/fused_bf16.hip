@@ -8,12 +8,14 @@
 // The slice's tokens are taken in rounds of one 32-token pair per wave.
 //   Phase A (per wave, its pair): S^T = U Q^T on the MFMA (lanes = tokens, registers =
 //     anchors), softmax over anchors in registers plus two permlane swaps, A rounded to
-//     bf16.  Selection MFMAs move A and V into the token-in-register layout; the
-//     resulting operand chunks go to LDS.
+//     bf16.  The pair's rows of A ([token][anchor]) and of V ([token][dim]) go to LDS as
+//     they are.
 //   Phase B (after one barrier): every wave owns distinct (16-anchor, 16-dim) tiles of
-//     A^T V and accumulates them, and the matching column sums Delta (A times ones),
-//     over all pairs of the round from LDS.  No partial sums are ever added across
-//     waves, so the result does not depend on scheduling.
+//     A^T V and accumulates them, and the matching column sums Delta (A^T times ones),
+//     over all pairs of the round.  Both operands need the tokens on the contraction
+//     axis; the transposing LDS read delivers them in that layout straight from the row
+//     copies.  No partial sums are ever added across waves, so the result does not
+//     depend on scheduling.
 // After the last round each wave turns its tiles into W = P / Delta (0 where Delta == 0)
 // and stores them as bf16 MFMA operands in LDS; then every wave writes H^T = W^T A^T for
 // its tokens, with A kept in registers (KEEP_A) or recomputed from Q.
@@ -34,17 +36,19 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   constexpr int KS = D / 32, DT = D / 16, AT = 2 * MP;
   constexpr int TILES = AT * DT, TPW = (TILES + NW - 1) / NW;
   constexpr int NDA = (TPW + DT - 1) / DT;   // anchor tiles per wave that need a Delta
+  constexpr int AS = tr_stride<32 * MP>(), VS = tr_stride<D>();
   static_assert(TILES % NW == 0 || NW % TILES == 0, "tiles split evenly over the waves");
   const int slice = blockIdx.x;
   const int head = slice % h;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int c = lane & 15, g = lane >> 4;
   const size_t base = (size_t)slice * (size_t)n * D;
   const int npairs = (n + 31) >> 5;
 
   __shared__ u32x4 u_lds[AT][KS][kWave];
-  __shared__ u32x4 ax_lds[AT][NW][kWave];   // A^T left operands, one chunk per pair
-  __shared__ u32x4 vy_lds[DT][NW][kWave];   // V^T right operands, one chunk per pair
+  __shared__ __attribute__((aligned(16))) __bf16 a_lds[NW * 32 * AS];   // rows of A, this round
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[NW * 32 * VS];   // rows of V, this round
   __shared__ u32x4 w_lds[DT][MP][kWave];    // W^T left operands
 
   // This wave's first pair goes out to memory before anything else.
@@ -63,9 +67,9 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + 8 * KS * (l >> 4) + 8 * kk);
     u_lds[j][kk][l] = v;
   }
-  const bf16x8 asel0 = sel_a(0, c, g), asel1 = sel_a(1, c, g);
-  const bf16x8 vsel0 = sel_v(0, c, g), vsel1 = sel_v(1, c, g);
   const bf16x8 ones = splat_bf16(1.f);
+  f32x4 mask[2];
+  pad_mask<MP>(g, m, mask);
   __syncthreads();
 
   // Wave w owns the contiguous tiles w*TPW .. w*TPW + TPW - 1 (tile t: anchor tile t / DT,
@@ -91,29 +95,28 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         load_rows<D>(V, base, 32 * (p + NW) + 16 * tt + c, n, g, vn[tt]);
       }
     }
-    // Phase A.
+    // Phase A: rows 32w .. 32w + 31 of the round's LDS blocks hold this wave's pair.
     if (p < npairs) {
-      f32x4 at[2][AT], vt[2][DT];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         bf16x8 ab[MP];
-        tile_softmax<D, MP>(u_lds, qc[tt], lane, g, m, 32 * p + 16 * tt + c < n, c2, ab);
+        tile_softmax<D, MP>(u_lds, qc[tt], lane, mask, 32 * p + 16 * tt + c < n, c2, ab);
         if constexpr (KEEP_A) {
 #pragma unroll
           for (int jj = 0; jj < MP; ++jj) keep[r][tt][jj] = ab[jj];
         }
-        // A^T: lane (c,g) -> anchor 16ja + c, tokens 4g + r' of this tile.
+        // ab[jj] holds anchors 32jj + 4g .. + 3 and 32jj + 16 + 4g .. + 3 of token c.
+        __bf16* arow = a_lds + (32 * w + 16 * tt + c) * AS + 4 * g;
 #pragma unroll
-        for (int ja = 0; ja < AT; ++ja) at[tt][ja] = mfma_bf16(ab[ja >> 1], (ja & 1) ? asel1 : asel0, zero4());
-        // V^T: lane (c,g) -> dim vt_dim(dt, c), tokens 4g + r' of this tile.
+        for (int jj = 0; jj < MP; ++jj) {
+          const u32x4 v = as_u32x4(ab[jj]);
+          *(u32x2*)(arow + 32 * jj) = u32x2{v[0], v[1]};
+          *(u32x2*)(arow + 32 * jj + 16) = u32x2{v[2], v[3]};
+        }
+        __bf16* vrow = v_lds + (32 * w + 16 * tt + c) * VS + 8 * KS * g;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vt[tt][dt] = mfma_bf16(as_bf16x8(vc[tt][dt >> 1]), (dt & 1) ? vsel1 : vsel0, zero4());
+        for (int kk = 0; kk < KS; ++kk) *(u32x4*)(vrow + 8 * kk) = vc[tt][kk];
       }
-      // Token order inside a chunk: {4g + s of tile 0, 4g + s - 4 of tile 1}.
-#pragma unroll
-      for (int ja = 0; ja < AT; ++ja) ax_lds[ja][w][lane] = as_u32x4(pack_bf16(at[0][ja], at[1][ja]));
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) vy_lds[dt][w][lane] = as_u32x4(pack_bf16(vt[0][dt], vt[1][dt]));
     }
     __syncthreads();
     // Phase B: this wave's tiles, accumulated over the round's pairs.
@@ -126,8 +129,9 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 #pragma unroll
       for (int ps = 0; ps < NW; ++ps) {
         if (ps < pairs_here) {
-          const bf16x8 x = as_bf16x8(ax_lds[ja][ps][lane]);
-          pa = mfma_bf16(x, as_bf16x8(vy_lds[dt][ps][lane]), pa);
+          const bf16x8 x = lds_operand_tr(a_lds + 32 * ps * AS, AS, 16 * ja, c, g);
+          const bf16x8 y = lds_operand_tr(v_lds + 32 * ps * VS, VS, 16 * dt, c, g);
+          pa = mfma_bf16(x, y, pa);
           if (dt == 0) da = mfma_bf16(x, ones, da);
         }
       }
@@ -143,6 +147,7 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     }
   }
 
+  // Tile (ja, dt) of P holds P[16ja + 4g + r][16dt + c] in lane (c,g), register r.
   // W = P / Delta for this wave's tiles, stored as bf16 left operands of H^T = W^T A^T:
   // [dt2][jj][lane'][slot] with lane' (c', g') holding dim out_dim(dt2, c') and anchors
   // {32jj + 4g' + s, 32jj + 16 + 4g' + s - 4}.  The Delta of each anchor tile goes
@@ -165,7 +170,7 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       const int t = w * TPW + k;
       if (t >= TILES) break;
       const int ja = t / DT, dt = t - (t / DT) * DT;
-      const int dim = vt_dim<D>(dt, c);
+      const int dim = 16 * dt + c;
       const int rem = dim % (D / 4);
       const int dt2 = rem >> 2, cc = 4 * (dim / (D / 4)) + (rem & 3);
 #pragma unroll
@@ -203,7 +208,7 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 #pragma unroll
           for (int jj = 0; jj < MP; ++jj) ab[jj] = keep[r][tt][jj];
         } else {
-          tile_softmax<D, MP>(u_lds, qr[tt], lane, g, m, row < n, c2, ab);
+          tile_softmax<D, MP>(u_lds, qr[tt], lane, mask, row < n, c2, ab);
         }
         f32x4 hacc[DT];
 #pragma unroll

@@ -268,6 +268,8 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   const bf16x8 asel0 = sel_a(0, c, g), asel1 = sel_a(1, c, g);
   const bf16x8 vsel0 = sel_v(0, c, g), vsel1 = sel_v(1, c, g);
   const bf16x8 ones = splat_bf16(1.f);
+  f32x4 mask[2];
+  pad_mask<MP>(g, m, mask);
   __syncthreads();
 
   // Wave w owns the contiguous tiles w*TPW .. w*TPW + TPW - 1 (tile t: anchor tile t / DT,
@@ -295,7 +297,7 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       bf16x8 ab[2][MP];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
-        tile_softmax<D, MP>(u_lds, qc[tt], lane, g, m, t_begin + 32 * p + 16 * tt + c < t_end, c2, ab[tt]);
+        tile_softmax<D, MP>(u_lds, qc[tt], lane, mask, t_begin + 32 * p + 16 * tt + c < t_end, c2, ab[tt]);
       // A^T: lane (c,g) -> anchor 16ja + c, tokens {4g+s of tile 0, 4g+s-4 of tile 1}.
 #pragma unroll
       for (int ja = 0; ja < AT; ++ja) {

@@ -28,23 +28,29 @@ __device__ __forceinline__ bf16x8 sel_v(int p, int c, int g) {
 
 // Logits and softmax for one 16-token tile, transposed: returns A as the right operand
 // of H^T = W^T A^T, ab[jj] = anchors {32jj + 4g + s, 32jj + 16 + 4g + s - 4} of token c.
+// Padded anchors (>= m) exist only in the last 32.  Their logits start from -inf in the
+// MFMA accumulator (U's padded rows are zero, so they stay -inf) and drop out of the
+// softmax.  mask[h] is the initial accumulator of anchor tile AT - 2 + h.
+template <int MP>
+__device__ __forceinline__ void pad_mask(int g, int m, f32x4* mask) {
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      mask[hh][r] = (32 * MP - 32 + 16 * hh + 4 * g + r < m) ? 0.f : -INFINITY;
+}
+
 template <int D, int MP>
 __device__ __forceinline__ void tile_softmax(const u32x4 (*u_lds)[D / 32][kWave], const u32x4* q,
-                                             int lane, int g, int m, bool token_ok, float c2,
+                                             int lane, const f32x4* mask, bool token_ok, float c2,
                                              bf16x8* ab) {
   constexpr int KS = D / 32, AT = 2 * MP;
   f32x4 s[AT];
 #pragma unroll
   for (int j = 0; j < AT; ++j) {
-    f32x4 acc = zero4();
+    f32x4 acc = (j >= AT - 2) ? mask[j - (AT - 2)] : zero4();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(q[kk]), acc);
-    // padded anchors (>= m) exist only in the last 32 when m is not a multiple of 32
-    if (j >= AT - 2 && m < 32 * MP) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * j + 4 * g + r >= m) acc[r] = -INFINITY;
-    }
     s[j] = acc;
   }
   float mx = s[0][0];
@@ -64,9 +70,39 @@ __device__ __forceinline__ void tile_softmax(const u32x4 (*u_lds)[D / 32][kWave]
       z += e;
     }
   z = xor32_sum(xor16_sum(z));
-  const float inv = token_ok ? 1.f / z : 0.f;
+  const float inv = token_ok ? __builtin_amdgcn_rcpf(z) : 0.f;   // z >= 1 (the maximum adds 1)
 #pragma unroll
   for (int jj = 0; jj < MP; ++jj) ab[jj] = pack_bf16(s[2 * jj] * inv, s[2 * jj + 1] * inv);
+}
+
+// ---- transposing LDS reads (gfx950 ds_read_b64_tr_b16) ----------------------------------
+// Within each 16-lane group every lane reads 8 bytes (4 x 16-bit) at its own address;
+// lane i receives, in slot k, element i % 4 of what lane 4k + i / 4 read.
+typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef short s16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ s16x4 lds_read_tr(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(__attribute__((address_space(3))) char*)(p));
+}
+
+// Row stride (bf16 elements) of a row-major LDS block with rows of L = 32 or 64 values:
+// 16 values of padding put the eight rows that one transposing read serves per pass on
+// distinct banks.
+template <int L>
+constexpr int tr_stride() { return L + 16; }
+
+// MFMA operand whose contraction axis runs over the 32 rows of a row-major bf16 LDS
+// block: lane (c, g) gets column col0 + c of rows 4g + s (slot s < 4) and 16 + 4g + s - 4
+// (s >= 4).  Lane 4k + q of group g points at row 4g + k, columns col0 + 4q .. + 3.
+__device__ __forceinline__ bf16x8 lds_operand_tr(const __bf16* blk, int stride, int col0, int c,
+                                                 int g) {
+  const __bf16* p = blk + (4 * g + (c >> 2)) * stride + col0 + 4 * (c & 3);
+  const s16x4 lo = lds_read_tr(p);
+  const s16x4 hi = lds_read_tr(p + 16 * stride);
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // Loads rows of Q or V in operand layout (lane (c,g): dims 8*KS*g ..), streaming (each
