@@ -107,13 +107,20 @@ def _fused_applies(shape, dtype):
     return dtype == "bf16" and m <= 64 and n <= 1024
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("shape", EDGE, ids=lambda s: "x".join(map(str, s)))
-@pytest.mark.parametrize("plan", ["auto", "split", "fused"])
+# Every (plan, shape, dtype) combination the plan accepts; the fused plan's refusal of
+# the others is checked by test_fused_plan_rejects_what_it_cannot_run.
+EDGE_CASES = [
+    pytest.param(plan, shape, dtype, id=f"{plan}-{'x'.join(map(str, shape))}-{dtype}")
+    for plan in ("auto", "split", "fused")
+    for shape in EDGE
+    for dtype in ("fp32", "bf16")
+    if plan != "fused" or _fused_applies(shape, dtype)
+]
+
+
+@pytest.mark.parametrize("plan,shape,dtype", EDGE_CASES)
 def test_edge_shapes(ctxs, dev, shape, dtype, plan):
     B, h, n, m, d = shape
-    if plan == "fused" and not _fused_applies(shape, dtype):
-        pytest.skip("the fused plan covers bf16, m <= 64, n <= 1024")
     x = random_case(7 + n + m, B, h, n, m, d, dtype=dtype, q_scale=1.5)
     got = _run(ctxs[plan], x, dev)
     ref = oracle.anchor_attn(x.Q, x.U, x.V)
