@@ -100,7 +100,7 @@ enum class Chosen { Fused, Split, Unsupported };
 
 Chosen choose(const anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t dtype,
               FusedPlan* fp) {
-  const bool fused_ok = (dtype == ANCHOR_ATTN_BF16) && aa::fused_supported(g, fp);
+  const bool fused_ok = (dtype == ANCHOR_ATTN_BF16) && aa::fused_supported(g, ctx->num_cus, fp);
   switch (ctx->plan) {
     case ANCHOR_ATTN_PLAN_FUSED: return fused_ok ? Chosen::Fused : Chosen::Unsupported;
     case ANCHOR_ATTN_PLAN_SPLIT: return Chosen::Split;
@@ -206,8 +206,10 @@ anchor_attn_status_t anchor_attn_describe_plan(anchor_attn_ctx* ctx, int B, int 
     if (c == Chosen::Unsupported) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
     if (c == Chosen::Fused) {
       std::snprintf(buf, (size_t)len,
-                    "fused: grid=%lld wg=%d waves pairs_per_wave=%d %s m_pad=%d workspace=0",
-                    (long long)g.slices, fp.waves, fp.pairs_per_wave,
+                    "fused: grid=%lld (%lld whole slices + %lld shared by two) wg=%d waves "
+                    "pairs_per_wave=%d %s m_pad=%d workspace=0",
+                    (long long)(g.slices + fp.shared), (long long)(g.slices - fp.shared),
+                    (long long)fp.shared, fp.waves, fp.pairs_per_wave,
                     fp.keep_a ? "A kept" : "A recomputed", g.m_pad);
     } else {
       const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);

@@ -28,6 +28,7 @@ struct FusedPlan {
   int waves;          // waves per workgroup
   int pairs_per_wave; // 32-token pairs handled by each wave
   bool keep_a;        // A kept in registers (else recomputed from Q for the output)
+  long long shared;   // slices handled by two workgroups (one per half of the output dims)
 };
 
 constexpr int kPass1Waves = 4;    // pass 1 block = 4 pairs = 128 tokens
@@ -41,7 +42,7 @@ hipError_t launch_split_bf16(const Geometry& g, const SplitPlan& p, const void* 
 hipError_t launch_split_fp32(const Geometry& g, const SplitPlan& p, const void* Q,
                              const void* U, const void* V, void* H, void* workspace,
                              hipStream_t stream);
-bool fused_supported(const Geometry& g, FusedPlan* plan);
+bool fused_supported(const Geometry& g, int num_cus, FusedPlan* plan);
 hipError_t launch_fused_bf16(const Geometry& g, const FusedPlan& p, const void* Q,
                              const void* U, const void* V, void* H, hipStream_t stream);
 

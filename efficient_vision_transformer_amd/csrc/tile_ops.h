@@ -118,4 +118,23 @@ __device__ __forceinline__ void load_rows(const __bf16* __restrict__ X, size_t b
   for (int kk = 0; kk < KS; ++kk) out[kk] = __builtin_nontemporal_load((const u32x4*)(X + off + 8 * kk));
 }
 
+// Rows of Q or V, DW dims from d0, with lane (c,g) holding dims d0 + 32kk + 8g .. + 7 in
+// chunk kk: each load instruction reads one contiguous 64-byte run per row (a whole row
+// when d = 32).  Rows past the slice's end read its last row, as in load_rows.
+template <int D, int DW>
+__device__ __forceinline__ void load_rows_c(const __bf16* __restrict__ X, size_t base, int row,
+                                            int n, int g, int d0, u32x4* out) {
+  const size_t off = base + (size_t)min(row, n - 1) * D + d0 + 8 * g;
+#pragma unroll
+  for (int kk = 0; kk < DW / 32; ++kk)
+    out[kk] = __builtin_nontemporal_load((const u32x4*)(X + off + 32 * kk));
+}
+
+// Output dim of accumulator row i (= 4g + r) of output dim tile dt2, chosen so that lane
+// group g owns dims 32h + 8g .. + 7 for h = dt2 / 2: two adjacent tiles pack into one
+// 16-byte store, and each store instruction covers a contiguous 64-byte run per row.
+__host__ __device__ constexpr int out_dim_c(int dt2, int i) {
+  return 32 * (dt2 >> 1) + 8 * (i >> 2) + 4 * (dt2 & 1) + (i & 3);
+}
+
 }  // namespace aa

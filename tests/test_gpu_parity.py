@@ -153,6 +153,31 @@ def test_fused_plan_shapes(ctxs, dev, shape):
     assert err_for("bf16", got, ref) <= 1e-2
 
 
+# Slice counts around the CU count: with d = 64 the fused plan lets two workgroups share
+# up to 2 * CUs - slices slices (one per half of the output dims), pairing workgroup ids in
+# runs of 16 with a neighbour-pair tail.  These counts cover: all slices shared, complete
+# runs plus a tail, a single shared slice, and none shared.
+SHARED_SLICES = [(1, 1), (3, 3), (9, 1), (4, 25), (50, 6), (100, 3), (64, 6), (73, 7),
+                 (128, 4), (130, 4)]
+
+
+@pytest.mark.parametrize("m", [30, 64])
+@pytest.mark.parametrize("bh", SHARED_SLICES, ids=lambda t: f"{t[0]}x{t[1]}")
+def test_fused_shared_slices(ctxs, dev, bh, m):
+    B, h = bh
+    ctx = ctxs["fused"]
+    plan = ctx.describe(B, h, 40, m, 64, "bf16")
+    print(f"  {plan}", flush=True)
+    x = random_case(500 + B * h + m, B, h, 40, m, 64, dtype="bf16", q_scale=1.5)
+    got = _run(ctx, x, dev)
+    ref = oracle.anchor_attn(x.Q, x.U, x.V)
+    assert err_for("bf16", got, ref) <= 1e-2
+    # every slice on its own: a mis-paired half would leave one slice far off
+    for b in range(B):
+        for hh in range(h):
+            assert err_for("bf16", got[b, hh], ref[b, hh]) <= 2e-2, (b, hh)
+
+
 def test_fused_plan_rejects_what_it_cannot_run(ctxs, dev):
     import torch
     Q = torch.zeros((1, 1, 64, 64), device=dev, dtype=torch.float32)
