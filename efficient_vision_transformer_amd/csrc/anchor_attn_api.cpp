@@ -62,7 +62,9 @@ anchor_attn_status_t check_shape(int B, int h, int n, int m, int d, anchor_attn_
   // Index limits: per-slice offsets are 64-bit, but grids and token indices are 32-bit.
   if (slices > (1LL << 24) || (long long)n > (1LL << 28)) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   g->B = B; g->h = h; g->n = n; g->m = m; g->d = d;
-  g->m_pad = (m + 31) / 32 * 32;
+  // anchors padded to a multiple of 32, or of 64 above 128 anchors (the split plan's
+  // anchor-split pass 1 divides the tiles among four waves)
+  g->m_pad = (m <= 128) ? (m + 31) / 32 * 32 : (m + 63) / 64 * 64;
   g->at = g->m_pad / 16;
   g->slices = slices;
   g->c2 = (float)(1.4426950408889634 / std::sqrt((double)d));

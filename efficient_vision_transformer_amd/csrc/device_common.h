@@ -90,6 +90,23 @@ __device__ __forceinline__ float xor32_sum(float v) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- padded anchors ----------------------------------------------------------------------
+// m is rounded up to a multiple of 32 (m <= 128) or 64 (m > 128), so padded anchors (index
+// >= m) occupy at most the last pad_tiles(AT) 16-anchor tiles.
+__host__ __device__ constexpr int pad_tiles(int at) { return at > 8 ? 4 : 2; }
+
+// mask[hh] is the initial logits accumulator of anchor tile AT - NPAD + hh, accumulator rows
+// 4g + r: -inf on padded anchors, 0 elsewhere.  The padded U rows are finite, so those
+// logits stay -inf and drop out of the softmax without any per-element select.
+template <int AT, int NPAD>
+__device__ __forceinline__ void pad_mask_tiles(int g, int m, f32x4* mask) {
+#pragma unroll
+  for (int hh = 0; hh < NPAD; ++hh)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      mask[hh][r] = (16 * (AT - NPAD + hh) + 4 * g + r < m) ? 0.f : -INFINITY;
+}
+
 // ---- bf16 operand selectors -----------------------------------------------------------
 // Multiplying by a 0/1 selection matrix moves data between the lane axis and the
 // register axis exactly (each output is one bf16 input times 1, summed with zeros).

@@ -445,6 +445,9 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   const u32x4* Ws = Wop + (size_t)slice * DT * MP * kWave;
   for (int idx = threadIdx.x; idx < DT * MP * kWave; idx += NW * kWave)
     (&w_lds[0][0][0])[idx] = Ws[idx];
+  constexpr int NPAD = pad_tiles(AT);
+  f32x4 mask[NPAD];
+  pad_mask_tiles<AT, NPAD>(g, m, mask);
   __syncthreads();
 
   // Software pipeline: the next tile's Q rows are requested before this tile is computed.
@@ -468,12 +471,10 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     for (int j = 0; j < AT; ++j) {
       // keeps the LDS operand loads of later tiles from being hoisted (register budget)
       if (AT >= 8 && j % 4 == 0) asm volatile("" ::: "memory");
-      f32x4 acc = zero4();
+      // padded anchors (>= m) lie in the last NPAD tiles and start from -inf
+      f32x4 acc = (j >= AT - NPAD) ? mask[j - (AT - NPAD)] : zero4();
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(q[kk]), acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * j + 4 * g + r >= m) acc[r] = -INFINITY;
       s[j] = acc;
     }
     // a2
@@ -494,7 +495,7 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         z += e;
       }
     z = xor32_sum(xor16_sum(z));
-    const float inv = 1.f / z;
+    const float inv = __builtin_amdgcn_rcpf(z);   // z >= 1 (the maximum adds 1)
     bf16x8 abf[MP];
 #pragma unroll
     for (int jj = 0; jj < MP; ++jj) abf[jj] = pack_bf16(s[2 * jj] * inv, s[2 * jj + 1] * inv);
@@ -528,7 +529,7 @@ static hipError_t launch_split_bf16_t(const Geometry& geo, const SplitPlan& p, c
                                       const void* U, const void* V, void* H, void* ws,
                                       hipStream_t stream) {
   constexpr int NA = (AT % 4 == 0) ? 4 : 2;
-  constexpr int PX = (AT >= 16) ? 2 : 4;   // pairs per softmax exchange (register budget)
+  constexpr int PX = (AT > 8) ? 2 : 4;   // pairs per softmax exchange (register budget)
   char* wsb = (char*)ws;
   float* part = (float*)wsb;
   float* dpart = (float*)(wsb + p.part_bytes);
@@ -560,9 +561,7 @@ static hipError_t dispatch_at(const Geometry& g, const SplitPlan& p, const void*
     case 4: return launch_split_bf16_t<D, 4>(g, p, Q, U, V, H, ws, s);
     case 6: return launch_split_bf16_t<D, 6>(g, p, Q, U, V, H, ws, s);
     case 8: return launch_split_bf16_t<D, 8>(g, p, Q, U, V, H, ws, s);
-    case 10: return launch_split_bf16_t<D, 10>(g, p, Q, U, V, H, ws, s);
     case 12: return launch_split_bf16_t<D, 12>(g, p, Q, U, V, H, ws, s);
-    case 14: return launch_split_bf16_t<D, 14>(g, p, Q, U, V, H, ws, s);
     case 16: return launch_split_bf16_t<D, 16>(g, p, Q, U, V, H, ws, s);
     default: return hipErrorInvalidValue;
   }

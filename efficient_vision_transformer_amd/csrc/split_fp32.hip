@@ -273,6 +273,9 @@ void pass2_fp32(const float* __restrict__ Q, const float* __restrict__ U,
   const float* Ws = Wop + (size_t)slice * DT * AT * 4 * kWave;
   for (int idx = threadIdx.x; idx < DT * AT * 4 * kWave; idx += NW * kWave)
     (&w_lds[0][0][0][0])[idx] = Ws[idx];
+  constexpr int NPAD = pad_tiles(AT);
+  f32x4 mask[NPAD];
+  pad_mask_tiles<AT, NPAD>(g, m, mask);
   __syncthreads();
 
   // Software pipeline: the next tile's Q rows are requested before this tile is computed.
@@ -295,16 +298,14 @@ void pass2_fp32(const float* __restrict__ Q, const float* __restrict__ U,
     for (int j = 0; j < AT; ++j) {
       // keeps the LDS operand loads of later tiles from being hoisted (register budget)
       if (j % 4 == 0) asm volatile("" ::: "memory");
-      f32x4 acc = zero4();
+      // padded anchors (>= m) lie in the last NPAD tiles and start from -inf
+      f32x4 acc = (j >= AT - NPAD) ? mask[j - (AT - NPAD)] : zero4();
 #pragma unroll
       for (int kq = 0; kq < KQ; ++kq) {
         const f32x4 uu = u_lds[j][kq][lane];
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc = mfma_f32(uu[e], q[kq][e], acc);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (16 * j + 4 * g + r >= m) acc[r] = -INFINITY;
       s[j] = acc;
     }
     float mx = s[0][0];
@@ -380,9 +381,7 @@ static hipError_t dispatch_at(const Geometry& g, const SplitPlan& p, const void*
     case 4: return launch_split_fp32_t<D, 4>(g, p, Q, U, V, H, ws, s);
     case 6: return launch_split_fp32_t<D, 6>(g, p, Q, U, V, H, ws, s);
     case 8: return launch_split_fp32_t<D, 8>(g, p, Q, U, V, H, ws, s);
-    case 10: return launch_split_fp32_t<D, 10>(g, p, Q, U, V, H, ws, s);
     case 12: return launch_split_fp32_t<D, 12>(g, p, Q, U, V, H, ws, s);
-    case 14: return launch_split_fp32_t<D, 14>(g, p, Q, U, V, H, ws, s);
     case 16: return launch_split_fp32_t<D, 16>(g, p, Q, U, V, H, ws, s);
     default: return hipErrorInvalidValue;
   }

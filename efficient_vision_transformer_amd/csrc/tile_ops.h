@@ -28,16 +28,12 @@ __device__ __forceinline__ bf16x8 sel_v(int p, int c, int g) {
 
 // Logits and softmax for one 16-token tile, transposed: returns A as the right operand
 // of H^T = W^T A^T, ab[jj] = anchors {32jj + 4g + s, 32jj + 16 + 4g + s - 4} of token c.
-// Padded anchors (>= m) exist only in the last 32.  Their logits start from -inf in the
-// MFMA accumulator (U's padded rows are zero, so they stay -inf) and drop out of the
-// softmax.  mask[h] is the initial accumulator of anchor tile AT - 2 + h.
+// With at most 64 anchors padding lies in the last two tiles: mask[h] is the initial
+// accumulator of anchor tile 2MP - 2 + h.
 template <int MP>
 __device__ __forceinline__ void pad_mask(int g, int m, f32x4* mask) {
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      mask[hh][r] = (32 * MP - 32 + 16 * hh + 4 * g + r < m) ? 0.f : -INFINITY;
+  static_assert(pad_tiles(2 * MP) == 2, "tile_softmax masks the last two tiles");
+  pad_mask_tiles<2 * MP, 2>(g, m, mask);
 }
 
 template <int D, int MP>

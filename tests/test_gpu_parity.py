@@ -99,6 +99,8 @@ EDGE = [
     (1, 1, 1, 1, 32), (1, 1, 15, 7, 64), (1, 1, 17, 30, 32), (1, 7, 196, 33, 64),
     (7, 1, 577, 64, 64), (1, 1, 129, 256, 64), (2, 3, 300, 1, 64), (1, 1, 5, 40, 32),
     (1, 1, 1000, 100, 64), (1, 2, 2051, 128, 32),
+    # m > 128 is padded to a multiple of 64: padding spread over the last four tiles
+    (1, 2, 300, 130, 64), (2, 1, 257, 200, 32), (1, 1, 77, 193, 64),
 ]
 
 
