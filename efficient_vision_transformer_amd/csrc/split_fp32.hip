@@ -246,13 +246,17 @@ void finalize_fp32(const float* __restrict__ part, const float* __restrict__ dpa
 
 // Pass 2 (fp32): transposed logits S^T = U Q^T (lanes = tokens), softmax in registers
 // plus two permlane swaps, then H^T = W^T A^T with A feeding the right operand one
-// anchor per K step.
+// anchor per K step.  U and W in fp32 take AT * D * 128 bytes of LDS; when that leaves
+// room for one workgroup per CU, the workgroup has eight waves (two per SIMD).
 template <int D, int AT>
-__global__ __launch_bounds__(kPass2Waves * kWave)
+constexpr int pass2_fp32_waves() { return AT * D * 128 > 80 * 1024 ? 8 : kPass2Waves; }
+
+template <int D, int AT>
+__global__ __launch_bounds__((pass2_fp32_waves<D, AT>() * kWave))
 void pass2_fp32(const float* __restrict__ Q, const float* __restrict__ U,
                 const float* __restrict__ Wop, float* __restrict__ H, int h, int n, int m,
                 int chunks, int chunk_len, float c2) {
-  constexpr int NW = kPass2Waves, DT = D / 16, KQ = D / 16;
+  constexpr int NW = pass2_fp32_waves<D, AT>(), DT = D / 16, KQ = D / 16;
   const int slice = blockIdx.x / chunks;
   const int chunk = blockIdx.x - slice * chunks;
   const int head = slice % h;
@@ -367,7 +371,7 @@ static hipError_t launch_split_fp32_t(const Geometry& geo, const SplitPlan& p, c
   finalize_fp32<D><<<dim3((unsigned)(geo.slices * AT)), dim3(256), 0, stream>>>(
       part, dpart, Wop, p.chunks1, AT);
   const long long g2 = geo.slices * p.chunks2;
-  pass2_fp32<D, AT><<<dim3((unsigned)g2), dim3(kPass2Waves * kWave), 0, stream>>>(
+  pass2_fp32<D, AT><<<dim3((unsigned)g2), dim3(pass2_fp32_waves<D, AT>() * kWave), 0, stream>>>(
       (const float*)Q, (const float*)U, Wop, (float*)H, geo.h, geo.n, geo.m, p.chunks2,
       p.chunk_len2, geo.c2);
   return hipGetLastError();
