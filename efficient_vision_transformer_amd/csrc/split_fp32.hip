@@ -16,7 +16,7 @@ namespace aa {
 // (one token row per K step, 16 consecutive dims across lanes) is read from a plain
 // row-major LDS copy.
 template <int D, int AT, int NA>
-__global__ __launch_bounds__(kPass1Waves * kWave)
+__global__ __launch_bounds__(kPass1Waves * kWave, 2)
 void pass1_fp32(const float* __restrict__ Q, const float* __restrict__ U,
                 const float* __restrict__ V, float* __restrict__ part,
                 float* __restrict__ dpart, int h, int n, int m, int chunks, int chunk_len,
