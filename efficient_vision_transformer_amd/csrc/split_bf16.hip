@@ -211,11 +211,12 @@ void pass1_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 // ---------------------------------------------------------------------------------------
 // Pass 1 for up to 128 anchors.  The waves split the chunk's tokens in rounds of one
 // 32-token pair per wave.  Phase A (per wave, its pair): S^T = U Q^T (lanes = tokens), the
-// softmax over all anchors in registers plus two permlane swaps, then A and V moved to
-// the token-in-register layout by selection MFMAs and their operand chunks written to
-// LDS.  Phase B (after one barrier): each wave owns distinct (16-anchor, 16-dim) tiles
-// of A^T V and of Delta and accumulates them over the round's pairs.  Partials leave in
-// the same accumulator layout as the anchor-split pass 1.
+// softmax over all anchors in registers plus two permlane swaps; the pair's rows of A
+// ([token][anchor]) and V ([token][dim]) go to LDS as they are.  Phase B (after one
+// barrier): each wave owns distinct (16-anchor, 16-dim) tiles of A^T V and of Delta and
+// accumulates them over the round's pairs, reading both operands (tokens on the
+// contraction axis) from the row copies with the transposing LDS read.  Partials leave in
+// accumulator layout with dim tile dt holding dims 16dt .. 16dt + 15.
 template <int D, int MP, int NW>
 __global__ __launch_bounds__(NW * kWave, 2)
 void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
@@ -229,16 +230,18 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   const int slice = blockIdx.x / chunks;
   const int chunk = blockIdx.x - slice * chunks;
   const int head = slice % h;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int c = lane & 15, g = lane >> 4;
   const size_t base = (size_t)slice * (size_t)n * D;
   const int t_begin = chunk * chunk_len;
   const int t_end = min(n, t_begin + chunk_len);
   const int npairs = (t_end - t_begin + 31) >> 5;
 
+  constexpr int AS = tr_stride<32 * MP>(), VS = tr_stride<D>();
   __shared__ u32x4 u_lds[AT][KS][kWave];
-  __shared__ u32x4 ax_lds[AT][NW][kWave];   // A^T left operands, one chunk per pair
-  __shared__ u32x4 vy_lds[DT][NW][kWave];   // V^T right operands, one chunk per pair
+  __shared__ __attribute__((aligned(16))) __bf16 a_lds[NW * 32 * AS];   // rows of A, this round
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[NW * 32 * VS];   // rows of V, this round
 
   // U first (L2-resident after the first workgroups), then this wave's first pair.
   constexpr int UCH = AT * KS * kWave;
@@ -265,8 +268,6 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     const int idx = threadIdx.x + i * NW * kWave;
     if (idx < UCH) (&u_lds[0][0][0])[idx] = ust[i];
   }
-  const bf16x8 asel0 = sel_a(0, c, g), asel1 = sel_a(1, c, g);
-  const bf16x8 vsel0 = sel_v(0, c, g), vsel1 = sel_v(1, c, g);
   const bf16x8 ones = splat_bf16(1.f);
   f32x4 mask[2];
   pad_mask<MP>(g, m, mask);
@@ -293,45 +294,27 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         load_rows<D>(V, base, t_begin + 32 * (p + NW) + 16 * tt + c, n, g, vn[tt]);
       }
     }
+    // Phase A: rows 32w .. 32w + 31 of the round's LDS blocks hold this wave's pair.
     if (p < npairs) {
-      bf16x8 ab[2][MP];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-        tile_softmax<D, MP>(u_lds, qc[tt], lane, mask, t_begin + 32 * p + 16 * tt + c < t_end, c2, ab[tt]);
-      // A^T: lane (c,g) -> anchor 16ja + c, tokens {4g+s of tile 0, 4g+s-4 of tile 1}.
+      for (int tt = 0; tt < 2; ++tt) {
+        bf16x8 ab[MP];
+        tile_softmax<D, MP>(u_lds, qc[tt], lane, mask, t_begin + 32 * p + 16 * tt + c < t_end, c2, ab);
+        // ab[jj] holds anchors 32jj + 4g .. + 3 and 32jj + 16 + 4g .. + 3 of token c.
+        __bf16* arow = a_lds + (32 * w + 16 * tt + c) * AS + 4 * g;
 #pragma unroll
-      for (int ja = 0; ja < AT; ++ja) {
-        const bf16x8 sel = (ja & 1) ? asel1 : asel0;
-        const f32x4 a0 = mfma_bf16(ab[0][ja >> 1], sel, zero4());
-        const f32x4 a1 = mfma_bf16(ab[1][ja >> 1], sel, zero4());
-        ax_lds[ja][w][lane] = as_u32x4(pack_bf16(a0, a1));
-      }
-      // V^T: lane (c,g) -> dim vt_dim(dt, c), same token order.
+        for (int jj = 0; jj < MP; ++jj) {
+          const u32x4 v = as_u32x4(ab[jj]);
+          *(u32x2*)(arow + 32 * jj) = u32x2{v[0], v[1]};
+          *(u32x2*)(arow + 32 * jj + 16) = u32x2{v[2], v[3]};
+        }
+        __bf16* vrow = v_lds + (32 * w + 16 * tt + c) * VS + 8 * KS * g;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 sel = (dt & 1) ? vsel1 : vsel0;
-        const f32x4 v0 = mfma_bf16(as_bf16x8(vc[0][dt >> 1]), sel, zero4());
-        const f32x4 v1 = mfma_bf16(as_bf16x8(vc[1][dt >> 1]), sel, zero4());
-        vy_lds[dt][w][lane] = as_u32x4(pack_bf16(v0, v1));
+        for (int kk = 0; kk < KS; ++kk) *(u32x4*)(vrow + 8 * kk) = vc[tt][kk];
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-      const int t = w * TPW + k;
-      const int ja = t / DT, dt = t - (t / DT) * DT;
-      f32x4 pa = pacc[k], da = dacc[k / DT];
-#pragma unroll
-      for (int ps = 0; ps < NW; ++ps) {
-        if (ps < pairs_here) {
-          const bf16x8 x = as_bf16x8(ax_lds[ja][ps][lane]);
-          pa = mfma_bf16(x, as_bf16x8(vy_lds[dt][ps][lane]), pa);
-          if (dt == 0) da = mfma_bf16(x, ones, da);
-        }
-      }
-      pacc[k] = pa;
-      if (dt == 0) dacc[k / DT] = da;
-    }
+    accumulate_tiles<TPW, DT, AS, VS>(a_lds, v_lds, w * TPW, pairs_here, c, g, ones, pacc, dacc);
     __syncthreads();
     if (more) {
 #pragma unroll
@@ -341,7 +324,7 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     }
   }
 
-  // Partials: [slice][chunk][jt][dt][r][lane] holds P[16jt + 4g + r][vt_dim(dt, c)];
+  // Partials: [slice][chunk][jt][dt][r][lane] holds P[16jt + 4g + r][16dt + c];
   // Delta as [slice][chunk][anchor] (from the dt == 0 tile of each anchor tile).
   const size_t sc = (size_t)slice * chunks + chunk;
 #pragma unroll
@@ -362,8 +345,10 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 // Finalize: W = Delta^-1 (sum over chunks of P), chunk order fixed.  One workgroup per
 // (slice, 16-anchor tile).  Output layout = the left operand of pass 2's H^T = W^T A^T:
 // [slice][dt2][jj][lane'][slot] with lane' (c',g') holding dim out_dim(dt2, c') and
-// anchors {32jj + 4g' + slot (slot<4), 32jj + 16 + 4g' + slot - 4 (slot>=4)}.
-template <int D>
+// anchors {32jj + 4g' + slot (slot<4), 32jj + 16 + 4g' + slot - 4 (slot>=4)}.  Column c of
+// a partial's dim tile dt is dim 16dt + c (NATURAL, token-split pass 1) or vt_dim(dt, c)
+// (anchor-split pass 1).
+template <int D, bool NATURAL>
 __global__ __launch_bounds__(256)
 void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpart,
                    __bf16* __restrict__ Wop, int chunks, int AT) {
@@ -404,7 +389,7 @@ void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpa
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     const float wv = (delta > 0.f) ? p[dt] * rinv : 0.f;
-    const int dim = vt_dim<D>(dt, c);
+    const int dim = NATURAL ? 16 * dt + c : vt_dim<D>(dt, c);
     const int rem = dim % (D / 4);
     const int dt2 = rem >> 2;
     const int cc = 4 * (dim / (D / 4)) + (rem & 3);
@@ -544,7 +529,7 @@ static hipError_t launch_split_bf16_t(const Geometry& geo, const SplitPlan& p, c
         (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, part, dpart, geo.h, geo.n, geo.m,
         p.chunks1, p.chunk_len1, geo.c2);
   }
-  finalize_bf16<D><<<dim3((unsigned)(geo.slices * AT)), dim3(256), 0, stream>>>(
+  finalize_bf16<D, (AT <= 8)><<<dim3((unsigned)(geo.slices * AT)), dim3(256), 0, stream>>>(
       part, dpart, (__bf16*)Wop, p.chunks1, AT);
   const long long g2 = geo.slices * p.chunks2;
   pass2_bf16<D, AT><<<dim3((unsigned)g2), dim3(kPass2Waves * kWave), 0, stream>>>(

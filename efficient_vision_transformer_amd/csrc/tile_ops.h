@@ -101,6 +101,51 @@ __device__ __forceinline__ bf16x8 lds_operand_tr(const __bf16* blk, int stride, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Phase B of a wave that owns the TPW contiguous tiles t0 .. t0 + TPW - 1 (t0 a multiple
+// of TPW) of an (anchor tile, dim tile) grid with DT dim tiles per anchor tile (tile t:
+// anchor tile t / DT, dim tile t % DT): accumulates P += A^T V for each tile (pacc[k])
+// and, for a tile in dim tile 0, Delta += A^T 1 of its anchor tile (dacc[k / DT]), over
+// `pairs` 32-row blocks of the row-major LDS copies of A (stride AS) and V (stride VS).
+// When TPW is a multiple or a divisor of DT each distinct operand is read once per block;
+// otherwise every tile reads its own two operands.
+template <int TPW, int DT, int AS, int VS>
+__device__ __forceinline__ void accumulate_tiles(const __bf16* a_lds, const __bf16* v_lds, int t0,
+                                                 int pairs, int c, int g, bf16x8 ones,
+                                                 f32x4* pacc, f32x4* dacc) {
+  if constexpr (TPW % DT == 0 || DT % TPW == 0) {
+    constexpr bool BYROW = TPW % DT == 0;          // whole anchor tiles per wave
+    constexpr int NJ = BYROW ? TPW / DT : 1;       // anchor tiles of the wave
+    constexpr int NY = BYROW ? DT : TPW;           // dim tiles of the wave
+    const int ja0 = t0 / DT, dt0 = t0 - ja0 * DT;  // dt0 == 0 when BYROW
+    for (int ps = 0; ps < pairs; ++ps) {
+      bf16x8 xs[NJ], ys[NY];
+#pragma unroll
+      for (int jl = 0; jl < NJ; ++jl)
+        xs[jl] = lds_operand_tr(a_lds + 32 * ps * AS, AS, 16 * (ja0 + jl), c, g);
+#pragma unroll
+      for (int iy = 0; iy < NY; ++iy)
+        ys[iy] = lds_operand_tr(v_lds + 32 * ps * VS, VS, 16 * (dt0 + iy), c, g);
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        const int jl = BYROW ? k / DT : 0, iy = BYROW ? k % DT : k;
+        pacc[k] = mfma_bf16(xs[jl], ys[iy], pacc[k]);
+        if (dt0 + iy == 0) dacc[k / DT] = mfma_bf16(xs[jl], ones, dacc[k / DT]);
+      }
+    }
+  } else {
+    for (int ps = 0; ps < pairs; ++ps) {
+#pragma unroll
+      for (int k = 0; k < TPW; ++k) {
+        const int t = t0 + k, ja = t / DT, dt = t - ja * DT;
+        const bf16x8 x = lds_operand_tr(a_lds + 32 * ps * AS, AS, 16 * ja, c, g);
+        const bf16x8 y = lds_operand_tr(v_lds + 32 * ps * VS, VS, 16 * dt, c, g);
+        pacc[k] = mfma_bf16(x, y, pacc[k]);
+        if (dt == 0) dacc[k / DT] = mfma_bf16(x, ones, dacc[k / DT]);
+      }
+    }
+  }
+}
+
 // Loads rows of Q or V in operand layout (lane (c,g): dims 8*KS*g ..), streaming (each
 // byte is read once, so the loads are marked non-temporal).  Rows past the
 // slice's end read its last row instead; their softmax weights are zeroed, so they add

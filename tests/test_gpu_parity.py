@@ -101,6 +101,8 @@ EDGE = [
     (1, 1, 1000, 100, 64), (1, 2, 2051, 128, 32),
     # m > 128 is padded to a multiple of 64: padding spread over the last four tiles
     (1, 2, 300, 130, 64), (2, 1, 257, 200, 32), (1, 1, 77, 193, 64),
+    # six anchor tiles: the token-split pass 1 takes its generic per-tile operand reads
+    (1, 2, 200, 80, 64), (1, 1, 150, 70, 32),
 ]
 
 
