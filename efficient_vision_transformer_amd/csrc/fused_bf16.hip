@@ -132,25 +132,10 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
       }
     }
     __syncthreads();
-    // Phase B: this wave's tiles, accumulated over the round's pairs.
-#pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-      const int t = w * TPW + k;
-      if (t >= TILES) break;   // uniform per wave
-      const int ja = t / DTW, dt = t - (t / DTW) * DTW;
-      f32x4 pa = pacc[k], da = dacc[k / DTW];
-#pragma unroll
-      for (int ps = 0; ps < NW; ++ps) {
-        if (ps < pairs_here) {
-          const bf16x8 x = lds_operand_tr(L.a + 32 * ps * AS, AS, 16 * ja, c, g);
-          const bf16x8 y = lds_operand_tr(L.v + 32 * ps * VS, VS, 16 * dt, c, g);
-          pa = mfma_bf16(x, y, pa);
-          if (dt == 0) da = mfma_bf16(x, ones, da);
-        }
-      }
-      pacc[k] = pa;
-      if (dt == 0) dacc[k / DTW] = da;
-    }
+    // Phase B: this wave's tiles (all TPW of them, or none when there are fewer tiles
+    // than waves), accumulated over the round's pairs.
+    if (w * TPW < TILES)
+      accumulate_tiles<TPW, DTW, AS, VS>(L.a, L.v, w * TPW, pairs_here, c, g, ones, pacc, dacc);
     __syncthreads();
     if (more) {
 #pragma unroll
