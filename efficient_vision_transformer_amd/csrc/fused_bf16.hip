@@ -83,6 +83,16 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
   f32x4 mask[2];
   pad_mask<MP>(g, m, mask);
   __syncthreads();
+  // With several rounds U's operands stay in registers instead of being read from LDS
+  // every round.
+  constexpr bool UREG = KEEP_A && ROUNDS > 2;
+  bf16x8 ureg[UREG ? AT : 1][KS];
+  if constexpr (UREG) {
+#pragma unroll
+    for (int j = 0; j < AT; ++j)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) ureg[j][kk] = as_bf16x8(L.u[j][kk][lane]);
+  }
 
   // Wave w owns the contiguous tiles w*TPW .. w*TPW + TPW - 1 (tile t: anchor tile t / DTW,
   // dim tile t % DTW of this part); the Delta of an anchor tile is accumulated with its
@@ -113,7 +123,11 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         bf16x8 ab[MP];
-        tile_softmax<D, MP>(L.u, qc[tt], lane, mask, 32 * p + 16 * tt + c < n, c2, ab);
+        if constexpr (UREG)
+          tile_softmax_op<D, MP>([&](int j, int kk) { return ureg[j][kk]; }, qc[tt], mask,
+                                 32 * p + 16 * tt + c < n, c2, ab);
+        else
+          tile_softmax<D, MP>(L.u, qc[tt], lane, mask, 32 * p + 16 * tt + c < n, c2, ab);
         if constexpr (KEEP_A) {
 #pragma unroll
           for (int jj = 0; jj < MP; ++jj) keep[r][tt][jj] = ab[jj];

@@ -36,17 +36,18 @@ __device__ __forceinline__ void pad_mask(int g, int m, f32x4* mask) {
   pad_mask_tiles<2 * MP, 2>(g, m, mask);
 }
 
-template <int D, int MP>
-__device__ __forceinline__ void tile_softmax(const u32x4 (*u_lds)[D / 32][kWave], const u32x4* q,
-                                             int lane, const f32x4* mask, bool token_ok, float c2,
-                                             bf16x8* ab) {
+// UOP: U's left operands, uop(j, kk) for anchor tile j and dim chunk kk (from LDS or
+// registers).
+template <int D, int MP, typename UOP>
+__device__ __forceinline__ void tile_softmax_op(UOP uop, const u32x4* q, const f32x4* mask,
+                                                bool token_ok, float c2, bf16x8* ab) {
   constexpr int KS = D / 32, AT = 2 * MP;
   f32x4 s[AT];
 #pragma unroll
   for (int j = 0; j < AT; ++j) {
     f32x4 acc = (j >= AT - 2) ? mask[j - (AT - 2)] : zero4();
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(q[kk]), acc);
+    for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(uop(j, kk), as_bf16x8(q[kk]), acc);
     s[j] = acc;
   }
   float mx = s[0][0];
@@ -69,6 +70,14 @@ __device__ __forceinline__ void tile_softmax(const u32x4 (*u_lds)[D / 32][kWave]
   const float inv = token_ok ? __builtin_amdgcn_rcpf(z) : 0.f;   // z >= 1 (the maximum adds 1)
 #pragma unroll
   for (int jj = 0; jj < MP; ++jj) ab[jj] = pack_bf16(s[2 * jj] * inv, s[2 * jj + 1] * inv);
+}
+
+template <int D, int MP>
+__device__ __forceinline__ void tile_softmax(const u32x4 (*u_lds)[D / 32][kWave], const u32x4* q,
+                                             int lane, const f32x4* mask, bool token_ok, float c2,
+                                             bf16x8* ab) {
+  tile_softmax_op<D, MP>([&](int j, int kk) { return as_bf16x8(u_lds[j][kk][lane]); }, q, mask,
+                         token_ok, c2, ab);
 }
 
 // ---- transposing LDS reads (gfx950 ds_read_b64_tr_b16) ----------------------------------
