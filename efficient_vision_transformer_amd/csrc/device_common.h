@@ -127,22 +127,6 @@ __device__ __forceinline__ int vt_dim(int dt, int c) {
   constexpr int KS = D / 32;
   return 8 * KS * (2 * (dt & 1) + (c >> 3)) + 8 * (dt >> 1) + (c & 7);
 }
-__host__ __device__ constexpr int vt_dim_h(int D, int dt, int c) {
-  return 8 * (D / 32) * (2 * (dt & 1) + (c >> 3)) + 8 * (dt >> 1) + (c & 7);
-}
-
-// A transpose.  Input X: lane (c,g) holds token c, anchors {32jj + 4g + s (s<4),
-// 32jj + 16 + 4g + s - 4 (s>=4)}.  Output anchor tile half (0: anchors 32jj..+15,
-// 1: 32jj+16..+31): Y[K = 8g+s][N = c] = 1 iff that input anchor is column c.
-__device__ __forceinline__ bf16x8 asel_operand(int half, int c, int g) {
-  bf16x8 r;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const bool hit = (half == 0) ? (s < 4 && c == 4 * g + s) : (s >= 4 && c == 4 * g + s - 4);
-    r[s] = (__bf16)(hit ? 1.f : 0.f);
-  }
-  return r;
-}
 
 // Output dim of accumulator row i (= 4g + r) of a5 dim tile dt2: lane group g owns the
 // contiguous dims 4*DT*g .. 4*DT*g + 4*DT - 1, so each lane stores one run per token.

@@ -1,33 +1,11 @@
-// tile_ops.h -- bf16 tile building blocks shared by the fused kernel and the split pass 1:
-// selection operands, the transposed-logits softmax of one 16-token tile, and streaming
-// row loads in MFMA operand layout.
+// tile_ops.h -- bf16 tile building blocks shared by the fused kernel and the split passes:
+// the transposed-logits softmax of one 16-token tile, transposing LDS reads and the
+// phase-B tile accumulation built on them, and streaming row loads in MFMA operand layout.
 #pragma once
 #include "device_common.h"
 
 namespace aa {
 
-// bf16 0/1 selection operands (8 slots, two per dword; bf16 1.0 = 0x3F80), built in
-// registers.  A transpose, output anchor half `half`: slot s is 1 iff it holds anchor c,
-// i.e. s - 4*half == c - 4g.  V transpose, output dim group p: slot c&7 is 1 iff
-// g == 2p + (c >> 3).  (Same matrices as asel_operand / vsel_operand.)
-__device__ __forceinline__ bf16x8 sel_slot(bool hit, int slot) {
-  const unsigned val = (slot & 1) ? 0x3F800000u : 0x00003F80u;
-  const int dw = slot >> 1;
-  u32x4 r;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) r[k] = (hit && dw == k) ? val : 0u;
-  return as_bf16x8(r);
-}
-__device__ __forceinline__ bf16x8 sel_a(int half, int c, int g) {
-  const int idx = c - 4 * g;
-  return sel_slot((unsigned)idx < 4u, 4 * half + (idx & 3));
-}
-__device__ __forceinline__ bf16x8 sel_v(int p, int c, int g) {
-  return sel_slot(g == 2 * p + (c >> 3), c & 7);
-}
-
-// Logits and softmax for one 16-token tile, transposed: returns A as the right operand
-// of H^T = W^T A^T, ab[jj] = anchors {32jj + 4g + s, 32jj + 16 + 4g + s - 4} of token c.
 // With at most 64 anchors padding lies in the last two tiles: mask[h] is the initial
 // accumulator of anchor tile 2MP - 2 + h.
 template <int MP>
