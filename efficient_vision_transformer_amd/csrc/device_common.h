@@ -41,6 +41,13 @@ __device__ __forceinline__ bf16x8 pack_bf16(f32x4 lo, f32x4 hi) {
   return r;
 }
 
+// Round-to-nearest-even conversion of one accumulator into four packed bf16.
+__device__ __forceinline__ u32x2 pack4_bf16(f32x4 a) {
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+  const bf16x4 r = {(__bf16)a[0], (__bf16)a[1], (__bf16)a[2], (__bf16)a[3]};
+  return __builtin_bit_cast(u32x2, r);
+}
+
 __device__ __forceinline__ bf16x8 splat_bf16(float v) {
   const __bf16 b = (__bf16)v;
   return bf16x8{b, b, b, b, b, b, b, b};
@@ -105,27 +112,6 @@ __device__ __forceinline__ void pad_mask_tiles(int g, int m, f32x4* mask) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       mask[hh][r] = (16 * (AT - NPAD + hh) + 4 * g + r < m) ? 0.f : -INFINITY;
-}
-
-// ---- bf16 operand selectors -----------------------------------------------------------
-// Multiplying by a 0/1 selection matrix moves data between the lane axis and the
-// register axis exactly (each output is one bf16 input times 1, summed with zeros).
-//
-// V tile transpose.  Input X: lane (c,g) holds token c, dims 8*KS*g + 8*kk + s.  Output
-// column c of dim tile dt = 2*kk + p holds dim 8*KS*(2p + (c>>3)) + 8*kk + (c&7):
-// Y[K = 8g+s][N = c] = 1 iff g == 2p + (c>>3) and s == (c&7).
-__device__ __forceinline__ bf16x8 vsel_operand(int p, int c, int g) {
-  bf16x8 r;
-  const bool grp = (g == 2 * p + (c >> 3));
-#pragma unroll
-  for (int s = 0; s < 8; ++s) r[s] = (__bf16)((grp && s == (c & 7)) ? 1.f : 0.f);
-  return r;
-}
-// Dim of column c of V-transpose dim tile dt (matches vsel_operand).
-template <int D>
-__device__ __forceinline__ int vt_dim(int dt, int c) {
-  constexpr int KS = D / 32;
-  return 8 * KS * (2 * (dt & 1) + (c >> 3)) + 8 * (dt >> 1) + (c & 7);
 }
 
 // Output dim of accumulator row i (= 4g + r) of a5 dim tile dt2: lane group g owns the

@@ -19,189 +19,178 @@
 namespace aa {
 
 // ---------------------------------------------------------------------------------------
-// Pass 1.  Four waves split the anchors (NA groups) and, when there are few anchor tiles,
-// the dims of A^T V (4/NA groups).  Blocks of 128 tokens are staged through LDS: every
-// wave loads one 32-token pair of Q (kept in its MFMA operand layout) and of V (moved to
-// the token-in-register layout by a selection MFMA); the next block's rows are already
-// in flight while the current block is computed.  Logits are formed as S = Q U^T
-// (lanes = anchors, registers = tokens), so the softmax over anchors is a 16-lane DPP
-// reduction plus one exchange of per-token maxima and one of sums between the anchor
-// groups for every PX pairs, and the normalised A is directly the left operand of A^T V.
-template <int D, int AT, int NA, int PX>
-__global__ __launch_bounds__(kPass1Waves * kWave, 2)
-void pass1_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
-                const __bf16* __restrict__ V, float* __restrict__ part,
-                float* __restrict__ dpart, int h, int n, int m, int chunks, int chunk_len,
-                float c2) {
-  constexpr int NW = kPass1Waves, ND = NW / NA, KS = D / 32, DT = D / 16;
-  constexpr int J = AT / NA, DTW = DT / ND;
-  static_assert(AT % NA == 0 && DT % ND == 0 && NW % PX == 0, "wave split must tile the work");
+// Pass 1 for more than 128 anchors (AT = 12 or 16 tiles).  The four waves split the
+// anchors into groups of J = AT / 4 tiles.  Blocks of 128 tokens are staged through LDS:
+// every wave loads one 32-token pair of Q (kept in its MFMA operand layout) and of V (kept
+// as rows); the next block's rows are in flight while the current block is computed.
+// For each pair, every wave forms S^T = U_group Q^T (lanes = tokens, registers = its
+// anchors), reduces the maximum and then the sum over its anchors in registers plus two
+// permlane swaps, and the four groups' partial maxima and sums of every token are
+// combined through LDS.  The wave writes the pair's rows of A for its anchors to its own
+// LDS block and accumulates its (16-anchor, 16-dim) tiles of A^T V and Delta, reading
+// both operands (tokens on the contraction axis) with the transposing LDS read.
+// Partials leave in accumulator layout with dim tile dt holding dims 16dt .. 16dt + 15.
+template <int D, int AT>
+__global__ __launch_bounds__(4 * kWave, 2)
+void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
+                 const __bf16* __restrict__ V, float* __restrict__ part,
+                 float* __restrict__ dpart, int h, int n, int m, int chunks, int chunk_len,
+                 float c2) {
+  constexpr int NW = 4, J = AT / NW, KS = D / 32, DT = D / 16;
+  constexpr int AS = 80;                     // A row stride (16J + padding, bank-spread)
+  constexpr int VS = tr_stride<D>();
+  static_assert(AT % NW == 0 && J >= 2 && J <= 4, "four anchor groups of 2 to 4 tiles");
   const int slice = blockIdx.x / chunks;
   const int chunk = blockIdx.x - slice * chunks;
   const int head = slice % h;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // anchor group
   const int c = lane & 15, g = lane >> 4;
-  const int ag = w % NA, dg = w / NA;
   const size_t base = (size_t)slice * (size_t)n * D;
   const int t_begin = chunk * chunk_len;
   const int t_end = min(n, t_begin + chunk_len);
 
   __shared__ u32x4 q_lds[NW][2][KS][kWave];
-  __shared__ u32x4 v_lds[NW][DT][kWave];
-  __shared__ float st_max[NA][32 * PX];
-  __shared__ float st_sum[NA][32 * PX];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[NW * 32 * VS];   // V rows, this block
+  __shared__ __attribute__((aligned(16))) __bf16 a_lds[NW][32 * AS];    // A rows, per wave
+  __shared__ __attribute__((aligned(16))) float st_max[128][NW];        // per token, per group
+  __shared__ __attribute__((aligned(16))) float st_sum[128][NW];
 
-  // Rows of this wave's pair of the block starting at blk (clamped to the slice; rows
-  // past the chunk get zero softmax weight below).
   auto load_pair = [&](int blk, u32x4 (*qv)[KS], u32x4 (*vv)[KS]) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const size_t off = base + (size_t)min(blk + 32 * w + 16 * tt + c, n - 1) * D + 8 * KS * g;
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        qv[tt][kk] = *(const u32x4*)(Q + off + 8 * kk);   // read again by pass 2
-        vv[tt][kk] = __builtin_nontemporal_load((const u32x4*)(V + off + 8 * kk));
-      }
+      load_rows<D>(Q, base, blk + 32 * w + 16 * tt + c, n, g, qv[tt]);
+      load_rows<D>(V, base, blk + 32 * w + 16 * tt + c, n, g, vv[tt]);
     }
   };
   u32x4 qv[2][KS], vv[2][KS];
   load_pair(t_begin, qv, vv);
 
-  // This wave's anchors as right operands of S = Q U^T: lane (c,g) holds anchor 16j + c,
-  // dims 8*KS*g + 8*kk + s.  Padded anchors (>= m) are masked below.
+  // This group's anchors as left operands of S^T = U Q^T: lane (c,g) of tile jl holds
+  // anchor 16(wJ + jl) + c (zero rows past m).  mask[jl]: initial accumulators, -inf on
+  // padded anchors.
   bf16x8 uop[J][KS];
+  f32x4 mask[J];
   const __bf16* Uh = U + (size_t)head * m * D;
 #pragma unroll
   for (int jl = 0; jl < J; ++jl) {
-    const int a = min(16 * (ag * J + jl) + c, m - 1);
+    const int a = 16 * (w * J + jl) + c;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) uop[jl][kk] = as_bf16x8(*(const u32x4*)(Uh + (size_t)a * D + 8 * KS * g + 8 * kk));
+    for (int kk = 0; kk < KS; ++kk) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + 8 * KS * g + 8 * kk);
+      uop[jl][kk] = as_bf16x8(v);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mask[jl][r] = (16 * (w * J + jl) + 4 * g + r < m) ? 0.f : -INFINITY;
   }
-  const bf16x8 vsel0 = vsel_operand(0, c, g), vsel1 = vsel_operand(1, c, g);
   const bf16x8 ones = splat_bf16(1.f);
-  f32x4 pacc[J][DTW];
-  f32x4 dacc[J];
+  f32x4 pacc[J][DT], dacc[J];
 #pragma unroll
   for (int jl = 0; jl < J; ++jl) {
     dacc[jl] = zero4();
 #pragma unroll
-    for (int dl = 0; dl < DTW; ++dl) pacc[jl][dl] = zero4();
+    for (int dt = 0; dt < DT; ++dt) pacc[jl][dt] = zero4();
   }
 
   for (int blk = t_begin; blk < t_end; blk += 32 * NW) {
     {  // stage pair w of this block, then request the next block's rows
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) q_lds[w][tt][kk][lane] = qv[tt][kk];
-      f32x4 vt[2][DT];
+        __bf16* vrow = v_lds + (32 * w + 16 * tt + c) * VS + 8 * KS * g;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          vt[tt][dt] = mfma_bf16(as_bf16x8(vv[tt][dt >> 1]), (dt & 1) ? vsel1 : vsel0, zero4());
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) v_lds[w][dt][lane] = as_u32x4(pack_bf16(vt[0][dt], vt[1][dt]));
+        for (int kk = 0; kk < KS; ++kk) *(u32x4*)(vrow + 8 * kk) = vv[tt][kk];
+      }
       if (blk + 32 * NW < t_end) load_pair(blk + 32 * NW, qv, vv);
     }
     __syncthreads();
 
-    for (int px = 0; px < NW; px += PX) {
-      if (blk + 32 * px >= t_end) break;  // uniform over the workgroup
-      // a1: s[pp][tt][jl] lane (c,g): anchor 16(ag*J + jl) + c, token 4g + r of tile tt of
-      // pair px + pp.
-      f32x4 s[PX][2][J];
+    for (int ps = 0; ps < NW; ++ps) {
+      if (blk + 32 * ps >= t_end) break;  // uniform over the workgroup
+      // a1: s[tt][jl] lane (c,g): token c of tile tt, anchors 16(wJ + jl) + 4g + r.
+      f32x4 s[2][J];
 #pragma unroll
-      for (int pp = 0; pp < PX; ++pp)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int jl = 0; jl < J; ++jl) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk)
-              acc = mfma_bf16(as_bf16x8(q_lds[px + pp][tt][kk][lane]), uop[jl][kk], acc);
-            if (16 * (ag * J + jl) + c >= m) acc = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            s[pp][tt][jl] = acc;
-          }
-      // a2: per-token maxima and sums over anchors, combined across anchor groups.
-#pragma unroll
-      for (int pp = 0; pp < PX; ++pp)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float v = s[pp][tt][0][r];
-#pragma unroll
-            for (int jl = 1; jl < J; ++jl) v = fmaxf(v, s[pp][tt][jl][r]);
-            v = row16_max(v);
-            if (c == 0) st_max[ag][32 * pp + 16 * tt + 4 * g + r] = v;
-          }
-      __syncthreads();
-#pragma unroll
-      for (int pp = 0; pp < PX; ++pp)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int tok = 32 * pp + 16 * tt + 4 * g + r;
-            float M = st_max[0][tok];
-#pragma unroll
-            for (int a2 = 1; a2 < NA; ++a2) M = fmaxf(M, st_max[a2][tok]);
-            const float mneg = -M * c2;
-            float zz = 0.f;
-#pragma unroll
-            for (int jl = 0; jl < J; ++jl) {
-              const float e = exp2_fast(fmaf(s[pp][tt][jl][r], c2, mneg));
-              s[pp][tt][jl][r] = e;
-              zz += e;
-            }
-            zz = row16_sum(zz);
-            if (c == 0) st_sum[ag][tok] = zz;
-          }
-      __syncthreads();
-      // a3: Delta and A^T V.  The left operand holds anchor c and tokens
-      // {4g+s of tile 0, 4g+s-4 of tile 1}; the staged V^T uses the same token order.
-#pragma unroll
-      for (int pp = 0; pp < PX; ++pp) {
-        f32x4 inv[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int tok = 32 * pp + 16 * tt + 4 * g + r;
-            float Z = st_sum[0][tok];
-#pragma unroll
-            for (int a2 = 1; a2 < NA; ++a2) Z += st_sum[a2][tok];
-            inv[tt][r] = (blk + 32 * px + tok < t_end) ? 1.f / Z : 0.f;
-          }
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int jl = 0; jl < J; ++jl) {
-          const bf16x8 ax = pack_bf16(s[pp][0][jl] * inv[0], s[pp][1][jl] * inv[1]);
+          f32x4 acc = mask[jl];
 #pragma unroll
-          for (int dl = 0; dl < DTW; ++dl)
-            pacc[jl][dl] = mfma_bf16(ax, as_bf16x8(v_lds[px + pp][dg * DTW + dl][lane]), pacc[jl][dl]);
-          if (dg == 0) dacc[jl] = mfma_bf16(ax, ones, dacc[jl]);
+          for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(uop[jl][kk], as_bf16x8(q_lds[ps][tt][kk][lane]), acc);
+          s[tt][jl] = acc;
+        }
+      // a2: this group's maximum per token, combined over the groups through LDS.
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float mx = s[tt][0][0];
+#pragma unroll
+        for (int jl = 0; jl < J; ++jl)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[tt][jl][r]);
+        mx = xor32_max(xor16_max(mx));
+        if (g == 0) st_max[32 * ps + 16 * tt + c][w] = mx;
+      }
+      __syncthreads();
+      float zp[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const f32x4 mg = *(const f32x4*)&st_max[32 * ps + 16 * tt + c][0];
+        const float mneg = -fmaxf(fmaxf(mg[0], mg[1]), fmaxf(mg[2], mg[3])) * c2;
+        f32x4 zt = zero4();
+#pragma unroll
+        for (int jl = 0; jl < J; ++jl) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) s[tt][jl][r] = exp2_fast(fmaf(s[tt][jl][r], c2, mneg));
+          zt += s[tt][jl];
+        }
+        zp[tt] = xor32_sum(xor16_sum((zt[0] + zt[1]) + (zt[2] + zt[3])));
+        if (g == 0) st_sum[32 * ps + 16 * tt + c][w] = zp[tt];
+      }
+      __syncthreads();
+      // a3: normalised A rows of this group's anchors -> this wave's LDS block.
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int tok = 32 * ps + 16 * tt + c;
+        const f32x4 zg = *(const f32x4*)&st_sum[tok][0];
+        const float Z = (zg[0] + zg[1]) + (zg[2] + zg[3]);
+        const float inv = (blk + tok < t_end) ? __builtin_amdgcn_rcpf(Z) : 0.f;   // Z >= 1
+        __bf16* arow = a_lds[w] + (16 * tt + c) * AS + 4 * g;
+#pragma unroll
+        for (int jl = 0; jl < J; ++jl) {
+          *(u32x2*)(arow + 16 * jl) = pack4_bf16(s[tt][jl] * inv);
         }
       }
-      __syncthreads();   // st_max / st_sum are reused by the next group
+      // A^T V and Delta for this group's tiles over the pair's 32 tokens (the wave reads
+      // back only its own A rows, so no barrier is needed here).
+      bf16x8 xs[J], ys[DT];
+#pragma unroll
+      for (int jl = 0; jl < J; ++jl) xs[jl] = lds_operand_tr(a_lds[w], AS, 16 * jl, c, g);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) ys[dt] = lds_operand_tr(v_lds + 32 * ps * VS, VS, 16 * dt, c, g);
+#pragma unroll
+      for (int jl = 0; jl < J; ++jl) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) pacc[jl][dt] = mfma_bf16(xs[jl], ys[dt], pacc[jl][dt]);
+        dacc[jl] = mfma_bf16(xs[jl], ones, dacc[jl]);
+      }
     }
+    __syncthreads();   // q_lds / v_lds are restaged for the next block
   }
 
-  // Partials in accumulator layout: [slice][chunk][jt][dt][r][lane] holds
-  // P[16jt + 4g + r][vt_dim(dt, c)]; Delta as [slice][chunk][anchor].
+  // Partials: [slice][chunk][jt][dt][r][lane] holds P[16jt + 4g + r][16dt + c];
+  // Delta as [slice][chunk][anchor].
   const size_t sc = (size_t)slice * chunks + chunk;
 #pragma unroll
   for (int jl = 0; jl < J; ++jl) {
-    const int jt = ag * J + jl;
+    const int jt = w * J + jl;
 #pragma unroll
-    for (int dl = 0; dl < DTW; ++dl) {
-      const int dt = dg * DTW + dl;
+    for (int dt = 0; dt < DT; ++dt) {
       float* dst = part + ((sc * AT + jt) * DT + dt) * 256;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[r * 64 + lane] = pacc[jl][dl][r];
+      for (int r = 0; r < 4; ++r) dst[r * 64 + lane] = pacc[jl][dt][r];
     }
-    if (dg == 0 && c == 0) {
+    if (c == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) dpart[sc * (16 * AT) + 16 * jt + 4 * g + r] = dacc[jl][r];
     }
@@ -346,9 +335,8 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 // (slice, 16-anchor tile).  Output layout = the left operand of pass 2's H^T = W^T A^T:
 // [slice][dt2][jj][lane'][slot] with lane' (c',g') holding dim out_dim(dt2, c') and
 // anchors {32jj + 4g' + slot (slot<4), 32jj + 16 + 4g' + slot - 4 (slot>=4)}.  Column c of
-// a partial's dim tile dt is dim 16dt + c (NATURAL, token-split pass 1) or vt_dim(dt, c)
-// (anchor-split pass 1).
-template <int D, bool NATURAL>
+// a partial's dim tile dt is dim 16dt + c.
+template <int D>
 __global__ __launch_bounds__(256)
 void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpart,
                    __bf16* __restrict__ Wop, int chunks, int AT) {
@@ -389,7 +377,7 @@ void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpa
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     const float wv = (delta > 0.f) ? p[dt] * rinv : 0.f;
-    const int dim = NATURAL ? 16 * dt + c : vt_dim<D>(dt, c);
+    const int dim = 16 * dt + c;
     const int rem = dim % (D / 4);
     const int dt2 = rem >> 2;
     const int cc = 4 * (dim / (D / 4)) + (rem & 3);
@@ -513,8 +501,6 @@ template <int D, int AT>
 static hipError_t launch_split_bf16_t(const Geometry& geo, const SplitPlan& p, const void* Q,
                                       const void* U, const void* V, void* H, void* ws,
                                       hipStream_t stream) {
-  constexpr int NA = (AT % 4 == 0) ? 4 : 2;
-  constexpr int PX = (AT > 8) ? 2 : 4;   // pairs per softmax exchange (register budget)
   char* wsb = (char*)ws;
   float* part = (float*)wsb;
   float* dpart = (float*)(wsb + p.part_bytes);
@@ -525,11 +511,11 @@ static hipError_t launch_split_bf16_t(const Geometry& geo, const SplitPlan& p, c
         (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, part, dpart, geo.h, geo.n, geo.m,
         p.chunks1, p.chunk_len1, geo.c2);
   } else {
-    pass1_bf16<D, AT, NA, PX><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, stream>>>(
+    pass1a_bf16<D, AT><<<dim3((unsigned)g1), dim3(4 * kWave), 0, stream>>>(
         (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, part, dpart, geo.h, geo.n, geo.m,
         p.chunks1, p.chunk_len1, geo.c2);
   }
-  finalize_bf16<D, (AT <= 8)><<<dim3((unsigned)(geo.slices * AT)), dim3(256), 0, stream>>>(
+  finalize_bf16<D><<<dim3((unsigned)(geo.slices * AT)), dim3(256), 0, stream>>>(
       part, dpart, (__bf16*)Wop, p.chunks1, AT);
   const long long g2 = geo.slices * p.chunks2;
   pass2_bf16<D, AT><<<dim3((unsigned)g2), dim3(kPass2Waves * kWave), 0, stream>>>(
