@@ -32,8 +32,8 @@ MEASURED_TRAFFIC = {
     ("vit_s16_224", "fused"): {"sources": ["efficient_vision_transformer_amd/csrc/fused_bf16.hip",
                                            "efficient_vision_transformer_amd/csrc/tile_ops.h",
                                            "efficient_vision_transformer_amd/csrc/device_common.h"],
-                               "sha": "d34bbcc927300843", "read_bytes": 19481325,
-                               "write_bytes": 11010330},
+                               "sha": "d129ae9080ce8a72", "read_bytes": 19459756,
+                               "write_bytes": 11012922},
 }
 
 
