@@ -1,9 +1,10 @@
-// fused_bf16.hip -- one workgroup per (batch, head) slice for short token sequences.
+// fused_bf16.hip -- one or two workgroups per (batch, head) slice for short sequences.
 //
 // Computes, per slice (AnchorFormer, Pith verdict page: referee summary, Eq. (11) in the
 // Eq. (12) order; desk-editor letter: A row-stochastic, Delta its column sums):
 //   A = rowsoftmax(Q U^T / sqrt(d)),  W = Delta^-1 (A^T V),  H = A W
-// with Q and V read from HBM once and H written once.
+// with Q and V read from HBM once and H written once (a slice shared by two workgroups,
+// one per half of the output dims, reads Q twice; the second read is meant to hit L2).
 //
 // The slice's tokens are taken in rounds of one 32-token pair per wave.
 //   Phase A (per wave, its pair): S^T = U Q^T on the MFMA (lanes = tokens, registers =

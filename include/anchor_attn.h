@@ -54,8 +54,11 @@ typedef enum {
     ANCHOR_ATTN_ERROR_HIP = 4              /* HIP runtime error (no device, launch failure) */
 } anchor_attn_status_t;
 
-/* Plans: how a call is mapped onto kernels.  AUTO picks per shape.  FUSED keeps a whole
- * (batch, head) slice in one workgroup (short sequences, m <= 64, bf16 only).  SPLIT
+/* Plans: how a call is mapped onto kernels.  AUTO picks per shape.  FUSED computes a
+ * (batch, head) slice in one kernel without workspace (short sequences, n <= 1024,
+ * m <= 64, bf16 only): one workgroup per slice, or, when there are fewer than two slices
+ * per CU and d = 64, two workgroups for some slices, each writing one half of the output
+ * dims.  SPLIT
  * splits the tokens of a slice over workgroups: pass 1 writes per-chunk partial column
  * sums and A^T V, a finalize kernel reduces them in a fixed order into
  * Delta^-1 A^T V, and pass 2 recomputes A and writes H. */
