@@ -119,6 +119,34 @@ def full_attention_gap(x, H, slices=4) -> dict:
             "rows": "all" if rows is None else "2048 sampled"}
 
 
+def copy_reference(algo_bytes: int, steps: int, warmup: int) -> dict:
+    """A plain device copy moving the same bytes (half read, half written) per launch,
+    rotated over >= 1 GiB like the benchmark: the bandwidth a single kernel of this size
+    reaches on this machine, for context beside the roofline fraction."""
+    import torch
+    dev = torch.device("cuda:0")
+    n = max(1, (algo_bytes // 2) // 4)
+    R = max(1, -(-ROTATE_BYTES // (8 * n)))
+    pairs = [(torch.ones(n, dtype=torch.int32, device=dev), torch.empty(n, dtype=torch.int32, device=dev))
+             for _ in range(R)]
+    stream = torch.cuda.current_stream(dev)
+    for i in range(warmup):
+        s, d = pairs[i % R]
+        d.copy_(s)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        s, d = pairs[i % R]
+        d.copy_(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    return {"bytes_per_launch": 8 * n, "avg_duration_us": round(us, 3),
+            "gbs": round(8 * n / (us * 1e-6) / 1e9, 1)}
+
+
 def main():
     args = parse()
     if args.calibrate_copy_mib:
@@ -209,6 +237,10 @@ def main():
         "achieved_tflops": round(tflops, 3),
         "roofline": roof,
     }
+    out["slice_tokens_per_s"] = round(w.B * w.h * w.n / (ms * 1e-3), 1)
+    ref = copy_reference(algo_bytes, min(args.steps, 200), min(args.warmup, 20))
+    ref["frac_of_copy"] = round(gbs / ref["gbs"], 4) if ref["gbs"] > 0 else None
+    out["copy_reference"] = ref
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     out["diagnostic"] = full_attention_gap(x, H)
