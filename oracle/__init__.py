@@ -56,6 +56,10 @@ def _load():
         lib.oracle_anchor_attn_f64.argtypes = [_DBL, _DBL, _DBL, _DBL, _L, _L, _L, _L, _L, ctypes.c_int]
         lib.oracle_anchor_bruteforce_f64.argtypes = [_DBL, _DBL, _DBL, _L, _L, _L, _DBL, _DBL]
         lib.oracle_full_attn_slice_f64.argtypes = [_DBL, _DBL, _DBL, _L, _L, _LONGP, _L, _DBL]
+        lib.oracle_anchor_backward_slice_f64.argtypes = [_DBL, _DBL, _DBL, _DBL, _L, _L, _L,
+                                                         _DBL, _DBL, _DBL]
+        lib.oracle_anchor_backward_f64.argtypes = [_DBL, _DBL, _DBL, _DBL, _DBL, _DBL, _DBL,
+                                                   _L, _L, _L, _L, _L, ctypes.c_int]
         for f in (lib.oracle_anchor_slice_f64, lib.oracle_anchor_attn_f64,
                   lib.oracle_anchor_bruteforce_f64, lib.oracle_full_attn_slice_f64):
             f.restype = ctypes.c_int
@@ -106,6 +110,34 @@ def anchor_attn(Q, U, V, nthreads: int | None = None) -> np.ndarray:
     _check(_load().oracle_anchor_attn_f64(_p(Q), _p(U), _p(V), _p(H), B, h, n, m, d,
                                          int(nthreads)), "anchor_attn")
     return H
+
+
+def anchor_backward_slice(q, u, v, gh):
+    """Gradients of one slice for dL/dH = gh -> (dq [n,d], du [m,d], dv [n,d])."""
+    q, u, v, gh = _f64(q), _f64(u), _f64(v), _f64(gh)
+    n, d = q.shape
+    m = u.shape[0]
+    assert u.shape == (m, d) and v.shape == (n, d) and gh.shape == (n, d)
+    dq = np.zeros((n, d)); du = np.zeros((m, d)); dv = np.zeros((n, d))
+    _check(_load().oracle_anchor_backward_slice_f64(_p(q), _p(u), _p(v), _p(gh), n, m, d,
+                                                   _p(dq), _p(du), _p(dv)), "backward_slice")
+    return dq, du, dv
+
+
+def anchor_backward(Q, U, V, G, nthreads: int | None = None):
+    """Q, V, G [B,h,n,d]; U [h,m,d] -> (dQ [B,h,n,d], dU [h,m,d] summed over the batch,
+    dV [B,h,n,d]) in fp64."""
+    Q, U, V, G = _f64(Q), _f64(U), _f64(V), _f64(G)
+    B, h, n, d = Q.shape
+    m = U.shape[1]
+    assert U.shape == (h, m, d) and V.shape == Q.shape and G.shape == Q.shape
+    if nthreads is None:
+        nthreads = default_threads()
+    dQ = np.zeros_like(Q); dV = np.zeros_like(Q); dU = np.zeros_like(U)
+    _check(_load().oracle_anchor_backward_f64(_p(Q), _p(U), _p(V), _p(G), _p(dQ), _p(dU),
+                                             _p(dV), B, h, n, m, d, int(nthreads)),
+           "backward")
+    return dQ, dU, dV
 
 
 def anchor_bruteforce(q, u, v):

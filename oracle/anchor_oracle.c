@@ -17,6 +17,9 @@
  *          read off F^2), skeptic critique (column normalisation Delta^-1 A^T as the
  *          correct back-transition; the full-attention gap protocol).
  *
+ * Also the gradients of the forward (dL/dQ, dL/dU summed over the batch, dL/dV for a
+ * given dL/dH): the anchors are learnable ([ABS]), so the layer is trained through.
+ *
  * Readings where the pages leave a step open (each is listed in the design doc):
  *   - A = row-softmax over the m anchors of (Q U^T) / sqrt(d): the anchors enter the
  *     logits directly as the weight rows of a bias-free layer ([ABS], [PITH]
@@ -164,6 +167,166 @@ int oracle_anchor_attn_f64(const double* Q, const double* U, const double* V, do
             batch_worker(&jobs[t]);  /* could not spawn: run it inline */
     }
     batch_worker(&jobs[0]);
+    int rc = jobs[0].rc;
+    for (int t = 1; t < nthreads; ++t) {
+        if (spawned[t]) pthread_join(tid[t], NULL);
+        if (jobs[t].rc != 0) rc = jobs[t].rc;
+    }
+    free(jobs);
+    free(tid);
+    free(spawned);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Gradients of the forward above for a loss whose gradient with respect to H is
+ * gH ([ABS]: the anchors are learnable, i.e. trained by gradient descent through
+ * this layer, which needs dL/dQ, dL/dU and dL/dV).  Plain chain rule through the
+ * forward steps in reverse, one slice (q, v, gH: n x d; u: m x d), fp64:
+ *   Step 6  H = A W          ->  dW = A^T gH,          dA  = gH W^T
+ *   Step 5  W_l = P_l / D_l  ->  dP_l = dW_l / D_l,    dD_l = -(dW_l . W_l) / D_l
+ *           (an anchor with D_l == 0 has W_l = 0 fixed: dP_l = 0, dD_l = 0)
+ *   Step 4  P = A^T V        ->  dA += V dP^T,         dV  = A dP
+ *   Step 3  D = 1^T A        ->  dA_il += dD_l
+ *   Step 2  A_i = softmax(S_i) -> dS_i = A_i * (dA_i - <A_i, dA_i>)
+ *   Step 1  S = Q U^T / sqrt(d) -> dQ = dS U / sqrt(d), dU = dS^T Q / sqrt(d)
+ * dq, dv: n x d; du: m x d (this slice's share; U is shared by the batch, so the
+ * batched call sums du over the batch).                                          */
+int oracle_anchor_backward_slice_f64(const double* q, const double* u, const double* v,
+                                     const double* gh, long n, long m, long d,
+                                     double* dq, double* du, double* dv) {
+    if (n < 0 || m < 1 || d < 1) return -1;
+    for (long l = 0; l < m * d; ++l) du[l] = 0.0;
+    if (n == 0) return 0;
+    const double scale = 1.0 / sqrt((double)d);
+    double* A = (double*)malloc(sizeof(double) * (size_t)(n * m));
+    double* dA = (double*)malloc(sizeof(double) * (size_t)(n * m));
+    double* delta = (double*)malloc(sizeof(double) * (size_t)m);
+    double* W = (double*)malloc(sizeof(double) * (size_t)(m * d));
+    double* dW = (double*)malloc(sizeof(double) * (size_t)(m * d));
+    double* dP = (double*)malloc(sizeof(double) * (size_t)(m * d));
+    double* dD = (double*)malloc(sizeof(double) * (size_t)m);
+    int rc = 0;
+    if (!A || !dA || !delta || !W || !dW || !dP || !dD) {
+        rc = -2;
+        goto done;
+    }
+    anchor_softmax(q, u, n, m, d, A);
+    anchor_reduce(A, v, n, m, d, delta, W);
+    /* step 6 */
+    for (long l = 0; l < m; ++l)
+        for (long k = 0; k < d; ++k) {
+            double s = 0.0;
+            for (long i = 0; i < n; ++i) s += A[i * m + l] * gh[i * d + k];
+            dW[l * d + k] = s;
+        }
+    for (long i = 0; i < n; ++i)
+        for (long l = 0; l < m; ++l) {
+            double s = 0.0;
+            for (long k = 0; k < d; ++k) s += gh[i * d + k] * W[l * d + k];
+            dA[i * m + l] = s;
+        }
+    /* step 5 */
+    for (long l = 0; l < m; ++l) {
+        double dot = 0.0;
+        for (long k = 0; k < d; ++k) dot += dW[l * d + k] * W[l * d + k];
+        dD[l] = (delta[l] > 0.0) ? -dot / delta[l] : 0.0;
+        for (long k = 0; k < d; ++k)
+            dP[l * d + k] = (delta[l] > 0.0) ? dW[l * d + k] / delta[l] : 0.0;
+    }
+    /* step 4 */
+    for (long i = 0; i < n; ++i)
+        for (long l = 0; l < m; ++l) {
+            double s = 0.0;
+            for (long k = 0; k < d; ++k) s += v[i * d + k] * dP[l * d + k];
+            dA[i * m + l] += s;
+        }
+    for (long i = 0; i < n; ++i)
+        for (long k = 0; k < d; ++k) {
+            double s = 0.0;
+            for (long l = 0; l < m; ++l) s += A[i * m + l] * dP[l * d + k];
+            dv[i * d + k] = s;
+        }
+    /* step 3 */
+    for (long i = 0; i < n; ++i)
+        for (long l = 0; l < m; ++l) dA[i * m + l] += dD[l];
+    /* step 2 (dA becomes dS in place) */
+    for (long i = 0; i < n; ++i) {
+        double dot = 0.0;
+        for (long l = 0; l < m; ++l) dot += A[i * m + l] * dA[i * m + l];
+        for (long l = 0; l < m; ++l) dA[i * m + l] = A[i * m + l] * (dA[i * m + l] - dot);
+    }
+    /* step 1 */
+    for (long i = 0; i < n; ++i)
+        for (long k = 0; k < d; ++k) {
+            double s = 0.0;
+            for (long l = 0; l < m; ++l) s += dA[i * m + l] * u[l * d + k];
+            dq[i * d + k] = s * scale;
+        }
+    for (long l = 0; l < m; ++l)
+        for (long k = 0; k < d; ++k) {
+            double s = 0.0;
+            for (long i = 0; i < n; ++i) s += dA[i * m + l] * q[i * d + k];
+            du[l * d + k] = s * scale;
+        }
+done:
+    free(A); free(dA); free(delta); free(W); free(dW); free(dP); free(dD);
+    return rc;
+}
+
+/* Batched gradients over [B, h, n, d] tensors, U [h, m, d]: dQ, dV per slice and dU
+ * summed over the batch for each head (slices of one head summed in batch order).
+ * Threads own whole heads.                                                       */
+typedef struct {
+    const double *Q, *U, *V, *G;
+    double *dQ, *dU, *dV;
+    long B, h, n, m, d;
+    long h0, h1;
+    int rc;
+} bwd_job;
+
+static void* bwd_worker(void* arg) {
+    bwd_job* j = (bwd_job*)arg;
+    const long nd = j->n * j->d, md = j->m * j->d;
+    double* part = (double*)malloc(sizeof(double) * (size_t)md);
+    if (!part) { j->rc = -2; return NULL; }
+    for (long hd = j->h0; hd < j->h1; ++hd) {
+        double* du = j->dU + hd * md;
+        for (long e = 0; e < md; ++e) du[e] = 0.0;
+        for (long b = 0; b < j->B; ++b) {
+            const long s = b * j->h + hd;
+            int rc = oracle_anchor_backward_slice_f64(j->Q + s * nd, j->U + hd * md, j->V + s * nd,
+                                                      j->G + s * nd, j->n, j->m, j->d,
+                                                      j->dQ + s * nd, part, j->dV + s * nd);
+            if (rc != 0) { j->rc = rc; free(part); return NULL; }
+            for (long e = 0; e < md; ++e) du[e] += part[e];
+        }
+    }
+    free(part);
+    return NULL;
+}
+
+int oracle_anchor_backward_f64(const double* Q, const double* U, const double* V,
+                               const double* G, double* dQ, double* dU, double* dV,
+                               long B, long h, long n, long m, long d, int nthreads) {
+    if (B < 0 || h < 0 || n < 0 || m < 1 || d < 1) return -1;
+    if (h == 0) return 0;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > h) nthreads = (int)h;
+    bwd_job* jobs = (bwd_job*)calloc((size_t)nthreads, sizeof(bwd_job));
+    pthread_t* tid = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    char* spawned = (char*)calloc((size_t)nthreads, 1);
+    if (!jobs || !tid || !spawned) { free(jobs); free(tid); free(spawned); return -2; }
+    for (int t = 0; t < nthreads; ++t)
+        jobs[t] = (bwd_job){Q, U, V, G, dQ, dU, dV, B, h, n, m, d,
+                            h * t / nthreads, h * (t + 1) / nthreads, 0};
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&tid[t], NULL, bwd_worker, &jobs[t]) == 0)
+            spawned[t] = 1;
+        else
+            bwd_worker(&jobs[t]);
+    }
+    bwd_worker(&jobs[0]);
     int rc = jobs[0].rc;
     for (int t = 1; t < nthreads; ++t) {
         if (spawned[t]) pthread_join(tid[t], NULL);
