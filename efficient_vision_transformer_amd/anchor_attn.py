@@ -41,13 +41,16 @@ def load_library():
         lib.anchor_attn_create.argtypes = [ctypes.POINTER(vp)]
         lib.anchor_attn_destroy.argtypes = [vp]
         lib.anchor_attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        lib.anchor_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                             i32, i32, i32, i32, i32, i32, vp]
         lib.anchor_attn_set_plan.argtypes = [vp, i32]
         lib.anchor_attn_describe_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32,
                                                   ctypes.c_char_p, i32]
         lib.anchor_attn_status_string.argtypes = [i32]
         lib.anchor_attn_status_string.restype = ctypes.c_char_p
         for f in (lib.anchor_attn_create, lib.anchor_attn_destroy, lib.anchor_attn_forward,
-                  lib.anchor_attn_set_plan, lib.anchor_attn_describe_plan):
+                  lib.anchor_attn_backward, lib.anchor_attn_set_plan,
+                  lib.anchor_attn_describe_plan):
             f.restype = i32
         _lib = lib
         return lib
@@ -129,6 +132,42 @@ class AnchorAttention:
         return out
 
     __call__ = forward
+
+    def backward(self, Q, U, V, dH, out=None, stream=None):
+        """Gradients for dL/dH = dH: returns (dQ [B,h,n,d], dU [h,m,d] summed over the
+        batch, dV [B,h,n,d]), bf16, enqueued on ``stream``; no synchronisation.
+        ``out`` may give the three result tensors (dQ, dU, dV) to write into."""
+        import torch
+        if Q.dim() != 4 or V.shape != Q.shape or dH.shape != Q.shape or U.dim() != 3:
+            raise ValueError(f"bad shapes Q{tuple(Q.shape)} U{tuple(U.shape)} V{tuple(V.shape)} "
+                             f"dH{tuple(dH.shape)}")
+        B, h, n, d = Q.shape
+        if U.shape[0] != h or U.shape[2] != d:
+            raise ValueError(f"U must be [h={h}, m, d={d}], got {tuple(U.shape)}")
+        m = U.shape[1]
+        for name, t in (("Q", Q), ("U", U), ("V", V), ("dH", dH)):
+            if not t.is_cuda or t.device != self.device:
+                raise ValueError(f"{name} must live on {self.device}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            if t.dtype != Q.dtype:
+                raise TypeError("Q, U, V and dH must share one dtype")
+        if out is None:
+            dQ, dU, dV = torch.empty_like(Q), torch.empty_like(U), torch.empty_like(V)
+        else:
+            dQ, dU, dV = out
+            for name, t, like in (("dQ", dQ, Q), ("dU", dU, U), ("dV", dV, V)):
+                if t.shape != like.shape or t.dtype != like.dtype or t.device != like.device \
+                        or not t.is_contiguous():
+                    raise ValueError(f"{name} must be a contiguous {like.dtype} tensor of shape "
+                                     f"{tuple(like.shape)} on {like.device}")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        _check(self._lib.anchor_attn_backward(
+            self._h, Q.data_ptr(), U.data_ptr(), V.data_ptr(), dH.data_ptr(), dQ.data_ptr(),
+            dU.data_ptr(), dV.data_ptr(), B, h, n, m, d, _dtype_code(Q),
+            ctypes.c_void_p(stream.cuda_stream)), "anchor_attn_backward")
+        return dQ, dU, dV
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:

@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libanchor_attn.so")
-SOURCES = ["anchor_attn_api.cpp", "split_bf16.hip", "split_fp32.hip", "fused_bf16.hip"]
+SOURCES = ["anchor_attn_api.cpp", "split_bf16.hip", "split_fp32.hip", "fused_bf16.hip",
+           "backward_bf16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

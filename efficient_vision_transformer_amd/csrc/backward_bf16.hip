@@ -1,0 +1,361 @@
+// backward_bf16.hip -- gradients of anchor attention, bf16 in / bf16 out, fp32 accumulate.
+//
+// For each slice (AnchorFormer abstract: the anchors are learnable, so the layer is
+// trained through; Pith verdict page: the forward is Eq. (11) in the Eq. (12) order),
+// with c = 1/sqrt(d), given G = dL/dH (chain rule through the forward steps in reverse):
+//   dW = A^T G,   dP = dW / Delta,   dDelta = -rowsum(dW * W) / Delta   (0 where Delta = 0)
+//   dA = G W^T + V dP^T + 1 dDelta^T,   dS = A * (dA - rowsum(A * dA))
+//   dQ = c dS U,   dV = A dP,   dU = c sum over the batch of dS^T Q.
+// Kernels (on top of the split plan's pass 1, run on (Q, U, V) and on (Q, U, G)):
+//   bwd_finalize (per slice x 16 anchors): chunk sums of P, dW and Delta in chunk order;
+//     W, dP and dDelta as ready-made MFMA operands;
+//   bwd_tokens (per slice x token chunk, rounds of one 32-token pair per wave): A
+//     recomputed; dA^T = dDelta + W G^T + dP V^T on the MFMA (lanes = tokens); dS in
+//     registers; dQ^T = c U^T dS^T and dV^T = dP^T A^T written out; the pair's rows of dS
+//     and Q go to LDS and every wave accumulates its tiles of dS^T Q (transposing LDS
+//     reads) into per-chunk partials of dU;
+//   bwd_du (per head x 16 anchors): dU = c x (partials summed over batch and chunks, in
+//     order).
+#include <algorithm>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "tile_ops.h"
+
+namespace aa {
+
+// Anchor a, dim k of an m_pad x D matrix -> position in the "U layout" left operand of a
+// logits-like product (lane (c,g) of (tile j, chunk kk): anchor 16j + c, dims
+// 8*KS*g + 8kk .. + 7) and in the "W^T layout" left operand of an output-like product
+// ([dt2][jj][lane'][slot], lane' (c',g') holding dim out_dim(dt2, c') and anchors
+// {32jj + 4g' + slot, 32jj + 16 + 4g' + slot - 4}).
+template <int D>
+__device__ __forceinline__ size_t u_layout_index(int AT, int a, int k) {
+  constexpr int KS = D / 32;
+  const int j = a >> 4, cc = a & 15, gg = k / (8 * KS), rem = k % (8 * KS);
+  return ((((size_t)j * KS + (rem >> 3)) * kWave) + 16 * gg + cc) * 8 + (rem & 7);
+}
+template <int D>
+__device__ __forceinline__ size_t wt_layout_index(int MP, int a, int k) {
+  const int rem = k % (D / 4), dt2 = rem >> 2, cc = 4 * (k / (D / 4)) + (rem & 3);
+  const int jj = a >> 5, half = (a >> 4) & 1, gg = (a >> 2) & 3;
+  return ((((size_t)dt2 * MP + jj) * kWave) + 16 * gg + cc) * 8 + 4 * half + (a & 3);
+}
+
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256)
+void bwd_finalize(const float* __restrict__ partP, const float* __restrict__ partG,
+                  const float* __restrict__ dpart, __bf16* __restrict__ wu,
+                  __bf16* __restrict__ dpu, __bf16* __restrict__ dpw, float* __restrict__ dd,
+                  int chunks, int AT) {
+  constexpr int DT = D / 16, KS = D / 32;
+  const int MP = AT / 2;
+  const int slice = blockIdx.x / AT;
+  const int jt = blockIdx.x - slice * AT;
+  const int r = (threadIdx.x >> 6) & 3, lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int anchor = 16 * jt + 4 * g + r;
+  float p[DT], q[DT], delta = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) { p[dt] = 0.f; q[dt] = 0.f; }
+  for (int ch = 0; ch < chunks; ++ch) {
+    const size_t sc = (size_t)slice * chunks + ch;
+    delta += dpart[sc * (16 * AT) + anchor];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const size_t e = ((sc * AT + jt) * DT + dt) * 256 + r * 64 + lane;
+      p[dt] += partP[e];
+      q[dt] += partG[e];
+    }
+  }
+  const float rinv = (delta > 0.f) ? 1.f / delta : 0.f;
+  float dot = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    p[dt] *= rinv;                 // W
+    dot += q[dt] * p[dt];          // dW . W over this lane's dims
+    q[dt] *= rinv;                 // dP
+  }
+  dot = row16_sum(dot);            // over the 16 lanes c: all D dims of the anchor
+  if (c == 0) dd[(size_t)slice * (16 * AT) + anchor] = -dot * rinv;
+  const size_t su = (size_t)slice * AT * KS * kWave * 8;
+  const size_t sw = (size_t)slice * DT * MP * kWave * 8;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int k = 16 * dt + c;
+    wu[su + u_layout_index<D>(AT, anchor, k)] = (__bf16)p[dt];
+    dpu[su + u_layout_index<D>(AT, anchor, k)] = (__bf16)q[dt];
+    dpw[sw + wt_layout_index<D>(MP, anchor, k)] = (__bf16)q[dt];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+template <int D, int MP>
+__global__ __launch_bounds__(4 * kWave, 1)
+void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
+                const __bf16* __restrict__ V, const __bf16* __restrict__ G,
+                const u32x4* __restrict__ wu, const u32x4* __restrict__ dpu,
+                const u32x4* __restrict__ dpw, const float* __restrict__ dd,
+                __bf16* __restrict__ dQ, __bf16* __restrict__ dV, float* __restrict__ partU,
+                int h, int n, int m, int chunks, int chunk_len, float c2, float cs) {
+  constexpr int NW = 4, KS = D / 32, DT = D / 16, AT = 2 * MP;
+  constexpr int TILES = AT * DT, TPW = TILES / NW;
+  constexpr int AS = tr_stride<32 * MP>(), VS = tr_stride<D>();
+  static_assert(TILES % NW == 0, "tiles split evenly over the waves");
+  const int slice = blockIdx.x / chunks;
+  const int chunk = blockIdx.x - slice * chunks;
+  const int head = slice % h;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const size_t base = (size_t)slice * (size_t)n * D;
+  const int t_begin = chunk * chunk_len;
+  const int t_end = min(n, t_begin + chunk_len);
+  const int npairs = (t_end - t_begin + 31) >> 5;
+
+  __shared__ u32x4 u_lds[AT][KS][kWave];     // U, logits layout
+  __shared__ u32x4 wu_lds[AT][KS][kWave];    // W, logits layout
+  __shared__ u32x4 dpu_lds[AT][KS][kWave];   // dP, logits layout
+  __shared__ u32x4 dpw_lds[DT][MP][kWave];   // dP^T, output layout
+  __shared__ u32x4 ut_lds[DT][MP][kWave];    // U^T, output layout
+  __shared__ __attribute__((aligned(16))) float dd_lds[16 * AT];
+  __shared__ __attribute__((aligned(16))) __bf16 s_rows[NW * 32 * AS];   // rows of dS
+  __shared__ __attribute__((aligned(16))) __bf16 q_rows[NW * 32 * VS];   // rows of Q
+
+  // Stage the slice's operands.
+  const __bf16* Uh = U + (size_t)head * m * D;
+  for (int idx = threadIdx.x; idx < AT * KS * kWave; idx += NW * kWave) {
+    const int j = idx / (KS * kWave), kk = (idx / kWave) % KS, l = idx & 63;
+    const int a = 16 * j + (l & 15);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + 8 * KS * (l >> 4) + 8 * kk);
+    (&u_lds[0][0][0])[idx] = v;
+    (&wu_lds[0][0][0])[idx] = wu[(size_t)slice * AT * KS * kWave + idx];
+    (&dpu_lds[0][0][0])[idx] = dpu[(size_t)slice * AT * KS * kWave + idx];
+  }
+  for (int idx = threadIdx.x; idx < DT * MP * kWave; idx += NW * kWave)
+    (&dpw_lds[0][0][0])[idx] = dpw[(size_t)slice * DT * MP * kWave + idx];
+  {
+    __bf16* ut = (__bf16*)&ut_lds[0][0][0];
+    for (int e = threadIdx.x; e < 16 * AT * D; e += NW * kWave) {
+      const int a = e / D, k = e - (e / D) * D;
+      ut[wt_layout_index<D>(MP, a, k)] = (a < m) ? Uh[(size_t)a * D + k] : (__bf16)0.f;
+    }
+  }
+  for (int e = threadIdx.x; e < 16 * AT; e += NW * kWave) dd_lds[e] = dd[(size_t)slice * 16 * AT + e];
+  f32x4 mask[2];
+  pad_mask<MP>(g, m, mask);
+  const bf16x8 ones = splat_bf16(1.f);
+  __syncthreads();
+
+  f32x4 pacc[TPW], dummy[1];
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) pacc[k] = zero4();
+  dummy[0] = zero4();
+
+  const int rounds = (npairs + NW - 1) / NW;
+  for (int r = 0; r < rounds; ++r) {
+    const int pairs_here = min(NW, npairs - r * NW);  // uniform over the workgroup
+    const int p = r * NW + w;
+    if (p < npairs) {
+#pragma unroll 1
+      for (int tt = 0; tt < 2; ++tt) {
+        const int row = t_begin + 32 * p + 16 * tt + c;
+        const bool ok = row < t_end;
+        u32x4 qv[KS], vv[KS], gv[KS];
+        load_rows<D>(Q, base, row, n, g, qv);
+        load_rows<D>(V, base, row, n, g, vv);
+        load_rows<D>(G, base, row, n, g, gv);
+        // A (fp32, normalised) in the transposed layout: s[j] lane (c,g): token c,
+        // anchors 16j + 4g + r'.
+        f32x4 s[AT];
+#pragma unroll
+        for (int j = 0; j < AT; ++j) {
+          f32x4 acc = (j >= AT - 2) ? mask[j - (AT - 2)] : zero4();
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(qv[kk]), acc);
+          s[j] = acc;
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int j = 0; j < AT; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) mx = fmaxf(mx, s[j][q]);
+        mx = xor32_max(xor16_max(mx));
+        const float mneg = -mx * c2;
+        f32x4 zt = zero4();
+#pragma unroll
+        for (int j = 0; j < AT; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) s[j][q] = exp2_fast(fmaf(s[j][q], c2, mneg));
+          zt += s[j];
+        }
+        const float z = xor32_sum(xor16_sum((zt[0] + zt[1]) + (zt[2] + zt[3])));
+        const float inv = ok ? 1.f / z : 0.f;
+#pragma unroll
+        for (int j = 0; j < AT; ++j) s[j] *= inv;
+        // dA^T = dDelta + W G^T + dP V^T, then dS = A * (dA - rowsum(A * dA)).
+        f32x4 da[AT];
+        float rs = 0.f;
+#pragma unroll
+        for (int j = 0; j < AT; ++j) {
+          f32x4 acc = *(const f32x4*)&dd_lds[16 * j + 4 * g];
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) {
+            acc = mfma_bf16(as_bf16x8(wu_lds[j][kk][lane]), as_bf16x8(gv[kk]), acc);
+            acc = mfma_bf16(as_bf16x8(dpu_lds[j][kk][lane]), as_bf16x8(vv[kk]), acc);
+          }
+          da[j] = acc;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) rs = fmaf(s[j][q], acc[q], rs);
+        }
+        rs = xor32_sum(xor16_sum(rs));
+        bf16x8 ab[MP], dsb[MP];
+#pragma unroll
+        for (int jj = 0; jj < MP; ++jj) {
+          ab[jj] = pack_bf16(s[2 * jj], s[2 * jj + 1]);
+          const f32x4 d0 = s[2 * jj] * (da[2 * jj] - rs), d1 = s[2 * jj + 1] * (da[2 * jj + 1] - rs);
+          dsb[jj] = pack_bf16(d0, d1);
+        }
+        // dQ^T = c U^T dS^T and dV^T = dP^T A^T: lane (c,g) ends with token c, dims
+        // (D/4)g + 4dt2 + r'.
+        f32x4 hq[DT], hv[DT];
+#pragma unroll
+        for (int dt2 = 0; dt2 < DT; ++dt2) {
+          f32x4 aq = zero4(), av = zero4();
+#pragma unroll
+          for (int jj = 0; jj < MP; ++jj) {
+            aq = mfma_bf16(as_bf16x8(ut_lds[dt2][jj][lane]), dsb[jj], aq);
+            av = mfma_bf16(as_bf16x8(dpw_lds[dt2][jj][lane]), ab[jj], av);
+          }
+          hq[dt2] = aq * cs;
+          hv[dt2] = av;
+        }
+        if (ok) {
+          const size_t off = base + (size_t)row * D + (D / 4) * g;
+#pragma unroll
+          for (int hh = 0; hh < DT / 2; ++hh) {
+            __builtin_nontemporal_store(as_u32x4(pack_bf16(hq[2 * hh], hq[2 * hh + 1])), (u32x4*)(dQ + off + 8 * hh));
+            __builtin_nontemporal_store(as_u32x4(pack_bf16(hv[2 * hh], hv[2 * hh + 1])), (u32x4*)(dV + off + 8 * hh));
+          }
+        }
+        // Rows of dS ([token][anchor], dsb[jj] holds anchors 32jj + 4g .. + 3 and
+        // 32jj + 16 + 4g .. + 3) and of Q ([token][dim]) for the dU tiles.
+        __bf16* srow = s_rows + (32 * w + 16 * tt + c) * AS + 4 * g;
+#pragma unroll
+        for (int jj = 0; jj < MP; ++jj) {
+          const u32x4 v = as_u32x4(dsb[jj]);
+          *(u32x2*)(srow + 32 * jj) = u32x2{v[0], v[1]};
+          *(u32x2*)(srow + 32 * jj + 16) = u32x2{v[2], v[3]};
+        }
+        __bf16* qrow = q_rows + (32 * w + 16 * tt + c) * VS + 8 * KS * g;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) *(u32x4*)(qrow + 8 * kk) = qv[kk];
+      }
+    }
+    __syncthreads();
+    // dS^T Q over the round's pairs, this wave's (16-anchor, 16-dim) tiles.
+    accumulate_tiles<TPW, DT, AS, VS, false>(s_rows, q_rows, w * TPW, pairs_here, c, g, ones,
+                                             pacc, dummy);
+    __syncthreads();
+  }
+
+  // dU partials: [slice][chunk][jt][dt][r][lane] holds sum over the chunk's tokens of
+  // dS[token][16jt + 4g + r] Q[token][16dt + c].
+  const size_t sc = (size_t)slice * chunks + chunk;
+#pragma unroll
+  for (int k = 0; k < TPW; ++k) {
+    const int t = w * TPW + k;
+    const int ja = t / DT, dt = t - (t / DT) * DT;
+    float* dst = partU + ((sc * AT + ja) * DT + dt) * 256;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q * 64 + lane] = pacc[k][q];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256)
+void bwd_du(const float* __restrict__ partU, __bf16* __restrict__ dU, int B, int h, int m,
+            int chunks, int AT, float cs) {
+  constexpr int DT = D / 16;
+  const int head = blockIdx.x / AT;
+  const int jt = blockIdx.x - head * AT;
+  const int r = (threadIdx.x >> 6) & 3, lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int anchor = 16 * jt + 4 * g + r;
+  float acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = 0.f;
+  for (int b = 0; b < B; ++b) {
+    const size_t slice = (size_t)b * h + head;
+    for (int ch = 0; ch < chunks; ++ch) {
+      const size_t sc = slice * chunks + ch;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] += partU[((sc * AT + jt) * DT + dt) * 256 + r * 64 + lane];
+    }
+  }
+  if (anchor < m) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) dU[((size_t)head * m + anchor) * D + 16 * dt + c] = (__bf16)(acc[dt] * cs);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+template <int D, int AT>
+static hipError_t go_bwd(const Geometry& g, const SplitPlan& p, const BackwardBuffers& wb,
+                         const void* Q, const void* U, const void* V, const void* G, void* dQ,
+                         void* dU, void* dV, hipStream_t s) {
+  constexpr int MP = AT / 2;
+  const float cs = 1.0f / sqrtf((float)D);
+  hipError_t e = launch_pass1_bf16(g, p, Q, U, V, wb.partP, wb.dpart, s);
+  if (e != hipSuccess) return e;
+  e = launch_pass1_bf16(g, p, Q, U, G, wb.partG, wb.dpart, s);
+  if (e != hipSuccess) return e;
+  bwd_finalize<D><<<dim3((unsigned)(g.slices * AT)), dim3(256), 0, s>>>(
+      wb.partP, wb.partG, wb.dpart, (__bf16*)wb.wu, (__bf16*)wb.dpu, (__bf16*)wb.dpw, wb.dd,
+      p.chunks1, AT);
+  bwd_tokens<D, MP><<<dim3((unsigned)(g.slices * p.chunks1)), dim3(4 * kWave), 0, s>>>(
+      (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (const __bf16*)G,
+      (const u32x4*)wb.wu, (const u32x4*)wb.dpu, (const u32x4*)wb.dpw, wb.dd, (__bf16*)dQ,
+      (__bf16*)dV, wb.partU, g.h, g.n, g.m, p.chunks1, p.chunk_len1, g.c2, cs);
+  bwd_du<D><<<dim3((unsigned)(g.h * AT)), dim3(256), 0, s>>>(wb.partU, (__bf16*)dU, g.B, g.h,
+                                                             g.m, p.chunks1, AT, cs);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t dispatch_bwd(const Geometry& g, const SplitPlan& p, const BackwardBuffers& wb,
+                               const void* Q, const void* U, const void* V, const void* G,
+                               void* dQ, void* dU, void* dV, hipStream_t s) {
+  switch (g.at) {
+    case 2: return go_bwd<D, 2>(g, p, wb, Q, U, V, G, dQ, dU, dV, s);
+    case 4: return go_bwd<D, 4>(g, p, wb, Q, U, V, G, dQ, dU, dV, s);
+    case 6: return go_bwd<D, 6>(g, p, wb, Q, U, V, G, dQ, dU, dV, s);
+    case 8: return go_bwd<D, 8>(g, p, wb, Q, U, V, G, dQ, dU, dV, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_u32(unsigned* __restrict__ p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 4;   // callers pass 16-byte aligned buffers of bf16 pairs
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<size_t>(1024, (n + 255) / 256);
+  fill_zero_u32<<<dim3(blocks), dim3(256), 0, s>>>((unsigned*)p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_bf16(const Geometry& g, const SplitPlan& p, const BackwardBuffers& wb,
+                                const void* Q, const void* U, const void* V, const void* G,
+                                void* dQ, void* dU, void* dV, hipStream_t s) {
+  if (g.d == 64) return dispatch_bwd<64>(g, p, wb, Q, U, V, G, dQ, dU, dV, s);
+  if (g.d == 32) return dispatch_bwd<32>(g, p, wb, Q, U, V, G, dQ, dU, dV, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace aa

@@ -39,6 +39,27 @@ constexpr int kPass2Block = 64;
 hipError_t launch_split_bf16(const Geometry& g, const SplitPlan& p, const void* Q,
                              const void* U, const void* V, void* H, void* workspace,
                              hipStream_t stream);
+// Split pass 1 alone on (Q, U, X): per-chunk partials of A^T X and of the column sums of
+// A, in the layout the finalize kernels read (used by the backward with X = V and
+// X = dH).
+hipError_t launch_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* Q, const void* U,
+                             const void* X, float* part, float* dpart, hipStream_t stream);
+// Workspace sections of the backward (see bwd_finalize / bwd_tokens).
+struct BackwardBuffers {
+  float* partP;   // pass-1 partials of A^T V      [slice][chunk][AT][DT][256]
+  float* partG;   // pass-1 partials of A^T dH     [slice][chunk][AT][DT][256]
+  float* dpart;   // pass-1 partials of Delta      [slice][chunk][16 AT]
+  void* wu;       // W, logits-layout operands     [slice][AT][KS][64] x 16 B
+  void* dpu;      // dP, logits-layout operands    [slice][AT][KS][64] x 16 B
+  void* dpw;      // dP^T, output-layout operands  [slice][DT][MP][64] x 16 B
+  float* dd;      // dDelta                        [slice][16 AT]
+  float* partU;   // partials of dS^T Q            [slice][chunk][AT][DT][256]
+};
+// Zeroes `bytes` (a multiple of 4) with a fill kernel (safe under stream capture).
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+hipError_t launch_backward_bf16(const Geometry& g, const SplitPlan& p, const BackwardBuffers& wb,
+                                const void* Q, const void* U, const void* V, const void* G,
+                                void* dQ, void* dU, void* dV, hipStream_t stream);
 hipError_t launch_split_fp32(const Geometry& g, const SplitPlan& p, const void* Q,
                              const void* U, const void* V, void* H, void* workspace,
                              hipStream_t stream);

@@ -12,6 +12,8 @@
 //           as bf16 MFMA operands;
 //   pass 2  (one workgroup per chunk): recomputes A from Q and writes H = A W.
 // All products run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "tile_ops.h"
@@ -498,6 +500,21 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 
 // ---------------------------------------------------------------------------------------
 template <int D, int AT>
+static void launch_pass1_t(const Geometry& geo, const SplitPlan& p, const void* Q, const void* U,
+                           const void* X, float* part, float* dpart, hipStream_t stream) {
+  const long long g1 = geo.slices * p.chunks1;
+  if constexpr (AT <= 8) {
+    pass1x_bf16<D, AT / 2, kPass1Waves><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, stream>>>(
+        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)X, part, dpart, geo.h, geo.n, geo.m,
+        p.chunks1, p.chunk_len1, geo.c2);
+  } else {
+    pass1a_bf16<D, AT><<<dim3((unsigned)g1), dim3(4 * kWave), 0, stream>>>(
+        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)X, part, dpart, geo.h, geo.n, geo.m,
+        p.chunks1, p.chunk_len1, geo.c2);
+  }
+}
+
+template <int D, int AT>
 static hipError_t launch_split_bf16_t(const Geometry& geo, const SplitPlan& p, const void* Q,
                                       const void* U, const void* V, void* H, void* ws,
                                       hipStream_t stream) {
@@ -505,16 +522,7 @@ static hipError_t launch_split_bf16_t(const Geometry& geo, const SplitPlan& p, c
   float* part = (float*)wsb;
   float* dpart = (float*)(wsb + p.part_bytes);
   void* Wop = (void*)(wsb + p.part_bytes + p.dpart_bytes);
-  const long long g1 = geo.slices * p.chunks1;
-  if constexpr (AT <= 8) {
-    pass1x_bf16<D, AT / 2, kPass1Waves><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, stream>>>(
-        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, part, dpart, geo.h, geo.n, geo.m,
-        p.chunks1, p.chunk_len1, geo.c2);
-  } else {
-    pass1a_bf16<D, AT><<<dim3((unsigned)g1), dim3(4 * kWave), 0, stream>>>(
-        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, part, dpart, geo.h, geo.n, geo.m,
-        p.chunks1, p.chunk_len1, geo.c2);
-  }
+  launch_pass1_t<D, AT>(geo, p, Q, U, V, part, dpart, stream);
   finalize_bf16<D><<<dim3((unsigned)(geo.slices * AT)), dim3(256), 0, stream>>>(
       part, dpart, (__bf16*)Wop, p.chunks1, AT);
   const long long g2 = geo.slices * p.chunks2;
@@ -542,6 +550,26 @@ hipError_t launch_split_bf16(const Geometry& g, const SplitPlan& p, const void* 
                              const void* V, void* H, void* ws, hipStream_t stream) {
   if (g.d == 64) return dispatch_at<64>(g, p, Q, U, V, H, ws, stream);
   if (g.d == 32) return dispatch_at<32>(g, p, Q, U, V, H, ws, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* Q, const void* U,
+                             const void* X, float* part, float* dpart, hipStream_t s) {
+  auto at = [&](auto D) -> hipError_t {
+    constexpr int d = decltype(D)::value;
+    switch (g.at) {
+      case 2: launch_pass1_t<d, 2>(g, p, Q, U, X, part, dpart, s); break;
+      case 4: launch_pass1_t<d, 4>(g, p, Q, U, X, part, dpart, s); break;
+      case 6: launch_pass1_t<d, 6>(g, p, Q, U, X, part, dpart, s); break;
+      case 8: launch_pass1_t<d, 8>(g, p, Q, U, X, part, dpart, s); break;
+      case 12: launch_pass1_t<d, 12>(g, p, Q, U, X, part, dpart, s); break;
+      case 16: launch_pass1_t<d, 16>(g, p, Q, U, X, part, dpart, s); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  };
+  if (g.d == 64) return at(std::integral_constant<int, 64>{});
+  if (g.d == 32) return at(std::integral_constant<int, 32>{});
   return hipErrorInvalidValue;
 }
 

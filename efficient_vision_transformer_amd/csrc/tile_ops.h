@@ -94,8 +94,8 @@ __device__ __forceinline__ bf16x8 lds_operand_tr(const __bf16* blk, int stride, 
 // and, for a tile in dim tile 0, Delta += A^T 1 of its anchor tile (dacc[k / DT]), over
 // `pairs` 32-row blocks of the row-major LDS copies of A (stride AS) and V (stride VS).
 // When TPW is a multiple or a divisor of DT each distinct operand is read once per block;
-// otherwise every tile reads its own two operands.
-template <int TPW, int DT, int AS, int VS>
+// otherwise every tile reads its own two operands.  DELTA = false skips the column sums.
+template <int TPW, int DT, int AS, int VS, bool DELTA = true>
 __device__ __forceinline__ void accumulate_tiles(const __bf16* a_lds, const __bf16* v_lds, int t0,
                                                  int pairs, int c, int g, bf16x8 ones,
                                                  f32x4* pacc, f32x4* dacc) {
@@ -116,7 +116,7 @@ __device__ __forceinline__ void accumulate_tiles(const __bf16* a_lds, const __bf
       for (int k = 0; k < TPW; ++k) {
         const int jl = BYROW ? k / DT : 0, iy = BYROW ? k % DT : k;
         pacc[k] = mfma_bf16(xs[jl], ys[iy], pacc[k]);
-        if (dt0 + iy == 0) dacc[k / DT] = mfma_bf16(xs[jl], ones, dacc[k / DT]);
+        if (DELTA && dt0 + iy == 0) dacc[k / DT] = mfma_bf16(xs[jl], ones, dacc[k / DT]);
       }
     }
   } else {
@@ -127,7 +127,7 @@ __device__ __forceinline__ void accumulate_tiles(const __bf16* a_lds, const __bf
         const bf16x8 x = lds_operand_tr(a_lds + 32 * ps * AS, AS, 16 * ja, c, g);
         const bf16x8 y = lds_operand_tr(v_lds + 32 * ps * VS, VS, 16 * dt, c, g);
         pacc[k] = mfma_bf16(x, y, pacc[k]);
-        if (dt == 0) dacc[k / DT] = mfma_bf16(x, ones, dacc[k / DT]);
+        if (DELTA && dt == 0) dacc[k / DT] = mfma_bf16(x, ones, dacc[k / DT]);
       }
     }
   }

@@ -170,3 +170,13 @@ def random_case(seed: int, B: int, h: int, n: int, m: int, d: int, dtype: str = 
     w = Workload(f"case_{B}x{h}x{n}x{m}x{d}_{dtype}", B=B, h=h, n=n, m=m, d=d, dtype=dtype,
                  seed=seed, q_scale=q_scale)
     return make_inputs(w, with_k=False)
+
+
+def make_upstream_grad(x: Inputs, seed: int) -> tuple[np.ndarray, np.ndarray | None]:
+    """A seeded upstream gradient dL/dH of the shape of ``x.Q`` (N(0,1), fp32 draws in
+    one call of ``default_rng(seed)``), rounded once to the workload's storage dtype.
+
+    Returns (stored values as float32, uint16 bf16 bit patterns or None for fp32)."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal(x.Q.shape, dtype=np.float32)
+    return _store(g, x.workload.dtype)

@@ -87,6 +87,25 @@ anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx,
                                          int B, int h, int n, int m, int d,
                                          anchor_attn_dtype_t dtype, void* stream);
 
+/* Enqueues the gradients of the forward above for a loss L with dL/dH = dH (AnchorFormer
+ * abstract: the anchors are learnable, so the layer is trained through; the Pith verdict
+ * page's Eq. (11) in the Eq. (12) order is the function differentiated), on `stream`,
+ * without waiting:
+ *   Q, V, dH, dQ, dV : [B, h, n, d]  device, bf16
+ *   U, dU            : [h, m, d]     device, bf16; dU is summed over the batch (U is
+ *                                    shared by every batch element)
+ * Accumulation is fp32; results are rounded to bf16.  dQ, dU and dV are written in full
+ * (dU is zero when B*h*n == 0); they must not overlap each other or any input.  The
+ * context's workspace grows as for the split plan (the first call of a larger shape may
+ * synchronize).  Domain: as anchor_attn_forward with dtype BF16 and m <= 128; other
+ * dtypes or larger m return NOT_SUPPORTED.  Errors as anchor_attn_forward: nothing is
+ * enqueued and no output is touched. */
+anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx,
+                                          const void* Q, const void* U, const void* V,
+                                          const void* dH, void* dQ, void* dU, void* dV,
+                                          int B, int h, int n, int m, int d,
+                                          anchor_attn_dtype_t dtype, void* stream);
+
 /* Forces a plan for later forward calls on this context (tests and tuning); AUTO
  * restores the default choice.  A forced plan that cannot run a given shape makes that
  * forward call return NOT_SUPPORTED. */
