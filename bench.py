@@ -1,10 +1,11 @@
 """Anchor-attention throughput on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--plan auto|fused|split]
-                [--no-cpu-baseline]
+                [--pass forward|backward] [--no-cpu-baseline]
 
 One step = one forward of the whole hot path (logits, softmax, column sums and A^T V,
-normalisation, H = A W) over one batch of the workload.  Inputs are resident in HBM:
+normalisation, H = A W) over one batch of the workload; with --pass backward, one
+backward (dQ, dU, dV for a given dL/dH) instead.  Inputs are resident in HBM:
 R copies of the batch (R * bytes >= 1 GiB, well beyond the 256 MB Infinity Cache) are
 cycled so every step reads cold HBM.  K steps are bracketed by events on the launch
 stream.  Prints one JSON line.
@@ -58,6 +59,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--plan", default="auto", choices=["auto", "fused", "split"])
+    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -97,6 +99,92 @@ def cpu_baseline(x, seconds: float) -> dict:
     return {"value": reps * w.B * w.n / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} full batch(es) of {w.name} (B={w.B} h={w.h} n={w.n} m={w.m} d={w.d}) "
                       f"in fp64, {el:.1f} s wall"}
+
+
+def cpu_baseline_backward(x, G, seconds: float) -> dict:
+    """The fp64 oracle's gradients as they stand, timed like cpu_baseline."""
+    import numpy as np
+    import oracle
+    cores = oracle.default_threads()
+    Q, U, V, G = (np.asarray(a, dtype=np.float64) for a in (x.Q, x.U, x.V, G))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.anchor_backward(Q, U, V, G, nthreads=cores)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    w = x.workload
+    return {"value": reps * w.B * w.n / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} full backward(s) of {w.name} (B={w.B} h={w.h} n={w.n} m={w.m} "
+                      f"d={w.d}) in fp64, {el:.1f} s wall"}
+
+
+def backward_bytes_flops(w) -> tuple[int, int]:
+    """Algorithmic bytes and flops of one backward: Q, V, dH read and dQ, dV written once,
+    U read and dU written once; 2nmd flops each for the logits, A^T V, A^T dH, dH W^T,
+    V dP^T, dS U, A dP and dS^T Q per slice."""
+    es = w.elem_bytes
+    act = w.B * w.h * w.n * w.d * es
+    return 5 * act + 2 * w.h * w.m * w.d * es, 16 * w.B * w.h * w.n * w.m * w.d
+
+
+def bench_backward(args, ctx, x, dev, plan_desc) -> dict:
+    import numpy as np
+    import torch
+    from efficient_vision_transformer_amd.inputs import make_upstream_grad
+    w = x.workload
+    if w.dtype != "bf16":
+        raise SystemExit("the backward runs in bf16 only")
+    G, gbits = make_upstream_grad(x, w.seed + 1)
+    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    Q0, U, V0, G0 = up(x.bits["Q"]), up(x.bits["U"]), up(x.bits["V"]), up(gbits)
+    algo_bytes, flops = backward_bytes_flops(w)
+    R = max(1, -(-ROTATE_BYTES // algo_bytes))
+    mk = lambda q, v, g: (q, v, g, (torch.empty_like(q), torch.empty_like(U), torch.empty_like(v)))
+    sets = [mk(Q0, V0, G0)] + [mk(Q0.clone(), V0.clone(), G0.clone()) for _ in range(R - 1)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        q, v, g, o = sets[i % R]
+        ctx.backward(q, U, v, g, out=o, stream=stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        q, v, g, o = sets[i % R]
+        ctx.backward(q, U, v, g, out=o, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "whole backward (pass1 x2 + finalize + tokens + dU reduction)",
+            "per_launch": {"algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
+                           "avg_duration_us": round(ms * 1e3, 3)}}
+    out = {
+        "metric": f"anchor-attention backward tokens/sec ({w.name})",
+        "value": round(w.B * w.n / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "backward", "B": w.B, "h": w.h, "n": w.n,
+                   "m": w.m, "d": w.d, "global_batch": w.B, "seq_len": w.n,
+                   "parallelism": "single-gpu", "forward_plan": plan_desc, "rotating_sets": R},
+        "achieved_hbm_gbs": round(gbs, 1),
+        "achieved_tflops": round(tflops, 3),
+        "roofline": roof,
+    }
+    ref = copy_reference(algo_bytes, min(args.steps, 200), min(args.warmup, 20))
+    ref["frac_of_copy"] = round(gbs / ref["gbs"], 4) if ref["gbs"] > 0 else None
+    out["copy_reference"] = ref
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_backward(x, G, args.cpu_seconds)
+    return out
 
 
 def full_attention_gap(x, H, slices=4) -> dict:
@@ -166,6 +254,11 @@ def main():
     x = make_inputs(w, with_k=True)
     ctx = AnchorAttention(dev, plan=args.plan)
     plan_desc = ctx.describe(w.B, w.h, w.n, w.m, w.d, w.dtype)
+    if args.which == "backward":
+        out = bench_backward(args, ctx, x, dev, plan_desc)
+        ctx.close()
+        print(json.dumps(out), flush=True)
+        return
 
     if w.dtype == "bf16":
         up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)

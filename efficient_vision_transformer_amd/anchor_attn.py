@@ -87,11 +87,13 @@ class AnchorAttention:
             _check(lib.anchor_attn_create(ctypes.byref(handle)), "anchor_attn_create")
         self._h = handle
         self._lib = lib
+        self.plan = "auto"
         if plan != "auto":
             self.set_plan(plan)
 
     def set_plan(self, plan: str) -> None:
         _check(self._lib.anchor_attn_set_plan(self._h, _PLANS[plan]), "anchor_attn_set_plan")
+        self.plan = plan
 
     def describe(self, B, h, n, m, d, dtype: str = "bf16") -> str:
         buf = ctypes.create_string_buffer(512)

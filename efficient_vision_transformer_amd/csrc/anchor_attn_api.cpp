@@ -112,6 +112,22 @@ Chosen choose(const anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t
   }
 }
 
+// The backward (bf16, m <= 128): one workgroup per slice when that plan applies, else the
+// split passes; the context's plan setting is honoured as for the forward.
+Chosen choose_backward(const anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t dtype) {
+  if (dtype != ANCHOR_ATTN_BF16 || g.at > 8) return Chosen::Unsupported;
+  const bool fused_ok = aa::bwd_fused_supported(g);
+  switch (ctx->plan) {
+    case ANCHOR_ATTN_PLAN_FUSED: return fused_ok ? Chosen::Fused : Chosen::Unsupported;
+    case ANCHOR_ATTN_PLAN_SPLIT: return Chosen::Split;
+    default: return (fused_ok && g.slices * 2 >= ctx->num_cus) ? Chosen::Fused : Chosen::Split;
+  }
+}
+
+const char* chosen_name(Chosen c) {
+  return c == Chosen::Fused ? "fused" : (c == Chosen::Split ? "split" : "unsupported");
+}
+
 anchor_attn_status_t ensure_workspace(anchor_attn_ctx* ctx, size_t bytes) {
   if (bytes <= ctx->workspace_bytes) return ANCHOR_ATTN_SUCCESS;
   if (ctx->workspace) {
@@ -209,18 +225,20 @@ anchor_attn_status_t anchor_attn_describe_plan(anchor_attn_ctx* ctx, int B, int 
     if (c == Chosen::Fused) {
       std::snprintf(buf, (size_t)len,
                     "fused: grid=%lld (%lld whole slices + %lld shared by two) wg=%d waves "
-                    "pairs_per_wave=%d %s m_pad=%d workspace=0",
+                    "pairs_per_wave=%d %s m_pad=%d workspace=0; backward: %s",
                     (long long)(g.slices + fp.shared), (long long)(g.slices - fp.shared),
                     (long long)fp.shared, fp.waves, fp.pairs_per_wave,
-                    fp.keep_a ? "A kept" : "A recomputed", g.m_pad);
+                    fp.keep_a ? "A kept" : "A recomputed", g.m_pad,
+                    chosen_name(choose_backward(ctx, g, dtype)));
     } else {
       const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
       std::snprintf(buf, (size_t)len,
                     "split: pass1 grid=%lld chunk=%d x%d | finalize grid=%lld | pass2 grid=%lld "
-                    "chunk=%d x%d | m_pad=%d workspace=%zu",
+                    "chunk=%d x%d | m_pad=%d workspace=%zu; backward: %s",
                     (long long)(g.slices * p.chunks1), p.chunk_len1, p.chunks1,
                     (long long)(g.slices * g.at), (long long)(g.slices * p.chunks2), p.chunk_len2,
-                    p.chunks2, g.m_pad, p.workspace_bytes());
+                    p.chunks2, g.m_pad, p.workspace_bytes(),
+                    chosen_name(choose_backward(ctx, g, dtype)));
     }
     return ANCHOR_ATTN_SUCCESS;
   } catch (...) {
@@ -285,7 +303,8 @@ anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx, const void* Q, c
     bool empty = false;
     anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype, &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
-    if (dtype != ANCHOR_ATTN_BF16 || g.at > 8) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+    const Chosen plan = choose_backward(ctx, g, dtype);
+    if (plan == Chosen::Unsupported) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
     const size_t es = 2;
     const size_t act = (size_t)g.slices * (size_t)n * (size_t)d * es;
     const size_t ub = (size_t)h * (size_t)m * (size_t)d * es;
@@ -317,8 +336,19 @@ anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx, const void* Q, c
       }
       return ANCHOR_ATTN_SUCCESS;
     }
-    const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    if (plan == Chosen::Fused) {
+      st = ensure_workspace(ctx, al((size_t)g.slices * g.m_pad * g.d * sizeof(float)));
+      if (st != ANCHOR_ATTN_SUCCESS) return st;
+      const hipError_t e = aa::launch_backward_fused_bf16(g, Q, U, V, dH, dQ, dU, dV,
+                                                          (float*)ctx->workspace, s);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return ANCHOR_ATTN_ERROR_HIP;
+      }
+      return ANCHOR_ATTN_SUCCESS;
+    }
+    const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
     const size_t part = al((size_t)g.slices * p.chunks1 * g.m_pad * g.d * sizeof(float));
     const size_t dpart = al((size_t)g.slices * p.chunks1 * g.m_pad * sizeof(float));
     const size_t ops = al((size_t)g.slices * g.m_pad * g.d * es);

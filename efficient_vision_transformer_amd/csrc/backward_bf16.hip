@@ -14,8 +14,8 @@
 //     registers; dQ^T = c U^T dS^T and dV^T = dP^T A^T written out; the pair's rows of dS
 //     and Q go to LDS and every wave accumulates its tiles of dS^T Q (transposing LDS
 //     reads) into per-chunk partials of dU;
-//   bwd_du (per head x 16 anchors): dU = c x (partials summed over batch and chunks, in
-//     order).
+//   du_reduce (per head x 16 anchors x 16 dims): dU = c x (partials summed over batch and
+//     chunks in a fixed order).
 #include <algorithm>
 
 #include "device_common.h"
@@ -275,31 +275,59 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 }
 
 // ---------------------------------------------------------------------------------------
+// dU[head][16jt + 4g + r][16dt + c] = cs x the sum of the partial tiles over batch and
+// chunk.  One workgroup per (head, anchor tile, dim tile); wave q sums the entries
+// e = b * chunks + ch with e = q (mod 8) in increasing e, and the eight wave sums are then
+// added in wave order, so the result does not depend on scheduling.
 template <int D>
-__global__ __launch_bounds__(256)
-void bwd_du(const float* __restrict__ partU, __bf16* __restrict__ dU, int B, int h, int m,
-            int chunks, int AT, float cs) {
-  constexpr int DT = D / 16;
-  const int head = blockIdx.x / AT;
-  const int jt = blockIdx.x - head * AT;
-  const int r = (threadIdx.x >> 6) & 3, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(512)
+void du_reduce(const float* __restrict__ partU, __bf16* __restrict__ dU, int B, int h, int m,
+               int chunks, int AT, float cs) {
+  constexpr int DT = D / 16, NWR = 8;
+  __shared__ f32x4 red[NWR][kWave];
+  const int tile = blockIdx.x;
+  const int dt = tile % DT, jt = (tile / DT) % AT, head = tile / (DT * AT);
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int anchor = 16 * jt + 4 * g + r;
-  float acc[DT];
+  f32x4 acc = zero4();
+  const long long total = (long long)B * chunks;
+  for (long long e = q; e < total; e += NWR) {
+    const long long b = e / chunks, ch = e - b * chunks;
+    const size_t sc = ((size_t)b * h + head) * chunks + ch;
+    const float* src = partU + ((sc * AT + jt) * DT + dt) * 256 + lane;
+    acc[0] += src[0];
+    acc[1] += src[64];
+    acc[2] += src[128];
+    acc[3] += src[192];
+  }
+  red[q][lane] = acc;
+  __syncthreads();
+  if (q == 0) {
+    f32x4 s = red[0][lane];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = 0.f;
-  for (int b = 0; b < B; ++b) {
-    const size_t slice = (size_t)b * h + head;
-    for (int ch = 0; ch < chunks; ++ch) {
-      const size_t sc = slice * chunks + ch;
+    for (int i = 1; i < NWR; ++i) s += red[i][lane];
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] += partU[((sc * AT + jt) * DT + dt) * 256 + r * 64 + lane];
+    for (int r = 0; r < 4; ++r) {
+      const int anchor = 16 * jt + 4 * g + r;
+      if (anchor < m) dU[((size_t)head * m + anchor) * D + 16 * dt + c] = (__bf16)(s[r] * cs);
     }
   }
-  if (anchor < m) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) dU[((size_t)head * m + anchor) * D + 16 * dt + c] = (__bf16)(acc[dt] * cs);
-  }
+}
+
+hipError_t launch_du_reduce_bf16(const Geometry& g, const float* partU, int chunks, void* dU,
+                                 hipStream_t s) {
+  const long long grid = (long long)g.h * g.at * (g.d / 16);
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  const float cs = 1.0f / sqrtf((float)g.d);
+  if (g.d == 64)
+    du_reduce<64><<<dim3((unsigned)grid), dim3(512), 0, s>>>(partU, (__bf16*)dU, g.B, g.h, g.m,
+                                                            chunks, g.at, cs);
+  else if (g.d == 32)
+    du_reduce<32><<<dim3((unsigned)grid), dim3(512), 0, s>>>(partU, (__bf16*)dU, g.B, g.h, g.m,
+                                                            chunks, g.at, cs);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------
@@ -320,9 +348,9 @@ static hipError_t go_bwd(const Geometry& g, const SplitPlan& p, const BackwardBu
       (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (const __bf16*)G,
       (const u32x4*)wb.wu, (const u32x4*)wb.dpu, (const u32x4*)wb.dpw, wb.dd, (__bf16*)dQ,
       (__bf16*)dV, wb.partU, g.h, g.n, g.m, p.chunks1, p.chunk_len1, g.c2, cs);
-  bwd_du<D><<<dim3((unsigned)(g.h * AT)), dim3(256), 0, s>>>(wb.partU, (__bf16*)dU, g.B, g.h,
-                                                             g.m, p.chunks1, AT, cs);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_du_reduce_bf16(g, wb.partU, p.chunks1, dU, s);
 }
 
 template <int D>

@@ -60,6 +60,16 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_backward_bf16(const Geometry& g, const SplitPlan& p, const BackwardBuffers& wb,
                                 const void* Q, const void* U, const void* V, const void* G,
                                 void* dQ, void* dU, void* dV, hipStream_t stream);
+// dU = (1/sqrt(d)) x the sum over batch and chunks of per-(slice, chunk) partial tiles
+// [slice][chunk][AT][DT][256] of dS^T Q.
+hipError_t launch_du_reduce_bf16(const Geometry& g, const float* partU, int chunks, void* dU,
+                                 hipStream_t stream);
+// Short-sequence backward: one workgroup per slice (n <= 1024, m <= 64, d = 32 or 64),
+// then the dU reduction; partU holds slices x m_pad x d floats.
+bool bwd_fused_supported(const Geometry& g);
+hipError_t launch_backward_fused_bf16(const Geometry& g, const void* Q, const void* U,
+                                      const void* V, const void* G, void* dQ, void* dU, void* dV,
+                                      float* partU, hipStream_t stream);
 hipError_t launch_split_fp32(const Geometry& g, const SplitPlan& p, const void* Q,
                              const void* U, const void* V, void* H, void* workspace,
                              hipStream_t stream);

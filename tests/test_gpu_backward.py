@@ -27,11 +27,17 @@ def dev():
 
 
 @pytest.fixture(scope="module")
-def ctx(dev):
+def ctxs(dev):
     from efficient_vision_transformer_amd import AnchorAttention
-    c = AnchorAttention(dev)
-    yield c
-    c.close()
+    out = {p: AnchorAttention(dev, plan=p) for p in ("auto", "split", "fused")}
+    yield out
+    for c in out.values():
+        c.close()
+
+
+@pytest.fixture(scope="module")
+def ctx(ctxs):
+    return ctxs["auto"]
 
 
 def _bits_to_dev(bits, dev):
@@ -42,7 +48,8 @@ def _bits_to_dev(bits, dev):
 def _grads(ctx, dev, x, gseed):
     import torch
     w = x.workload
-    print(f"  backward {w.name} B={w.B} h={w.h} n={w.n} m={w.m} d={w.d}", flush=True)
+    print(f"  backward {w.name} B={w.B} h={w.h} n={w.n} m={w.m} d={w.d} plan={ctx.plan}",
+          flush=True)
     G, gbits = make_upstream_grad(x, gseed)
     Q, U, V = to_device(x, dev)
     dH = _bits_to_dev(gbits, dev)
@@ -78,22 +85,43 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_backward_shapes(ctx, dev, shape):
+def _fused_applies(n, m):
+    """The one-workgroup-per-slice backward: n <= 1024 and m <= 64."""
+    return n <= 1024 and m <= 64
+
+
+CASES = [(s, "split") for s in SHAPES] + [(s, "fused") for s in SHAPES if _fused_applies(s[2], s[3])]
+
+
+@pytest.mark.parametrize("shape,plan", CASES, ids=lambda v: "x".join(map(str, v)) if isinstance(v, tuple) else v)
+def test_backward_shapes(ctxs, dev, shape, plan):
     B, h, n, m, d = shape
     x = random_case(7000 + n + m, B, h, n, m, d, "bf16")
-    got, G = _grads(ctx, dev, x, 8000 + n)
+    got, G = _grads(ctxs[plan], dev, x, 8000 + n)
     ref = oracle.anchor_backward(x.Q, x.U, x.V, G)
-    _check_all(got, ref, "x".join(map(str, shape)))
+    _check_all(got, ref, "x".join(map(str, shape)) + " " + plan)
 
 
-@pytest.mark.parametrize("name", ["vit_s16_224", "vit_b16_384", "dense_64x64"])
-def test_backward_workloads_full(ctx, dev, name):
+@pytest.mark.parametrize("name,plan", [("vit_s16_224", "auto"), ("vit_s16_224", "split"),
+                                       ("vit_b16_384", "auto"), ("vit_b16_384", "split"),
+                                       ("dense_64x64", "auto")])
+def test_backward_workloads_full(ctxs, dev, name, plan):
     """Full workload sizes, every gradient element against the oracle."""
     x = make_inputs(name)
-    got, G = _grads(ctx, dev, x, 9000)
+    got, G = _grads(ctxs[plan], dev, x, 9000)
     ref = oracle.anchor_backward(x.Q, x.U, x.V, G)
-    _check_all(got, ref, name)
+    _check_all(got, ref, f"{name} {plan}")
+
+
+def test_backward_plans_agree_headline(ctxs, dev):
+    """Both backward plans on the headline workload agree with each other to the gate."""
+    x = make_inputs("vit_s16_224")
+    a, _ = _grads(ctxs["fused"], dev, x, 9200)
+    b, _ = _grads(ctxs["split"], dev, x, 9200)
+    for name, ga, gb in zip(("dQ", "dU", "dV"), a, b):
+        e = bf16_err(ga, gb)
+        print(f"  fused vs split {name}: {e:.3e}", flush=True)
+        assert e <= BWD_TOL
 
 
 def test_backward_deterministic_bitwise(ctx, dev):
@@ -122,8 +150,9 @@ def test_backward_empty_inputs(ctx, dev):
         assert torch.count_nonzero(dU).item() == 0
 
 
-def test_backward_rejects_what_it_cannot_run(ctx, dev):
+def test_backward_rejects_what_it_cannot_run(ctxs, dev):
     import torch
+    ctx = ctxs["auto"]
     x = random_case(7200, 1, 1, 40, 16, 32, "fp32")
     Q, U, V = to_device(x, dev)
     with pytest.raises(RuntimeError, match="status 2"):
@@ -132,6 +161,14 @@ def test_backward_rejects_what_it_cannot_run(ctx, dev):
     Ub = torch.zeros((1, 129, 32), dtype=torch.bfloat16, device=dev)
     with pytest.raises(RuntimeError, match="status 2"):
         ctx.backward(Qb, Ub, Qb.clone(), Qb.clone())
+    # the one-workgroup-per-slice plan, forced, rejects m > 64 and n > 1024
+    Ub = torch.zeros((1, 65, 32), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(RuntimeError, match="status 2"):
+        ctxs["fused"].backward(Qb, Ub, Qb.clone(), Qb.clone())
+    Qb = torch.zeros((1, 1, 1025, 32), dtype=torch.bfloat16, device=dev)
+    Ub = torch.zeros((1, 16, 32), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(RuntimeError, match="status 2"):
+        ctxs["fused"].backward(Qb, Ub, Qb.clone(), Qb.clone())
 
 
 def test_backward_anchor_sum_invariant_full_size(ctx, dev):
