@@ -18,7 +18,8 @@
 // The slice's dS^T Q tiles go to a workspace; a second kernel sums them over the batch
 // in a fixed order (deterministic, no atomics).
 // Rows of Q, V and G stay in registers between the phases when every wave has at most
-// two pairs (KEEP); otherwise phase 3 reads them again and recomputes A.
+// two pairs (KEEP); otherwise phase 3 reads them again (one round ahead, like phase 1)
+// and recomputes A.
 #include <algorithm>
 
 #include "device_common.h"
@@ -236,18 +237,23 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   __syncthreads();
 
   // ---- phase 3: dQ, dV and the dS^T Q tiles ---------------------------------------------
+  if constexpr (!KEEP) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) load_tile_rows<D>(Q, V, G, base, 32 * w + 16 * tt + c, n, g, rows[0][tt]);
+  }
 #pragma unroll (KEEP ? RK : 1)
   for (int r = 0; r < rounds; ++r) {
     const int pairs_here = min(NW, npairs - r * NW);
     if (pairs_here <= 0) break;
     const int p = r * NW + w;
     const int ri = KEEP ? r : 0;
-    if (p < npairs) {
-      if constexpr (!KEEP) {
+    TileRows<D> nxt[KEEP ? 1 : 2];
+    const bool more = !KEEP && (p + NW < npairs);
+    if (more) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          load_tile_rows<D>(Q, V, G, base, 32 * p + 16 * tt + c, n, g, rows[0][tt]);
-      }
+      for (int tt = 0; tt < 2; ++tt) load_tile_rows<D>(Q, V, G, base, 32 * (p + NW) + 16 * tt + c, n, g, nxt[tt]);
+    }
+    if (p < npairs) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int row = 32 * p + 16 * tt + c;
@@ -310,6 +316,12 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     __syncthreads();
     accumulate_tiles<TPW, DT, AS, VS, false>(L.a, L.v, w * TPW, pairs_here, c, g, ones, uacc, dummy);
     __syncthreads();
+    if constexpr (!KEEP) {
+      if (more) {
+        rows[0][0] = nxt[0];
+        rows[0][1] = nxt[1];
+      }
+    }
   }
 
   // dS^T Q tiles of this slice: [slice][ja][dt][r][lane].
@@ -322,16 +334,22 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   }
 }
 
-// Plans: n <= 1024 (32 pairs), m <= 64, d = 32 or 64; four waves; the rows stay in
-// registers when every wave has at most two pairs (n <= 256).
+// Plans: n <= 1024 (32 pairs), m <= 64, d = 32 or 64; the rows stay in registers when
+// every wave has at most two pairs.
 bool bwd_fused_supported(const Geometry& g) {
   return (g.d == 32 || g.d == 64) && g.m_pad <= 64 && (g.n + 31) / 32 <= 32;
 }
 
+// Waves per workgroup: four for m <= 32; two for m <= 64, where four waves would need
+// more than half of the LDS and leave one workgroup per CU (measured: 87 instead of
+// 107 us at B = 32, h = 12, n = 576, m = 64, d = 64).
+template <int D, int MP>
+constexpr int bwd_waves() { return MP == 2 ? 2 : 4; }
+
 template <int D, int MP, int ROUNDS>
 static hipError_t go_fused(const Geometry& g, const void* Q, const void* U, const void* V,
                            const void* G, void* dQ, void* dV, float* partU, hipStream_t s) {
-  constexpr int NW = 4;
+  constexpr int NW = bwd_waves<D, MP>();
   if (g.slices > 0x7fffffffLL) return hipErrorInvalidValue;
   bwd_fused<D, MP, NW, ROUNDS><<<dim3((unsigned)g.slices), dim3(NW * kWave), 0, s>>>(
       (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (const __bf16*)G, (__bf16*)dQ,
@@ -342,7 +360,8 @@ static hipError_t go_fused(const Geometry& g, const void* Q, const void* U, cons
 template <int D, int MP>
 static hipError_t fused_rounds(const Geometry& g, const void* Q, const void* U, const void* V,
                                const void* G, void* dQ, void* dV, float* partU, hipStream_t s) {
-  const int rounds = ((g.n + 31) / 32 + 3) / 4;
+  constexpr int NW = bwd_waves<D, MP>();
+  const int rounds = ((g.n + 31) / 32 + NW - 1) / NW;
   if (rounds <= 1) return go_fused<D, MP, 1>(g, Q, U, V, G, dQ, dV, partU, s);
   if (rounds == 2) return go_fused<D, MP, 2>(g, Q, U, V, G, dQ, dV, partU, s);
   return go_fused<D, MP, 0>(g, Q, U, V, G, dQ, dV, partU, s);
