@@ -41,6 +41,9 @@ def load_library():
         lib.anchor_attn_create.argtypes = [ctypes.POINTER(vp)]
         lib.anchor_attn_destroy.argtypes = [vp]
         lib.anchor_attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        llp = ctypes.POINTER(ctypes.c_longlong)
+        lib.anchor_attn_forward_strided.argtypes = [vp, vp, llp, vp, vp, llp, vp, llp,
+                                                    i32, i32, i32, i32, i32, i32, vp]
         lib.anchor_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                              i32, i32, i32, i32, i32, i32, vp]
         lib.anchor_attn_set_plan.argtypes = [vp, i32]
@@ -49,7 +52,7 @@ def load_library():
         lib.anchor_attn_status_string.argtypes = [i32]
         lib.anchor_attn_status_string.restype = ctypes.c_char_p
         for f in (lib.anchor_attn_create, lib.anchor_attn_destroy, lib.anchor_attn_forward,
-                  lib.anchor_attn_backward, lib.anchor_attn_set_plan,
+                  lib.anchor_attn_forward_strided, lib.anchor_attn_backward, lib.anchor_attn_set_plan,
                   lib.anchor_attn_describe_plan):
             f.restype = i32
         _lib = lib
@@ -103,9 +106,12 @@ class AnchorAttention:
         return buf.value.decode()
 
     def forward(self, Q, U, V, out=None, stream=None):
-        """Q, V: [B, h, n, d]; U: [h, m, d]; same dtype, contiguous, on this device.
-        Returns H [B, h, n, d] (``out`` if given).  Enqueued on ``stream`` (default: the
-        current torch stream); no synchronisation."""
+        """Q, V: [B, h, n, d]; U: [h, m, d] contiguous; same dtype, on this device.
+        Q, V and ``out`` may be strided views (say the halves of a packed [B, n, 2, h, d]
+        projection, or an output view of a [B, n, h, d] tensor) as long as the d values
+        of each token are contiguous.  Returns H [B, h, n, d] (``out`` if given, else a
+        new contiguous tensor).  Enqueued on ``stream`` (default: the current torch
+        stream); no synchronisation."""
         import torch
         if Q.dim() != 4 or V.shape != Q.shape or U.dim() != 3:
             raise ValueError(f"bad shapes Q{tuple(Q.shape)} U{tuple(U.shape)} V{tuple(V.shape)}")
@@ -116,21 +122,31 @@ class AnchorAttention:
         for name, t in (("Q", Q), ("U", U), ("V", V)):
             if not t.is_cuda or t.device != self.device:
                 raise ValueError(f"{name} must live on {self.device}")
-            if not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
             if t.dtype != Q.dtype:
                 raise TypeError("Q, U and V must share one dtype")
+        if not U.is_contiguous():
+            raise ValueError("U must be contiguous")
         if out is None:
-            out = torch.empty_like(V)
-        elif out.shape != Q.shape or out.dtype != Q.dtype or not out.is_contiguous() \
-                or out.device != self.device:
-            raise ValueError("out must be a contiguous tensor like V")
+            out = torch.empty(Q.shape, dtype=Q.dtype, device=Q.device)
+        elif out.shape != Q.shape or out.dtype != Q.dtype or out.device != self.device:
+            raise ValueError("out must be a tensor of Q's shape, dtype and device")
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
-        _check(self._lib.anchor_attn_forward(
-            self._h, Q.data_ptr(), U.data_ptr(), V.data_ptr(), out.data_ptr(),
-            B, h, n, m, d, _dtype_code(Q), ctypes.c_void_p(stream.cuda_stream)),
-            "anchor_attn_forward")
+        sv = ctypes.c_void_p(stream.cuda_stream)
+        if Q.is_contiguous() and V.is_contiguous() and out.is_contiguous():
+            _check(self._lib.anchor_attn_forward(
+                self._h, Q.data_ptr(), U.data_ptr(), V.data_ptr(), out.data_ptr(),
+                B, h, n, m, d, _dtype_code(Q), sv), "anchor_attn_forward")
+            return out
+        strides = []
+        for name, t in (("Q", Q), ("V", V), ("out", out)):
+            if t.stride(3) != 1 and d > 1:
+                raise ValueError(f"{name}: the d values of a token must be contiguous")
+            strides.append((ctypes.c_longlong * 3)(t.stride(0), t.stride(1), t.stride(2)))
+        _check(self._lib.anchor_attn_forward_strided(
+            self._h, Q.data_ptr(), strides[0], U.data_ptr(), V.data_ptr(), strides[1],
+            out.data_ptr(), strides[2], B, h, n, m, d, _dtype_code(Q), sv),
+            "anchor_attn_forward_strided")
         return out
 
     __call__ = forward

@@ -48,6 +48,40 @@ bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
   return a0 < b0 + bbytes && b0 < a0 + abytes;
 }
 
+// Element strides (batch, head, token) from the caller: null keeps *w (the contiguous
+// layout); otherwise each stride must be non-negative and a multiple of 16 bytes.
+bool take_view(const long long* s3, size_t es, aa::View* w) {
+  if (!s3) return true;
+  for (int i = 0; i < 3; ++i)
+    if (s3[i] < 0 || ((unsigned long long)s3[i] * es) % 16 != 0) return false;
+  *w = aa::View{s3[0], s3[1], s3[2]};
+  return true;
+}
+
+// Bytes from a view's first element to one past its last (B, h, n >= 1).
+size_t view_extent(const aa::View& w, int B, int h, int n, int d, size_t es) {
+  const long long last = (long long)(B - 1) * w.sb + (long long)(h - 1) * w.sh +
+                         (long long)(n - 1) * w.st;
+  return ((size_t)last + (size_t)d) * es;
+}
+
+// True when distinct (batch, head, token) rows of a view never share an element: taken
+// in increasing stride, every stride of a dimension with more than one index is at least
+// the span of the rows below it.
+bool view_injective(const aa::View& w, int B, int h, int n, int d) {
+  struct Dim {
+    long long stride, count;
+  } dims[3] = {{w.sb, B}, {w.sh, h}, {w.st, n}};
+  std::sort(dims, dims + 3, [](const Dim& a, const Dim& b) { return a.stride < b.stride; });
+  long long span = d;
+  for (const Dim& dm : dims) {
+    if (dm.count <= 1) continue;
+    if (dm.stride < span) return false;
+    span += dm.stride * (dm.count - 1);
+  }
+  return true;
+}
+
 // Argument checks shared by forward and describe.  Returns SUCCESS and fills *g, or the
 // error.  *empty is set when there is no work (B*h*n == 0).
 anchor_attn_status_t check_shape(int B, int h, int n, int m, int d, anchor_attn_dtype_t dtype,
@@ -68,6 +102,8 @@ anchor_attn_status_t check_shape(int B, int h, int n, int m, int d, anchor_attn_
   g->at = g->m_pad / 16;
   g->slices = slices;
   g->c2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  const aa::View contiguous{(long long)h * n * d, (long long)n * d, (long long)d};
+  g->vw = aa::Views{contiguous, contiguous, contiguous};
   return ANCHOR_ATTN_SUCCESS;
 }
 
@@ -246,23 +282,31 @@ anchor_attn_status_t anchor_attn_describe_plan(anchor_attn_ctx* ctx, int B, int 
   }
 }
 
-anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx, const void* Q, const void* U,
-                                         const void* V, void* H, int B, int h, int n, int m,
-                                         int d, anchor_attn_dtype_t dtype, void* stream) {
+anchor_attn_status_t anchor_attn_forward_strided(anchor_attn_ctx* ctx, const void* Q,
+                                                 const long long* q_strides, const void* U,
+                                                 const void* V, const long long* v_strides,
+                                                 void* H, const long long* h_strides, int B,
+                                                 int h, int n, int m, int d,
+                                                 anchor_attn_dtype_t dtype, void* stream) {
   if (!ctx) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
   try {
     Geometry g{};
     bool empty = false;
     anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype, &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
+    const size_t es = (dtype == ANCHOR_ATTN_BF16) ? 2 : 4;
+    if (!take_view(q_strides, es, &g.vw.q) || !take_view(v_strides, es, &g.vw.v) ||
+        !take_view(h_strides, es, &g.vw.o))
+      return ANCHOR_ATTN_ERROR_INVALID_VALUE;
     if (empty) return ANCHOR_ATTN_SUCCESS;
     if (!Q || !U || !V || !H) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
     const uintptr_t mis = ((uintptr_t)Q | (uintptr_t)U | (uintptr_t)V | (uintptr_t)H) & 15u;
     if (mis) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
-    const size_t es = (dtype == ANCHOR_ATTN_BF16) ? 2 : 4;
-    const size_t act = (size_t)g.slices * (size_t)n * (size_t)d * es;
+    if (!view_injective(g.vw.o, B, h, n, d)) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    const size_t qx = view_extent(g.vw.q, B, h, n, d, es), vx = view_extent(g.vw.v, B, h, n, d, es);
+    const size_t hx = view_extent(g.vw.o, B, h, n, d, es);
     const size_t ub = (size_t)h * (size_t)m * (size_t)d * es;
-    if (overlaps(H, act, Q, act) || overlaps(H, act, V, act) || overlaps(H, act, U, ub))
+    if (overlaps(H, hx, Q, qx) || overlaps(H, hx, V, vx) || overlaps(H, hx, U, ub))
       return ANCHOR_ATTN_ERROR_INVALID_VALUE;
 
     FusedPlan fp{};
@@ -291,6 +335,13 @@ anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx, const void* Q, co
   } catch (...) {
     return ANCHOR_ATTN_ERROR_HIP;
   }
+}
+
+anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx, const void* Q, const void* U,
+                                         const void* V, void* H, int B, int h, int n, int m,
+                                         int d, anchor_attn_dtype_t dtype, void* stream) {
+  return anchor_attn_forward_strided(ctx, Q, nullptr, U, V, nullptr, H, nullptr, B, h, n, m, d,
+                                     dtype, stream);
 }
 
 anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx, const void* Q, const void* U,

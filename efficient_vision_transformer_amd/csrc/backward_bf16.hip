@@ -164,9 +164,9 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         const int row = t_begin + 32 * p + 16 * tt + c;
         const bool ok = row < t_end;
         u32x4 qv[KS], vv[KS], gv[KS];
-        load_rows<D>(Q, base, row, n, g, qv);
-        load_rows<D>(V, base, row, n, g, vv);
-        load_rows<D>(G, base, row, n, g, gv);
+        load_rows<D>(Q, base, D, row, n, g, qv);
+        load_rows<D>(V, base, D, row, n, g, vv);
+        load_rows<D>(G, base, D, row, n, g, gv);
         // A (fp32, normalised) in the transposed layout: s[j] lane (c,g): token c,
         // anchors 16j + 4g + r'.
         f32x4 s[AT];

@@ -68,9 +68,9 @@ template <int D>
 __device__ __forceinline__ void load_tile_rows(const __bf16* Q, const __bf16* V, const __bf16* G,
                                                size_t base, int row, int n, int g,
                                                TileRows<D>& t) {
-  load_rows_c<D, D>(Q, base, row, n, g, 0, t.q);
-  load_rows_c<D, D>(V, base, row, n, g, 0, t.v);
-  load_rows_c<D, D>(G, base, row, n, g, 0, t.g);
+  load_rows_c<D, D>(Q, base, D, row, n, g, 0, t.q);
+  load_rows_c<D, D>(V, base, D, row, n, g, 0, t.v);
+  load_rows_c<D, D>(G, base, D, row, n, g, 0, t.g);
 }
 
 // Row-major copies of a tile's rows ([token][anchor] for A or dS, [token][dim] for the

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace aa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -96,6 +98,15 @@ __device__ __forceinline__ float xor32_sum(float v) {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- tensor views (View: element strides of a [B, h, n, d] view, see kernels.h) ---------
+__device__ __forceinline__ size_t view_base(const View& w, int slice, int h) {
+  const int b = slice / h, hd = slice - b * h;
+  return (size_t)((long long)b * w.sb + (long long)hd * w.sh);
+}
+__device__ __forceinline__ size_t view_row(const View& w, int row) {
+  return (size_t)((long long)row * w.st);
+}
 
 // ---- padded anchors ----------------------------------------------------------------------
 // m is rounded up to a multiple of 32 (m <= 128) or 64 (m > 128), so padded anchors (index

@@ -49,7 +49,8 @@ template <int D, int DW, int MP, int NW, int ROUNDS, bool KEEP_A>
 __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16* __restrict__ Q,
                                            const __bf16* __restrict__ U,
                                            const __bf16* __restrict__ V, __bf16* __restrict__ H,
-                                           int slice, int d0, int h, int n, int m, float c2) {
+                                           const Views& vw, int slice, int d0, int h, int n, int m,
+                                           float c2) {
   constexpr int KS = D / 32, KV = DW / 32, DTW = DW / 16, AT = 2 * MP;
   constexpr int TILES = AT * DTW, TPW = (TILES + NW - 1) / NW;
   constexpr int NDA = (TPW + DTW - 1) / DTW;   // anchor tiles per wave that need a Delta
@@ -59,7 +60,9 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int c = lane & 15, g = lane >> 4;
-  const size_t base = (size_t)slice * (size_t)n * D;
+  const size_t qb = view_base(vw.q, slice, h), vb = view_base(vw.v, slice, h);
+  const size_t ob = view_base(vw.o, slice, h);
+  const long long qs = vw.q.st, vs = vw.v.st;
   const int npairs = (n + 31) >> 5;
 
   // This wave's first pair goes out to memory before anything else.  Lane (c,g) holds
@@ -67,8 +70,8 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
   u32x4 qc[2][KS], vc[2][KV];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    load_rows_c<D, D>(Q, base, 32 * w + 16 * tt + c, n, g, 0, qc[tt]);
-    load_rows_c<D, DW>(V, base, 32 * w + 16 * tt + c, n, g, d0, vc[tt]);
+    load_rows_c<D, D>(Q, qb, qs, 32 * w + 16 * tt + c, n, g, 0, qc[tt]);
+    load_rows_c<D, DW>(V, vb, vs, 32 * w + 16 * tt + c, n, g, d0, vc[tt]);
   }
   // U as left operands of S^T = U Q^T: lane (c,g) of tile j holds anchor 16j + c with
   // the dims of Q's chunk layout.
@@ -115,8 +118,8 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
     if (more) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        load_rows_c<D, D>(Q, base, 32 * (p + NW) + 16 * tt + c, n, g, 0, qn[tt]);
-        load_rows_c<D, DW>(V, base, 32 * (p + NW) + 16 * tt + c, n, g, d0, vn[tt]);
+        load_rows_c<D, D>(Q, qb, qs, 32 * (p + NW) + 16 * tt + c, n, g, 0, qn[tt]);
+        load_rows_c<D, DW>(V, vb, vs, 32 * (p + NW) + 16 * tt + c, n, g, d0, vn[tt]);
       }
     }
     // Phase A: rows 32w .. 32w + 31 of the round's LDS blocks hold this wave's pair.
@@ -212,7 +215,7 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
       u32x4 qr[2][KS];
       if constexpr (!KEEP_A) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) load_rows_c<D, D>(Q, base, 32 * p + 16 * tt + c, n, g, 0, qr[tt]);
+        for (int tt = 0; tt < 2; ++tt) load_rows_c<D, D>(Q, qb, qs, 32 * p + 16 * tt + c, n, g, 0, qr[tt]);
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -234,7 +237,7 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
         }
         // Lane group g holds local dims 32hh + 8g .. + 7 in tiles 2hh and 2hh + 1.
         if (row < n) {
-          __bf16* dst = H + base + (size_t)row * D + d0 + 8 * g;
+          __bf16* dst = H + ob + view_row(vw.o, row) + d0 + 8 * g;
 #pragma unroll
           for (int hh = 0; hh < DTW / 2; ++hh)
             __builtin_nontemporal_store(as_u32x4(pack_bf16(hacc[2 * hh], hacc[2 * hh + 1])),
@@ -252,12 +255,12 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
 template <int D, int MP, int NW, int ROUNDS, bool KEEP_A, int MINW>
 __global__ __launch_bounds__(NW * kWave, MINW)
 void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
-                const __bf16* __restrict__ V, __bf16* __restrict__ H, int h, int n, int m,
-                float c2, int full) {
+                const __bf16* __restrict__ V, __bf16* __restrict__ H, Views vw, int h, int n,
+                int m, float c2, int full) {
   __shared__ FusedLds<D, MP, NW> L;
   const int b = blockIdx.x;
   if (b < full) {
-    fused_part<D, D, MP, NW, ROUNDS, KEEP_A>(L, Q, U, V, H, b, 0, h, n, m, c2);
+    fused_part<D, D, MP, NW, ROUNDS, KEEP_A>(L, Q, U, V, H, vw, b, 0, h, n, m, c2);
   } else if constexpr (D == 64) {
     // Within each run of 16 shared workgroups, ids i and i + 8 take the two halves of one
     // slice: workgroups are dealt to the XCDs in turn, so both halves (which read the
@@ -273,8 +276,8 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       sl = k >> 1;
       hf = k & 1;
     }
-    fused_part<D, D / 2, MP, NW, ROUNDS, KEEP_A>(L, Q, U, V, H, full + sl, hf * (D / 2), h, n, m,
-                                                 c2);
+    fused_part<D, D / 2, MP, NW, ROUNDS, KEEP_A>(L, Q, U, V, H, vw, full + sl, hf * (D / 2), h, n,
+                                                 m, c2);
   }
 }
 
@@ -316,8 +319,8 @@ static hipError_t go(const Geometry& g, const FusedPlan& p, const void* Q, const
   const long long grid = full + 2 * p.shared;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   fused_bf16<D, MP, NW, ROUNDS, KEEP, MINW><<<dim3((unsigned)grid), dim3(NW * kWave), 0, s>>>(
-      (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (__bf16*)H, g.h, g.n, g.m, g.c2,
-      (int)full);
+      (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (__bf16*)H, g.vw, g.h, g.n, g.m,
+      g.c2, (int)full);
   return hipGetLastError();
 }
 

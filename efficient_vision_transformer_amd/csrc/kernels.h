@@ -5,13 +5,25 @@
 
 namespace aa {
 
-// Problem geometry of one forward call.  Q, V, H: [B, h, n, d]; U: [h, m, d].
+// Element strides (batch, head, token) of a [B, h, n, d] view whose d values per token are
+// contiguous; the contiguous layout is (h*n*d, n*d, d).  Strides are non-negative
+// multiples of 16 bytes, so every row is a whole number of 16-byte vectors.
+struct View {
+  long long sb, sh, st;
+};
+// The views of one forward call: Q and V (inputs) and H (output).
+struct Views {
+  View q, v, o;
+};
+
+// Problem geometry of one call.  Q, V, H: [B, h, n, d] views; U: [h, m, d] contiguous.
 struct Geometry {
   int B, h, n, m, d;
   int m_pad;          // m rounded up to a multiple of 32
   int at;             // anchor tiles of 16: m_pad / 16
   long long slices;   // B * h
   float c2;           // log2(e) / sqrt(d): logits are kept in base-2 units
+  Views vw;           // strides of Q, V, H (contiguous unless the caller gives others)
 };
 
 // Split plan: pass 1 over chunks1 chunks of chunk_len1 tokens per slice writes

@@ -36,8 +36,8 @@ template <int D, int AT>
 __global__ __launch_bounds__(4 * kWave, 2)
 void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                  const __bf16* __restrict__ V, float* __restrict__ part,
-                 float* __restrict__ dpart, int h, int n, int m, int chunks, int chunk_len,
-                 float c2) {
+                 float* __restrict__ dpart, View qw, View xw, int h, int n, int m, int chunks,
+                 int chunk_len, float c2) {
   constexpr int NW = 4, J = AT / NW, KS = D / 32, DT = D / 16;
   constexpr int AS = 80;                     // A row stride (16J + padding, bank-spread)
   constexpr int VS = tr_stride<D>();
@@ -48,7 +48,7 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // anchor group
   const int c = lane & 15, g = lane >> 4;
-  const size_t base = (size_t)slice * (size_t)n * D;
+  const size_t qb = view_base(qw, slice, h), xb = view_base(xw, slice, h);
   const int t_begin = chunk * chunk_len;
   const int t_end = min(n, t_begin + chunk_len);
 
@@ -61,8 +61,8 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   auto load_pair = [&](int blk, u32x4 (*qv)[KS], u32x4 (*vv)[KS]) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      load_rows<D>(Q, base, blk + 32 * w + 16 * tt + c, n, g, qv[tt]);
-      load_rows<D>(V, base, blk + 32 * w + 16 * tt + c, n, g, vv[tt]);
+      load_rows<D>(Q, qb, qw.st, blk + 32 * w + 16 * tt + c, n, g, qv[tt]);
+      load_rows<D>(V, xb, xw.st, blk + 32 * w + 16 * tt + c, n, g, vv[tt]);
     }
   };
   u32x4 qv[2][KS], vv[2][KS];
@@ -212,8 +212,8 @@ template <int D, int MP, int NW>
 __global__ __launch_bounds__(NW * kWave, 2)
 void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                  const __bf16* __restrict__ V, float* __restrict__ part,
-                 float* __restrict__ dpart, int h, int n, int m, int chunks, int chunk_len,
-                 float c2) {
+                 float* __restrict__ dpart, View qw, View xw, int h, int n, int m, int chunks,
+                 int chunk_len, float c2) {
   constexpr int KS = D / 32, DT = D / 16, AT = 2 * MP;
   constexpr int TILES = AT * DT, TPW = (TILES + NW - 1) / NW;
   constexpr int NDA = (TPW + DT - 1) / DT;   // anchor tiles per wave needing a Delta
@@ -224,7 +224,7 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int c = lane & 15, g = lane >> 4;
-  const size_t base = (size_t)slice * (size_t)n * D;
+  const size_t qb = view_base(qw, slice, h), xb = view_base(xw, slice, h);
   const int t_begin = chunk * chunk_len;
   const int t_end = min(n, t_begin + chunk_len);
   const int npairs = (t_end - t_begin + 31) >> 5;
@@ -251,8 +251,8 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   u32x4 qc[2][KS], vc[2][KS];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    load_rows<D>(Q, base, t_begin + 32 * w + 16 * tt + c, n, g, qc[tt]);
-    load_rows<D>(V, base, t_begin + 32 * w + 16 * tt + c, n, g, vc[tt]);
+    load_rows<D>(Q, qb, qw.st, t_begin + 32 * w + 16 * tt + c, n, g, qc[tt]);
+    load_rows<D>(V, xb, xw.st, t_begin + 32 * w + 16 * tt + c, n, g, vc[tt]);
   }
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
@@ -281,8 +281,8 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     if (more) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        load_rows<D>(Q, base, t_begin + 32 * (p + NW) + 16 * tt + c, n, g, qn[tt]);
-        load_rows<D>(V, base, t_begin + 32 * (p + NW) + 16 * tt + c, n, g, vn[tt]);
+        load_rows<D>(Q, qb, qw.st, t_begin + 32 * (p + NW) + 16 * tt + c, n, g, qn[tt]);
+        load_rows<D>(V, xb, xw.st, t_begin + 32 * (p + NW) + 16 * tt + c, n, g, vn[tt]);
       }
     }
     // Phase A: rows 32w .. 32w + 31 of the round's LDS blocks hold this wave's pair.
@@ -395,15 +395,15 @@ void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpa
 template <int D, int AT>
 __global__ __launch_bounds__(kPass2Waves * kWave, 2)
 void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
-                const u32x4* __restrict__ Wop, __bf16* __restrict__ H, int h, int n, int m,
-                int chunks, int chunk_len, float c2) {
+                const u32x4* __restrict__ Wop, __bf16* __restrict__ H, View qw, View ow, int h,
+                int n, int m, int chunks, int chunk_len, float c2) {
   constexpr int NW = kPass2Waves, KS = D / 32, DT = D / 16, MP = AT / 2;
   const int slice = blockIdx.x / chunks;
   const int chunk = blockIdx.x - slice * chunks;
   const int head = slice % h;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const size_t base = (size_t)slice * (size_t)n * D;
+  const size_t qb = view_base(qw, slice, h), ob = view_base(ow, slice, h);
   const int t_begin = chunk * chunk_len;
   const int t_end = min(n, t_begin + chunk_len);
 
@@ -428,7 +428,7 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   // Software pipeline: the next tile's Q rows are requested before this tile is computed.
   // Rows past the chunk read the slice's last row (clamped) and are not stored.
   auto load_q = [&](int t0, u32x4* q) {
-    const size_t off = base + (size_t)min(t0 + c, n - 1) * D + 8 * KS * g;
+    const size_t off = qb + view_row(qw, min(t0 + c, n - 1)) + 8 * KS * g;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) q[kk] = __builtin_nontemporal_load((const u32x4*)(Q + off + 8 * kk));
   };
@@ -485,7 +485,7 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       hacc[dt2] = acc;
     }
     if (ok) {
-      __bf16* dst = H + base + (size_t)row * D + (D / 4) * g;
+      __bf16* dst = H + ob + view_row(ow, row) + (D / 4) * g;
 #pragma unroll
       for (int half = 0; half < DT / 2; ++half)
         __builtin_nontemporal_store(as_u32x4(pack_bf16(hacc[2 * half], hacc[2 * half + 1])),
@@ -505,12 +505,12 @@ static void launch_pass1_t(const Geometry& geo, const SplitPlan& p, const void* 
   const long long g1 = geo.slices * p.chunks1;
   if constexpr (AT <= 8) {
     pass1x_bf16<D, AT / 2, kPass1Waves><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, stream>>>(
-        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)X, part, dpart, geo.h, geo.n, geo.m,
-        p.chunks1, p.chunk_len1, geo.c2);
+        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)X, part, dpart, geo.vw.q, geo.vw.v,
+        geo.h, geo.n, geo.m, p.chunks1, p.chunk_len1, geo.c2);
   } else {
     pass1a_bf16<D, AT><<<dim3((unsigned)g1), dim3(4 * kWave), 0, stream>>>(
-        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)X, part, dpart, geo.h, geo.n, geo.m,
-        p.chunks1, p.chunk_len1, geo.c2);
+        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)X, part, dpart, geo.vw.q, geo.vw.v,
+        geo.h, geo.n, geo.m, p.chunks1, p.chunk_len1, geo.c2);
   }
 }
 
@@ -527,8 +527,8 @@ static hipError_t launch_split_bf16_t(const Geometry& geo, const SplitPlan& p, c
       part, dpart, (__bf16*)Wop, p.chunks1, AT);
   const long long g2 = geo.slices * p.chunks2;
   pass2_bf16<D, AT><<<dim3((unsigned)g2), dim3(kPass2Waves * kWave), 0, stream>>>(
-      (const __bf16*)Q, (const __bf16*)U, (const u32x4*)Wop, (__bf16*)H, geo.h, geo.n, geo.m,
-      p.chunks2, p.chunk_len2, geo.c2);
+      (const __bf16*)Q, (const __bf16*)U, (const u32x4*)Wop, (__bf16*)H, geo.vw.q, geo.vw.o,
+      geo.h, geo.n, geo.m, p.chunks2, p.chunk_len2, geo.c2);
   return hipGetLastError();
 }
 

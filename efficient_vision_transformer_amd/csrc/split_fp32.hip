@@ -19,8 +19,8 @@ template <int D, int AT, int NA>
 __global__ __launch_bounds__(kPass1Waves * kWave, 2)
 void pass1_fp32(const float* __restrict__ Q, const float* __restrict__ U,
                 const float* __restrict__ V, float* __restrict__ part,
-                float* __restrict__ dpart, int h, int n, int m, int chunks, int chunk_len,
-                float c2) {
+                float* __restrict__ dpart, View qw, View vw, int h, int n, int m, int chunks,
+                int chunk_len, float c2) {
   constexpr int NW = kPass1Waves, ND = NW / NA, DT = D / 16, KQ = D / 16;
   constexpr int J = AT / NA, DTW = DT / ND, VS = D + 4;
   static_assert(AT % NA == 0 && DT % ND == 0, "wave split must tile the anchors and dims");
@@ -30,7 +30,7 @@ void pass1_fp32(const float* __restrict__ Q, const float* __restrict__ U,
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int ag = w % NA, dg = w / NA;
-  const size_t base = (size_t)slice * (size_t)n * D;
+  const size_t qb = view_base(qw, slice, h), vb = view_base(vw, slice, h);
   const int t_begin = chunk * chunk_len;
   const int t_end = min(n, t_begin + chunk_len);
 
@@ -66,11 +66,12 @@ void pass1_fp32(const float* __restrict__ Q, const float* __restrict__ U,
       for (int tt = 0; tt < 2; ++tt) {
         const int row = p0 + 16 * tt + c;
         const bool ok = row < t_end;
-        const size_t off = base + (size_t)(ok ? row : 0) * D + (D / 4) * g;
+        const size_t qo = qb + view_row(qw, ok ? row : 0) + (D / 4) * g;
+        const size_t vo = vb + view_row(vw, ok ? row : 0) + (D / 4) * g;
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq) {
-          const f32x4 qv = ok ? *(const f32x4*)(Q + off + 4 * kq) : zero4();
-          const f32x4 vv = ok ? *(const f32x4*)(V + off + 4 * kq) : zero4();
+          const f32x4 qv = ok ? *(const f32x4*)(Q + qo + 4 * kq) : zero4();
+          const f32x4 vv = ok ? *(const f32x4*)(V + vo + 4 * kq) : zero4();
           q_lds[w][tt][kq][lane] = qv;
           *(f32x4*)&v_lds[w][16 * tt + c][(D / 4) * g + 4 * kq] = vv;
         }
@@ -254,15 +255,15 @@ constexpr int pass2_fp32_waves() { return AT * D * 128 > 80 * 1024 ? 8 : kPass2W
 template <int D, int AT>
 __global__ __launch_bounds__((pass2_fp32_waves<D, AT>() * kWave))
 void pass2_fp32(const float* __restrict__ Q, const float* __restrict__ U,
-                const float* __restrict__ Wop, float* __restrict__ H, int h, int n, int m,
-                int chunks, int chunk_len, float c2) {
+                const float* __restrict__ Wop, float* __restrict__ H, View qw, View ow, int h,
+                int n, int m, int chunks, int chunk_len, float c2) {
   constexpr int NW = pass2_fp32_waves<D, AT>(), DT = D / 16, KQ = D / 16;
   const int slice = blockIdx.x / chunks;
   const int chunk = blockIdx.x - slice * chunks;
   const int head = slice % h;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const size_t base = (size_t)slice * (size_t)n * D;
+  const size_t qb = view_base(qw, slice, h), ob = view_base(ow, slice, h);
   const int t_begin = chunk * chunk_len;
   const int t_end = min(n, t_begin + chunk_len);
 
@@ -285,7 +286,7 @@ void pass2_fp32(const float* __restrict__ Q, const float* __restrict__ U,
   // Software pipeline: the next tile's Q rows are requested before this tile is computed.
   // Rows past the chunk read the slice's last row (clamped) and are not stored.
   auto load_q = [&](int t0, f32x4* q) {
-    const size_t off = base + (size_t)min(t0 + c, n - 1) * D + (D / 4) * g;
+    const size_t off = qb + view_row(qw, min(t0 + c, n - 1)) + (D / 4) * g;
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq) q[kq] = __builtin_nontemporal_load((const f32x4*)(Q + off + 4 * kq));
   };
@@ -344,7 +345,7 @@ void pass2_fp32(const float* __restrict__ Q, const float* __restrict__ U,
       }
     }
     if (ok) {
-      float* dst = H + base + (size_t)row * D + (D / 4) * g;
+      float* dst = H + ob + view_row(ow, row) + (D / 4) * g;
 #pragma unroll
       for (int dt2 = 0; dt2 < DT; ++dt2) __builtin_nontemporal_store(hacc[dt2], (f32x4*)(dst + 4 * dt2));
     }
@@ -366,14 +367,14 @@ static hipError_t launch_split_fp32_t(const Geometry& geo, const SplitPlan& p, c
   float* Wop = (float*)(wsb + p.part_bytes + p.dpart_bytes);
   const long long g1 = geo.slices * p.chunks1;
   pass1_fp32<D, AT, NA><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, stream>>>(
-      (const float*)Q, (const float*)U, (const float*)V, part, dpart, geo.h, geo.n, geo.m,
-      p.chunks1, p.chunk_len1, geo.c2);
+      (const float*)Q, (const float*)U, (const float*)V, part, dpart, geo.vw.q, geo.vw.v, geo.h,
+      geo.n, geo.m, p.chunks1, p.chunk_len1, geo.c2);
   finalize_fp32<D><<<dim3((unsigned)(geo.slices * AT)), dim3(256), 0, stream>>>(
       part, dpart, Wop, p.chunks1, AT);
   const long long g2 = geo.slices * p.chunks2;
   pass2_fp32<D, AT><<<dim3((unsigned)g2), dim3(pass2_fp32_waves<D, AT>() * kWave), 0, stream>>>(
-      (const float*)Q, (const float*)U, Wop, (float*)H, geo.h, geo.n, geo.m, p.chunks2,
-      p.chunk_len2, geo.c2);
+      (const float*)Q, (const float*)U, Wop, (float*)H, geo.vw.q, geo.vw.o, geo.h, geo.n, geo.m,
+      p.chunks2, p.chunk_len2, geo.c2);
   return hipGetLastError();
 }
 

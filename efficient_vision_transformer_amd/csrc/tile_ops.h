@@ -134,14 +134,15 @@ __device__ __forceinline__ void accumulate_tiles(const __bf16* a_lds, const __bf
 }
 
 // Loads rows of Q or V in operand layout (lane (c,g): dims 8*KS*g ..), streaming (each
-// byte is read once, so the loads are marked non-temporal).  Rows past the
+// byte is read once, so the loads are marked non-temporal).  Row r starts at element
+// base + r * st.  Rows past the
 // slice's end read its last row instead; their softmax weights are zeroed, so they add
 // nothing (and a non-finite value there belongs to the same slice anyway).
 template <int D>
-__device__ __forceinline__ void load_rows(const __bf16* __restrict__ X, size_t base, int row, int n,
-                                          int g, u32x4* out) {
+__device__ __forceinline__ void load_rows(const __bf16* __restrict__ X, size_t base, long long st,
+                                          int row, int n, int g, u32x4* out) {
   constexpr int KS = D / 32;
-  const size_t off = base + (size_t)min(row, n - 1) * D + 8 * KS * g;
+  const size_t off = base + (size_t)((long long)min(row, n - 1) * st) + 8 * KS * g;
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) out[kk] = __builtin_nontemporal_load((const u32x4*)(X + off + 8 * kk));
 }
@@ -150,9 +151,9 @@ __device__ __forceinline__ void load_rows(const __bf16* __restrict__ X, size_t b
 // chunk kk: each load instruction reads one contiguous 64-byte run per row (a whole row
 // when d = 32).  Rows past the slice's end read its last row, as in load_rows.
 template <int D, int DW>
-__device__ __forceinline__ void load_rows_c(const __bf16* __restrict__ X, size_t base, int row,
-                                            int n, int g, int d0, u32x4* out) {
-  const size_t off = base + (size_t)min(row, n - 1) * D + d0 + 8 * g;
+__device__ __forceinline__ void load_rows_c(const __bf16* __restrict__ X, size_t base, long long st,
+                                            int row, int n, int g, int d0, u32x4* out) {
+  const size_t off = base + (size_t)((long long)min(row, n - 1) * st) + d0 + 8 * g;
 #pragma unroll
   for (int kk = 0; kk < DW / 32; ++kk)
     out[kk] = __builtin_nontemporal_load((const u32x4*)(X + off + 32 * kk));

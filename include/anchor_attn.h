@@ -87,6 +87,27 @@ anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx,
                                          int B, int h, int n, int m, int d,
                                          anchor_attn_dtype_t dtype, void* stream);
 
+/* The same forward on strided views, so that Q and V can be read where a fused projection
+ * left them (for example the two halves of a packed [B, n, 2, h, d] or [B, n, 3, h, d]
+ * tensor) and H written straight into a [B, n, h, d] layout for the output projection
+ * (the block around the attention: Pith verdict page, supporting citations of the DeiT /
+ * LeViT backbones the layer is dropped into).
+ *   q_strides, v_strides, h_strides: host arrays of three element strides (batch, head,
+ *     token) of the [B, h, n, d] views of Q, V and H; the d values of a token are
+ *     contiguous.  NULL means the contiguous layout (h*n*d, n*d, d).
+ * Each stride must be >= 0 and a multiple of 16 bytes, and the base pointers 16-byte
+ * aligned; distinct rows of H must not share an element, and H's span (first to last
+ * element) must not overlap the spans of Q, V or U.  Otherwise INVALID_VALUE.  Inputs may
+ * alias each other.  Everything else as anchor_attn_forward, which is this call with
+ * three NULL stride arrays. */
+anchor_attn_status_t anchor_attn_forward_strided(anchor_attn_ctx* ctx,
+                                                 const void* Q, const long long* q_strides,
+                                                 const void* U,
+                                                 const void* V, const long long* v_strides,
+                                                 void* H, const long long* h_strides,
+                                                 int B, int h, int n, int m, int d,
+                                                 anchor_attn_dtype_t dtype, void* stream);
+
 /* Enqueues the gradients of the forward above for a loss L with dL/dH = dH (AnchorFormer
  * abstract: the anchors are learnable, so the layer is trained through; the Pith verdict
  * page's Eq. (11) in the Eq. (12) order is the function differentiated), on `stream`,
