@@ -180,3 +180,48 @@ def make_upstream_grad(x: Inputs, seed: int) -> tuple[np.ndarray, np.ndarray | N
     rng = np.random.default_rng(seed)
     g = rng.standard_normal(x.Q.shape, dtype=np.float32)
     return _store(g, x.workload.dtype)
+
+
+@dataclass
+class BlockInputs:
+    """Inputs of the attention block around the layer; float32 stored values plus bf16
+    bit patterns (name -> uint16 array) for bf16."""
+    B: int
+    n: int
+    h: int
+    m: int
+    d: int
+    dtype: str
+    X: np.ndarray
+    Wqv: np.ndarray
+    bqv: np.ndarray
+    U: np.ndarray
+    Wo: np.ndarray
+    bo: np.ndarray
+    bits: dict = field(default_factory=dict)
+
+
+def make_block_inputs(B: int, n: int, h: int, m: int, d: int, seed: int,
+                      dtype: str = "bf16") -> BlockInputs:
+    """Seeded block inputs (numpy PCG64 ``default_rng(seed)``, drawn in this order):
+    X [B, n, C] ~ N(0, 1); Wqv [C, 2C] ~ N(0, 1/C) (so Q and V entries have unit
+    variance); bqv [2C] ~ N(0, 0.1^2); U [h, m, d] ~ N(0, 1); Wo [C, C] ~ N(0, 1/C);
+    bo [C] ~ N(0, 0.1^2); each rounded once to the storage dtype."""
+    rng = np.random.default_rng(seed)
+    C = h * d
+    sc = np.float32(1.0 / np.sqrt(C))
+    raw = {
+        "X": rng.standard_normal((B, n, C), dtype=np.float32),
+        "Wqv": rng.standard_normal((C, 2 * C), dtype=np.float32) * sc,
+        "bqv": rng.standard_normal((2 * C,), dtype=np.float32) * np.float32(0.1),
+        "U": rng.standard_normal((h, m, d), dtype=np.float32),
+        "Wo": rng.standard_normal((C, C), dtype=np.float32) * sc,
+        "bo": rng.standard_normal((C,), dtype=np.float32) * np.float32(0.1),
+    }
+    vals, bits = {}, {}
+    for k, a in raw.items():
+        v, b = _store(a, dtype)
+        vals[k] = v
+        if b is not None:
+            bits[k] = b
+    return BlockInputs(B=B, n=n, h=h, m=m, d=d, dtype=dtype, bits=bits, **vals)

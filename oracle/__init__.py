@@ -16,6 +16,10 @@ anchor_slice(q, u, v)               -- one slice, returns (A, delta, W, H)
 anchor_bruteforce(q, u, v)          -- one slice via the bipartite chain F = D^-1 G, F^2;
                                        returns (S_t, H)
 full_attention_slice(q, k, v, rows) -- report-only softmax(QK^T/sqrt(d))V for chosen rows
+anchor_backward(Q, U, V, G)         -- dQ, dU (summed over the batch), dV for dL/dH = G
+anchor_block_forward(X, Wqv, bqv, U, Wo, bo)
+                                    -- the attention block around the layer: numpy fp64
+                                       projections (a library primitive) around anchor_attn
 """
 from __future__ import annotations
 
@@ -164,3 +168,28 @@ def full_attention_slice(q, k, v, rows=None) -> np.ndarray:
     _check(_load().oracle_full_attn_slice_f64(_p(q), _p(k), _p(v), n, d, rp, nrows, _p(out)),
            "full_attention_slice")
     return out
+
+
+def anchor_block_forward(X, Wqv, bqv, U, Wo, bo) -> np.ndarray:
+    """The attention block in which the layer replaces a ViT block's self-attention
+    (AnchorFormer as a drop-in attention module in DeiT / LeViT backbones, Pith verdict
+    page; the pages print no projections, so the plain multi-head reading): for X
+    [B, n, C] with C = h*d,
+        [Q | V] = X Wqv + bqv       (head j: columns j*d .. j*d + d - 1 of each half)
+        H = anchor_attn per (batch, head) with U [h, m, d]
+        Y = H Wo + bo               (H's columns head-major, as Q's)
+    bqv or bo may be None.  fp64; the matrix products are numpy's."""
+    X, Wqv, U, Wo = _f64(X), _f64(Wqv), _f64(U), _f64(Wo)
+    B, n, C = X.shape
+    h, m, d = U.shape
+    assert h * d == C and Wqv.shape == (C, 2 * C) and Wo.shape == (C, C)
+    QV = X @ Wqv
+    if bqv is not None:
+        QV = QV + _f64(bqv)
+    Q = QV[..., :C].reshape(B, n, h, d).transpose(0, 2, 1, 3)
+    V = QV[..., C:].reshape(B, n, h, d).transpose(0, 2, 1, 3)
+    H = anchor_attn(np.ascontiguousarray(Q), U, np.ascontiguousarray(V))
+    Y = H.transpose(0, 2, 1, 3).reshape(B, n, C) @ Wo
+    if bo is not None:
+        Y = Y + _f64(bo)
+    return Y
