@@ -1,11 +1,13 @@
 """Anchor-attention throughput on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--plan auto|fused|split]
-                [--pass forward|backward] [--no-cpu-baseline]
+                [--pass forward|backward|block] [--no-cpu-baseline]
 
 One step = one forward of the whole hot path (logits, softmax, column sums and A^T V,
 normalisation, H = A W) over one batch of the workload; with --pass backward, one
-backward (dQ, dU, dV for a given dL/dH) instead.  Inputs are resident in HBM:
+backward (dQ, dU, dV for a given dL/dH) instead; with --pass block, one attention block
+(Q|V projection, the layer on the projection in place, output projection) with the
+workload's B, n, h, m, d.  Inputs are resident in HBM:
 R copies of the batch (R * bytes >= 1 GiB, well beyond the 256 MB Infinity Cache) are
 cycled so every step reads cold HBM.  K steps are bracketed by events on the launch
 stream.  Prints one JSON line.
@@ -59,7 +61,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--plan", default="auto", choices=["auto", "fused", "split"])
-    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"])
+    ap.add_argument("--pass", dest="which", default="forward",
+                    choices=["forward", "backward", "block"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -187,6 +190,88 @@ def bench_backward(args, ctx, x, dev, plan_desc) -> dict:
     return out
 
 
+def block_bytes_flops(w) -> tuple[int, int]:
+    """Algorithmic bytes and flops of one attention block (C = h*d, T = B*n tokens): X
+    read, [Q|V] written and read, H written and read, Y written, the weights and biases
+    read once; flops of the two projections (2*T*C*2C and 2*T*C*C) plus the layer."""
+    C, T, es = w.h * w.d, w.B * w.n, w.elem_bytes
+    act = T * C * es
+    return (act + 2 * 2 * act + 2 * act + act + (3 * C * C + 3 * C + w.h * w.m * w.d) * es,
+            6 * T * C * C + w.algorithmic_flops())
+
+
+def cpu_baseline_block(x, seconds: float) -> dict:
+    """The fp64 oracle's block as it stands, timed like cpu_baseline."""
+    import oracle
+    cores = oracle.default_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.anchor_block_forward(x.X, x.Wqv, x.bqv, x.U, x.Wo, x.bo)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": reps * x.B * x.n / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} full block(s) (B={x.B} n={x.n} h={x.h} m={x.m} d={x.d}) in fp64 "
+                      f"with numpy projections, {el:.1f} s wall"}
+
+
+def bench_block(args, ctx, w, dev) -> dict:
+    import numpy as np
+    import torch
+    from efficient_vision_transformer_amd.inputs import make_block_inputs
+    if w.dtype != "bf16":
+        raise SystemExit("the block runs in bf16 only")
+    x = make_block_inputs(w.B, w.n, w.h, w.m, w.d, seed=w.seed)
+    conv = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    t = {k: conv(v) for k, v in x.bits.items()}
+    algo_bytes, flops = block_bytes_flops(w)
+    act = w.B * w.n * w.h * w.d * 2
+    R = max(1, -(-ROTATE_BYTES // (2 * act)))
+    sets = [(t["X"], torch.empty_like(t["X"]))] + [(t["X"].clone(), torch.empty_like(t["X"]))
+                                                   for _ in range(R - 1)]
+    stream = torch.cuda.current_stream(dev)
+    step = lambda i: ctx.block_forward(sets[i % R][0], t["Wqv"], t["bqv"], t["U"], t["Wo"],
+                                       t["bo"], out=sets[i % R][1], stream=stream)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    hbm_bound = algo_bytes / (HBM_PEAK_GBS * 1e9) >= flops / (BF16_PEAK_TFLOPS * 1e12)
+    roof = ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(gbs / HBM_PEAK_GBS, 4)} if hbm_bound else
+            {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4)})
+    roof.update({"traffic": None,
+                 "kernel": "whole block (hipBLASLt projection, the layer, hipBLASLt projection)",
+                 "per_launch": {"algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
+                                "avg_duration_us": round(ms * 1e3, 3)}})
+    out = {
+        "metric": f"anchor-attention block tokens/sec ({w.name} shape, C={w.h * w.d})",
+        "value": round(w.B * w.n / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "block", "B": w.B, "n": w.n, "h": w.h, "m": w.m,
+                   "d": w.d, "C": w.h * w.d, "global_batch": w.B, "seq_len": w.n,
+                   "parallelism": "single-gpu", "rotating_sets": R},
+        "achieved_hbm_gbs": round(gbs, 1), "achieved_tflops": round(tflops, 3),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_block(x, args.cpu_seconds)
+    return out
+
+
 def full_attention_gap(x, H, slices=4) -> dict:
     """Report-only: relative Frobenius gap between softmax(QK^T/sqrt(d))V and H on a few
     slices (inputs exactly as stored)."""
@@ -254,6 +339,11 @@ def main():
     x = make_inputs(w, with_k=True)
     ctx = AnchorAttention(dev, plan=args.plan)
     plan_desc = ctx.describe(w.B, w.h, w.n, w.m, w.d, w.dtype)
+    if args.which == "block":
+        out = bench_block(args, ctx, w, dev)
+        ctx.close()
+        print(json.dumps(out), flush=True)
+        return
     if args.which == "backward":
         out = bench_backward(args, ctx, x, dev, plan_desc)
         ctx.close()

@@ -44,6 +44,8 @@ def load_library():
         llp = ctypes.POINTER(ctypes.c_longlong)
         lib.anchor_attn_forward_strided.argtypes = [vp, vp, llp, vp, vp, llp, vp, llp,
                                                     i32, i32, i32, i32, i32, i32, vp]
+        lib.anchor_attn_block_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                                  i32, i32, i32, i32, i32, i32, vp]
         lib.anchor_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                              i32, i32, i32, i32, i32, i32, vp]
         lib.anchor_attn_set_plan.argtypes = [vp, i32]
@@ -52,7 +54,8 @@ def load_library():
         lib.anchor_attn_status_string.argtypes = [i32]
         lib.anchor_attn_status_string.restype = ctypes.c_char_p
         for f in (lib.anchor_attn_create, lib.anchor_attn_destroy, lib.anchor_attn_forward,
-                  lib.anchor_attn_forward_strided, lib.anchor_attn_backward, lib.anchor_attn_set_plan,
+                  lib.anchor_attn_forward_strided, lib.anchor_attn_block_forward,
+                  lib.anchor_attn_backward, lib.anchor_attn_set_plan,
                   lib.anchor_attn_describe_plan):
             f.restype = i32
         _lib = lib
@@ -150,6 +153,42 @@ class AnchorAttention:
         return out
 
     __call__ = forward
+
+    def block_forward(self, X, Wqv, bqv, U, Wo, bo, out=None, stream=None):
+        """The attention block: Y = anchor_attention(X Wqv + bqv split into Q | V) Wo + bo.
+        X [B, n, C] (C = h*d), Wqv [C, 2C], bqv [2C] or None, U [h, m, d], Wo [C, C],
+        bo [C] or None; bf16, contiguous, on this device.  Returns Y [B, n, C] (``out`` if
+        given)."""
+        import torch
+        if X.dim() != 3 or U.dim() != 3:
+            raise ValueError(f"bad shapes X{tuple(X.shape)} U{tuple(U.shape)}")
+        B, n, C = X.shape
+        h, m, d = U.shape
+        if h * d != C or Wqv.shape != (C, 2 * C) or Wo.shape != (C, C):
+            raise ValueError(f"need C = h*d and Wqv [C, 2C], Wo [C, C]: X{tuple(X.shape)} "
+                             f"U{tuple(U.shape)} Wqv{tuple(Wqv.shape)} Wo{tuple(Wo.shape)}")
+        if bqv is not None and bqv.shape != (2 * C,):
+            raise ValueError("bqv must be [2C]")
+        if bo is not None and bo.shape != (C,):
+            raise ValueError("bo must be [C]")
+        for name, t in (("X", X), ("Wqv", Wqv), ("bqv", bqv), ("U", U), ("Wo", Wo), ("bo", bo)):
+            if t is None:
+                continue
+            if not t.is_cuda or t.device != self.device or not t.is_contiguous() or t.dtype != X.dtype:
+                raise ValueError(f"{name} must be a contiguous {X.dtype} tensor on {self.device}")
+        if out is None:
+            out = torch.empty_like(X)
+        elif out.shape != X.shape or out.dtype != X.dtype or not out.is_contiguous() \
+                or out.device != self.device:
+            raise ValueError("out must be a contiguous tensor like X")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        ptr = lambda t: None if t is None else t.data_ptr()
+        _check(self._lib.anchor_attn_block_forward(
+            self._h, X.data_ptr(), Wqv.data_ptr(), ptr(bqv), U.data_ptr(), Wo.data_ptr(),
+            ptr(bo), out.data_ptr(), B, n, h, m, d, _dtype_code(X),
+            ctypes.c_void_p(stream.cuda_stream)), "anchor_attn_block_forward")
+        return out
 
     def backward(self, Q, U, V, dH, out=None, stream=None):
         """Gradients for dL/dH = dH: returns (dQ [B,h,n,d], dU [h,m,d] summed over the

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libanchor_attn.so")
 SOURCES = ["anchor_attn_api.cpp", "split_bf16.hip", "split_fp32.hip", "fused_bf16.hip",
-           "backward_bf16.hip", "backward_fused_bf16.hip"]
+           "backward_bf16.hip", "backward_fused_bf16.hip", "block_gemm.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
@@ -42,7 +42,8 @@ def build() -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
+           "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, OUT)
     return OUT

@@ -18,9 +18,12 @@
 struct anchor_attn_ctx {
   int device = 0;
   int num_cus = 256;
-  void* workspace = nullptr;
+  void* workspace = nullptr;        // split plan and backward partials
   size_t workspace_bytes = 0;
   anchor_attn_plan_t plan = ANCHOR_ATTN_PLAN_AUTO;
+  aa::GemmCache* gemm = nullptr;    // block projections (created on first use)
+  void* block_ws = nullptr;         // block: projected Q|V, H and the GEMM workspace
+  size_t block_ws_bytes = 0;
 };
 
 namespace {
@@ -182,6 +185,42 @@ anchor_attn_status_t ensure_workspace(anchor_attn_ctx* ctx, size_t bytes) {
   return ANCHOR_ATTN_SUCCESS;
 }
 
+// Everything a forward of geometry g needs before it can be enqueued without failing: a
+// plan, and the split plan's workspace.  Call with the device current.
+anchor_attn_status_t prepare_forward(anchor_attn_ctx* ctx, const Geometry& g,
+                                     anchor_attn_dtype_t dtype) {
+  FusedPlan fp{};
+  const Chosen c = choose(ctx, g, dtype, &fp);
+  if (c == Chosen::Unsupported) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  if (c == Chosen::Split) return ensure_workspace(ctx, make_split_plan(g, dtype, ctx->num_cus).workspace_bytes());
+  return ANCHOR_ATTN_SUCCESS;
+}
+
+// Enqueues the forward (after prepare_forward succeeded for g).
+anchor_attn_status_t run_forward(anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t dtype,
+                                 const void* Q, const void* U, const void* V, void* H,
+                                 hipStream_t s) {
+  FusedPlan fp{};
+  const Chosen c = choose(ctx, g, dtype, &fp);
+  hipError_t e;
+  if (c == Chosen::Fused) {
+    e = aa::launch_fused_bf16(g, fp, Q, U, V, H, s);
+  } else if (c == Chosen::Split) {
+    const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
+    if (ctx->workspace_bytes < p.workspace_bytes()) return ANCHOR_ATTN_ERROR_OUT_OF_MEMORY;
+    e = (dtype == ANCHOR_ATTN_BF16) ? aa::launch_split_bf16(g, p, Q, U, V, H, ctx->workspace, s)
+                                    : aa::launch_split_fp32(g, p, Q, U, V, H, ctx->workspace, s);
+  } else {
+    return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  }
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return ANCHOR_ATTN_ERROR_HIP;
+  }
+  return ANCHOR_ATTN_SUCCESS;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -225,9 +264,11 @@ anchor_attn_status_t anchor_attn_create(anchor_attn_ctx** out) {
 anchor_attn_status_t anchor_attn_destroy(anchor_attn_ctx* ctx) {
   if (!ctx) return ANCHOR_ATTN_SUCCESS;
   anchor_attn_status_t st = ANCHOR_ATTN_SUCCESS;
-  if (ctx->workspace) {
+  if (ctx->workspace || ctx->block_ws || ctx->gemm) {
     DeviceGuard guard(ctx->device);
-    if (hipFree(ctx->workspace) != hipSuccess) st = ANCHOR_ATTN_ERROR_HIP;
+    if (ctx->workspace && hipFree(ctx->workspace) != hipSuccess) st = ANCHOR_ATTN_ERROR_HIP;
+    if (ctx->block_ws && hipFree(ctx->block_ws) != hipSuccess) st = ANCHOR_ATTN_ERROR_HIP;
+    aa::gemm_cache_destroy(ctx->gemm);
   }
   delete ctx;
   return st;
@@ -309,29 +350,11 @@ anchor_attn_status_t anchor_attn_forward_strided(anchor_attn_ctx* ctx, const voi
     if (overlaps(H, hx, Q, qx) || overlaps(H, hx, V, vx) || overlaps(H, hx, U, ub))
       return ANCHOR_ATTN_ERROR_INVALID_VALUE;
 
-    FusedPlan fp{};
-    const Chosen c = choose(ctx, g, dtype, &fp);
-    if (c == Chosen::Unsupported) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
-
     DeviceGuard guard(ctx->device);
     if (!guard.ok) return ANCHOR_ATTN_ERROR_HIP;
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e;
-    if (c == Chosen::Fused) {
-      e = aa::launch_fused_bf16(g, fp, Q, U, V, H, s);
-    } else {
-      const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
-      st = ensure_workspace(ctx, p.workspace_bytes());
-      if (st != ANCHOR_ATTN_SUCCESS) return st;
-      e = (dtype == ANCHOR_ATTN_BF16)
-              ? aa::launch_split_bf16(g, p, Q, U, V, H, ctx->workspace, s)
-              : aa::launch_split_fp32(g, p, Q, U, V, H, ctx->workspace, s);
-    }
-    if (e != hipSuccess) {
-      (void)hipGetLastError();
-      return ANCHOR_ATTN_ERROR_HIP;
-    }
-    return ANCHOR_ATTN_SUCCESS;
+    st = prepare_forward(ctx, g, dtype);
+    if (st != ANCHOR_ATTN_SUCCESS) return st;
+    return run_forward(ctx, g, dtype, Q, U, V, H, (hipStream_t)stream);
   } catch (...) {
     return ANCHOR_ATTN_ERROR_HIP;
   }
@@ -342,6 +365,84 @@ anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx, const void* Q, co
                                          int d, anchor_attn_dtype_t dtype, void* stream) {
   return anchor_attn_forward_strided(ctx, Q, nullptr, U, V, nullptr, H, nullptr, B, h, n, m, d,
                                      dtype, stream);
+}
+
+anchor_attn_status_t anchor_attn_block_forward(anchor_attn_ctx* ctx, const void* X, const void* Wqv,
+                                               const void* bqv, const void* U, const void* Wo,
+                                               const void* bo, void* Y, int B, int n, int h,
+                                               int m, int d, anchor_attn_dtype_t dtype,
+                                               void* stream) {
+  if (!ctx) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+  try {
+    Geometry g{};
+    bool empty = false;
+    anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype, &g, &empty);
+    if (st != ANCHOR_ATTN_SUCCESS) return st;
+    if (dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+    const long long C = (long long)h * d, T = (long long)B * n;
+    if (2 * C > (1LL << 30) || T > (1LL << 31)) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+    if (empty) return ANCHOR_ATTN_SUCCESS;   // no tokens, or C = 0: Y is empty
+    if (!X || !Wqv || !U || !Wo || !Y) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    const uintptr_t mis = ((uintptr_t)X | (uintptr_t)Wqv | (uintptr_t)bqv | (uintptr_t)U |
+                           (uintptr_t)Wo | (uintptr_t)bo | (uintptr_t)Y) & 15u;
+    if (mis) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    const size_t es = 2;
+    const size_t yb = (size_t)T * C * es;
+    const void* ins[6] = {X, Wqv, bqv, U, Wo, bo};
+    const size_t insz[6] = {(size_t)T * C * es, (size_t)C * 2 * C * es, (size_t)2 * C * es,
+                            (size_t)h * m * d * es, (size_t)C * C * es, (size_t)C * es};
+    for (int i = 0; i < 6; ++i)
+      if (ins[i] && overlaps(Y, yb, ins[i], insz[i])) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+
+    // The attention reads Q and V from the projection [T, 2C] (head j's dims at columns
+    // j*d .. and C + j*d ..) and writes H as [T, C] with the same head-major columns.
+    g.vw.q = aa::View{(long long)n * 2 * C, d, 2 * C};
+    g.vw.v = g.vw.q;
+    g.vw.o = aa::View{(long long)n * C, d, C};
+
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok) return ANCHOR_ATTN_ERROR_HIP;
+    if (!ctx->gemm && !(ctx->gemm = aa::gemm_cache_create())) return ANCHOR_ATTN_ERROR_HIP;
+    if (!aa::gemm_prepare(ctx->gemm, T, (int)C, (int)(2 * C), bqv != nullptr) ||
+        !aa::gemm_prepare(ctx->gemm, T, (int)C, (int)C, bo != nullptr))
+      return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+    st = prepare_forward(ctx, g, dtype);
+    if (st != ANCHOR_ATTN_SUCCESS) return st;
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t qvb = al((size_t)T * 2 * C * es), hb = al((size_t)T * C * es);
+    const size_t need = qvb + hb + aa::kGemmWorkspaceBytes;
+    if (need > ctx->block_ws_bytes) {
+      if (ctx->block_ws) {
+        if (hipFree(ctx->block_ws) != hipSuccess) return ANCHOR_ATTN_ERROR_HIP;
+        ctx->block_ws = nullptr;
+        ctx->block_ws_bytes = 0;
+      }
+      if (hipMalloc(&ctx->block_ws, need) != hipSuccess) {
+        (void)hipGetLastError();
+        ctx->block_ws = nullptr;
+        return ANCHOR_ATTN_ERROR_OUT_OF_MEMORY;
+      }
+      ctx->block_ws_bytes = need;
+    }
+    char* w = (char*)ctx->block_ws;
+    void* QV = w;
+    void* Hb = w + qvb;
+    void* gws = w + qvb + hb;
+    hipStream_t s = (hipStream_t)stream;
+    if (aa::gemm_run(ctx->gemm, X, Wqv, bqv, QV, T, (int)C, (int)(2 * C), gws, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return ANCHOR_ATTN_ERROR_HIP;
+    }
+    st = run_forward(ctx, g, dtype, QV, U, (const char*)QV + C * es, Hb, s);
+    if (st != ANCHOR_ATTN_SUCCESS) return st;
+    if (aa::gemm_run(ctx->gemm, Hb, Wo, bo, Y, T, (int)C, (int)C, gws, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return ANCHOR_ATTN_ERROR_HIP;
+    }
+    return ANCHOR_ATTN_SUCCESS;
+  } catch (...) {
+    return ANCHOR_ATTN_ERROR_HIP;
+  }
 }
 
 anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx, const void* Q, const void* U,

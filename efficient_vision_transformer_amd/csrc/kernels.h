@@ -82,6 +82,17 @@ bool bwd_fused_supported(const Geometry& g);
 hipError_t launch_backward_fused_bf16(const Geometry& g, const void* Q, const void* U,
                                       const void* V, const void* G, void* dQ, void* dU, void* dV,
                                       float* partU, hipStream_t stream);
+// Projections of the attention block (hipBLASLt): D[T, N] = X[T, K] W[K, N] + bias[N],
+// row-major bf16, fp32 accumulation; bias may be null.  gemm_prepare finds descriptors
+// and an algorithm for a shape (false: none), gemm_run enqueues with a workspace of
+// kGemmWorkspaceBytes.
+constexpr size_t kGemmWorkspaceBytes = size_t(32) << 20;
+struct GemmCache;
+GemmCache* gemm_cache_create();
+void gemm_cache_destroy(GemmCache* c);
+bool gemm_prepare(GemmCache* c, long long T, int K, int N, bool bias);
+hipError_t gemm_run(GemmCache* c, const void* X, const void* W, const void* bias, void* D,
+                    long long T, int K, int N, void* ws, hipStream_t stream);
 hipError_t launch_split_fp32(const Geometry& g, const SplitPlan& p, const void* Q,
                              const void* U, const void* V, void* H, void* workspace,
                              hipStream_t stream);

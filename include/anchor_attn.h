@@ -108,7 +108,30 @@ anchor_attn_status_t anchor_attn_forward_strided(anchor_attn_ctx* ctx,
                                                  int B, int h, int n, int m, int d,
                                                  anchor_attn_dtype_t dtype, void* stream);
 
-/* Enqueues the gradients of the forward above for a loss L with dL/dH = dH (AnchorFormer
+/* The attention block around the layer, the way a ViT block's self-attention is replaced
+ * by it (Pith verdict page: AnchorFormer as a drop-in attention module in DeiT / LeViT
+ * backbones; the pages print no projections, so this is the plain reading): for tokens
+ * X [B, n, C] with C = h*d,
+ *   [Q | V] = X Wqv + bqv       Wqv [C, 2C], bqv [2C]; head j owns columns j*d .. j*d+d-1
+ *                               of Q and C + j*d .. of V (no key projection: the anchors
+ *                               U take the keys' place)
+ *   H       = anchor attention of every (batch, head) slice with U [h, m, d]
+ *   Y       = H Wo + bo         H [B, n, C] with head-major columns, Wo [C, C], bo [C]
+ * All row-major bf16 device arrays; fp32 accumulation; Q, V and H are rounded to bf16
+ * between the steps.  bqv and bo may be NULL (no bias).  The two projections run through
+ * hipBLASLt, the attention through the kernels of anchor_attn_forward_strided reading the
+ * projection in place.  The context keeps a second workspace for the projection, H and
+ * hipBLASLt (grown on demand; growth synchronizes).  Y must not overlap any input.
+ * Domain: dtype BF16 (else NOT_SUPPORTED); B, n, h >= 0 (no tokens: a no-op); m and d as
+ * anchor_attn_forward.  Argument errors: nothing is enqueued; a HIP error in a later step
+ * can leave the earlier steps enqueued. */
+anchor_attn_status_t anchor_attn_block_forward(anchor_attn_ctx* ctx,
+                                               const void* X, const void* Wqv, const void* bqv,
+                                               const void* U, const void* Wo, const void* bo,
+                                               void* Y, int B, int n, int h, int m, int d,
+                                               anchor_attn_dtype_t dtype, void* stream);
+
+/* Enqueues the gradients of anchor_attn_forward for a loss L with dL/dH = dH (AnchorFormer
  * abstract: the anchors are learnable, so the layer is trained through; the Pith verdict
  * page's Eq. (11) in the Eq. (12) order is the function differentiated), on `stream`,
  * without waiting:
