@@ -34,9 +34,10 @@ ROTATE_BYTES = 1 << 30
 MEASURED_TRAFFIC = {
     ("vit_s16_224", "fused"): {"sources": ["efficient_vision_transformer_amd/csrc/fused_bf16.hip",
                                            "efficient_vision_transformer_amd/csrc/tile_ops.h",
-                                           "efficient_vision_transformer_amd/csrc/device_common.h"],
-                               "sha": "d129ae9080ce8a72", "read_bytes": 19459756,
-                               "write_bytes": 11012922},
+                                           "efficient_vision_transformer_amd/csrc/device_common.h",
+                                           "efficient_vision_transformer_amd/csrc/kernels.h"],
+                               "sha": "bb7ba8c87f7d3eca", "read_bytes": 19474177,
+                               "write_bytes": 11032317},
 }
 
 

@@ -121,7 +121,9 @@ anchor_attn_status_t anchor_attn_forward_strided(anchor_attn_ctx* ctx,
  * between the steps.  bqv and bo may be NULL (no bias).  The two projections run through
  * hipBLASLt, the attention through the kernels of anchor_attn_forward_strided reading the
  * projection in place.  The context keeps a second workspace for the projection, H and
- * hipBLASLt (grown on demand; growth synchronizes).  Y must not overlap any input.
+ * hipBLASLt (grown on demand; growth synchronizes).  The first call of a new shape also
+ * times hipBLASLt's candidate algorithms on the call's own operands and synchronizes the
+ * stream; later calls of that shape only enqueue.  Y must not overlap any input.
  * Domain: dtype BF16 (else NOT_SUPPORTED); B, n, h >= 0 (no tokens: a no-op); m and d as
  * anchor_attn_forward.  Argument errors: nothing is enqueued; a HIP error in a later step
  * can leave the earlier steps enqueued. */
