@@ -20,6 +20,8 @@ anchor_backward(Q, U, V, G)         -- dQ, dU (summed over the batch), dV for dL
 anchor_block_forward(X, Wqv, bqv, U, Wo, bo)
                                     -- the attention block around the layer: numpy fp64
                                        projections (a library primitive) around anchor_attn
+relu_linear_attn(Q, K, V, cmin, qscale)
+                                    -- L2ViT's ReLU linear attention (numpy fp64)
 """
 from __future__ import annotations
 
@@ -193,3 +195,22 @@ def anchor_block_forward(X, Wqv, bqv, U, Wo, bo) -> np.ndarray:
     if bo is not None:
         Y = Y + _f64(bo)
     return Y
+
+
+def relu_linear_attn(Q, K, V, cmin: float = 100.0, qscale: float = 1.0) -> np.ndarray:
+    """ReLU kernel linear attention (L2ViT page, the decomposable kernel identity of its
+    Eq. (4) with phi = ReLU and the denominator clamped below at Cmin), per (batch, head)
+    slice of Q, K, V [B, h, n, d]:
+        S = phi(K)^T V (d x d),  z = phi(K)^T 1 (d),
+        out_i = phi(qscale * q_i) S / max(phi(qscale * q_i) . z, cmin).
+    qscale stands for 1/s, the page's learnable scale (initialised to sqrt(C)) read as a
+    divisor of the query-key products; for qscale > 0 it only moves the clamp.  fp64."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    assert Q.shape == K.shape == V.shape and Q.ndim == 4
+    phq = np.maximum(Q * float(qscale), 0.0)
+    phk = np.maximum(K, 0.0)
+    S = np.matmul(phk.transpose(0, 1, 3, 2), V)          # [B, h, d, d]
+    z = phk.sum(axis=2)                                   # [B, h, d]
+    num = np.matmul(phq, S)                               # [B, h, n, d]
+    den = np.einsum("bhnd,bhd->bhn", phq, z)
+    return num / np.maximum(den, float(cmin))[..., None]
