@@ -1,13 +1,14 @@
 """Anchor-attention throughput on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--plan auto|fused|split]
-                [--pass forward|backward|block] [--no-cpu-baseline]
+                [--pass forward|backward|block|linear] [--no-cpu-baseline]
 
 One step = one forward of the whole hot path (logits, softmax, column sums and A^T V,
 normalisation, H = A W) over one batch of the workload; with --pass backward, one
 backward (dQ, dU, dV for a given dL/dH) instead; with --pass block, one attention block
 (Q|V projection, the layer on the projection in place, output projection) with the
-workload's B, n, h, m, d.  Inputs are resident in HBM:
+workload's B, n, h, m, d; with --pass linear, the ReLU kernel linear attention (L2ViT
+page) on the workload's Q, K, V.  Inputs are resident in HBM:
 R copies of the batch (R * bytes >= 1 GiB, well beyond the 256 MB Infinity Cache) are
 cycled so every step reads cold HBM.  K steps are bracketed by events on the launch
 stream.  Prints one JSON line.
@@ -63,7 +64,7 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--plan", default="auto", choices=["auto", "fused", "split"])
     ap.add_argument("--pass", dest="which", default="forward",
-                    choices=["forward", "backward", "block"])
+                    choices=["forward", "backward", "block", "linear"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -273,6 +274,70 @@ def bench_block(args, ctx, w, dev) -> dict:
     return out
 
 
+def bench_linear(args, ctx, x, dev) -> dict:
+    import numpy as np
+    import torch
+    w = x.workload
+    if w.dtype != "bf16":
+        raise SystemExit("the linear attention runs in bf16 only")
+    conv = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    Q0, K0, V0 = conv(x.bits["Q"]), conv(x.bits["K"]), conv(x.bits["V"])
+    act = w.B * w.h * w.n * w.d * 2
+    algo_bytes, flops = 4 * act, 4 * w.B * w.h * w.n * w.d * w.d
+    R = max(1, -(-ROTATE_BYTES // algo_bytes))
+    sets = [(Q0, K0, V0, torch.empty_like(Q0))] + [
+        (Q0.clone(), K0.clone(), V0.clone(), torch.empty_like(Q0)) for _ in range(R - 1)]
+    stream = torch.cuda.current_stream(dev)
+    step = lambda i: ctx.relu_linear(*sets[i % R][:3], 100.0, 1.0, out=sets[i % R][3], stream=stream)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": f"ReLU linear attention tokens/sec ({w.name} shape)",
+        "value": round(w.B * w.n / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "linear", "B": w.B, "h": w.h, "n": w.n, "d": w.d,
+                   "cmin": 100.0, "global_batch": w.B, "seq_len": w.n,
+                   "parallelism": "single-gpu", "rotating_sets": R},
+        "achieved_hbm_gbs": round(gbs, 1),
+        "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "relu_linear_bf16 (the whole step is this one kernel)",
+                     "per_launch": {"algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
+                                    "avg_duration_us": round(ms * 1e3, 3)}},
+    }
+    ref = copy_reference(algo_bytes, min(args.steps, 200), min(args.warmup, 20))
+    ref["frac_of_copy"] = round(gbs / ref["gbs"], 4) if ref["gbs"] > 0 else None
+    out["copy_reference"] = ref
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_limits
+        reps, t0 = 0, time.perf_counter()
+        with threadpool_limits(limits=1):
+            while True:
+                oracle.relu_linear_attn(x.Q, x.K, x.V)
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= args.cpu_seconds:
+                    break
+        out["cpu_baseline"] = {"value": reps * w.B * w.n / el, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{reps} full batch(es) of {w.name} in fp64 numpy, {el:.1f} s wall"}
+    return out
+
+
 def full_attention_gap(x, H, slices=4) -> dict:
     """Report-only: relative Frobenius gap between softmax(QK^T/sqrt(d))V and H on a few
     slices (inputs exactly as stored)."""
@@ -340,6 +405,11 @@ def main():
     x = make_inputs(w, with_k=True)
     ctx = AnchorAttention(dev, plan=args.plan)
     plan_desc = ctx.describe(w.B, w.h, w.n, w.m, w.d, w.dtype)
+    if args.which == "linear":
+        out = bench_linear(args, ctx, x, dev)
+        ctx.close()
+        print(json.dumps(out), flush=True)
+        return
     if args.which == "block":
         out = bench_block(args, ctx, w, dev)
         ctx.close()

@@ -44,6 +44,9 @@ def load_library():
         llp = ctypes.POINTER(ctypes.c_longlong)
         lib.anchor_attn_forward_strided.argtypes = [vp, vp, llp, vp, vp, llp, vp, llp,
                                                     i32, i32, i32, i32, i32, i32, vp]
+        lib.anchor_attn_relu_linear_forward.argtypes = [vp, vp, llp, vp, llp, vp, llp, vp, llp,
+                                                        i32, i32, i32, i32, ctypes.c_float,
+                                                        ctypes.c_float, i32, vp]
         lib.anchor_attn_block_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                                   i32, i32, i32, i32, i32, i32, vp]
         lib.anchor_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
@@ -55,6 +58,7 @@ def load_library():
         lib.anchor_attn_status_string.restype = ctypes.c_char_p
         for f in (lib.anchor_attn_create, lib.anchor_attn_destroy, lib.anchor_attn_forward,
                   lib.anchor_attn_forward_strided, lib.anchor_attn_block_forward,
+                  lib.anchor_attn_relu_linear_forward,
                   lib.anchor_attn_backward, lib.anchor_attn_set_plan,
                   lib.anchor_attn_describe_plan):
             f.restype = i32
@@ -153,6 +157,36 @@ class AnchorAttention:
         return out
 
     __call__ = forward
+
+    def relu_linear(self, Q, K, V, cmin: float = 100.0, qscale: float = 1.0, out=None,
+                    stream=None):
+        """ReLU kernel linear attention: relu(qscale q_i) (relu(K)^T V) /
+        max(relu(qscale q_i) . relu(K)^T 1, cmin) per (batch, head) slice.  Q, K, V and
+        ``out`` are [B, h, n, d] bf16 tensors or views whose d values per token are
+        contiguous.  Returns out (a new contiguous tensor unless given)."""
+        import torch
+        if Q.dim() != 4 or K.shape != Q.shape or V.shape != Q.shape:
+            raise ValueError(f"bad shapes Q{tuple(Q.shape)} K{tuple(K.shape)} V{tuple(V.shape)}")
+        B, h, n, d = Q.shape
+        if out is None:
+            out = torch.empty(Q.shape, dtype=Q.dtype, device=Q.device)
+        elif out.shape != Q.shape or out.dtype != Q.dtype:
+            raise ValueError("out must be a tensor of Q's shape and dtype")
+        strides = []
+        for name, t in (("Q", Q), ("K", K), ("V", V), ("out", out)):
+            if not t.is_cuda or t.device != self.device or t.dtype != Q.dtype:
+                raise ValueError(f"{name} must be a {Q.dtype} tensor on {self.device}")
+            if t.stride(3) != 1 and d > 1:
+                raise ValueError(f"{name}: the d values of a token must be contiguous")
+            strides.append((ctypes.c_longlong * 3)(t.stride(0), t.stride(1), t.stride(2)))
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        _check(self._lib.anchor_attn_relu_linear_forward(
+            self._h, Q.data_ptr(), strides[0], K.data_ptr(), strides[1], V.data_ptr(),
+            strides[2], out.data_ptr(), strides[3], B, h, n, d, float(cmin), float(qscale),
+            _dtype_code(Q), ctypes.c_void_p(stream.cuda_stream)),
+            "anchor_attn_relu_linear_forward")
+        return out
 
     def block_forward(self, X, Wqv, bqv, U, Wo, bo, out=None, stream=None):
         """The attention block: Y = anchor_attention(X Wqv + bqv split into Q | V) Wo + bo.

@@ -139,6 +139,29 @@ SplitPlan make_split_plan(const Geometry& g, anchor_attn_dtype_t dtype, int num_
 
 enum class Chosen { Fused, Split, Unsupported };
 
+// Linear attention split plan: chunks of whole 128-token blocks (four waves x one
+// 32-token pair), about two pass-1 and four pass-2 workgroups per CU.
+aa::LinearSplitPlan make_linear_plan(const Geometry& g, int num_cus) {
+  aa::LinearSplitPlan p{};
+  const int n = g.n, blk = 128;
+  auto chunking = [&](long long want, int* chunks, int* len) {
+    const int maxc = (n + blk - 1) / blk;
+    const int c = (int)std::min<long long>(maxc, std::max<long long>(1, (want + g.slices - 1) / g.slices));
+    int l = (n + c - 1) / c;
+    l = (l + blk - 1) / blk * blk;
+    *len = l;
+    *chunks = (n + l - 1) / l;
+  };
+  chunking(2LL * num_cus, &p.chunks1, &p.chunk_len1);
+  chunking(4LL * num_cus, &p.chunks2, &p.chunk_len2);
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  p.part_bytes = al((size_t)g.slices * p.chunks1 * g.d * g.d * sizeof(float));
+  p.zpart_bytes = al((size_t)g.slices * p.chunks1 * g.d * sizeof(float));
+  p.sop_bytes = al((size_t)g.slices * g.d * g.d * 2);
+  p.z_bytes = al((size_t)g.slices * g.d * sizeof(float));
+  return p;
+}
+
 Chosen choose(const anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t dtype,
               FusedPlan* fp) {
   const bool fused_ok = (dtype == ANCHOR_ATTN_BF16) && aa::fused_supported(g, ctx->num_cus, fp);
@@ -436,6 +459,62 @@ anchor_attn_status_t anchor_attn_block_forward(anchor_attn_ctx* ctx, const void*
     st = run_forward(ctx, g, dtype, QV, U, (const char*)QV + C * es, Hb, s);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
     if (aa::gemm_run(ctx->gemm, Hb, Wo, bo, Y, T, (int)C, (int)C, gws, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return ANCHOR_ATTN_ERROR_HIP;
+    }
+    return ANCHOR_ATTN_SUCCESS;
+  } catch (...) {
+    return ANCHOR_ATTN_ERROR_HIP;
+  }
+}
+
+anchor_attn_status_t anchor_attn_relu_linear_forward(
+    anchor_attn_ctx* ctx, const void* Q, const long long* q_strides, const void* K,
+    const long long* k_strides, const void* V, const long long* v_strides, void* O,
+    const long long* o_strides, int B, int h, int n, int d, float cmin, float qscale,
+    anchor_attn_dtype_t dtype, void* stream) {
+  if (!ctx) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+  try {
+    Geometry g{};
+    bool empty = false;
+    anchor_attn_status_t st = check_shape(B, h, n, 1, d, dtype, &g, &empty);
+    if (st != ANCHOR_ATTN_SUCCESS) return st;
+    if (!(cmin > 0.f) || !std::isfinite(cmin) || !(qscale > 0.f) || !std::isfinite(qscale))
+      return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    if (dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+    const size_t es = 2;
+    aa::View qw = g.vw.q, kw = g.vw.q, vw = g.vw.q, ow = g.vw.q;
+    if (!take_view(q_strides, es, &qw) || !take_view(k_strides, es, &kw) ||
+        !take_view(v_strides, es, &vw) || !take_view(o_strides, es, &ow))
+      return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    if (empty) return ANCHOR_ATTN_SUCCESS;
+    if (!Q || !K || !V || !O) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15u)
+      return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    if (!view_injective(ow, B, h, n, d)) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    const size_t ox = view_extent(ow, B, h, n, d, es);
+    if (overlaps(O, ox, Q, view_extent(qw, B, h, n, d, es)) ||
+        overlaps(O, ox, K, view_extent(kw, B, h, n, d, es)) ||
+        overlaps(O, ox, V, view_extent(vw, B, h, n, d, es)))
+      return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok) return ANCHOR_ATTN_ERROR_HIP;
+    // One workgroup per slice once the slices fill half of the CUs (or when forced);
+    // otherwise the split plan.
+    const bool split = ctx->plan == ANCHOR_ATTN_PLAN_SPLIT ||
+                       (ctx->plan == ANCHOR_ATTN_PLAN_AUTO && g.slices * 2 < ctx->num_cus);
+    hipError_t e;
+    if (split) {
+      const aa::LinearSplitPlan p = make_linear_plan(g, ctx->num_cus);
+      st = ensure_workspace(ctx, p.workspace_bytes());
+      if (st != ANCHOR_ATTN_SUCCESS) return st;
+      e = aa::launch_relu_linear_split_bf16(g, p, Q, qw, K, kw, V, vw, O, ow, cmin / qscale,
+                                            ctx->workspace, (hipStream_t)stream);
+    } else {
+      e = aa::launch_relu_linear_bf16(g, Q, qw, K, kw, V, vw, O, ow, cmin / qscale,
+                                      (hipStream_t)stream);
+    }
+    if (e != hipSuccess) {
       (void)hipGetLastError();
       return ANCHOR_ATTN_ERROR_HIP;
     }

@@ -93,6 +93,22 @@ void gemm_cache_destroy(GemmCache* c);
 bool gemm_prepare(GemmCache* c, long long T, int K, int N, bool bias);
 hipError_t gemm_run(GemmCache* c, const void* X, const void* W, const void* bias, void* D,
                     long long T, int K, int N, void* ws, hipStream_t stream);
+// ReLU kernel linear attention, one workgroup per slice (bf16, d = 32 or 64): out =
+// phi(Q) (phi(K)^T V) / max(phi(Q) phi(K)^T 1, cmin) on strided views.
+hipError_t launch_relu_linear_bf16(const Geometry& g, const void* Q, const View& qw, const void* K,
+                                   const View& kw, const void* V, const View& vw, void* O,
+                                   const View& ow, float cmin, hipStream_t stream);
+// Split plan of the linear attention: pass 1 over chunks1 chunks of chunk_len1 tokens
+// writes partial S tiles and z; finalize sums them; pass 2 applies over chunks2 chunks.
+struct LinearSplitPlan {
+  int chunks1, chunk_len1, chunks2, chunk_len2;
+  size_t part_bytes, zpart_bytes, sop_bytes, z_bytes;
+  size_t workspace_bytes() const { return part_bytes + zpart_bytes + sop_bytes + z_bytes; }
+};
+hipError_t launch_relu_linear_split_bf16(const Geometry& g, const LinearSplitPlan& p, const void* Q,
+                                         const View& qw, const void* K, const View& kw,
+                                         const void* V, const View& vw, void* O, const View& ow,
+                                         float cmin, void* workspace, hipStream_t stream);
 hipError_t launch_split_fp32(const Geometry& g, const SplitPlan& p, const void* Q,
                              const void* U, const void* V, void* H, void* workspace,
                              hipStream_t stream);

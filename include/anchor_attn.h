@@ -133,6 +133,31 @@ anchor_attn_status_t anchor_attn_block_forward(anchor_attn_ctx* ctx,
                                                void* Y, int B, int n, int h, int m, int d,
                                                anchor_attn_dtype_t dtype, void* stream);
 
+/* A second O(n) attention from the pages, sharing the reduce-then-apply structure: the
+ * ReLU kernel linear attention of the L2ViT page (Eq. (4): the decomposable kernel
+ * identity with phi = ReLU, the denominator clamped below at Cmin = 1e2 there), per
+ * (batch, head) slice of Q, K, V, O [B, h, n, d] (strided views as in
+ * anchor_attn_forward_strided; NULL strides = contiguous):
+ *   out_i = phi(qscale * q_i) (phi(K)^T V) / max(phi(qscale * q_i) . (phi(K)^T 1), cmin)
+ * qscale stands for 1/s, the page's learnable scale; since phi(a q) = a phi(q) it only
+ * moves the clamp.  bf16 in and out, fp32 accumulation (phi(K)^T V rounded to bf16 as a
+ * matrix-core operand).  With enough slices one workgroup per slice (Q, K, V read once,
+ * O written once); with fewer than half a slice per CU, or under PLAN_SPLIT, the tokens of
+ * a slice are split over workgroups (partial sums in the context's workspace, reduced in
+ * a fixed order).
+ * Domain: dtype BF16 (else NOT_SUPPORTED), d in {32, 64}, B, h, n >= 0 (no tokens: a
+ * no-op), cmin > 0 and qscale > 0 finite (else INVALID_VALUE); views as for
+ * anchor_attn_forward_strided (O's rows distinct, O's span disjoint from the inputs').
+ * Errors: nothing is enqueued. */
+anchor_attn_status_t anchor_attn_relu_linear_forward(anchor_attn_ctx* ctx,
+                                                     const void* Q, const long long* q_strides,
+                                                     const void* K, const long long* k_strides,
+                                                     const void* V, const long long* v_strides,
+                                                     void* O, const long long* o_strides,
+                                                     int B, int h, int n, int d, float cmin,
+                                                     float qscale, anchor_attn_dtype_t dtype,
+                                                     void* stream);
+
 /* Enqueues the gradients of anchor_attn_forward for a loss L with dL/dH = dH (AnchorFormer
  * abstract: the anchors are learnable, so the layer is trained through; the Pith verdict
  * page's Eq. (11) in the Eq. (12) order is the function differentiated), on `stream`,

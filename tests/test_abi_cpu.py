@@ -58,6 +58,8 @@ def test_null_arguments(lib):
     assert lib.anchor_attn_forward(None, None, None, None, None, 1, 1, 1, 1, 32, 0, None) == 1
     assert lib.anchor_attn_forward_strided(None, None, None, None, None, None, None, None,
                                            1, 1, 1, 1, 32, 0, None) == 1
+    assert lib.anchor_attn_relu_linear_forward(None, None, None, None, None, None, None, None,
+                                               None, 1, 1, 1, 32, 100.0, 1.0, 1, None) == 1
     assert lib.anchor_attn_block_forward(None, None, None, None, None, None, None, None,
                                          1, 1, 1, 1, 32, 1, None) == 1
     assert lib.anchor_attn_backward(None, None, None, None, None, None, None, None,

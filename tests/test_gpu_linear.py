@@ -1,0 +1,112 @@
+"""GPU parity of the ReLU kernel linear attention (L2ViT page, Eq. (4) with phi = ReLU and
+the Cmin clamp) against the oracle's fp64 version on the same bf16-rounded inputs.
+Gate: relative Frobenius error <= 1e-2 (the bf16 gate)."""
+import numpy as np
+import pytest
+
+import oracle
+from efficient_vision_transformer_amd.inputs import make_inputs
+
+from gpu_util import bf16_err
+
+pytestmark = pytest.mark.gpu
+
+LIN_TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def ctxs():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from efficient_vision_transformer_amd import AnchorAttention
+    out = {p: AnchorAttention(torch.device("cuda:0"), plan=p) for p in ("auto", "split", "fused")}
+    yield out
+    for c in out.values():
+        c.close()
+
+
+@pytest.fixture(scope="module")
+def ctx(ctxs):
+    return ctxs["auto"]
+
+
+def _conv(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def _run(ctx, x, cmin=100.0, qscale=1.0):
+    import torch
+    w = x.workload
+    print(f"  relu-linear B={w.B} h={w.h} n={w.n} d={w.d} cmin={cmin} qscale={qscale} "
+          f"plan={ctx.plan}", flush=True)
+    O = ctx.relu_linear(_conv(x.bits["Q"]), _conv(x.bits["K"]), _conv(x.bits["V"]), cmin, qscale)
+    torch.cuda.synchronize()
+    got = O.float().cpu().numpy().astype(np.float64)
+    ref = oracle.relu_linear_attn(x.Q, x.K, x.V, cmin, qscale)
+    e = bf16_err(got, ref)
+    print(f"  relative Frobenius error {e:.3e}", flush=True)
+    return e
+
+
+SHAPES = [(64, 6, 196, 64), (2, 3, 77, 32), (1, 1, 1, 64), (1, 2, 33, 32), (2, 2, 1000, 64),
+          (1, 4, 4096, 64)]
+
+
+@pytest.mark.parametrize("plan", ["split", "fused"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_relu_linear_shapes(ctxs, shape, plan):
+    B, h, n, d = shape
+    x = make_inputs("vit_s16_224", seed=4000 + n + d, shape={"B": B, "h": h, "n": n, "d": d, "m": 1})
+    assert _run(ctxs[plan], x) <= LIN_TOL
+
+
+def test_relu_linear_plans_agree_long(ctxs):
+    """A long slice (n = 16384, d = 64) through the split plan (many chunks) and through
+    one workgroup per slice, against each other and against the oracle on sampled rows."""
+    import torch
+    x = make_inputs("long_16k_bf16", shape={"B": 1, "h": 2})
+    outs = {}
+    for plan in ("split", "fused"):
+        O = ctxs[plan].relu_linear(_conv(x.bits["Q"]), _conv(x.bits["K"]), _conv(x.bits["V"]))
+        torch.cuda.synchronize()
+        outs[plan] = O.float().cpu().numpy().astype(np.float64)
+    ref = oracle.relu_linear_attn(x.Q, x.K, x.V)
+    for plan, got in outs.items():
+        e = bf16_err(got, ref)
+        print(f"  long {plan}: relative Frobenius error {e:.3e}", flush=True)
+        assert e <= LIN_TOL
+    assert bf16_err(outs["split"], outs["fused"]) <= LIN_TOL
+
+
+@pytest.mark.parametrize("cmin,qscale", [(100.0, 0.125), (1e-3, 1.0), (5000.0, 1.0)])
+def test_relu_linear_clamp_and_scale(ctx, cmin, qscale):
+    """Clamp inactive (cmin tiny), mostly binding (cmin large) and moved by the scale."""
+    x = make_inputs("vit_s16_224", seed=4100, shape={"B": 4})
+    assert _run(ctx, x, cmin, qscale) <= LIN_TOL
+
+
+def test_relu_linear_packed_views(ctx):
+    """Q, K, V read from a packed [B, n, 3, h, d] tensor, out written into [B, n, h, d]."""
+    import torch
+    x = make_inputs("vit_s16_224", seed=4200, shape={"B": 8})
+    arrs = [x.bits[k].transpose(0, 2, 1, 3) for k in ("Q", "K", "V")]
+    qkv = _conv(np.stack(arrs, axis=2))
+    Y = torch.zeros((8, 196, 6, 64), dtype=torch.bfloat16, device="cuda:0")
+    view = lambda i: qkv[:, :, i].permute(0, 2, 1, 3)
+    ctx.relu_linear(view(0), view(1), view(2), out=Y.permute(0, 2, 1, 3))
+    torch.cuda.synchronize()
+    got = Y.permute(0, 2, 1, 3).float().cpu().numpy().astype(np.float64)
+    assert bf16_err(got, oracle.relu_linear_attn(x.Q, x.K, x.V)) <= LIN_TOL
+
+
+def test_relu_linear_rejects_bad_arguments(ctx):
+    import torch
+    Q = torch.zeros((1, 1, 8, 32), dtype=torch.bfloat16, device="cuda:0")
+    for cmin, qscale in ((0.0, 1.0), (100.0, 0.0), (float("nan"), 1.0)):
+        with pytest.raises(RuntimeError, match="status 1"):
+            ctx.relu_linear(Q, Q, Q, cmin, qscale)
+    with pytest.raises(RuntimeError, match="status 2"):
+        ctx.relu_linear(Q.float(), Q.float(), Q.float())
+    with pytest.raises(RuntimeError, match="status 1"):
+        ctx.relu_linear(Q, Q, Q, out=Q)
