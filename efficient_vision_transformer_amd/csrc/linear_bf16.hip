@@ -243,31 +243,35 @@ void relu_linear_pass1(const __bf16* __restrict__ K, const __bf16* __restrict__ 
   }
 }
 
-// Split plan, finalize (one workgroup per slice): chunk sums in chunk order, S as bf16
-// operands [slice][DT][KS][64] x 16 B, z [slice][D].
+// Split plan, finalize: chunk sums in chunk order, S as bf16 operands
+// [slice][DT][KS][64] x 16 B and z [slice][D].  Workgroup (slice, group): wave w sums
+// tile 4 * group + w; group 0 also sums z.
 template <int D>
 __global__ __launch_bounds__(256)
 void relu_linear_finalize(const float* __restrict__ part, const float* __restrict__ zpart,
                           __bf16* __restrict__ sops, float* __restrict__ zs, int chunks) {
-  constexpr int DT = D / 16, TILES = DT * DT;
-  const int slice = blockIdx.x;
+  constexpr int DT = D / 16, TILES = DT * DT, GROUPS = (TILES + 3) / 4;
+  const int slice = blockIdx.x / GROUPS, grp = blockIdx.x - slice * GROUPS;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  __bf16* so = sops + (size_t)slice * D * D;
-  for (int t = w; t < TILES; t += 4) {
+  const int t = 4 * grp + w;
+  if (t < TILES) {
     const int ja = t / DT, dt = t - (t / DT) * DT;
     f32x4 acc = zero4();
     for (int ch = 0; ch < chunks; ++ch) {
       const float* src = part + (((size_t)slice * chunks + ch) * TILES + t) * 256 + lane;
       acc[0] += src[0]; acc[1] += src[64]; acc[2] += src[128]; acc[3] += src[192];
     }
+    __bf16* so = sops + (size_t)slice * D * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r) so[sop_pos<D>(16 * ja + 4 * g + r, 16 * dt + c)] = (__bf16)acc[r];
   }
-  for (int i = threadIdx.x; i < D; i += 256) {
-    float z = 0.f;
-    for (int ch = 0; ch < chunks; ++ch) z += zpart[((size_t)slice * chunks + ch) * D + i];
-    zs[(size_t)slice * D + i] = z;
+  if (grp == 0) {
+    for (int i = threadIdx.x; i < D; i += 256) {
+      float z = 0.f;
+      for (int ch = 0; ch < chunks; ++ch) z += zpart[((size_t)slice * chunks + ch) * D + i];
+      zs[(size_t)slice * D + i] = z;
+    }
   }
 }
 
@@ -324,8 +328,9 @@ static hipError_t lin_split_t(const Geometry& g, const LinearSplitPlan& p, const
   if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidValue;
   relu_linear_pass1<D, NW><<<dim3((unsigned)g1), dim3(NW * kWave), 0, s>>>(
       (const __bf16*)K, (const __bf16*)V, kw, vw, part, zpart, g.h, g.n, p.chunks1, p.chunk_len1);
-  relu_linear_finalize<D><<<dim3((unsigned)g.slices), dim3(256), 0, s>>>(part, zpart, sops, zs,
-                                                                         p.chunks1);
+  constexpr int GROUPS = ((D / 16) * (D / 16) + 3) / 4;
+  relu_linear_finalize<D><<<dim3((unsigned)(g.slices * GROUPS)), dim3(256), 0, s>>>(
+      part, zpart, sops, zs, p.chunks1);
   relu_linear_pass2<D, NW><<<dim3((unsigned)g2), dim3(NW * kWave), 0, s>>>(
       (const __bf16*)Q, (__bf16*)O, qw, ow, (const u32x4*)sops, zs, g.h, g.n, p.chunks2,
       p.chunk_len2, cmin);
