@@ -59,14 +59,30 @@ void bwd_finalize(const float* __restrict__ partP, const float* __restrict__ par
   float p[DT], q[DT], delta = 0.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) { p[dt] = 0.f; q[dt] = 0.f; }
-  for (int ch = 0; ch < chunks; ++ch) {
-    const size_t sc = (size_t)slice * chunks + ch;
-    delta += dpart[sc * (16 * AT) + anchor];
+  constexpr int U = 4;   // loads of U chunks in flight, then the adds in chunk order
+  for (int ch0 = 0; ch0 < chunks; ch0 += U) {
+    float dv[U], pv[U][DT], qv[U][DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const size_t e = ((sc * AT + jt) * DT + dt) * 256 + r * 64 + lane;
-      p[dt] += partP[e];
-      q[dt] += partG[e];
+    for (int u = 0; u < U; ++u) {
+      const size_t sc = (size_t)slice * chunks + min(ch0 + u, chunks - 1);
+      dv[u] = dpart[sc * (16 * AT) + anchor];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const size_t e = ((sc * AT + jt) * DT + dt) * 256 + r * 64 + lane;
+        pv[u][dt] = partP[e];
+        qv[u][dt] = partG[e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (ch0 + u < chunks) {
+        delta += dv[u];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          p[dt] += pv[u][dt];
+          q[dt] += qv[u][dt];
+        }
+      }
     }
   }
   const float rinv = (delta > 0.f) ? 1.f / delta : 0.f;
@@ -291,14 +307,20 @@ void du_reduce(const float* __restrict__ partU, __bf16* __restrict__ dU, int B, 
   const int c = lane & 15, g = lane >> 4;
   f32x4 acc = zero4();
   const long long total = (long long)B * chunks;
-  for (long long e = q; e < total; e += NWR) {
-    const long long b = e / chunks, ch = e - b * chunks;
-    const size_t sc = ((size_t)b * h + head) * chunks + ch;
-    const float* src = partU + ((sc * AT + jt) * DT + dt) * 256 + lane;
-    acc[0] += src[0];
-    acc[1] += src[64];
-    acc[2] += src[128];
-    acc[3] += src[192];
+  constexpr int U = 8;   // loads of U entries in flight, then the adds in entry order
+  for (long long e0 = q; e0 < total; e0 += (long long)U * NWR) {
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long e = min(e0 + (long long)u * NWR, total - 1);
+      const long long b = e / chunks, ch = e - b * chunks;
+      const size_t sc = ((size_t)b * h + head) * chunks + ch;
+      const float* src = partU + ((sc * AT + jt) * DT + dt) * 256 + lane;
+      v[u] = f32x4{src[0], src[64], src[128], src[192]};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (e0 + (long long)u * NWR < total) acc += v[u];
   }
   red[q][lane] = acc;
   __syncthreads();

@@ -258,9 +258,18 @@ void relu_linear_finalize(const float* __restrict__ part, const float* __restric
   if (t < TILES) {
     const int ja = t / DT, dt = t - (t / DT) * DT;
     f32x4 acc = zero4();
-    for (int ch = 0; ch < chunks; ++ch) {
-      const float* src = part + (((size_t)slice * chunks + ch) * TILES + t) * 256 + lane;
-      acc[0] += src[0]; acc[1] += src[64]; acc[2] += src[128]; acc[3] += src[192];
+    constexpr int U = 8;   // loads of U chunks in flight, then the adds in chunk order
+    for (int ch0 = 0; ch0 < chunks; ch0 += U) {
+      f32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ch = min(ch0 + u, chunks - 1);
+        const float* src = part + (((size_t)slice * chunks + ch) * TILES + t) * 256 + lane;
+        v[u] = f32x4{src[0], src[64], src[128], src[192]};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (ch0 + u < chunks) acc += v[u];
     }
     __bf16* so = sops + (size_t)slice * D * D;
 #pragma unroll
