@@ -1,0 +1,48 @@
+"""torch.autograd integration: anchor attention as a differentiable function, so that Q, U
+(the learnable anchors) and V receive gradients in an ordinary training step.
+
+Both directions run in the HIP library through the C ABI (anchor_attn_forward and
+anchor_attn_backward); this module only hands tensors over.  bf16, m <= 128 for the
+backward (the library's domain); U's gradient is summed over the batch.
+"""
+from __future__ import annotations
+
+import torch
+
+from .anchor_attn import AnchorAttention
+
+_ctx_by_device: dict = {}
+
+
+def _context(device) -> AnchorAttention:
+    key = device.index
+    ctx = _ctx_by_device.get(key)
+    if ctx is None:
+        ctx = _ctx_by_device[key] = AnchorAttention(device)
+    return ctx
+
+
+class AnchorAttentionFunction(torch.autograd.Function):
+    """H = A (Delta^-1 (A^T V)), A = rowsoftmax(Q U^T / sqrt(d)); Q, V [B, h, n, d], U
+    [h, m, d], all contiguous on one GPU."""
+
+    @staticmethod
+    def forward(fctx, Q, U, V):
+        ctx = _context(Q.device)
+        H = ctx.forward(Q, U, V)
+        fctx.save_for_backward(Q, U, V)
+        return H
+
+    @staticmethod
+    def backward(fctx, dH):
+        Q, U, V = fctx.saved_tensors
+        ctx = _context(Q.device)
+        if not dH.is_contiguous():
+            dH = dH.contiguous()
+        dQ, dU, dV = ctx.backward(Q, U, V, dH)
+        return dQ, dU, dV
+
+
+def anchor_attention(Q, U, V):
+    """Differentiable anchor attention (see AnchorAttentionFunction)."""
+    return AnchorAttentionFunction.apply(Q, U, V)
