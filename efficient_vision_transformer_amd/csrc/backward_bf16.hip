@@ -177,41 +177,52 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     if (p < npairs) {
 #pragma unroll 1
       for (int tt = 0; tt < 2; ++tt) {
+        // The LDS operands are loop-invariant; keeping the compiler from hoisting all of
+        // them into registers (which spills at m = 128) costs only LDS reads.
+        asm volatile("" ::: "memory");
         const int row = t_begin + 32 * p + 16 * tt + c;
         const bool ok = row < t_end;
         u32x4 qv[KS], vv[KS], gv[KS];
         load_rows<D>(Q, base, D, row, n, g, qv);
         load_rows<D>(V, base, D, row, n, g, vv);
         load_rows<D>(G, base, D, row, n, g, gv);
-        // A (fp32, normalised) in the transposed layout: s[j] lane (c,g): token c,
-        // anchors 16j + 4g + r'.
-        f32x4 s[AT];
+        // A (normalised, rounded to bf16) in the transposed layout: ab[jj] lane (c,g) holds
+        // token c, anchors 32jj + 4g .. + 3 (slots 0-3) and 32jj + 16 + 4g .. + 3 (4-7).
+        bf16x8 ab[MP];
+        {
+          f32x4 s[AT];
 #pragma unroll
-        for (int j = 0; j < AT; ++j) {
-          f32x4 acc = (j >= AT - 2) ? mask[j - (AT - 2)] : zero4();
+          for (int j = 0; j < AT; ++j) {
+            f32x4 acc = (j >= AT - 2) ? mask[j - (AT - 2)] : zero4();
 #pragma unroll
-          for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(qv[kk]), acc);
-          s[j] = acc;
+            for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(qv[kk]), acc);
+            s[j] = acc;
+          }
+          float mx = s[0][0];
+#pragma unroll
+          for (int j = 0; j < AT; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) mx = fmaxf(mx, s[j][q]);
+          mx = xor32_max(xor16_max(mx));
+          const float mneg = -mx * c2;
+          f32x4 zt = zero4();
+#pragma unroll
+          for (int j = 0; j < AT; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) s[j][q] = exp2_fast(fmaf(s[j][q], c2, mneg));
+            zt += s[j];
+          }
+          const float z = xor32_sum(xor16_sum((zt[0] + zt[1]) + (zt[2] + zt[3])));
+          const float inv = ok ? 1.f / z : 0.f;
+#pragma unroll
+          for (int jj = 0; jj < MP; ++jj) ab[jj] = pack_bf16(s[2 * jj] * inv, s[2 * jj + 1] * inv);
         }
-        float mx = s[0][0];
+        // Rows of Q ([token][dim]) for the dU tiles.
+        __bf16* qrow = q_rows + (32 * w + 16 * tt + c) * VS + 8 * KS * g;
 #pragma unroll
-        for (int j = 0; j < AT; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) mx = fmaxf(mx, s[j][q]);
-        mx = xor32_max(xor16_max(mx));
-        const float mneg = -mx * c2;
-        f32x4 zt = zero4();
-#pragma unroll
-        for (int j = 0; j < AT; ++j) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) s[j][q] = exp2_fast(fmaf(s[j][q], c2, mneg));
-          zt += s[j];
-        }
-        const float z = xor32_sum(xor16_sum((zt[0] + zt[1]) + (zt[2] + zt[3])));
-        const float inv = ok ? 1.f / z : 0.f;
-#pragma unroll
-        for (int j = 0; j < AT; ++j) s[j] *= inv;
-        // dA^T = dDelta + W G^T + dP V^T, then dS = A * (dA - rowsum(A * dA)).
+        for (int kk = 0; kk < KS; ++kk) *(u32x4*)(qrow + 8 * kk) = qv[kk];
+        // dA^T = dDelta + W G^T + dP V^T, then dS = A * (dA - rowsum(A * dA)), with the
+        // bf16 A that also feeds dV.
         f32x4 da[AT];
         float rs = 0.f;
 #pragma unroll
@@ -224,40 +235,42 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
           }
           da[j] = acc;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) rs = fmaf(s[j][q], acc[q], rs);
+          for (int q = 0; q < 4; ++q) rs = fmaf((float)ab[j >> 1][4 * (j & 1) + q], acc[q], rs);
         }
         rs = xor32_sum(xor16_sum(rs));
-        bf16x8 ab[MP], dsb[MP];
+        bf16x8 dsb[MP];
 #pragma unroll
         for (int jj = 0; jj < MP; ++jj) {
-          ab[jj] = pack_bf16(s[2 * jj], s[2 * jj + 1]);
-          const f32x4 d0 = s[2 * jj] * (da[2 * jj] - rs), d1 = s[2 * jj + 1] * (da[2 * jj + 1] - rs);
+          f32x4 d0, d1;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            d0[q] = (float)ab[jj][q] * (da[2 * jj][q] - rs);
+            d1[q] = (float)ab[jj][4 + q] * (da[2 * jj + 1][q] - rs);
+          }
           dsb[jj] = pack_bf16(d0, d1);
         }
-        // dQ^T = c U^T dS^T and dV^T = dP^T A^T: lane (c,g) ends with token c, dims
-        // (D/4)g + 4dt2 + r'.
-        f32x4 hq[DT], hv[DT];
+        // dQ^T = c U^T dS^T and dV^T = dP^T A^T, two dim tiles at a time: lane (c,g) ends
+        // with token c, dims (D/4)g + 4dt2 + r'.
+        const size_t off = base + (size_t)row * D + (D / 4) * g;
 #pragma unroll
-        for (int dt2 = 0; dt2 < DT; ++dt2) {
-          f32x4 aq = zero4(), av = zero4();
+        for (int hh = 0; hh < DT / 2; ++hh) {
+          f32x4 q0 = zero4(), q1 = zero4();
 #pragma unroll
           for (int jj = 0; jj < MP; ++jj) {
-            aq = mfma_bf16(as_bf16x8(ut_lds[dt2][jj][lane]), dsb[jj], aq);
-            av = mfma_bf16(as_bf16x8(dpw_lds[dt2][jj][lane]), ab[jj], av);
+            q0 = mfma_bf16(as_bf16x8(ut_lds[2 * hh][jj][lane]), dsb[jj], q0);
+            q1 = mfma_bf16(as_bf16x8(ut_lds[2 * hh + 1][jj][lane]), dsb[jj], q1);
           }
-          hq[dt2] = aq * cs;
-          hv[dt2] = av;
-        }
-        if (ok) {
-          const size_t off = base + (size_t)row * D + (D / 4) * g;
+          if (ok) __builtin_nontemporal_store(as_u32x4(pack_bf16(q0 * cs, q1 * cs)), (u32x4*)(dQ + off + 8 * hh));
+          f32x4 v0 = zero4(), v1 = zero4();
 #pragma unroll
-          for (int hh = 0; hh < DT / 2; ++hh) {
-            __builtin_nontemporal_store(as_u32x4(pack_bf16(hq[2 * hh], hq[2 * hh + 1])), (u32x4*)(dQ + off + 8 * hh));
-            __builtin_nontemporal_store(as_u32x4(pack_bf16(hv[2 * hh], hv[2 * hh + 1])), (u32x4*)(dV + off + 8 * hh));
+          for (int jj = 0; jj < MP; ++jj) {
+            v0 = mfma_bf16(as_bf16x8(dpw_lds[2 * hh][jj][lane]), ab[jj], v0);
+            v1 = mfma_bf16(as_bf16x8(dpw_lds[2 * hh + 1][jj][lane]), ab[jj], v1);
           }
+          if (ok) __builtin_nontemporal_store(as_u32x4(pack_bf16(v0, v1)), (u32x4*)(dV + off + 8 * hh));
         }
         // Rows of dS ([token][anchor], dsb[jj] holds anchors 32jj + 4g .. + 3 and
-        // 32jj + 16 + 4g .. + 3) and of Q ([token][dim]) for the dU tiles.
+        // 32jj + 16 + 4g .. + 3).
         __bf16* srow = s_rows + (32 * w + 16 * tt + c) * AS + 4 * g;
 #pragma unroll
         for (int jj = 0; jj < MP; ++jj) {
@@ -265,9 +278,6 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
           *(u32x2*)(srow + 32 * jj) = u32x2{v[0], v[1]};
           *(u32x2*)(srow + 32 * jj + 16) = u32x2{v[2], v[3]};
         }
-        __bf16* qrow = q_rows + (32 * w + 16 * tt + c) * VS + 8 * KS * g;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) *(u32x4*)(qrow + 8 * kk) = qv[kk];
       }
     }
     __syncthreads();
