@@ -1,0 +1,109 @@
+"""Sizes at the edges of the index arithmetic, in the launch configuration the library
+picks: tensors of more than 2^31 elements (64-bit offsets in every plan), one slice of a
+quarter million tokens, and 65536 slices of three tokens.  Inputs are drawn on the device
+with a seeded torch generator (too large to draw on the host); whole slices are copied
+back and recomputed by the oracle: the first, the last (beyond element 2^31) and two
+random ones."""
+import numpy as np
+import pytest
+
+import oracle
+
+from gpu_util import err_for, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from efficient_vision_transformer_amd import AnchorAttention
+    c = AnchorAttention(torch.device("cuda:0"))
+    yield c
+    c.close()
+
+
+def _draw(shape, dtype, seed):
+    import torch
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device="cuda:0", dtype=torch.float32).to(dtype)
+
+
+def _check_slices(Q, U, V, H, dtype, picks, label):
+    import torch
+    B, h = Q.shape[0], Q.shape[1]
+    for b, j in picks:
+        q = Q[b, j].float().cpu().numpy().astype(np.float64)
+        v = V[b, j].float().cpu().numpy().astype(np.float64)
+        u = U[j].float().cpu().numpy().astype(np.float64)
+        got = H[b, j].float().cpu().numpy().astype(np.float64)
+        _, _, _, ref = oracle.anchor_slice(q, u, v)
+        e = err_for(dtype, got, ref)
+        print(f"  {label} slice ({b},{j}): {e:.3e}", flush=True)
+        assert np.all(np.isfinite(got)) and e <= tol_for(dtype)
+
+
+@pytest.mark.parametrize("B,h,n,m,d", [(40, 1000, 1000, 30, 64),   # fused, 2.56e9 elements
+                                       (16, 16, 140000, 32, 64)])  # split, 2.29e9 elements
+def test_more_than_2_31_elements(ctx, B, h, n, m, d):
+    import torch
+    print(f"  bf16 B={B} h={h} n={n} m={m} d={d}: {ctx.describe(B, h, n, m, d, 'bf16')[:60]}",
+          flush=True)
+    Q = _draw((B, h, n, d), torch.bfloat16, 11)
+    V = _draw((B, h, n, d), torch.bfloat16, 12)
+    U = _draw((h, m, d), torch.bfloat16, 13)
+    H = ctx.forward(Q, U, V)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(0)
+    picks = [(0, 0), (B - 1, h - 1)] + [(int(r.integers(B)), int(r.integers(h))) for _ in range(2)]
+    _check_slices(Q, U, V, H, "bf16", picks, f"{B}x{h}x{n}")
+    del Q, V, H
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_one_slice_of_a_quarter_million_tokens(ctx, dtype):
+    import torch
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    n, m, d = 262144, 64, 64
+    Q, V, U = _draw((1, 1, n, d), td, 21), _draw((1, 1, n, d), td, 22), _draw((1, m, d), td, 23)
+    H = ctx.forward(Q, U, V)
+    torch.cuda.synchronize()
+    _check_slices(Q, U, V, H, dtype, [(0, 0)], f"n={n} {dtype}")
+
+
+def test_many_slices_of_three_tokens(ctx):
+    import torch
+    B, h, n, m, d = 4096, 16, 3, 30, 64
+    Q, V, U = _draw((B, h, n, d), torch.bfloat16, 31), _draw((B, h, n, d), torch.bfloat16, 32), \
+        _draw((h, m, d), torch.bfloat16, 33)
+    H = ctx.forward(Q, U, V)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(1)
+    picks = [(0, 0), (B - 1, h - 1)] + [(int(r.integers(B)), int(r.integers(h))) for _ in range(6)]
+    _check_slices(Q, U, V, H, "bf16", picks, "65536 slices")
+
+
+def test_backward_more_than_2_31_elements(ctx):
+    """The one-workgroup-per-slice backward with every tensor beyond 2^31 elements: dQ and
+    dV of sampled heads and dU of those heads (summed over all 40 batch elements) against
+    the oracle's gradients."""
+    import torch
+    from gpu_util import bf16_err
+    B, h, n, m, d = 40, 1000, 1000, 30, 64
+    Q, V, G = (_draw((B, h, n, d), torch.bfloat16, s) for s in (41, 42, 43))
+    U = _draw((h, m, d), torch.bfloat16, 44)
+    print(f"  backward B={B} h={h} n={n} m={m} d={d}", flush=True)
+    dQ, dU, dV = ctx.backward(Q, U, V, G)
+    torch.cuda.synchronize()
+    host = lambda t: t.float().cpu().numpy().astype(np.float64)
+    for j in (0, h - 1, 517):
+        refs = oracle.anchor_backward(host(Q[:, j:j + 1]), host(U[j:j + 1]), host(V[:, j:j + 1]),
+                                      host(G[:, j:j + 1]))
+        gots = (host(dQ[:, j:j + 1]), host(dU[j:j + 1]), host(dV[:, j:j + 1]))
+        for name, got, ref in zip(("dQ", "dU", "dV"), gots, refs):
+            e = bf16_err(got, ref)
+            print(f"  head {j} {name}: {e:.3e}", flush=True)
+            assert e <= 1e-2
