@@ -112,11 +112,13 @@ __device__ __forceinline__ int sop_pos(int in, int out) {
 
 // Phase 3 over tokens [t0, t1): out = phi(Q) S / max(phi(Q) z, cmin) with S^T operands and
 // z in LDS.  Waves work independently (no barrier).
+// q_first, when given, holds this wave's first pair of Q rows, loaded by the caller.
 template <int D, int NW>
 __device__ __forceinline__ void lin_apply(const u32x4 (*sop)[D / 32][kWave], const float* zl,
                                           const __bf16* __restrict__ Q, size_t qb, long long qs,
                                           __bf16* __restrict__ O, size_t ob, const View& ow,
-                                          int t0, int t1, int n, float cmin) {
+                                          int t0, int t1, int n, float cmin,
+                                          const u32x4 (*q_first)[D / 32] = nullptr) {
   constexpr int DT = D / 16, KS = D / 32;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -128,8 +130,15 @@ __device__ __forceinline__ void lin_apply(const u32x4 (*sop)[D / 32][kWave], con
 #pragma unroll
     for (int s = 0; s < 8; ++s) zr[kk][s] = zl[32 * kk + 8 * g + s];
   u32x4 qc[2][KS];
+  if (q_first) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) load_rows_c<D, D>(Q, qb, qs, t0 + 32 * w + 16 * tt + c, n, g, 0, qc[tt]);
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) qc[tt][kk] = q_first[tt][kk];
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) load_rows_c<D, D>(Q, qb, qs, t0 + 32 * w + 16 * tt + c, n, g, 0, qc[tt]);
+  }
   for (int p = w; p < npairs; p += NW) {
     const bool more = p + NW < npairs;
     u32x4 qn[2][KS];
@@ -189,6 +198,13 @@ void relu_linear_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
+  constexpr int KS = D / 32;
+  // The first Q rows go out together with K and V, so their latency is hidden behind the
+  // reduction.
+  const size_t qb = view_base(qw, slice, h);
+  u32x4 q0[2][KS];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) load_rows_c<D, D>(Q, qb, qw.st, 32 * w + 16 * tt + c, n, g, 0, q0[tt]);
   f32x4 pacc[TPW], dacc[TPW];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) { pacc[k] = zero4(); dacc[k] = zero4(); }
@@ -206,8 +222,7 @@ void relu_linear_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     }
   }
   __syncthreads();
-  lin_apply<D, NW>(L.s, L.z, Q, view_base(qw, slice, h), qw.st, O, view_base(ow, slice, h), ow, 0,
-                   n, n, cmin);
+  lin_apply<D, NW>(L.s, L.z, Q, qb, qw.st, O, view_base(ow, slice, h), ow, 0, n, n, cmin, q0);
 }
 
 // Split plan, pass 1: per (slice, chunk) partial S tiles [slice][chunk][t][4][64] and z
