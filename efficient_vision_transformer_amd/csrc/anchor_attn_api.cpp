@@ -511,7 +511,7 @@ anchor_attn_status_t anchor_attn_relu_linear_forward(
       e = aa::launch_relu_linear_split_bf16(g, p, Q, qw, K, kw, V, vw, O, ow, cmin / qscale,
                                             ctx->workspace, (hipStream_t)stream);
     } else {
-      e = aa::launch_relu_linear_bf16(g, Q, qw, K, kw, V, vw, O, ow, cmin / qscale,
+      e = aa::launch_relu_linear_bf16(g, Q, qw, K, kw, V, vw, O, ow, cmin / qscale, ctx->num_cus,
                                       (hipStream_t)stream);
     }
     if (e != hipSuccess) {

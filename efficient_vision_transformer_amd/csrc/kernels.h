@@ -97,7 +97,7 @@ hipError_t gemm_run(GemmCache* c, const void* X, const void* W, const void* bias
 // phi(Q) (phi(K)^T V) / max(phi(Q) phi(K)^T 1, cmin) on strided views.
 hipError_t launch_relu_linear_bf16(const Geometry& g, const void* Q, const View& qw, const void* K,
                                    const View& kw, const void* V, const View& vw, void* O,
-                                   const View& ow, float cmin, hipStream_t stream);
+                                   const View& ow, float cmin, int num_cus, hipStream_t stream);
 // Split plan of the linear attention: pass 1 over chunks1 chunks of chunk_len1 tokens
 // writes partial S tiles and z; finalize sums them; pass 2 applies over chunks2 chunks.
 struct LinearSplitPlan {

@@ -22,12 +22,15 @@
 
 namespace aa {
 
-template <int D, int NW>
+// LDS of one workgroup that handles the DW output dims from d0 of a slice (DW = D, or
+// D / 2 when two workgroups share the slice).
+template <int D, int NW, int DW = D>
 struct LinLds {
-  static constexpr int DT = D / 16, KS = D / 32, VS = tr_stride<D>();
-  __attribute__((aligned(16))) __bf16 k[NW * 32 * VS];   // rows of phi(K), this round
-  __attribute__((aligned(16))) __bf16 v[NW * 32 * VS];   // rows of V, this round
-  u32x4 s[DT][KS][kWave];                                // S^T left operands
+  static constexpr int KS = D / 32, DTW = DW / 16;
+  static constexpr int KSTR = tr_stride<D>(), VS = tr_stride<DW>();
+  __attribute__((aligned(16))) __bf16 k[NW * 32 * KSTR];  // rows of phi(K), this round
+  __attribute__((aligned(16))) __bf16 v[NW * 32 * VS];    // rows of V (DW dims), this round
+  u32x4 s[DTW][KS][kWave];                                // S^T left operands
   __attribute__((aligned(16))) float z[D];
 };
 
@@ -39,37 +42,38 @@ __device__ __forceinline__ u32x4 relu_bf16x8(u32x4 x) {
 }
 
 // Phase 1 over tokens [t0, t1) of a slice: S and z tiles of this wave accumulated in
-// pacc / dacc (tile t = w*TPW + k: input-dim tile t / DT, rows 16ja + 4g + r; output-dim
-// tile t % DT, dim 16dt + c; z of an input tile with its output tile 0).
-template <int D, int NW>
-__device__ __forceinline__ void lin_reduce(LinLds<D, NW>& L, const __bf16* __restrict__ K,
+// pacc / dacc (tile t = w*TPW + k: input-dim tile t / DTW, rows 16ja + 4g + r; output-dim
+// tile t % DTW, dim d0 + 16dt + c; z of an input tile with its output tile 0).
+template <int D, int NW, int DW>
+__device__ __forceinline__ void lin_reduce(LinLds<D, NW, DW>& L, const __bf16* __restrict__ K,
                                            const __bf16* __restrict__ V, size_t kb, long long ks,
                                            size_t vb, long long vs, int t0, int t1, int n,
-                                           f32x4* pacc, f32x4* dacc) {
-  constexpr int DT = D / 16, KS = D / 32, VS = LinLds<D, NW>::VS;
-  constexpr int TPW = DT * DT / NW;
+                                           int d0, f32x4* pacc, f32x4* dacc) {
+  constexpr int DT = D / 16, KS = D / 32, KV = DW / 32, DTW = DW / 16;
+  constexpr int KSTR = LinLds<D, NW, DW>::KSTR, VS = LinLds<D, NW, DW>::VS;
+  constexpr int TPW = DT * DTW / NW;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int npairs = (t1 - t0 + 31) >> 5;
   const int rounds = (npairs + NW - 1) / NW;
   const bf16x8 ones = splat_bf16(1.f);
-  u32x4 kc[2][KS], vc[2][KS];
+  u32x4 kc[2][KS], vc[2][KV];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     load_rows_c<D, D>(K, kb, ks, t0 + 32 * w + 16 * tt + c, n, g, 0, kc[tt]);
-    load_rows_c<D, D>(V, vb, vs, t0 + 32 * w + 16 * tt + c, n, g, 0, vc[tt]);
+    load_rows_c<D, DW>(V, vb, vs, t0 + 32 * w + 16 * tt + c, n, g, d0, vc[tt]);
   }
   for (int r = 0; r < rounds; ++r) {
     const int pairs_here = min(NW, npairs - r * NW);  // uniform over the workgroup
     const int p = r * NW + w;
     const bool more = p + NW < npairs;
-    u32x4 kn[2][KS], vn[2][KS];
+    u32x4 kn[2][KS], vn[2][KV];
     if (more) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         load_rows_c<D, D>(K, kb, ks, t0 + 32 * (p + NW) + 16 * tt + c, n, g, 0, kn[tt]);
-        load_rows_c<D, D>(V, vb, vs, t0 + 32 * (p + NW) + 16 * tt + c, n, g, 0, vn[tt]);
+        load_rows_c<D, DW>(V, vb, vs, t0 + 32 * (p + NW) + 16 * tt + c, n, g, d0, vn[tt]);
       }
     }
     if (p < npairs) {
@@ -78,24 +82,26 @@ __device__ __forceinline__ void lin_reduce(LinLds<D, NW>& L, const __bf16* __res
         // Rows past the range hold other tokens (or the last row again): their keys are
         // zeroed, so they add nothing to S or z.
         const bool ok = t0 + 32 * p + 16 * tt + c < t1;
-        __bf16* krow = L.k + (32 * w + 16 * tt + c) * VS + 8 * g;
+        __bf16* krow = L.k + (32 * w + 16 * tt + c) * KSTR + 8 * g;
         __bf16* vrow = L.v + (32 * w + 16 * tt + c) * VS + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const u32x4 kr = ok ? relu_bf16x8(kc[tt][kk]) : u32x4{0u, 0u, 0u, 0u};
-          *(u32x4*)(krow + 32 * kk) = kr;
-          *(u32x4*)(vrow + 32 * kk) = vc[tt][kk];
-        }
+        for (int kk = 0; kk < KS; ++kk)
+          *(u32x4*)(krow + 32 * kk) = ok ? relu_bf16x8(kc[tt][kk]) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int kk = 0; kk < KV; ++kk) *(u32x4*)(vrow + 32 * kk) = vc[tt][kk];
       }
     }
     __syncthreads();
-    accumulate_tiles<TPW, DT, VS, VS, true>(L.k, L.v, w * TPW, pairs_here, c, g, ones, pacc, dacc);
+    accumulate_tiles<TPW, DTW, KSTR, VS, true>(L.k, L.v, w * TPW, pairs_here, c, g, ones, pacc, dacc);
     __syncthreads();
     if (more) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) { kc[tt][kk] = kn[tt][kk]; vc[tt][kk] = vn[tt][kk]; }
+        for (int kk = 0; kk < KS; ++kk) kc[tt][kk] = kn[tt][kk];
+#pragma unroll
+        for (int kk = 0; kk < KV; ++kk) vc[tt][kk] = vn[tt][kk];
+      }
     }
   }
 }
@@ -112,14 +118,15 @@ __device__ __forceinline__ int sop_pos(int in, int out) {
 
 // Phase 3 over tokens [t0, t1): out = phi(Q) S / max(phi(Q) z, cmin) with S^T operands and
 // z in LDS.  Waves work independently (no barrier).
-// q_first, when given, holds this wave's first pair of Q rows, loaded by the caller.
-template <int D, int NW>
+// Output dims d0 .. d0 + DW - 1.  q_first, when given, holds this wave's first pair of Q
+// rows, loaded by the caller.
+template <int D, int NW, int DW = D>
 __device__ __forceinline__ void lin_apply(const u32x4 (*sop)[D / 32][kWave], const float* zl,
                                           const __bf16* __restrict__ Q, size_t qb, long long qs,
                                           __bf16* __restrict__ O, size_t ob, const View& ow,
                                           int t0, int t1, int n, float cmin,
-                                          const u32x4 (*q_first)[D / 32] = nullptr) {
-  constexpr int DT = D / 16, KS = D / 32;
+                                          const u32x4 (*q_first)[D / 32] = nullptr, int d0 = 0) {
+  constexpr int DT = DW / 16, KS = D / 32;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
@@ -168,7 +175,7 @@ __device__ __forceinline__ void lin_apply(const u32x4 (*sop)[D / 32][kWave], con
         acc[dt2] = a * inv;
       }
       if (row < t1) {
-        __bf16* dst = O + ob + view_row(ow, row) + 8 * g;
+        __bf16* dst = O + ob + view_row(ow, row) + d0 + 8 * g;
 #pragma unroll
         for (int hh = 0; hh < DT / 2; ++hh)
           __builtin_nontemporal_store(as_u32x4(pack_bf16(acc[2 * hh], acc[2 * hh + 1])),
@@ -184,21 +191,21 @@ __device__ __forceinline__ void lin_apply(const u32x4 (*sop)[D / 32][kWave], con
   }
 }
 
-// One workgroup per slice: reduce over all tokens, S to operands, apply to all tokens.
-template <int D, int NW>
-__global__ __launch_bounds__(NW * kWave, 2)
-void relu_linear_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-                      const __bf16* __restrict__ V, __bf16* __restrict__ O, View qw, View kw,
-                      View vw, View ow, int h, int n, float cmin) {
-  using L_t = LinLds<D, NW>;
-  constexpr int DT = D / 16, TILES = DT * DT, TPW = TILES / NW;
+// One workgroup's share of a slice: all tokens, output dims d0 .. d0 + DW - 1.  Reduce
+// over all tokens, S to operands, apply to all tokens.
+template <int D, int NW, int DW>
+__device__ __forceinline__ void lin_fused_part(LinLds<D, NW, DW>& L, const __bf16* __restrict__ Q,
+                                               const __bf16* __restrict__ K,
+                                               const __bf16* __restrict__ V, __bf16* __restrict__ O,
+                                               const View& qw, const View& kw, const View& vw,
+                                               const View& ow, int slice, int d0, int h, int n,
+                                               float cmin) {
+  constexpr int DT = D / 16, DTW = DW / 16, KS = D / 32;
+  constexpr int TILES = DT * DTW, TPW = TILES / NW;
   static_assert(TILES % NW == 0 && TPW >= 1, "tiles split evenly over the waves");
-  __shared__ L_t L;
-  const int slice = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
-  constexpr int KS = D / 32;
   // The first Q rows go out together with K and V, so their latency is hidden behind the
   // reduction.
   const size_t qb = view_base(qw, slice, h);
@@ -208,21 +215,54 @@ void relu_linear_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   f32x4 pacc[TPW], dacc[TPW];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) { pacc[k] = zero4(); dacc[k] = zero4(); }
-  lin_reduce<D, NW>(L, K, V, view_base(kw, slice, h), kw.st, view_base(vw, slice, h), vw.st, 0,
-                    n, n, pacc, dacc);
+  lin_reduce<D, NW, DW>(L, K, V, view_base(kw, slice, h), kw.st, view_base(vw, slice, h), vw.st,
+                        0, n, n, d0, pacc, dacc);
   __bf16* so = (__bf16*)&L.s[0][0][0];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
-    const int t = w * TPW + k, ja = t / DT, dt = t - (t / DT) * DT;
+    const int t = w * TPW + k, ja = t / DTW, dt = t - (t / DTW) * DTW;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int in = 16 * ja + 4 * g + r;
       so[sop_pos<D>(in, 16 * dt + c)] = (__bf16)pacc[k][r];
-      if (dt == 0 && c == 0) L.z[in] = dacc[k / DT][r];
+      if (dt == 0 && c == 0) L.z[in] = dacc[k / DTW][r];
     }
   }
   __syncthreads();
-  lin_apply<D, NW>(L.s, L.z, Q, qb, qw.st, O, view_base(ow, slice, h), ow, 0, n, n, cmin, q0);
+  lin_apply<D, NW, DW>(L.s, L.z, Q, qb, qw.st, O, view_base(ow, slice, h), ow, 0, n, n, cmin,
+                       q0, d0);
+}
+
+// Workgroups 0 .. full - 1 take slices 0 .. full - 1 whole; with d = 64 the remaining
+// slices are shared by two workgroups, one per half of the output dims (both compute z
+// and read all of Q and K; each reads half of V and writes half of the output), so that a
+// grid with between one and two slices per CU gives every CU about the same work.  Ids
+// i and i + 8 of each run of 16 shared workgroups take the two halves of one slice (the
+// same XCD, so the second reads of Q and K can hit its L2).
+template <int D, int NW>
+__global__ __launch_bounds__(NW * kWave, 2)
+void relu_linear_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                      const __bf16* __restrict__ V, __bf16* __restrict__ O, View qw, View kw,
+                      View vw, View ow, int h, int n, float cmin, int full) {
+  __shared__ LinLds<D, NW, D> L;
+  const int b = blockIdx.x;
+  if (b < full) {
+    lin_fused_part<D, NW, D>(L, Q, K, V, O, qw, kw, vw, ow, b, 0, h, n, cmin);
+  } else if constexpr (D == 64) {
+    const int k = b - full;
+    const int nsh = (int)(gridDim.x - full);
+    int sl, hf;
+    if ((k | 15) < (nsh & ~15)) {
+      sl = ((k >> 4) << 3) + (k & 7);
+      hf = (k >> 3) & 1;
+    } else {
+      sl = k >> 1;
+      hf = k & 1;
+    }
+    static_assert(sizeof(LinLds<D, NW, D / 2>) <= sizeof(LinLds<D, NW, D>), "half fits");
+    lin_fused_part<D, NW, D / 2>(*reinterpret_cast<LinLds<D, NW, D / 2>*>(&L), Q, K, V, O, qw, kw,
+                                 vw, ow, full + sl, hf * (D / 2), h, n, cmin);
+  }
 }
 
 // Split plan, pass 1: per (slice, chunk) partial S tiles [slice][chunk][t][4][64] and z
@@ -243,8 +283,8 @@ void relu_linear_pass1(const __bf16* __restrict__ K, const __bf16* __restrict__ 
   f32x4 pacc[TPW], dacc[TPW];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) { pacc[k] = zero4(); dacc[k] = zero4(); }
-  lin_reduce<D, NW>(L, K, V, view_base(kw, slice, h), kw.st, view_base(vw, slice, h), vw.st, t0,
-                    t1, n, pacc, dacc);
+  lin_reduce<D, NW, D>(L, K, V, view_base(kw, slice, h), kw.st, view_base(vw, slice, h), vw.st,
+                       t0, t1, n, 0, pacc, dacc);
   const size_t sc = (size_t)slice * chunks + chunk;
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
@@ -320,18 +360,21 @@ void relu_linear_pass2(const __bf16* __restrict__ Q, __bf16* __restrict__ O, Vie
 
 hipError_t launch_relu_linear_bf16(const Geometry& g, const void* Q, const View& qw, const void* K,
                                    const View& kw, const void* V, const View& vw, void* O,
-                                   const View& ow, float cmin, hipStream_t s) {
+                                   const View& ow, float cmin, int num_cus, hipStream_t s) {
   constexpr int NW = 4;
-  if (g.slices > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)g.slices), block(NW * kWave);
+  const long long shared =
+      (g.d == 64) ? std::min<long long>(g.slices, std::max<long long>(0, 2LL * num_cus - g.slices)) : 0;
+  const long long full = g.slices - shared, grid = full + 2 * shared;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 gr((unsigned)grid), block(NW * kWave);
   if (g.d == 64)
-    relu_linear_bf16<64, NW><<<grid, block, 0, s>>>((const __bf16*)Q, (const __bf16*)K,
-                                                    (const __bf16*)V, (__bf16*)O, qw, kw, vw, ow,
-                                                    g.h, g.n, cmin);
+    relu_linear_bf16<64, NW><<<gr, block, 0, s>>>((const __bf16*)Q, (const __bf16*)K,
+                                                  (const __bf16*)V, (__bf16*)O, qw, kw, vw, ow,
+                                                  g.h, g.n, cmin, (int)full);
   else if (g.d == 32)
-    relu_linear_bf16<32, NW><<<grid, block, 0, s>>>((const __bf16*)Q, (const __bf16*)K,
-                                                    (const __bf16*)V, (__bf16*)O, qw, kw, vw, ow,
-                                                    g.h, g.n, cmin);
+    relu_linear_bf16<32, NW><<<gr, block, 0, s>>>((const __bf16*)Q, (const __bf16*)K,
+                                                  (const __bf16*)V, (__bf16*)O, qw, kw, vw, ow,
+                                                  g.h, g.n, cmin, (int)full);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
