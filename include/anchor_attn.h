@@ -24,7 +24,11 @@
  * a grow-only device workspace used by long sequences: the first call that needs a
  * larger workspace allocates it (hipMalloc, which may synchronize); later calls of the
  * same or smaller size allocate nothing.  A context must not be used by two host
- * threads at once.
+ * threads at once, and calls on one context that may run concurrently on different
+ * streams share that workspace and race: give each stream its own context (contexts are
+ * cheap; each owns only its workspaces).  Once an eager call of a shape has sized the
+ * workspaces, calls of that shape allocate nothing, record no memset and can be captured
+ * into a HIP graph.
  *
  * Errors: every function returns a status; nothing is thrown, printed or aborted across
  * this boundary.  All arguments are validated before any work is enqueued, so on an
