@@ -49,6 +49,9 @@ def load_library():
                                                         ctypes.c_float, i32, vp]
         lib.anchor_attn_block_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                                   i32, i32, i32, i32, i32, i32, vp]
+        lib.anchor_attn_backward_strided.argtypes = [vp, vp, llp, vp, vp, llp, vp, llp, vp, llp,
+                                                     vp, vp, llp, i32, i32, i32, i32, i32, i32,
+                                                     vp]
         lib.anchor_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                              i32, i32, i32, i32, i32, i32, vp]
         lib.anchor_attn_set_plan.argtypes = [vp, i32]
@@ -58,7 +61,7 @@ def load_library():
         lib.anchor_attn_status_string.restype = ctypes.c_char_p
         for f in (lib.anchor_attn_create, lib.anchor_attn_destroy, lib.anchor_attn_forward,
                   lib.anchor_attn_forward_strided, lib.anchor_attn_block_forward,
-                  lib.anchor_attn_relu_linear_forward,
+                  lib.anchor_attn_relu_linear_forward, lib.anchor_attn_backward_strided,
                   lib.anchor_attn_backward, lib.anchor_attn_set_plan,
                   lib.anchor_attn_describe_plan):
             f.restype = i32
@@ -226,8 +229,9 @@ class AnchorAttention:
 
     def backward(self, Q, U, V, dH, out=None, stream=None):
         """Gradients for dL/dH = dH: returns (dQ [B,h,n,d], dU [h,m,d] summed over the
-        batch, dV [B,h,n,d]), bf16, enqueued on ``stream``; no synchronisation.
-        ``out`` may give the three result tensors (dQ, dU, dV) to write into."""
+        batch, dV [B,h,n,d]), bf16, enqueued on ``stream``; no synchronisation.  Q, V, dH
+        (and dQ, dV in ``out``) may be strided views whose d values per token are
+        contiguous; U and dU are contiguous.  ``out`` may give (dQ, dU, dV) to write into."""
         import torch
         if Q.dim() != 4 or V.shape != Q.shape or dH.shape != Q.shape or U.dim() != 3:
             raise ValueError(f"bad shapes Q{tuple(Q.shape)} U{tuple(U.shape)} V{tuple(V.shape)} "
@@ -239,25 +243,41 @@ class AnchorAttention:
         for name, t in (("Q", Q), ("U", U), ("V", V), ("dH", dH)):
             if not t.is_cuda or t.device != self.device:
                 raise ValueError(f"{name} must live on {self.device}")
-            if not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
             if t.dtype != Q.dtype:
                 raise TypeError("Q, U, V and dH must share one dtype")
+        if not U.is_contiguous():
+            raise ValueError("U must be contiguous")
         if out is None:
-            dQ, dU, dV = torch.empty_like(Q), torch.empty_like(U), torch.empty_like(V)
+            dQ = torch.empty(Q.shape, dtype=Q.dtype, device=Q.device)
+            dU = torch.empty_like(U)
+            dV = torch.empty(Q.shape, dtype=Q.dtype, device=Q.device)
         else:
             dQ, dU, dV = out
             for name, t, like in (("dQ", dQ, Q), ("dU", dU, U), ("dV", dV, V)):
-                if t.shape != like.shape or t.dtype != like.dtype or t.device != like.device \
-                        or not t.is_contiguous():
-                    raise ValueError(f"{name} must be a contiguous {like.dtype} tensor of shape "
+                if t.shape != like.shape or t.dtype != like.dtype or t.device != like.device:
+                    raise ValueError(f"{name} must be a {like.dtype} tensor of shape "
                                      f"{tuple(like.shape)} on {like.device}")
+            if not dU.is_contiguous():
+                raise ValueError("dU must be contiguous")
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
-        _check(self._lib.anchor_attn_backward(
-            self._h, Q.data_ptr(), U.data_ptr(), V.data_ptr(), dH.data_ptr(), dQ.data_ptr(),
-            dU.data_ptr(), dV.data_ptr(), B, h, n, m, d, _dtype_code(Q),
-            ctypes.c_void_p(stream.cuda_stream)), "anchor_attn_backward")
+        sv = ctypes.c_void_p(stream.cuda_stream)
+        views = (Q, V, dH, dQ, dV)
+        if all(t.is_contiguous() for t in views):
+            _check(self._lib.anchor_attn_backward(
+                self._h, Q.data_ptr(), U.data_ptr(), V.data_ptr(), dH.data_ptr(), dQ.data_ptr(),
+                dU.data_ptr(), dV.data_ptr(), B, h, n, m, d, _dtype_code(Q), sv),
+                "anchor_attn_backward")
+            return dQ, dU, dV
+        st = []
+        for name, t in zip(("Q", "V", "dH", "dQ", "dV"), views):
+            if t.stride(3) != 1 and d > 1:
+                raise ValueError(f"{name}: the d values of a token must be contiguous")
+            st.append((ctypes.c_longlong * 3)(t.stride(0), t.stride(1), t.stride(2)))
+        _check(self._lib.anchor_attn_backward_strided(
+            self._h, Q.data_ptr(), st[0], U.data_ptr(), V.data_ptr(), st[1], dH.data_ptr(), st[2],
+            dQ.data_ptr(), st[3], dU.data_ptr(), dV.data_ptr(), st[4], B, h, n, m, d,
+            _dtype_code(Q), sv), "anchor_attn_backward_strided")
         return dQ, dU, dV
 
     def close(self) -> None:

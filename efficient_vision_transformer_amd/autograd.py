@@ -23,8 +23,9 @@ def _context(device) -> AnchorAttention:
 
 
 class AnchorAttentionFunction(torch.autograd.Function):
-    """H = A (Delta^-1 (A^T V)), A = rowsoftmax(Q U^T / sqrt(d)); Q, V [B, h, n, d], U
-    [h, m, d], all contiguous on one GPU."""
+    """H = A (Delta^-1 (A^T V)), A = rowsoftmax(Q U^T / sqrt(d)); Q, V [B, h, n, d] (views
+    whose d values per token are contiguous, e.g. halves of a packed projection), U [h, m, d]
+    contiguous, all on one GPU."""
 
     @staticmethod
     def forward(fctx, Q, U, V):
@@ -37,7 +38,7 @@ class AnchorAttentionFunction(torch.autograd.Function):
     def backward(fctx, dH):
         Q, U, V = fctx.saved_tensors
         ctx = _context(Q.device)
-        if not dH.is_contiguous():
+        if dH.stride(-1) != 1:
             dH = dH.contiguous()
         dQ, dU, dV = ctx.backward(Q, U, V, dH)
         return dQ, dU, dV

@@ -524,10 +524,11 @@ anchor_attn_status_t anchor_attn_relu_linear_forward(
   }
 }
 
-anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx, const void* Q, const void* U,
-                                          const void* V, const void* dH, void* dQ, void* dU,
-                                          void* dV, int B, int h, int n, int m, int d,
-                                          anchor_attn_dtype_t dtype, void* stream) {
+anchor_attn_status_t anchor_attn_backward_strided(
+    anchor_attn_ctx* ctx, const void* Q, const long long* q_strides, const void* U, const void* V,
+    const long long* v_strides, const void* dH, const long long* dh_strides, void* dQ,
+    const long long* dq_strides, void* dU, void* dV, const long long* dv_strides, int B, int h,
+    int n, int m, int d, anchor_attn_dtype_t dtype, void* stream) {
   if (!ctx) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
   try {
     Geometry g{};
@@ -537,23 +538,33 @@ anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx, const void* Q, c
     const Chosen plan = choose_backward(ctx, g, dtype);
     if (plan == Chosen::Unsupported) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
     const size_t es = 2;
-    const size_t act = (size_t)g.slices * (size_t)n * (size_t)d * es;
+    aa::BwdViews bv{g.vw.q, g.vw.q, g.vw.q, g.vw.q, g.vw.q};
+    if (!take_view(q_strides, es, &bv.q) || !take_view(v_strides, es, &bv.v) ||
+        !take_view(dh_strides, es, &bv.g) || !take_view(dq_strides, es, &bv.dq) ||
+        !take_view(dv_strides, es, &bv.dv))
+      return ANCHOR_ATTN_ERROR_INVALID_VALUE;
     const size_t ub = (size_t)h * (size_t)m * (size_t)d * es;
     if (ub > 0 && !dU) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
     if (!empty && (!Q || !U || !V || !dH || !dQ || !dV)) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
     const uintptr_t mis = ((uintptr_t)Q | (uintptr_t)U | (uintptr_t)V | (uintptr_t)dH |
                            (uintptr_t)dQ | (uintptr_t)dU | (uintptr_t)dV) & 15u;
     if (mis) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
-    const void* ins[4] = {Q, V, dH, U};
-    const size_t insz[4] = {act, act, act, ub};
-    void* outs[3] = {dQ, dV, dU};
-    const size_t outsz[3] = {act, act, ub};
-    for (int o = 0; o < 3; ++o) {
-      if (!outsz[o]) continue;
-      for (int i = 0; i < 4; ++i)
-        if (insz[i] && overlaps(outs[o], outsz[o], ins[i], insz[i])) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
-      for (int o2 = o + 1; o2 < 3; ++o2)
-        if (outsz[o2] && overlaps(outs[o], outsz[o], outs[o2], outsz[o2])) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    if (!empty) {
+      if (!view_injective(bv.dq, B, h, n, d) || !view_injective(bv.dv, B, h, n, d))
+        return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+      const void* ins[4] = {Q, V, dH, U};
+      const size_t insz[4] = {view_extent(bv.q, B, h, n, d, es), view_extent(bv.v, B, h, n, d, es),
+                              view_extent(bv.g, B, h, n, d, es), ub};
+      void* outs[3] = {dQ, dV, dU};
+      const size_t outsz[3] = {view_extent(bv.dq, B, h, n, d, es),
+                               view_extent(bv.dv, B, h, n, d, es), ub};
+      for (int o = 0; o < 3; ++o) {
+        if (!outsz[o]) continue;
+        for (int i = 0; i < 4; ++i)
+          if (insz[i] && overlaps(outs[o], outsz[o], ins[i], insz[i])) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+        for (int o2 = o + 1; o2 < 3; ++o2)
+          if (outsz[o2] && overlaps(outs[o], outsz[o], outs[o2], outsz[o2])) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+      }
     }
 
     DeviceGuard guard(ctx->device);
@@ -568,35 +579,31 @@ anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx, const void* Q, c
       return ANCHOR_ATTN_SUCCESS;
     }
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    hipError_t e;
     if (plan == Chosen::Fused) {
       st = ensure_workspace(ctx, al((size_t)g.slices * g.m_pad * g.d * sizeof(float)));
       if (st != ANCHOR_ATTN_SUCCESS) return st;
-      const hipError_t e = aa::launch_backward_fused_bf16(g, Q, U, V, dH, dQ, dU, dV,
-                                                          (float*)ctx->workspace, s);
-      if (e != hipSuccess) {
-        (void)hipGetLastError();
-        return ANCHOR_ATTN_ERROR_HIP;
-      }
-      return ANCHOR_ATTN_SUCCESS;
+      e = aa::launch_backward_fused_bf16(g, bv, Q, U, V, dH, dQ, dU, dV, (float*)ctx->workspace, s);
+    } else {
+      const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
+      const size_t part = al((size_t)g.slices * p.chunks1 * g.m_pad * g.d * sizeof(float));
+      const size_t dpart = al((size_t)g.slices * p.chunks1 * g.m_pad * sizeof(float));
+      const size_t ops = al((size_t)g.slices * g.m_pad * g.d * es);
+      const size_t ddb = al((size_t)g.slices * g.m_pad * sizeof(float));
+      st = ensure_workspace(ctx, 3 * part + dpart + 3 * ops + ddb);
+      if (st != ANCHOR_ATTN_SUCCESS) return st;
+      char* w = (char*)ctx->workspace;
+      aa::BackwardBuffers wb{};
+      wb.partP = (float*)w; w += part;
+      wb.partG = (float*)w; w += part;
+      wb.partU = (float*)w; w += part;
+      wb.dpart = (float*)w; w += dpart;
+      wb.wu = w; w += ops;
+      wb.dpu = w; w += ops;
+      wb.dpw = w; w += ops;
+      wb.dd = (float*)w;
+      e = aa::launch_backward_bf16(g, p, wb, bv, Q, U, V, dH, dQ, dU, dV, s);
     }
-    const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
-    const size_t part = al((size_t)g.slices * p.chunks1 * g.m_pad * g.d * sizeof(float));
-    const size_t dpart = al((size_t)g.slices * p.chunks1 * g.m_pad * sizeof(float));
-    const size_t ops = al((size_t)g.slices * g.m_pad * g.d * es);
-    const size_t ddb = al((size_t)g.slices * g.m_pad * sizeof(float));
-    st = ensure_workspace(ctx, 3 * part + dpart + 3 * ops + ddb);
-    if (st != ANCHOR_ATTN_SUCCESS) return st;
-    char* w = (char*)ctx->workspace;
-    aa::BackwardBuffers wb{};
-    wb.partP = (float*)w; w += part;
-    wb.partG = (float*)w; w += part;
-    wb.partU = (float*)w; w += part;
-    wb.dpart = (float*)w; w += dpart;
-    wb.wu = w; w += ops;
-    wb.dpu = w; w += ops;
-    wb.dpw = w; w += ops;
-    wb.dd = (float*)w;
-    const hipError_t e = aa::launch_backward_bf16(g, p, wb, Q, U, V, dH, dQ, dU, dV, s);
     if (e != hipSuccess) {
       (void)hipGetLastError();
       return ANCHOR_ATTN_ERROR_HIP;
@@ -605,6 +612,14 @@ anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx, const void* Q, c
   } catch (...) {
     return ANCHOR_ATTN_ERROR_HIP;
   }
+}
+
+anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx, const void* Q, const void* U,
+                                          const void* V, const void* dH, void* dQ, void* dU,
+                                          void* dV, int B, int h, int n, int m, int d,
+                                          anchor_attn_dtype_t dtype, void* stream) {
+  return anchor_attn_backward_strided(ctx, Q, nullptr, U, V, nullptr, dH, nullptr, dQ, nullptr,
+                                      dU, dV, nullptr, B, h, n, m, d, dtype, stream);
 }
 
 }  // extern "C"

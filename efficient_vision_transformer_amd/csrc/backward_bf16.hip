@@ -114,7 +114,7 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                 const u32x4* __restrict__ wu, const u32x4* __restrict__ dpu,
                 const u32x4* __restrict__ dpw, const float* __restrict__ dd,
                 __bf16* __restrict__ dQ, __bf16* __restrict__ dV, float* __restrict__ partU,
-                int h, int n, int m, int chunks, int chunk_len, float c2, float cs) {
+                BwdViews bv, int h, int n, int m, int chunks, int chunk_len, float c2, float cs) {
   constexpr int NW = 4, KS = D / 32, DT = D / 16, AT = 2 * MP;
   constexpr int TILES = AT * DT, TPW = TILES / NW;
   constexpr int AS = tr_stride<32 * MP>(), VS = tr_stride<D>();
@@ -125,7 +125,9 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const size_t base = (size_t)slice * (size_t)n * D;
+  const size_t qb = view_base(bv.q, slice, h), vb = view_base(bv.v, slice, h);
+  const size_t gb = view_base(bv.g, slice, h);
+  const size_t dqb = view_base(bv.dq, slice, h), dvb = view_base(bv.dv, slice, h);
   const int t_begin = chunk * chunk_len;
   const int t_end = min(n, t_begin + chunk_len);
   const int npairs = (t_end - t_begin + 31) >> 5;
@@ -183,9 +185,9 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         const int row = t_begin + 32 * p + 16 * tt + c;
         const bool ok = row < t_end;
         u32x4 qv[KS], vv[KS], gv[KS];
-        load_rows<D>(Q, base, D, row, n, g, qv);
-        load_rows<D>(V, base, D, row, n, g, vv);
-        load_rows<D>(G, base, D, row, n, g, gv);
+        load_rows<D>(Q, qb, bv.q.st, row, n, g, qv);
+        load_rows<D>(V, vb, bv.v.st, row, n, g, vv);
+        load_rows<D>(G, gb, bv.g.st, row, n, g, gv);
         // A (normalised, rounded to bf16) in the transposed layout: ab[jj] lane (c,g) holds
         // token c, anchors 32jj + 4g .. + 3 (slots 0-3) and 32jj + 16 + 4g .. + 3 (4-7).
         bf16x8 ab[MP];
@@ -251,7 +253,8 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         }
         // dQ^T = c U^T dS^T and dV^T = dP^T A^T, two dim tiles at a time: lane (c,g) ends
         // with token c, dims (D/4)g + 4dt2 + r'.
-        const size_t off = base + (size_t)row * D + (D / 4) * g;
+        const size_t oq = dqb + view_row(bv.dq, row) + (D / 4) * g;
+        const size_t ov = dvb + view_row(bv.dv, row) + (D / 4) * g;
 #pragma unroll
         for (int hh = 0; hh < DT / 2; ++hh) {
           f32x4 q0 = zero4(), q1 = zero4();
@@ -260,14 +263,14 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
             q0 = mfma_bf16(as_bf16x8(ut_lds[2 * hh][jj][lane]), dsb[jj], q0);
             q1 = mfma_bf16(as_bf16x8(ut_lds[2 * hh + 1][jj][lane]), dsb[jj], q1);
           }
-          if (ok) __builtin_nontemporal_store(as_u32x4(pack_bf16(q0 * cs, q1 * cs)), (u32x4*)(dQ + off + 8 * hh));
+          if (ok) __builtin_nontemporal_store(as_u32x4(pack_bf16(q0 * cs, q1 * cs)), (u32x4*)(dQ + oq + 8 * hh));
           f32x4 v0 = zero4(), v1 = zero4();
 #pragma unroll
           for (int jj = 0; jj < MP; ++jj) {
             v0 = mfma_bf16(as_bf16x8(dpw_lds[2 * hh][jj][lane]), ab[jj], v0);
             v1 = mfma_bf16(as_bf16x8(dpw_lds[2 * hh + 1][jj][lane]), ab[jj], v1);
           }
-          if (ok) __builtin_nontemporal_store(as_u32x4(pack_bf16(v0, v1)), (u32x4*)(dV + off + 8 * hh));
+          if (ok) __builtin_nontemporal_store(as_u32x4(pack_bf16(v0, v1)), (u32x4*)(dV + ov + 8 * hh));
         }
         // Rows of dS ([token][anchor], dsb[jj] holds anchors 32jj + 4g .. + 3 and
         // 32jj + 16 + 4g .. + 3).
@@ -365,13 +368,18 @@ hipError_t launch_du_reduce_bf16(const Geometry& g, const float* partU, int chun
 // ---------------------------------------------------------------------------------------
 template <int D, int AT>
 static hipError_t go_bwd(const Geometry& g, const SplitPlan& p, const BackwardBuffers& wb,
-                         const void* Q, const void* U, const void* V, const void* G, void* dQ,
-                         void* dU, void* dV, hipStream_t s) {
+                         const BwdViews& bv, const void* Q, const void* U, const void* V,
+                         const void* G, void* dQ, void* dU, void* dV, hipStream_t s) {
   constexpr int MP = AT / 2;
   const float cs = 1.0f / sqrtf((float)D);
-  hipError_t e = launch_pass1_bf16(g, p, Q, U, V, wb.partP, wb.dpart, s);
+  // pass 1 reads Q through the first view of its geometry and X through the second
+  Geometry gv = g, gg = g;
+  gv.vw.q = gg.vw.q = bv.q;
+  gv.vw.v = bv.v;
+  gg.vw.v = bv.g;
+  hipError_t e = launch_pass1_bf16(gv, p, Q, U, V, wb.partP, wb.dpart, s);
   if (e != hipSuccess) return e;
-  e = launch_pass1_bf16(g, p, Q, U, G, wb.partG, wb.dpart, s);
+  e = launch_pass1_bf16(gg, p, Q, U, G, wb.partG, wb.dpart, s);
   if (e != hipSuccess) return e;
   bwd_finalize<D><<<dim3((unsigned)(g.slices * AT)), dim3(256), 0, s>>>(
       wb.partP, wb.partG, wb.dpart, (__bf16*)wb.wu, (__bf16*)wb.dpu, (__bf16*)wb.dpw, wb.dd,
@@ -379,7 +387,7 @@ static hipError_t go_bwd(const Geometry& g, const SplitPlan& p, const BackwardBu
   bwd_tokens<D, MP><<<dim3((unsigned)(g.slices * p.chunks1)), dim3(4 * kWave), 0, s>>>(
       (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (const __bf16*)G,
       (const u32x4*)wb.wu, (const u32x4*)wb.dpu, (const u32x4*)wb.dpw, wb.dd, (__bf16*)dQ,
-      (__bf16*)dV, wb.partU, g.h, g.n, g.m, p.chunks1, p.chunk_len1, g.c2, cs);
+      (__bf16*)dV, wb.partU, bv, g.h, g.n, g.m, p.chunks1, p.chunk_len1, g.c2, cs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_du_reduce_bf16(g, wb.partU, p.chunks1, dU, s);
@@ -387,13 +395,13 @@ static hipError_t go_bwd(const Geometry& g, const SplitPlan& p, const BackwardBu
 
 template <int D>
 static hipError_t dispatch_bwd(const Geometry& g, const SplitPlan& p, const BackwardBuffers& wb,
-                               const void* Q, const void* U, const void* V, const void* G,
-                               void* dQ, void* dU, void* dV, hipStream_t s) {
+                               const BwdViews& bv, const void* Q, const void* U, const void* V,
+                               const void* G, void* dQ, void* dU, void* dV, hipStream_t s) {
   switch (g.at) {
-    case 2: return go_bwd<D, 2>(g, p, wb, Q, U, V, G, dQ, dU, dV, s);
-    case 4: return go_bwd<D, 4>(g, p, wb, Q, U, V, G, dQ, dU, dV, s);
-    case 6: return go_bwd<D, 6>(g, p, wb, Q, U, V, G, dQ, dU, dV, s);
-    case 8: return go_bwd<D, 8>(g, p, wb, Q, U, V, G, dQ, dU, dV, s);
+    case 2: return go_bwd<D, 2>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
+    case 4: return go_bwd<D, 4>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
+    case 6: return go_bwd<D, 6>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
+    case 8: return go_bwd<D, 8>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -411,10 +419,10 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
 }
 
 hipError_t launch_backward_bf16(const Geometry& g, const SplitPlan& p, const BackwardBuffers& wb,
-                                const void* Q, const void* U, const void* V, const void* G,
-                                void* dQ, void* dU, void* dV, hipStream_t s) {
-  if (g.d == 64) return dispatch_bwd<64>(g, p, wb, Q, U, V, G, dQ, dU, dV, s);
-  if (g.d == 32) return dispatch_bwd<32>(g, p, wb, Q, U, V, G, dQ, dU, dV, s);
+                                const BwdViews& bv, const void* Q, const void* U, const void* V,
+                                const void* G, void* dQ, void* dU, void* dV, hipStream_t s) {
+  if (g.d == 64) return dispatch_bwd<64>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
+  if (g.d == 32) return dispatch_bwd<32>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
   return hipErrorInvalidValue;
 }
 

@@ -64,13 +64,19 @@ struct TileRows {
   u32x4 q[D / 32], v[D / 32], g[D / 32];
 };
 
+// Start of the slice's rows in Q, V, G and their token strides.
+struct SliceRows {
+  size_t q, v, g;
+  long long qs, vs, gs;
+};
+
 template <int D>
 __device__ __forceinline__ void load_tile_rows(const __bf16* Q, const __bf16* V, const __bf16* G,
-                                               size_t base, int row, int n, int g,
+                                               const SliceRows& sr, int row, int n, int g,
                                                TileRows<D>& t) {
-  load_rows_c<D, D>(Q, base, D, row, n, g, 0, t.q);
-  load_rows_c<D, D>(V, base, D, row, n, g, 0, t.v);
-  load_rows_c<D, D>(G, base, D, row, n, g, 0, t.g);
+  load_rows_c<D, D>(Q, sr.q, sr.qs, row, n, g, 0, t.q);
+  load_rows_c<D, D>(V, sr.v, sr.vs, row, n, g, 0, t.v);
+  load_rows_c<D, D>(G, sr.g, sr.gs, row, n, g, 0, t.g);
 }
 
 // Row-major copies of a tile's rows ([token][anchor] for A or dS, [token][dim] for the
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(NW * kWave, 1)
 void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                const __bf16* __restrict__ V, const __bf16* __restrict__ G,
                __bf16* __restrict__ dQ, __bf16* __restrict__ dV, float* __restrict__ partU,
-               int h, int n, int m, float c2, float cs) {
+               BwdViews bv, int h, int n, int m, float c2, float cs) {
   using L_t = BwdLds<D, MP, NW>;
   constexpr int AT = 2 * MP, KS = D / 32, DT = D / 16;
   constexpr int AS = L_t::AS, VS = L_t::VS;
@@ -113,7 +119,9 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
-  const size_t base = (size_t)slice * (size_t)n * D;
+  const SliceRows sr{view_base(bv.q, slice, h), view_base(bv.v, slice, h),
+                     view_base(bv.g, slice, h), bv.q.st, bv.v.st, bv.g.st};
+  const size_t dqb = view_base(bv.dq, slice, h), dvb = view_base(bv.dv, slice, h);
   const int npairs = (n + 31) >> 5;
   const int rounds = KEEP ? ROUNDS : (npairs + NW - 1) / NW;
 
@@ -124,7 +132,7 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   for (int r = 0; r < RK; ++r)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
-      load_tile_rows<D>(Q, V, G, base, 32 * (r * NW + w) + 16 * tt + c, n, g, rows[r][tt]);
+      load_tile_rows<D>(Q, V, G, sr, 32 * (r * NW + w) + 16 * tt + c, n, g, rows[r][tt]);
 
   const __bf16* Uh = U + (size_t)head * m * D;
   for (int idx = threadIdx.x; idx < AT * KS * kWave; idx += NW * kWave) {
@@ -162,7 +170,7 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     const bool more = !KEEP && (p + NW < npairs);
     if (more) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) load_tile_rows<D>(Q, V, G, base, 32 * (p + NW) + 16 * tt + c, n, g, nxt[tt]);
+      for (int tt = 0; tt < 2; ++tt) load_tile_rows<D>(Q, V, G, sr, 32 * (p + NW) + 16 * tt + c, n, g, nxt[tt]);
     }
     if (p < npairs) {
 #pragma unroll
@@ -239,7 +247,7 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   // ---- phase 3: dQ, dV and the dS^T Q tiles ---------------------------------------------
   if constexpr (!KEEP) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) load_tile_rows<D>(Q, V, G, base, 32 * w + 16 * tt + c, n, g, rows[0][tt]);
+    for (int tt = 0; tt < 2; ++tt) load_tile_rows<D>(Q, V, G, sr, 32 * w + 16 * tt + c, n, g, rows[0][tt]);
   }
 #pragma unroll (KEEP ? RK : 1)
   for (int r = 0; r < rounds; ++r) {
@@ -251,7 +259,7 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     const bool more = !KEEP && (p + NW < npairs);
     if (more) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) load_tile_rows<D>(Q, V, G, base, 32 * (p + NW) + 16 * tt + c, n, g, nxt[tt]);
+      for (int tt = 0; tt < 2; ++tt) load_tile_rows<D>(Q, V, G, sr, 32 * (p + NW) + 16 * tt + c, n, g, nxt[tt]);
     }
     if (p < npairs) {
 #pragma unroll
@@ -309,24 +317,24 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
           const bool lo = c < 8;
           const int ta = row - c + (c & 7), tb = ta + 8;
           const int o2 = (lo ? 0 : 32) + 8 * g;
-          auto put = [&](const f32x4* hx, __bf16* X) {
+          auto put = [&](const f32x4* hx, __bf16* X, size_t xb, const View& xw) {
             const u32x4 x0 = as_u32x4(pack_bf16(hx[0], hx[1]));
             const u32x4 x1 = as_u32x4(pack_bf16(hx[2], hx[3]));
             const u32x4 y = lo ? x1 : x0;
             u32x4 sw;
 #pragma unroll
             for (int i = 0; i < 4; ++i) sw[i] = __builtin_amdgcn_update_dpp(0u, y[i], 0x128, 0xF, 0xF, false);
-            if (ta < n) __builtin_nontemporal_store(lo ? x0 : sw, (u32x4*)(X + base + (size_t)ta * D + o2));
-            if (tb < n) __builtin_nontemporal_store(lo ? sw : x1, (u32x4*)(X + base + (size_t)tb * D + o2));
+            if (ta < n) __builtin_nontemporal_store(lo ? x0 : sw, (u32x4*)(X + xb + view_row(xw, ta) + o2));
+            if (tb < n) __builtin_nontemporal_store(lo ? sw : x1, (u32x4*)(X + xb + view_row(xw, tb) + o2));
           };
-          put(hq, dQ);
-          put(hv, dV);
+          put(hq, dQ, dqb, bv.dq);
+          put(hv, dV, dvb, bv.dv);
         } else if (row < n) {
-          const size_t off = base + (size_t)row * D + 8 * g;
+          const size_t oq = dqb + view_row(bv.dq, row) + 8 * g, ov = dvb + view_row(bv.dv, row) + 8 * g;
 #pragma unroll
           for (int hh = 0; hh < DT / 2; ++hh) {
-            __builtin_nontemporal_store(as_u32x4(pack_bf16(hq[2 * hh], hq[2 * hh + 1])), (u32x4*)(dQ + off + 32 * hh));
-            __builtin_nontemporal_store(as_u32x4(pack_bf16(hv[2 * hh], hv[2 * hh + 1])), (u32x4*)(dV + off + 32 * hh));
+            __builtin_nontemporal_store(as_u32x4(pack_bf16(hq[2 * hh], hq[2 * hh + 1])), (u32x4*)(dQ + oq + 32 * hh));
+            __builtin_nontemporal_store(as_u32x4(pack_bf16(hv[2 * hh], hv[2 * hh + 1])), (u32x4*)(dV + ov + 32 * hh));
           }
         }
         put_anchor_row<MP, AS>(L.a, lrow, g, dsb);
@@ -367,37 +375,39 @@ template <int D, int MP>
 constexpr int bwd_waves() { return MP == 2 ? 2 : 4; }
 
 template <int D, int MP, int ROUNDS>
-static hipError_t go_fused(const Geometry& g, const void* Q, const void* U, const void* V,
-                           const void* G, void* dQ, void* dV, float* partU, hipStream_t s) {
+static hipError_t go_fused(const Geometry& g, const BwdViews& bv, const void* Q, const void* U,
+                           const void* V, const void* G, void* dQ, void* dV, float* partU,
+                           hipStream_t s) {
   constexpr int NW = bwd_waves<D, MP>();
   if (g.slices > 0x7fffffffLL) return hipErrorInvalidValue;
   bwd_fused<D, MP, NW, ROUNDS><<<dim3((unsigned)g.slices), dim3(NW * kWave), 0, s>>>(
       (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (const __bf16*)G, (__bf16*)dQ,
-      (__bf16*)dV, partU, g.h, g.n, g.m, g.c2, 1.0f / sqrtf((float)D));
+      (__bf16*)dV, partU, bv, g.h, g.n, g.m, g.c2, 1.0f / sqrtf((float)D));
   return hipGetLastError();
 }
 
 template <int D, int MP>
-static hipError_t fused_rounds(const Geometry& g, const void* Q, const void* U, const void* V,
-                               const void* G, void* dQ, void* dV, float* partU, hipStream_t s) {
+static hipError_t fused_rounds(const Geometry& g, const BwdViews& bv, const void* Q, const void* U,
+                               const void* V, const void* G, void* dQ, void* dV, float* partU,
+                               hipStream_t s) {
   constexpr int NW = bwd_waves<D, MP>();
   const int rounds = ((g.n + 31) / 32 + NW - 1) / NW;
-  if (rounds <= 1) return go_fused<D, MP, 1>(g, Q, U, V, G, dQ, dV, partU, s);
-  if (rounds == 2) return go_fused<D, MP, 2>(g, Q, U, V, G, dQ, dV, partU, s);
-  return go_fused<D, MP, 0>(g, Q, U, V, G, dQ, dV, partU, s);
+  if (rounds <= 1) return go_fused<D, MP, 1>(g, bv, Q, U, V, G, dQ, dV, partU, s);
+  if (rounds == 2) return go_fused<D, MP, 2>(g, bv, Q, U, V, G, dQ, dV, partU, s);
+  return go_fused<D, MP, 0>(g, bv, Q, U, V, G, dQ, dV, partU, s);
 }
 
-hipError_t launch_backward_fused_bf16(const Geometry& g, const void* Q, const void* U,
-                                      const void* V, const void* G, void* dQ, void* dU, void* dV,
-                                      float* partU, hipStream_t s) {
+hipError_t launch_backward_fused_bf16(const Geometry& g, const BwdViews& bv, const void* Q,
+                                      const void* U, const void* V, const void* G, void* dQ,
+                                      void* dU, void* dV, float* partU, hipStream_t s) {
   if (!bwd_fused_supported(g)) return hipErrorInvalidValue;
   hipError_t e;
   if (g.d == 64)
-    e = (g.m_pad == 32) ? fused_rounds<64, 1>(g, Q, U, V, G, dQ, dV, partU, s)
-                        : fused_rounds<64, 2>(g, Q, U, V, G, dQ, dV, partU, s);
+    e = (g.m_pad == 32) ? fused_rounds<64, 1>(g, bv, Q, U, V, G, dQ, dV, partU, s)
+                        : fused_rounds<64, 2>(g, bv, Q, U, V, G, dQ, dV, partU, s);
   else
-    e = (g.m_pad == 32) ? fused_rounds<32, 1>(g, Q, U, V, G, dQ, dV, partU, s)
-                        : fused_rounds<32, 2>(g, Q, U, V, G, dQ, dV, partU, s);
+    e = (g.m_pad == 32) ? fused_rounds<32, 1>(g, bv, Q, U, V, G, dQ, dV, partU, s)
+                        : fused_rounds<32, 2>(g, bv, Q, U, V, G, dQ, dV, partU, s);
   if (e != hipSuccess) return e;
   return launch_du_reduce_bf16(g, partU, 1, dU, s);
 }

@@ -67,11 +67,15 @@ struct BackwardBuffers {
   float* dd;      // dDelta                        [slice][16 AT]
   float* partU;   // partials of dS^T Q            [slice][chunk][AT][DT][256]
 };
+// Views of the backward's tensors: Q, V, dH (inputs) and dQ, dV (outputs).
+struct BwdViews {
+  View q, v, g, dq, dv;
+};
 // Zeroes `bytes` (a multiple of 4) with a fill kernel (safe under stream capture).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_backward_bf16(const Geometry& g, const SplitPlan& p, const BackwardBuffers& wb,
-                                const void* Q, const void* U, const void* V, const void* G,
-                                void* dQ, void* dU, void* dV, hipStream_t stream);
+                                const BwdViews& bv, const void* Q, const void* U, const void* V,
+                                const void* G, void* dQ, void* dU, void* dV, hipStream_t stream);
 // dU = (1/sqrt(d)) x the sum over batch and chunks of per-(slice, chunk) partial tiles
 // [slice][chunk][AT][DT][256] of dS^T Q.
 hipError_t launch_du_reduce_bf16(const Geometry& g, const float* partU, int chunks, void* dU,
@@ -79,9 +83,9 @@ hipError_t launch_du_reduce_bf16(const Geometry& g, const float* partU, int chun
 // Short-sequence backward: one workgroup per slice (n <= 1024, m <= 64, d = 32 or 64),
 // then the dU reduction; partU holds slices x m_pad x d floats.
 bool bwd_fused_supported(const Geometry& g);
-hipError_t launch_backward_fused_bf16(const Geometry& g, const void* Q, const void* U,
-                                      const void* V, const void* G, void* dQ, void* dU, void* dV,
-                                      float* partU, hipStream_t stream);
+hipError_t launch_backward_fused_bf16(const Geometry& g, const BwdViews& bv, const void* Q,
+                                      const void* U, const void* V, const void* G, void* dQ,
+                                      void* dU, void* dV, float* partU, hipStream_t stream);
 // Projections of the attention block (hipBLASLt): D[T, N] = X[T, K] W[K, N] + bias[N],
 // row-major bf16, fp32 accumulation; bias may be null.  gemm_prepare finds descriptors
 // and an algorithm for a shape (false: none), gemm_run enqueues with a workspace of

@@ -181,6 +181,22 @@ anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx,
                                           int B, int h, int n, int m, int d,
                                           anchor_attn_dtype_t dtype, void* stream);
 
+/* The backward on strided views (as anchor_attn_forward_strided: host arrays of three
+ * element strides (batch, head, token), NULL = contiguous) for Q, V, dH and the outputs
+ * dQ, dV; U and dU stay contiguous [h, m, d].  dQ's and dV's rows must be distinct and the
+ * outputs' spans must not overlap each other or any input's span.  Everything else as
+ * anchor_attn_backward, which is this call with five NULL stride arrays. */
+anchor_attn_status_t anchor_attn_backward_strided(anchor_attn_ctx* ctx,
+                                                  const void* Q, const long long* q_strides,
+                                                  const void* U,
+                                                  const void* V, const long long* v_strides,
+                                                  const void* dH, const long long* dh_strides,
+                                                  void* dQ, const long long* dq_strides,
+                                                  void* dU,
+                                                  void* dV, const long long* dv_strides,
+                                                  int B, int h, int n, int m, int d,
+                                                  anchor_attn_dtype_t dtype, void* stream);
+
 /* Forces a plan for later forward calls on this context (tests and tuning); AUTO
  * restores the default choice.  A forced plan that cannot run a given shape makes that
  * forward call return NOT_SUPPORTED. */

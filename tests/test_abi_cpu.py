@@ -62,6 +62,9 @@ def test_null_arguments(lib):
                                                None, 1, 1, 1, 32, 100.0, 1.0, 1, None) == 1
     assert lib.anchor_attn_block_forward(None, None, None, None, None, None, None, None,
                                          1, 1, 1, 1, 32, 1, None) == 1
+    assert lib.anchor_attn_backward_strided(None, None, None, None, None, None, None, None,
+                                            None, None, None, None, None, 1, 1, 1, 1, 32, 1,
+                                            None) == 1
     assert lib.anchor_attn_backward(None, None, None, None, None, None, None, None,
                                     1, 1, 1, 1, 32, 1, None) == 1
     buf = ctypes.create_string_buffer(64)

@@ -181,3 +181,35 @@ def test_backward_anchor_sum_invariant_full_size(ctx, dev):
     scale = np.abs(dU).max()
     print(f"  max |sum_a dU| / max |dU| = {col / scale:.3e}", flush=True)
     assert col <= 5e-2 * scale
+
+
+@pytest.mark.parametrize("plan", ["fused", "split"])
+def test_backward_strided_views(ctxs, dev, plan):
+    """Q and V read from a packed [B, n, 3, h, d] tensor, dH from a [B, n, h, d] tensor, dQ
+    and dV written into padded [B, n, h, d + 8] buffers whose gaps must stay untouched;
+    the gradients equal the contiguous call's bit for bit and match the oracle."""
+    import torch
+    x = make_inputs("vit_s16_224", shape={"B": 4})
+    G, gbits = make_upstream_grad(x, 9300)
+    w = x.workload
+    arrs = [x.bits[k].transpose(0, 2, 1, 3) for k in ("Q", "Q", "V")]
+    qkv = _bits_to_dev(np.stack(arrs, axis=2), dev)
+    Qv, Vv = qkv[:, :, 0].permute(0, 2, 1, 3), qkv[:, :, 2].permute(0, 2, 1, 3)
+    dHv = _bits_to_dev(np.ascontiguousarray(gbits.transpose(0, 2, 1, 3)), dev).permute(0, 2, 1, 3)
+    U = _bits_to_dev(x.bits["U"], dev)
+    bufs = [torch.full((w.B, w.n, w.h, w.d + 8), 5.0, dtype=torch.bfloat16, device=dev)
+            for _ in range(2)]
+    dQv, dVv = (b_[..., :w.d].permute(0, 2, 1, 3) for b_ in bufs)
+    dU = torch.empty_like(U)
+    print(f"  strided backward plan={plan}", flush=True)
+    ctxs[plan].backward(Qv, U, Vv, dHv, out=(dQv, dU, dVv))
+    torch.cuda.synchronize()
+    for b_ in bufs:
+        assert torch.all(b_[..., w.d:] == 5.0).item(), "writes outside the output views"
+    Q, V, dH = _bits_to_dev(x.bits["Q"], dev), _bits_to_dev(x.bits["V"], dev), _bits_to_dev(gbits, dev)
+    cq, cu, cv = ctxs[plan].backward(Q, U, V, dH)
+    torch.cuda.synchronize()
+    for a, b_ in ((dQv, cq), (dU, cu), (dVv, cv)):
+        assert torch.equal(a.contiguous().view(torch.int16), b_.view(torch.int16))
+    ref = oracle.anchor_backward(x.Q, x.U, x.V, G)
+    _check_all((to_host(cq), to_host(cu), to_host(cv)), ref, f"strided {plan}")
