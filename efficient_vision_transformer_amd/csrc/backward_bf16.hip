@@ -141,27 +141,50 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   __shared__ __attribute__((aligned(16))) __bf16 s_rows[NW * 32 * AS];   // rows of dS
   __shared__ __attribute__((aligned(16))) __bf16 q_rows[NW * 32 * VS];   // rows of Q
 
-  // Stage the slice's operands.
+  // Stage the slice's operands: every load is issued before the first LDS write.
+  constexpr int T = NW * kWave, UCH = AT * KS * kWave, UTC = 16 * AT * D / 8;
+  static_assert(16 * AT <= T, "one Delta-gradient value per thread");
   const __bf16* Uh = U + (size_t)head * m * D;
-  for (int idx = threadIdx.x; idx < AT * KS * kWave; idx += NW * kWave) {
+  const size_t so = (size_t)slice * UCH;
+  Stage<UCH, T> ust, wust, dpust;
+  stage_load(ust, [&](int idx) {
     const int j = idx / (KS * kWave), kk = (idx / kWave) % KS, l = idx & 63;
     const int a = 16 * j + (l & 15);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + 8 * KS * (l >> 4) + 8 * kk);
-    (&u_lds[0][0][0])[idx] = v;
-    (&wu_lds[0][0][0])[idx] = wu[(size_t)slice * AT * KS * kWave + idx];
-    (&dpu_lds[0][0][0])[idx] = dpu[(size_t)slice * AT * KS * kWave + idx];
-  }
-  for (int idx = threadIdx.x; idx < DT * MP * kWave; idx += NW * kWave)
-    (&dpw_lds[0][0][0])[idx] = dpw[(size_t)slice * DT * MP * kWave + idx];
+    return v;
+  });
+  stage_load(wust, [&](int idx) { return wu[so + idx]; });
+  stage_load(dpust, [&](int idx) { return dpu[so + idx]; });
+  Stage<DT * MP * kWave, T> dpwst;
+  stage_load(dpwst, [&](int idx) { return dpw[(size_t)slice * DT * MP * kWave + idx]; });
+  // rows of U (padded anchors zero) as chunks of 8 dims: chunk i = anchor i / (D/8)
+  Stage<UTC, T> utst;
+  stage_load(utst, [&](int idx) {
+    const int a = idx / (D / 8), k = 8 * (idx - a * (D / 8));
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + k);
+    return v;
+  });
+  const float ddv = ((int)threadIdx.x < 16 * AT) ? dd[(size_t)slice * 16 * AT + threadIdx.x] : 0.f;
+  stage_store(ust, &u_lds[0][0][0]);
+  stage_store(wust, &wu_lds[0][0][0]);
+  stage_store(dpust, &dpu_lds[0][0][0]);
+  stage_store(dpwst, &dpw_lds[0][0][0]);
   {
     __bf16* ut = (__bf16*)&ut_lds[0][0][0];
-    for (int e = threadIdx.x; e < 16 * AT * D; e += NW * kWave) {
-      const int a = e / D, k = e - (e / D) * D;
-      ut[wt_layout_index<D>(MP, a, k)] = (a < m) ? Uh[(size_t)a * D + k] : (__bf16)0.f;
+#pragma unroll
+    for (int i = 0; i < Stage<UTC, T>::kPer; ++i) {
+      const int idx = (int)threadIdx.x + i * T;
+      if (UTC % T == 0 || idx < UTC) {
+        const int a = idx / (D / 8), k = 8 * (idx - a * (D / 8));
+        const bf16x8 v = as_bf16x8(utst.r[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ut[wt_layout_index<D>(MP, a, k + e)] = v[e];
+      }
     }
   }
-  for (int e = threadIdx.x; e < 16 * AT; e += NW * kWave) dd_lds[e] = dd[(size_t)slice * 16 * AT + e];
+  if ((int)threadIdx.x < 16 * AT) dd_lds[threadIdx.x] = ddv;
   f32x4 mask[2];
   pad_mask<MP>(g, m, mask);
   const bf16x8 ones = splat_bf16(1.f);

@@ -134,19 +134,38 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     for (int tt = 0; tt < 2; ++tt)
       load_tile_rows<D>(Q, V, G, sr, 32 * (r * NW + w) + 16 * tt + c, n, g, rows[r][tt]);
 
+  // U twice: as the logits' left operands and transposed for dQ; every load is issued
+  // before the first LDS write.
   const __bf16* Uh = U + (size_t)head * m * D;
-  for (int idx = threadIdx.x; idx < AT * KS * kWave; idx += NW * kWave) {
+  Stage<AT * KS * kWave, NW * kWave> ust;
+  stage_load(ust, [&](int idx) {
     const int j = idx / (KS * kWave), kk = (idx / kWave) % KS, l = idx & 63;
     const int a = 16 * j + (l & 15);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + 8 * (l >> 4) + 32 * kk);
-    L.u[j][kk][l] = v;
-  }
+    return v;
+  });
+  // rows of U (padded anchors zero) as chunks of 8 dims: chunk i = anchor i / (D/8)
+  constexpr int UTC = 16 * AT * D / 8;
+  Stage<UTC, NW * kWave> utst;
+  stage_load(utst, [&](int idx) {
+    const int a = idx / (D / 8), k = 8 * (idx - a * (D / 8));
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + k);
+    return v;
+  });
+  stage_store(ust, &L.u[0][0][0]);
   {
     __bf16* ut = (__bf16*)&L.ut[0][0][0];
-    for (int e = threadIdx.x; e < 16 * AT * D; e += NW * kWave) {
-      const int a = e / D, k = e - (e / D) * D;
-      ut[output_pos(a, k, MP)] = (a < m) ? Uh[(size_t)a * D + k] : (__bf16)0.f;
+#pragma unroll
+    for (int i = 0; i < Stage<UTC, NW * kWave>::kPer; ++i) {
+      const int idx = (int)threadIdx.x + i * NW * kWave;
+      if (UTC % (NW * kWave) == 0 || idx < UTC) {
+        const int a = idx / (D / 8), k = 8 * (idx - a * (D / 8));
+        const bf16x8 v = as_bf16x8(utst.r[i]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ut[output_pos(a, k + e, MP)] = v[e];
+      }
     }
   }
   const bf16x8 ones = splat_bf16(1.f);

@@ -55,6 +55,35 @@ __device__ __forceinline__ bf16x8 splat_bf16(float v) {
   return bf16x8{b, b, b, b, b, b, b, b};
 }
 
+// ---- staging global memory into LDS ----------------------------------------------------
+// A loop "for (i = tid; i < N; i += T) lds[i] = src(i)" waits for each pass's load before
+// its LDS write: one memory round trip per pass.  Stage holds a thread's share of N
+// 16-byte chunks so that every load is issued first (stage_load) and LDS is written
+// afterwards (stage_store).  The block must have exactly T threads.
+template <int N, int T>
+struct Stage {
+  static constexpr int kPer = (N + T - 1) / T;
+  u32x4 r[kPer];
+};
+
+template <int N, int T, typename F>
+__device__ __forceinline__ void stage_load(Stage<N, T>& s, F src) {
+#pragma unroll
+  for (int i = 0; i < Stage<N, T>::kPer; ++i) {
+    const int idx = (int)threadIdx.x + i * T;
+    if (N % T == 0 || idx < N) s.r[i] = src(idx);
+  }
+}
+
+template <int N, int T>
+__device__ __forceinline__ void stage_store(const Stage<N, T>& s, u32x4* dst) {
+#pragma unroll
+  for (int i = 0; i < Stage<N, T>::kPer; ++i) {
+    const int idx = (int)threadIdx.x + i * T;
+    if (N % T == 0 || idx < N) dst[idx] = s.r[i];
+  }
+}
+
 // ---- cross-lane reductions ------------------------------------------------------------
 // Over the 16 lanes of one DPP row (lanes with the same g): butterfly with quad
 // permutations and the two row mirrors; every lane of the row ends with the same value.

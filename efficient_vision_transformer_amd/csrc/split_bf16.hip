@@ -391,7 +391,9 @@ void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpa
 // Pass 2.  Each wave takes 16-token tiles.  Logits are formed transposed, S^T = U Q^T
 // (lanes = tokens, registers = anchors), so the softmax is an in-register reduction plus
 // two permlane swaps and the normalised A is directly the right operand of
-// H^T = W^T A^T.  U and W stay in LDS for the whole chunk.
+// H^T = W^T A^T.  U and W stay in LDS for the whole chunk.  Each wave keeps kPass2Ahead
+// of its Q tiles in flight (a register ring refilled as soon as a tile's logits are
+// formed); the first ones are requested before U and W are staged.
 template <int D, int AT>
 __global__ __launch_bounds__(kPass2Waves * kWave, 2)
 void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
@@ -401,45 +403,56 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   const int slice = blockIdx.x / chunks;
   const int chunk = blockIdx.x - slice * chunks;
   const int head = slice % h;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int c = lane & 15, g = lane >> 4;
   const size_t qb = view_base(qw, slice, h), ob = view_base(ow, slice, h);
   const int t_begin = chunk * chunk_len;
   const int t_end = min(n, t_begin + chunk_len);
 
+  // U and W (L2-resident after the first workgroups) are requested first, then the wave's
+  // first Q tiles, so that writing U and W to LDS does not wait for Q.
   __shared__ u32x4 u_lds[AT][KS][kWave];
   __shared__ u32x4 w_lds[DT][MP][kWave];
   const __bf16* Uh = U + (size_t)head * m * D;
-  for (int idx = threadIdx.x; idx < AT * KS * kWave; idx += NW * kWave) {
+  Stage<AT * KS * kWave, NW * kWave> ust;
+  stage_load(ust, [&](int idx) {
     const int j = idx / (KS * kWave), kk = (idx / kWave) % KS, l = idx & 63;
     const int a = 16 * j + (l & 15);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + 8 * KS * (l >> 4) + 8 * kk);
-    u_lds[j][kk][l] = v;
-  }
+    return v;
+  });
   const u32x4* Ws = Wop + (size_t)slice * DT * MP * kWave;
-  for (int idx = threadIdx.x; idx < DT * MP * kWave; idx += NW * kWave)
-    (&w_lds[0][0][0])[idx] = Ws[idx];
-  constexpr int NPAD = pad_tiles(AT);
-  f32x4 mask[NPAD];
-  pad_mask_tiles<AT, NPAD>(g, m, mask);
-  __syncthreads();
+  Stage<DT * MP * kWave, NW * kWave> wst;
+  stage_load(wst, [&](int idx) { return Ws[idx]; });
 
-  // Software pipeline: the next tile's Q rows are requested before this tile is computed.
-  // Rows past the chunk read the slice's last row (clamped) and are not stored.
+  // Tiles past the chunk read the slice's last row (clamped) and are not stored; loads
+  // are unconditional so the wait before each tile is an exact count.
   auto load_q = [&](int t0, u32x4* q) {
     const size_t off = qb + view_row(qw, min(t0 + c, n - 1)) + 8 * KS * g;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) q[kk] = __builtin_nontemporal_load((const u32x4*)(Q + off + 8 * kk));
   };
-  u32x4 q[KS];
-  if (t_begin + 16 * w < t_end) load_q(t_begin + 16 * w, q);
-  for (int t0 = t_begin + 16 * w; t0 < t_end; t0 += 16 * NW) {
+  // Wave w takes the tiles t_begin + 16w + step*i; tile i lives in ring slot i % PF.
+  constexpr int PF = kPass2Ahead, step = 16 * NW;
+  u32x4 q[PF][KS];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load_q(t_begin + 16 * w + step * p, q[p]);
+  stage_store(ust, &u_lds[0][0][0]);
+  stage_store(wst, &w_lds[0][0][0]);
+  constexpr int NPAD = pad_tiles(AT);
+  f32x4 mask[NPAD];
+  pad_mask_tiles<AT, NPAD>(g, m, mask);
+  __syncthreads();
+
+  for (int tb = t_begin + 16 * w; tb < t_end; tb += step * PF) {
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    const int t0 = tb + step * p;
+    if (t0 >= t_end) break;   // uniform per wave
     const int row = t0 + c;
     const bool ok = row < t_end;
-    u32x4 qn[KS];
-    const bool more = t0 + 16 * NW < t_end;
-    if (more) load_q(t0 + 16 * NW, qn);
     // a1 (transposed): s[j] lane (c,g): token c, anchors 16j + 4g + r.
     f32x4 s[AT];
 #pragma unroll
@@ -449,9 +462,11 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       // padded anchors (>= m) lie in the last NPAD tiles and start from -inf
       f32x4 acc = (j >= AT - NPAD) ? mask[j - (AT - NPAD)] : zero4();
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(q[kk]), acc);
+      for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(q[p][kk]), acc);
       s[j] = acc;
     }
+    // the slot is free: request the wave's tile PF steps ahead into it
+    load_q(t0 + step * PF, q[p]);
     // a2
     float mx = s[0][0];
 #pragma unroll
@@ -491,10 +506,7 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         __builtin_nontemporal_store(as_u32x4(pack_bf16(hacc[2 * half], hacc[2 * half + 1])),
                                     (u32x4*)(dst + 8 * half));
     }
-    if (more) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) q[kk] = qn[kk];
-    }
+  }
   }
 }
 

@@ -269,15 +269,26 @@ void pass2_fp32(const float* __restrict__ Q, const float* __restrict__ U,
 
   __shared__ f32x4 u_lds[AT][KQ][kWave];      // lane (c,g): anchor 16j + c, dims (D/4)g + 4kq..
   __shared__ float w_lds[DT][AT][4][kWave];
+  // U, then W, each with all of its loads issued before the first LDS write.
   const float* Uh = U + (size_t)head * m * D;
-  for (int idx = threadIdx.x; idx < AT * KQ * kWave; idx += NW * kWave) {
-    const int j = idx / (KQ * kWave), kq = (idx / kWave) % KQ, l = idx & 63;
-    const int a = 16 * j + (l & 15);
-    u_lds[j][kq][l] = (a < m) ? *(const f32x4*)(Uh + (size_t)a * D + (D / 4) * (l >> 4) + 4 * kq) : zero4();
+  {
+    Stage<AT * KQ * kWave, NW * kWave> ust;
+    stage_load(ust, [&](int idx) {
+      const int j = idx / (KQ * kWave), kq = (idx / kWave) % KQ, l = idx & 63;
+      const int a = 16 * j + (l & 15);
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + (D / 4) * (l >> 4) + 4 * kq);
+      return v;
+    });
+    stage_store(ust, (u32x4*)&u_lds[0][0][0]);
   }
-  const float* Ws = Wop + (size_t)slice * DT * AT * 4 * kWave;
-  for (int idx = threadIdx.x; idx < DT * AT * 4 * kWave; idx += NW * kWave)
-    (&w_lds[0][0][0][0])[idx] = Ws[idx];
+  {
+    // W: DT * AT * 4 * kWave floats, copied as 16-byte chunks
+    const u32x4* Ws = (const u32x4*)(Wop + (size_t)slice * DT * AT * 4 * kWave);
+    Stage<DT * AT * kWave, NW * kWave> wst;
+    stage_load(wst, [&](int idx) { return Ws[idx]; });
+    stage_store(wst, (u32x4*)&w_lds[0][0][0][0]);
+  }
   constexpr int NPAD = pad_tiles(AT);
   f32x4 mask[NPAD];
   pad_mask_tiles<AT, NPAD>(g, m, mask);
