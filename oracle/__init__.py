@@ -22,6 +22,8 @@ anchor_block_forward(X, Wqv, bqv, U, Wo, bo)
                                        projections (a library primitive) around anchor_attn
 relu_linear_attn(Q, K, V, cmin, qscale)
                                     -- L2ViT's ReLU linear attention (numpy fp64)
+nystrom_attn(Q, K, V, idx)          -- Nystrom attention with given landmark tokens
+                                       (Fast Nystrom Attention page; numpy fp64)
 """
 from __future__ import annotations
 
@@ -214,3 +216,39 @@ def relu_linear_attn(Q, K, V, cmin: float = 100.0, qscale: float = 1.0) -> np.nd
     num = np.matmul(phq, S)                               # [B, h, n, d]
     den = np.einsum("bhnd,bhd->bhn", phq, z)
     return num / np.maximum(den, float(cmin))[..., None]
+
+
+def _row_softmax(x: np.ndarray) -> np.ndarray:
+    e = np.exp(x - x.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def nystrom_attn(Q, K, V, idx) -> np.ndarray:
+    """Nystrom attention (Fast Nystrom Attention page, key machinery: the attention matrix
+    taken as the product of three row softmaxes through s landmark rows q, k of Q and K,
+    the middle one inverted).  Per (batch b, head j) slice, with the landmarks the token
+    rows idx[b] (s distinct indices per batch element, shared by the heads) and c = 1/sqrt(d):
+        F1 = rowsoftmax(Q k^T c)   (n x s: tokens against the landmark keys)
+        F2 = rowsoftmax(q k^T c)   (s x s)
+        F3 = rowsoftmax(q K^T c)   (s x n: each landmark query over all tokens)
+        H  = F1 (F2^-1 (F3 V)),
+    the n x n product never formed.  F2^-1 is applied by a linear solve (numpy's LU with
+    partial pivoting, a library primitive; equal to the pseudo-inverse when F2 is
+    nonsingular).  Q, K, V [B, h, n, d]; idx [B, s] integers.  fp64."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    idx = np.asarray(idx)
+    assert Q.shape == K.shape == V.shape and Q.ndim == 4
+    B, h, n, d = Q.shape
+    assert idx.ndim == 2 and idx.shape[0] == B
+    c = 1.0 / np.sqrt(d)
+    H = np.empty_like(Q)
+    for b in range(B):
+        ib = idx[b]
+        for j in range(h):
+            q, k, v = Q[b, j], K[b, j], V[b, j]
+            ql, kl = q[ib], k[ib]
+            F1 = _row_softmax((q @ kl.T) * c)
+            F2 = _row_softmax((ql @ kl.T) * c)
+            F3 = _row_softmax((ql @ k.T) * c)
+            H[b, j] = F1 @ np.linalg.solve(F2, F3 @ v)
+    return H
