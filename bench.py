@@ -64,7 +64,9 @@ def parse():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--plan", default="auto", choices=["auto", "fused", "split"])
     ap.add_argument("--pass", dest="which", default="forward",
-                    choices=["forward", "backward", "block", "linear"])
+                    choices=["forward", "backward", "block", "linear", "nystrom"])
+    ap.add_argument("--landmarks", type=int, default=0,
+                    help="landmarks for --pass nystrom (default: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -338,6 +340,80 @@ def bench_linear(args, ctx, x, dev) -> dict:
     return out
 
 
+# Landmarks per workload for the Nystrom leg: the page's sample sizes are 32 to 64.
+NYSTROM_LANDMARKS = {"vit_s16_224": 32, "vit_b16_384": 64, "dense_64x64": 64,
+                     "long_16k_bf16": 64}
+
+
+def bench_nystrom(args, ctx, x, dev) -> dict:
+    """Nystrom attention with given landmarks (token 0 plus seeded distinct tokens per batch
+    element): one step = gather, landmark maxima, landmark pass, solve, output pass."""
+    import numpy as np
+    import torch
+    from efficient_vision_transformer_amd.inputs import make_landmarks
+    w = x.workload
+    if w.dtype != "bf16":
+        raise SystemExit("Nystrom attention runs in bf16 only")
+    s = args.landmarks or NYSTROM_LANDMARKS.get(w.name, 64)
+    idx = torch.from_numpy(make_landmarks(w.B, w.n, s, seed=w.seed + 77)).to(dev)
+    conv = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    Q0, K0, V0 = conv(x.bits["Q"]), conv(x.bits["K"]), conv(x.bits["V"])
+    act = w.B * w.h * w.n * w.d * 2
+    # Q, K, V read once and H written once; 2nsd flops for each of Q k^T, q K^T, F3 V, F1 Z
+    algo_bytes = 4 * act
+    flops = 8 * w.B * w.h * w.n * s * w.d
+    R = max(1, -(-ROTATE_BYTES // algo_bytes))
+    sets = [(Q0, K0, V0, torch.empty_like(Q0))] + [
+        (Q0.clone(), K0.clone(), V0.clone(), torch.empty_like(Q0)) for _ in range(R - 1)]
+    stream = torch.cuda.current_stream(dev)
+    step = lambda i: ctx.nystrom(*sets[i % R][:3], idx, out=sets[i % R][3], stream=stream)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = algo_bytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": f"Nystrom attention tokens/sec ({w.name} shape, s={s} landmarks)",
+        "value": round(w.B * w.n / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "pass": "nystrom", "B": w.B, "h": w.h, "n": w.n, "d": w.d,
+                   "landmarks": s, "global_batch": w.B, "seq_len": w.n,
+                   "parallelism": "single-gpu", "rotating_sets": R},
+        "achieved_hbm_gbs": round(gbs, 1),
+        "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "the whole step (five launches)",
+                     "per_launch": {"algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
+                                    "avg_duration_us": round(ms * 1e3, 3)}},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from threadpoolctl import threadpool_limits
+        idx_h = idx.cpu().numpy()
+        reps, t0 = 0, time.perf_counter()
+        with threadpool_limits(limits=1):
+            while True:
+                oracle.nystrom_attn(x.Q, x.K, x.V, idx_h)
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= args.cpu_seconds:
+                    break
+        out["cpu_baseline"] = {"value": reps * w.B * w.n / el, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{reps} full batch(es) of {w.name} in fp64 numpy, {el:.1f} s wall"}
+    return out
+
+
 def full_attention_gap(x, H, slices=4) -> dict:
     """Report-only: relative Frobenius gap between softmax(QK^T/sqrt(d))V and H on a few
     slices (inputs exactly as stored)."""
@@ -407,6 +483,11 @@ def main():
     plan_desc = ctx.describe(w.B, w.h, w.n, w.m, w.d, w.dtype)
     if args.which == "linear":
         out = bench_linear(args, ctx, x, dev)
+        ctx.close()
+        print(json.dumps(out), flush=True)
+        return
+    if args.which == "nystrom":
+        out = bench_nystrom(args, ctx, x, dev)
         ctx.close()
         print(json.dumps(out), flush=True)
         return

@@ -54,6 +54,8 @@ def load_library():
                                                      vp]
         lib.anchor_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                              i32, i32, i32, i32, i32, i32, vp]
+        lib.anchor_attn_nystrom_forward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                    i32, i32, vp]
         lib.anchor_attn_set_plan.argtypes = [vp, i32]
         lib.anchor_attn_describe_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32,
                                                   ctypes.c_char_p, i32]
@@ -62,7 +64,8 @@ def load_library():
         for f in (lib.anchor_attn_create, lib.anchor_attn_destroy, lib.anchor_attn_forward,
                   lib.anchor_attn_forward_strided, lib.anchor_attn_block_forward,
                   lib.anchor_attn_relu_linear_forward, lib.anchor_attn_backward_strided,
-                  lib.anchor_attn_backward, lib.anchor_attn_set_plan,
+                  lib.anchor_attn_backward, lib.anchor_attn_nystrom_forward,
+                  lib.anchor_attn_set_plan,
                   lib.anchor_attn_describe_plan):
             f.restype = i32
         _lib = lib
@@ -189,6 +192,35 @@ class AnchorAttention:
             strides[2], out.data_ptr(), strides[3], B, h, n, d, float(cmin), float(qscale),
             _dtype_code(Q), ctypes.c_void_p(stream.cuda_stream)),
             "anchor_attn_relu_linear_forward")
+        return out
+
+    def nystrom(self, Q, K, V, idx, out=None, stream=None):
+        """Nystrom attention with given landmarks: F1 (F2^-1 (F3 V)) per (batch, head)
+        slice with F1 = rowsoftmax(Q k^T c), F2 = rowsoftmax(q k^T c), F3 = rowsoftmax(q K^T c),
+        q, k the rows idx[b] of Q, K and c = 1/sqrt(d).  Q, K, V contiguous [B, h, n, d] bf16;
+        idx an int32 [B, s] tensor of token indices on the same device.  Returns out (a new
+        tensor unless given)."""
+        import torch
+        if Q.dim() != 4 or K.shape != Q.shape or V.shape != Q.shape:
+            raise ValueError(f"bad shapes Q{tuple(Q.shape)} K{tuple(K.shape)} V{tuple(V.shape)}")
+        B, h, n, d = Q.shape
+        if idx.dim() != 2 or idx.shape[0] != B or idx.dtype != torch.int32:
+            raise ValueError("idx must be an int32 tensor [B, s]")
+        if out is None:
+            out = torch.empty(Q.shape, dtype=Q.dtype, device=Q.device)
+        elif out.shape != Q.shape or out.dtype != Q.dtype:
+            raise ValueError("out must be a tensor of Q's shape and dtype")
+        for name, t in (("Q", Q), ("K", K), ("V", V), ("idx", idx), ("out", out)):
+            if not t.is_cuda or t.device != self.device:
+                raise ValueError(f"{name} must be on {self.device}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        _check(self._lib.anchor_attn_nystrom_forward(
+            self._h, Q.data_ptr(), K.data_ptr(), V.data_ptr(), idx.data_ptr(), out.data_ptr(),
+            B, h, n, idx.shape[1], d, _dtype_code(Q), ctypes.c_void_p(stream.cuda_stream)),
+            "anchor_attn_nystrom_forward")
         return out
 
     def block_forward(self, X, Wqv, bqv, U, Wo, bo, out=None, stream=None):

@@ -524,6 +524,54 @@ anchor_attn_status_t anchor_attn_relu_linear_forward(
   }
 }
 
+anchor_attn_status_t anchor_attn_nystrom_forward(anchor_attn_ctx* ctx, const void* Q,
+                                                 const void* K, const void* V, const int* idx,
+                                                 void* H, int B, int h, int n, int s, int d,
+                                                 anchor_attn_dtype_t dtype, void* stream) {
+  if (!ctx) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+  try {
+    if (B < 0 || h < 0 || n < 0) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    if ((long long)B * h * n == 0) return ANCHOR_ATTN_SUCCESS;
+    if (s < 1 || s > n) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    Geometry g{};
+    bool empty = false;
+    anchor_attn_status_t st = check_shape(B, h, n, s, d, dtype, &g, &empty);
+    if (st != ANCHOR_ATTN_SUCCESS) return st;
+    if (dtype != ANCHOR_ATTN_BF16 || s > 128) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+    if (!Q || !K || !V || !idx || !H) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)H) & 15u) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    if ((uintptr_t)idx & 3u) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    const size_t bytes = (size_t)B * h * n * d * 2;
+    if (overlaps(H, bytes, Q, bytes) || overlaps(H, bytes, K, bytes) ||
+        overlaps(H, bytes, V, bytes) || overlaps(H, bytes, idx, (size_t)B * s * sizeof(int)))
+      return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok) return ANCHOR_ATTN_ERROR_HIP;
+    const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t rows = al((size_t)g.slices * s * d * 2);
+    const size_t cmax = al((size_t)g.slices * p.chunks1 * g.m_pad * sizeof(float));
+    st = ensure_workspace(ctx, p.workspace_bytes() + 2 * rows + cmax);
+    if (st != ANCHOR_ATTN_SUCCESS) return st;
+    char* ws = (char*)ctx->workspace;
+    aa::NystromBuffers nb{};
+    nb.part = (float*)ws;
+    nb.dpart = (float*)(ws + p.part_bytes);
+    nb.wop = (__bf16*)(ws + p.part_bytes + p.dpart_bytes);
+    nb.qt = (__bf16*)(ws + p.workspace_bytes());
+    nb.kt = (__bf16*)(ws + p.workspace_bytes() + rows);
+    nb.cmax = (float*)(ws + p.workspace_bytes() + 2 * rows);
+    const hipError_t e = aa::launch_nystrom_bf16(g, p, Q, K, V, idx, H, nb, (hipStream_t)stream);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return ANCHOR_ATTN_ERROR_HIP;
+    }
+    return ANCHOR_ATTN_SUCCESS;
+  } catch (...) {
+    return ANCHOR_ATTN_ERROR_HIP;
+  }
+}
+
 anchor_attn_status_t anchor_attn_backward_strided(
     anchor_attn_ctx* ctx, const void* Q, const long long* q_strides, const void* U, const void* V,
     const long long* v_strides, const void* dH, const long long* dh_strides, void* dQ,

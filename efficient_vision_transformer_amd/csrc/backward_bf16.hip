@@ -35,12 +35,6 @@ __device__ __forceinline__ size_t u_layout_index(int AT, int a, int k) {
   const int j = a >> 4, cc = a & 15, gg = k / (8 * KS), rem = k % (8 * KS);
   return ((((size_t)j * KS + (rem >> 3)) * kWave) + 16 * gg + cc) * 8 + (rem & 7);
 }
-template <int D>
-__device__ __forceinline__ size_t wt_layout_index(int MP, int a, int k) {
-  const int rem = k % (D / 4), dt2 = rem >> 2, cc = 4 * (k / (D / 4)) + (rem & 3);
-  const int jj = a >> 5, half = (a >> 4) & 1, gg = (a >> 2) & 3;
-  return ((((size_t)dt2 * MP + jj) * kWave) + 16 * gg + cc) * 8 + 4 * half + (a & 3);
-}
 
 // ---------------------------------------------------------------------------------------
 template <int D>

@@ -208,12 +208,17 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 // accumulates them over the round's pairs, reading both operands (tokens on the
 // contraction axis) from the row copies with the transposing LDS read.  Partials leave in
 // accumulator layout with dim tile dt holding dims 16dt .. 16dt + 15.
-template <int D, int MP, int NW>
+//
+// NYS (Nystrom attention, landmark pass): U holds per-slice landmark query rows, Q the
+// keys, and the weights are exp(c q.k - c M) with M the landmark's maximum over all tokens
+// (from the per-chunk maxima in cmax) instead of a softmax over anchors; phase B then
+// accumulates F3 V and the row sums of F3 unnormalised.
+template <int D, int MP, int NW, bool NYS = false>
 __global__ __launch_bounds__(NW * kWave, 2)
 void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                  const __bf16* __restrict__ V, float* __restrict__ part,
                  float* __restrict__ dpart, View qw, View xw, int h, int n, int m, int chunks,
-                 int chunk_len, float c2) {
+                 int chunk_len, float c2, const float* __restrict__ cmax = nullptr) {
   constexpr int KS = D / 32, DT = D / 16, AT = 2 * MP;
   constexpr int TILES = AT * DT, TPW = (TILES + NW - 1) / NW;
   constexpr int NDA = (TPW + DT - 1) / DT;   // anchor tiles per wave needing a Delta
@@ -238,7 +243,7 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   constexpr int UCH = AT * KS * kWave;
   constexpr int UPT = (UCH + NW * kWave - 1) / (NW * kWave);
   u32x4 ust[UPT];
-  const __bf16* Uh = U + (size_t)head * m * D;
+  const __bf16* Uh = U + (size_t)(NYS ? slice : head) * m * D;
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     const int idx = threadIdx.x + i * NW * kWave;
@@ -258,6 +263,24 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   for (int i = 0; i < UPT; ++i) {
     const int idx = threadIdx.x + i * NW * kWave;
     if (idx < UCH) (&u_lds[0][0][0])[idx] = ust[i];
+  }
+  // NYS: mneg[a] = -c2 * (landmark a's maximum over the chunks' maxima), 0 for padding
+  __shared__ __attribute__((aligned(16))) float mneg[NYS ? 16 * AT : 4];
+  if constexpr (NYS) {
+    static_assert(16 * AT <= NW * kWave, "one landmark per thread");
+    const int a = threadIdx.x;
+    if (a < 16 * AT) {
+      const float* src = cmax + (size_t)slice * chunks * 16 * AT + a;
+      float M = -INFINITY;
+      for (int ch0 = 0; ch0 < chunks; ch0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[(size_t)min(ch0 + u, chunks - 1) * 16 * AT];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) M = fmaxf(M, v[u]);
+      }
+      mneg[a] = (a < m) ? -M * c2 : 0.f;
+    }
   }
   const bf16x8 ones = splat_bf16(1.f);
   f32x4 mask[2];
@@ -290,7 +313,11 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         bf16x8 ab[MP];
-        tile_softmax<D, MP>(u_lds, qc[tt], lane, mask, t_begin + 32 * p + 16 * tt + c < t_end, c2, ab);
+        const bool token_ok = t_begin + 32 * p + 16 * tt + c < t_end;
+        if constexpr (NYS)
+          tile_exp<D, MP>(u_lds, qc[tt], lane, mask, token_ok, c2, mneg, g, ab);
+        else
+          tile_softmax<D, MP>(u_lds, qc[tt], lane, mask, token_ok, c2, ab);
         // ab[jj] holds anchors 32jj + 4g .. + 3 and 32jj + 16 + 4g .. + 3 of token c.
         __bf16* arow = a_lds + (32 * w + 16 * tt + c) * AS + 4 * g;
 #pragma unroll
@@ -398,7 +425,7 @@ template <int D, int AT>
 __global__ __launch_bounds__(kPass2Waves * kWave, 2)
 void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                 const u32x4* __restrict__ Wop, __bf16* __restrict__ H, View qw, View ow, int h,
-                int n, int m, int chunks, int chunk_len, float c2) {
+                int n, int m, int chunks, int chunk_len, float c2, int u_per_slice = 0) {
   constexpr int NW = kPass2Waves, KS = D / 32, DT = D / 16, MP = AT / 2;
   const int slice = blockIdx.x / chunks;
   const int chunk = blockIdx.x - slice * chunks;
@@ -414,7 +441,7 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   // first Q tiles, so that writing U and W to LDS does not wait for Q.
   __shared__ u32x4 u_lds[AT][KS][kWave];
   __shared__ u32x4 w_lds[DT][MP][kWave];
-  const __bf16* Uh = U + (size_t)head * m * D;
+  const __bf16* Uh = U + (size_t)(u_per_slice ? slice : head) * m * D;
   Stage<AT * KS * kWave, NW * kWave> ust;
   stage_load(ust, [&](int idx) {
     const int j = idx / (KS * kWave), kk = (idx / kWave) % KS, l = idx & 63;
@@ -578,6 +605,60 @@ hipError_t launch_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* 
       case 16: launch_pass1_t<d, 16>(g, p, Q, U, X, part, dpart, s); break;
       default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+  };
+  if (g.d == 64) return at(std::integral_constant<int, 64>{});
+  if (g.d == 32) return at(std::integral_constant<int, 32>{});
+  return hipErrorInvalidValue;
+}
+
+// Nystrom attention: pass 1 in landmark mode (the keys K streamed as the tokens, the
+// per-slice landmark query rows qt as the anchors, cmax the per-chunk landmark maxima) and
+// pass 2 with the per-slice landmark key rows kt as the anchors.
+hipError_t launch_nystrom_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* K,
+                                     const View& kw, const void* qt, const void* V,
+                                     const View& vw, float* part, float* dpart,
+                                     const float* cmax, hipStream_t s) {
+  const long long g1 = g.slices * p.chunks1;
+  auto at = [&](auto D) -> hipError_t {
+    constexpr int d = decltype(D)::value;
+#define AA_NYS1(MP)                                                                          \
+  pass1x_bf16<d, MP, kPass1Waves, true><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, s>>>( \
+      (const __bf16*)K, (const __bf16*)qt, (const __bf16*)V, part, dpart, kw, vw, g.h, g.n, g.m, \
+      p.chunks1, p.chunk_len1, g.c2, cmax)
+    switch (g.at) {
+      case 2: AA_NYS1(1); break;
+      case 4: AA_NYS1(2); break;
+      case 6: AA_NYS1(3); break;
+      case 8: AA_NYS1(4); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef AA_NYS1
+    return hipGetLastError();
+  };
+  if (g.d == 64) return at(std::integral_constant<int, 64>{});
+  if (g.d == 32) return at(std::integral_constant<int, 32>{});
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_nystrom_pass2_bf16(const Geometry& g, const SplitPlan& p, const void* Q,
+                                     const View& qw, const void* kt, const void* Wop, void* H,
+                                     const View& ow, hipStream_t s) {
+  const long long g2 = g.slices * p.chunks2;
+  auto at = [&](auto D) -> hipError_t {
+    constexpr int d = decltype(D)::value;
+#define AA_NYS2(AT)                                                                           \
+  pass2_bf16<d, AT><<<dim3((unsigned)g2), dim3(kPass2Waves * kWave), 0, s>>>(                 \
+      (const __bf16*)Q, (const __bf16*)kt, (const u32x4*)Wop, (__bf16*)H, qw, ow, g.h, g.n, g.m, \
+      p.chunks2, p.chunk_len2, g.c2, 1)
+    switch (g.at) {
+      case 2: AA_NYS2(2); break;
+      case 4: AA_NYS2(4); break;
+      case 6: AA_NYS2(6); break;
+      case 8: AA_NYS2(8); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef AA_NYS2
     return hipGetLastError();
   };
   if (g.d == 64) return at(std::integral_constant<int, 64>{});

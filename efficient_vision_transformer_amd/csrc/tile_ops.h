@@ -58,6 +58,35 @@ __device__ __forceinline__ void tile_softmax(const u32x4 (*u_lds)[D / 32][kWave]
                          token_ok, c2, ab);
 }
 
+// Unnormalised weights exp(c (u_j . q) - c M_j) of one 16-token tile against the anchor
+// rows in u_lds, with mneg[j] = -c M_j (c = c2, log2 units) for a bound M_j >= every
+// logit of anchor j; zero for tokens past the end and for padded anchors (their logits
+// start from -inf).  Same lane layout as tile_softmax.
+template <int D, int MP>
+__device__ __forceinline__ void tile_exp(const u32x4 (*u_lds)[D / 32][kWave], const u32x4* q,
+                                         int lane, const f32x4* mask, bool token_ok, float c2,
+                                         const float* mneg, int g, bf16x8* ab) {
+  constexpr int KS = D / 32, AT = 2 * MP;
+  f32x4 s[AT];
+#pragma unroll
+  for (int j = 0; j < AT; ++j) {
+    f32x4 acc = (j >= AT - 2) ? mask[j - (AT - 2)] : zero4();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(q[kk]), acc);
+    s[j] = acc;
+  }
+  // keeps the loop-invariant reads of mneg from being hoisted out of the caller's loop
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < AT; ++j) {
+    const f32x4 mn = *(const f32x4*)(mneg + 16 * j + 4 * g);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[j][r] = token_ok ? exp2_fast(fmaf(s[j][r], c2, mn[r])) : 0.f;
+  }
+#pragma unroll
+  for (int jj = 0; jj < MP; ++jj) ab[jj] = pack_bf16(s[2 * jj], s[2 * jj + 1]);
+}
+
 // ---- transposing LDS reads (gfx950 ds_read_b64_tr_b16) ----------------------------------
 // Within each 16-lane group every lane reads 8 bytes (4 x 16-bit) at its own address;
 // lane i receives, in slot k, element i % 4 of what lane 4k + i / 4 read.

@@ -182,6 +182,19 @@ def make_upstream_grad(x: Inputs, seed: int) -> tuple[np.ndarray, np.ndarray | N
     return _store(g, x.workload.dtype)
 
 
+def make_landmarks(B: int, n: int, s: int, seed: int) -> np.ndarray:
+    """Landmark token indices for Nystrom attention, int32 [B, s]: token 0 (the class
+    token, always a landmark) and s - 1 distinct other tokens per batch element, drawn
+    with ``default_rng(seed)``; the heads of a batch element share them.  A seeded stand-in
+    for farthest-point sampling on token features."""
+    if not 1 <= s <= n:
+        raise ValueError("need 1 <= s <= n landmarks")
+    rng = np.random.default_rng(seed)
+    rows = [np.concatenate([[0], rng.choice(np.arange(1, n), size=s - 1, replace=False)])
+            for _ in range(B)]
+    return np.ascontiguousarray(np.stack(rows).astype(np.int32))
+
+
 @dataclass
 class BlockInputs:
     """Inputs of the attention block around the layer; float32 stored values plus bf16

@@ -162,6 +162,29 @@ anchor_attn_status_t anchor_attn_relu_linear_forward(anchor_attn_ctx* ctx,
                                                      float qscale, anchor_attn_dtype_t dtype,
                                                      void* stream);
 
+/* Nystrom attention with given landmark tokens (Fast Nystrom Attention page, key
+ * machinery): the attention matrix approximated by three row softmaxes through s landmark
+ * rows q = Q[idx], k = K[idx], the middle one inverted.  Per (batch b, head j) slice of
+ * Q, K, V, H [B, h, n, d] (contiguous, row-major), with c = 1/sqrt(d):
+ *   F1 = rowsoftmax(Q k^T c) (n x s),  F2 = rowsoftmax(q k^T c) (s x s),
+ *   F3 = rowsoftmax(q K^T c) (s x n),  H = F1 (F2^-1 (F3 V)),
+ * never forming an n x n matrix.  idx: device int32 [B, s], the landmark token indices of
+ * each batch element (shared by its heads; the page picks them by farthest-point
+ * sampling, which is the caller's business here).  Indices are expected distinct and in
+ * [0, n); out-of-range values are clamped to that range.  Repeated indices make F2
+ * singular and the output non-finite.  bf16 in and out, fp32 accumulation; F2 and the
+ * solve in fp32 (Gauss-Jordan with partial pivoting), F1, F3 and Z = F2^-1 F3 V rounded
+ * to bf16 as matrix-core operands.  Uses the context's workspace (grown on demand;
+ * growth synchronizes).
+ * Domain: dtype BF16 (else NOT_SUPPORTED), d in {32, 64} and 1 <= s <= 128 (else
+ * NOT_SUPPORTED), s <= n (else INVALID_VALUE); B, h, n >= 0 with no tokens a no-op.  All
+ * pointers 16-byte aligned (idx 4-byte); H must not overlap Q, K, V or idx.
+ * Errors: nothing is enqueued. */
+anchor_attn_status_t anchor_attn_nystrom_forward(anchor_attn_ctx* ctx, const void* Q,
+                                                 const void* K, const void* V, const int* idx,
+                                                 void* H, int B, int h, int n, int s, int d,
+                                                 anchor_attn_dtype_t dtype, void* stream);
+
 /* Enqueues the gradients of anchor_attn_forward for a loss L with dL/dH = dH (AnchorFormer
  * abstract: the anchors are learnable, so the layer is trained through; the Pith verdict
  * page's Eq. (11) in the Eq. (12) order is the function differentiated), on `stream`,

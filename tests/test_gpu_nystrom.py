@@ -1,0 +1,131 @@
+"""GPU parity of Nystrom attention with given landmarks (Fast Nystrom Attention page, key
+machinery) against the oracle's fp64 version on the same bf16-rounded inputs and the same
+landmark indices.  Gate: relative Frobenius error <= 1e-2 (the bf16 gate)."""
+import numpy as np
+import pytest
+
+import oracle
+from efficient_vision_transformer_amd.inputs import make_inputs, make_landmarks
+
+from gpu_util import bf16_err
+
+pytestmark = pytest.mark.gpu
+
+NYS_TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from efficient_vision_transformer_amd import AnchorAttention
+    c = AnchorAttention(torch.device("cuda:0"))
+    yield c
+    c.close()
+
+
+def _conv(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def _gpu(ctx, x, idx):
+    import torch
+    H = ctx.nystrom(_conv(x.bits["Q"]), _conv(x.bits["K"]), _conv(x.bits["V"]),
+                    torch.from_numpy(idx).to("cuda:0"))
+    torch.cuda.synchronize()
+    return H.float().cpu().numpy().astype(np.float64)
+
+
+def _case(name, shape, s, seed):
+    x = make_inputs(name, shape=shape)
+    w = x.workload
+    return x, make_landmarks(w.B, w.n, s, seed)
+
+
+# (workload whose value structure is kept, size overrides, landmarks s)
+CASES = [
+    ("vit_s16_224", {}, 32),                                  # ViT-S/16 shape, 384 slices
+    ("vit_b16_384", {}, 64),                                  # Q x 2: peaked rows
+    ("dense_64x64", {}, 64),                                  # 64 x 64 feature map
+    ("dense_64x64", {"B": 1, "h": 2}, 128),                   # most landmarks
+    ("vit_s16_224", {"B": 2, "h": 3, "n": 77, "d": 32}, 5),   # d = 32, ragged tiles
+    ("vit_s16_224", {"B": 1, "h": 2, "n": 40}, 40),           # every token a landmark
+    ("vit_s16_224", {"B": 1, "h": 1, "n": 1}, 1),             # one token
+    ("vit_s16_224", {"B": 3, "h": 1, "n": 1000, "d": 32}, 17),
+    ("vit_s16_224", {"B": 1, "h": 2, "n": 16384}, 64),        # many token chunks
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-{'-'.join(f'{k}{v}' for k, v in c[1].items())}-s{c[2]}")
+def test_nystrom_against_oracle(ctx, case):
+    name, shape, s = case
+    x, idx = _case(name, shape, s, seed=5000 + s)
+    w = x.workload
+    print(f"  nystrom {name} B={w.B} h={w.h} n={w.n} d={w.d} s={s}", flush=True)
+    got = _gpu(ctx, x, idx)
+    ref = oracle.nystrom_attn(x.Q, x.K, x.V, idx)
+    e = bf16_err(got, ref)
+    print(f"  relative Frobenius error {e:.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert e <= NYS_TOL
+
+
+def test_nystrom_every_token_a_landmark_is_full_attention(ctx):
+    """s = n in a shuffled order: the Nystrom product is exactly softmax(Q K^T c) V."""
+    x = make_inputs("vit_s16_224", shape={"B": 1, "h": 2, "n": 48})
+    idx = np.random.default_rng(5).permutation(48).astype(np.int32)[None, :]
+    got = _gpu(ctx, x, idx)
+    for j in range(2):
+        ref = oracle.full_attention_slice(x.Q[0, j], x.K[0, j], x.V[0, j])
+        e = bf16_err(got[0, j], ref)
+        print(f"  head {j}: relative Frobenius error against full attention {e:.3e}", flush=True)
+        assert e <= NYS_TOL
+
+
+def test_nystrom_constant_values_preserved(ctx):
+    """Rows of F1 F2^-1 F3 sum to one: constant V rows come back (bf16 rounding of the
+    operands only), at the ViT-S/16 shape."""
+    import torch
+    x, idx = _case("vit_s16_224", {}, 32, seed=6)
+    w = x.workload
+    V = torch.full((w.B, w.h, w.n, w.d), 1.5, dtype=torch.bfloat16, device="cuda:0")
+    H = ctx.nystrom(_conv(x.bits["Q"]), _conv(x.bits["K"]), V, torch.from_numpy(idx).to("cuda:0"))
+    torch.cuda.synchronize()
+    got = H.float().cpu().numpy()
+    print(f"  max |H - 1.5| = {np.abs(got - 1.5).max():.3e}", flush=True)
+    assert np.abs(got - 1.5).max() <= 1.5 * 1e-2
+
+
+def test_nystrom_deterministic(ctx):
+    x, idx = _case("vit_b16_384", {"B": 4}, 64, seed=7)
+    a = _gpu(ctx, x, idx)
+    b = _gpu(ctx, x, idx)
+    assert np.array_equal(a, b)
+
+
+def test_nystrom_sink_tokens_report(ctx):
+    """Sink tokens (1% of tokens x 10) make F2 nearly singular (condition numbers near
+    1e12 in fp64); the solve runs in fp32.  The error is printed, and the output must be
+    finite and within the bf16 gate."""
+    x, idx = _case("long_16k_bf16", {"B": 1, "h": 2, "n": 4096}, 64, seed=8)
+    got = _gpu(ctx, x, idx)
+    ref = oracle.nystrom_attn(x.Q, x.K, x.V, idx)
+    e = bf16_err(got, ref)
+    print(f"  sinks: relative Frobenius error {e:.3e}", flush=True)
+    assert np.isfinite(got).all()
+    assert e <= NYS_TOL
+
+
+def test_nystrom_rejects_what_it_cannot_run(ctx):
+    import torch
+    x, idx = _case("vit_s16_224", {"B": 1, "h": 1, "n": 20}, 4, seed=9)
+    Q, K, V = (_conv(x.bits[k]) for k in ("Q", "K", "V"))
+    with pytest.raises(RuntimeError):   # more landmarks than tokens
+        ctx.nystrom(Q, K, V, torch.zeros((1, 21), dtype=torch.int32, device="cuda:0"))
+    x2, _ = _case("vit_s16_224", {"B": 1, "h": 1, "n": 200}, 4, seed=9)
+    Q2, K2, V2 = (_conv(x2.bits[k]) for k in ("Q", "K", "V"))
+    with pytest.raises(RuntimeError):   # s > 128
+        ctx.nystrom(Q2, K2, V2, torch.arange(129, dtype=torch.int32, device="cuda:0")[None, :])
+    with pytest.raises(RuntimeError):   # fp32 is not built
+        ctx.nystrom(Q.float(), K.float(), V.float(), torch.from_numpy(idx).to("cuda:0"))
