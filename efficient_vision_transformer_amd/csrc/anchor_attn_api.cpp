@@ -92,7 +92,9 @@ anchor_attn_status_t check_shape(int B, int h, int n, int m, int d, anchor_attn_
   if (B < 0 || h < 0 || n < 0 || m < 0 || d < 0) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
   if (m == 0 || d == 0) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
   if (dtype != ANCHOR_ATTN_FP32 && dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
-  if (d != 32 && d != 64) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  if (d != 32 && d != 64 && d != 128) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  // d = 128: the bf16 split plan of the forward only
+  if (d == 128 && dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   if (m > 256) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   const long long slices = (long long)B * (long long)h;
   *empty = (slices == 0 || n == 0);
@@ -177,7 +179,7 @@ Chosen choose(const anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t
 // The backward (bf16, m <= 128): one workgroup per slice when that plan applies, else the
 // split passes; the context's plan setting is honoured as for the forward.
 Chosen choose_backward(const anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t dtype) {
-  if (dtype != ANCHOR_ATTN_BF16 || g.at > 8) return Chosen::Unsupported;
+  if (dtype != ANCHOR_ATTN_BF16 || g.at > 8 || g.d > 64) return Chosen::Unsupported;
   const bool fused_ok = aa::bwd_fused_supported(g);
   switch (ctx->plan) {
     case ANCHOR_ATTN_PLAN_FUSED: return fused_ok ? Chosen::Fused : Chosen::Unsupported;
@@ -479,6 +481,7 @@ anchor_attn_status_t anchor_attn_relu_linear_forward(
     bool empty = false;
     anchor_attn_status_t st = check_shape(B, h, n, 1, d, dtype, &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
+    if (d > 64) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
     if (!(cmin > 0.f) || !std::isfinite(cmin) || !(qscale > 0.f) || !std::isfinite(qscale))
       return ANCHOR_ATTN_ERROR_INVALID_VALUE;
     if (dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
@@ -537,7 +540,7 @@ anchor_attn_status_t anchor_attn_nystrom_forward(anchor_attn_ctx* ctx, const voi
     bool empty = false;
     anchor_attn_status_t st = check_shape(B, h, n, s, d, dtype, &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
-    if (dtype != ANCHOR_ATTN_BF16 || s > 128) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+    if (dtype != ANCHOR_ATTN_BF16 || s > 128 || d > 64) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
     if (!Q || !K || !V || !idx || !H) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
     if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)H) & 15u) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
     if ((uintptr_t)idx & 3u) return ANCHOR_ATTN_ERROR_INVALID_VALUE;

@@ -589,6 +589,7 @@ hipError_t launch_split_bf16(const Geometry& g, const SplitPlan& p, const void* 
                              const void* V, void* H, void* ws, hipStream_t stream) {
   if (g.d == 64) return dispatch_at<64>(g, p, Q, U, V, H, ws, stream);
   if (g.d == 32) return dispatch_at<32>(g, p, Q, U, V, H, ws, stream);
+  if (g.d == 128) return dispatch_at<128>(g, p, Q, U, V, H, ws, stream);
   return hipErrorInvalidValue;
 }
 

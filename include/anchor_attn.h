@@ -84,7 +84,9 @@ anchor_attn_status_t anchor_attn_destroy(anchor_attn_ctx* ctx);
  * and returns without waiting.
  *   Q, V, H : [B, h, n, d]  device, element type `dtype`
  *   U       : [h, m, d]     device, element type `dtype`
- * Domain: B, h, n >= 0 (B*h*n == 0 is a successful no-op); 1 <= m <= 256; d in {32, 64}.
+ * Domain: B, h, n >= 0 (B*h*n == 0 is a successful no-op); 1 <= m <= 256; d in {32, 64},
+ * or d = 128 with dtype BF16 (run by the split plan only: PLAN_FUSED gives NOT_SUPPORTED);
+ * other d, or d = 128 in FP32, give NOT_SUPPORTED.
  * m >= n is accepted (the result is still defined; the O(mn) saving needs m < n). */
 anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx,
                                          const void* Q, const void* U, const void* V, void* H,
@@ -195,8 +197,8 @@ anchor_attn_status_t anchor_attn_nystrom_forward(anchor_attn_ctx* ctx, const voi
  * Accumulation is fp32; results are rounded to bf16.  dQ, dU and dV are written in full
  * (dU is zero when B*h*n == 0); they must not overlap each other or any input.  The
  * context's workspace grows as for the split plan (the first call of a larger shape may
- * synchronize).  Domain: as anchor_attn_forward with dtype BF16 and m <= 128; other
- * dtypes or larger m return NOT_SUPPORTED.  Errors as anchor_attn_forward: nothing is
+ * synchronize).  Domain: as anchor_attn_forward with dtype BF16, m <= 128 and d in
+ * {32, 64}; other dtypes, larger m or d = 128 return NOT_SUPPORTED.  Errors as anchor_attn_forward: nothing is
  * enqueued and no output is touched. */
 anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx,
                                           const void* Q, const void* U, const void* V,
