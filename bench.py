@@ -37,8 +37,8 @@ MEASURED_TRAFFIC = {
                                            "efficient_vision_transformer_amd/csrc/tile_ops.h",
                                            "efficient_vision_transformer_amd/csrc/device_common.h",
                                            "efficient_vision_transformer_amd/csrc/kernels.h"],
-                               "sha": "bb7ba8c87f7d3eca", "read_bytes": 19474177,
-                               "write_bytes": 11032317},
+                               "sha": "b68f3118c0b27f14", "read_bytes": 19474139,
+                               "write_bytes": 11014496},
 }
 
 

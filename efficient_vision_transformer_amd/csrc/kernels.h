@@ -47,7 +47,6 @@ constexpr int kPass1Waves = 4;    // pass 1 block = 4 pairs = 128 tokens
 constexpr int kPass1Block = 128;
 constexpr int kPass2Waves = 4;    // pass 2 block = 4 tiles = 64 tokens
 constexpr int kPass2Block = 64;
-constexpr int kPass2Ahead = 4;    // pass 2: Q tiles in flight per wave
 
 hipError_t launch_split_bf16(const Geometry& g, const SplitPlan& p, const void* Q,
                              const void* U, const void* V, void* H, void* workspace,

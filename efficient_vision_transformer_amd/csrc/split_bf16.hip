@@ -415,6 +415,10 @@ void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpa
 }
 
 // ---------------------------------------------------------------------------------------
+// Q tiles in flight per wave in pass 2 (1, 2 and 4 measured: one ahead is fastest at the
+// dense and long shapes; more slots cost registers and occupancy)
+constexpr int kPass2Ahead = 1;
+
 // Pass 2.  Each wave takes 16-token tiles.  Logits are formed transposed, S^T = U Q^T
 // (lanes = tokens, registers = anchors), so the softmax is an in-register reduction plus
 // two permlane swaps and the normalised A is directly the right operand of
