@@ -138,7 +138,10 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   __shared__ float Mx[MPAD * LD];                         // set-up only
-  __shared__ __attribute__((aligned(16))) __bf16 ql[MPAD * D], kl[MPAD * D];
+  // landmark rows with a row stride of D + 8 bf16 (144 or 80 bytes), so that the rows read
+  // together by neighbouring threads fall on different LDS banks
+  constexpr int RS = D + 8;
+  __shared__ __attribute__((aligned(16))) __bf16 ql[MPAD * RS], kl[MPAD * RS];
   __shared__ float zl[MPAD];
   __shared__ float fbuf[2][MPAD];
   __shared__ int pbuf[2];
@@ -151,8 +154,15 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
     Stage<MPAD * D / 8, T> qst, kst;
     stage_load(qst, [&](int i) { return (i < m * D / 8) ? qs[i] : u32x4{0u, 0u, 0u, 0u}; });
     stage_load(kst, [&](int i) { return (i < m * D / 8) ? ks[i] : u32x4{0u, 0u, 0u, 0u}; });
-    stage_store(qst, (u32x4*)ql);
-    stage_store(kst, (u32x4*)kl);
+#pragma unroll
+    for (int i = 0; i < Stage<MPAD * D / 8, T>::kPer; ++i) {
+      const int c = tid + i * T;
+      if ((MPAD * D / 8) % T == 0 || c < MPAD * D / 8) {
+        const int a = c / (D / 8), k8 = c - a * (D / 8);
+        *(u32x4*)(ql + a * RS + 8 * k8) = qst.r[i];
+        *(u32x4*)(kl + a * RS + 8 * k8) = kst.r[i];
+      }
+    }
   }
   // chunk sums in chunk order into the right-hand side columns (element f of a chunk's
   // partial block: tile f / 256 = (jt, dt), slot r * 64 + l); every load of a chunk is in
@@ -193,8 +203,8 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
     const int a = e / MPAD, l = e - a * MPAD;
     float v;
     if (a < m && l < m) {
-      const u32x4* qa = (const u32x4*)(ql + a * D);
-      const u32x4* kb = (const u32x4*)(kl + l * D);
+      const u32x4* qa = (const u32x4*)(ql + a * RS);
+      const u32x4* kb = (const u32x4*)(kl + l * RS);
       v = 0.f;
 #pragma unroll
       for (int k8 = 0; k8 < D / 8; ++k8) {
