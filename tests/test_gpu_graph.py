@@ -103,3 +103,27 @@ def test_block_graph(ctxs):
     print("  block graph", flush=True)
     _capture_and_replay(lambda: ctxs["auto"].block_forward(t["X"], t["Wqv"], t["bqv"], t["U"],
                                                            t["Wo"], t["bo"], out=Y), [Y])
+
+
+@pytest.mark.parametrize("s", [32, 64])
+def test_nystrom_graph(ctxs, s):
+    """Nystrom attention (landmark maxima, landmark pass, solve, output pass) captured."""
+    import torch
+    from efficient_vision_transformer_amd.inputs import make_landmarks
+    x = make_inputs("vit_s16_224", shape={"B": 8, "n": 500})
+    Q, K, V = _conv(x.bits["Q"]), _conv(x.bits["K"]), _conv(x.bits["V"])
+    idx = torch.from_numpy(make_landmarks(8, 500, s, seed=3)).to("cuda:0")
+    H = torch.empty_like(Q)
+    print(f"  nystrom graph s={s}", flush=True)
+    _capture_and_replay(lambda: ctxs["auto"].nystrom(Q, K, V, idx, out=H), [H])
+
+
+def test_forward_d128_graph(ctxs):
+    """Head dim 128 (split plan) captured."""
+    import torch
+    from efficient_vision_transformer_amd.inputs import random_case
+    x = random_case(5, 2, 2, 700, 64, 128, dtype="bf16")
+    Q, U, V = _conv(x.bits["Q"]), _conv(x.bits["U"]), _conv(x.bits["V"])
+    H = torch.empty_like(Q)
+    print("  forward d=128 graph", flush=True)
+    _capture_and_replay(lambda: ctxs["auto"].forward(Q, U, V, out=H), [H])
