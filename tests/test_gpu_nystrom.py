@@ -129,3 +129,24 @@ def test_nystrom_rejects_what_it_cannot_run(ctx):
         ctx.nystrom(Q2, K2, V2, torch.arange(129, dtype=torch.int32, device="cuda:0")[None, :])
     with pytest.raises(RuntimeError):   # fp32 is not built
         ctx.nystrom(Q.float(), K.float(), V.float(), torch.from_numpy(idx).to("cuda:0"))
+
+
+def test_nystrom_clamps_out_of_range_indices(ctx):
+    """Indices below 0 or at/after n behave as 0 and n - 1 (the documented clamp)."""
+    import torch
+    x, _ = _case("vit_s16_224", {"B": 2, "h": 2, "n": 90}, 6, seed=10)
+    bad = np.array([[-7, 5, 17, 33, 60, 71], [2, 9, 40, 52, 88, 90 + 13]], dtype=np.int32)
+    good = np.clip(bad, 0, 89).astype(np.int32)
+    assert len(set(good[0])) == 6 and len(set(good[1])) == 6, "clamped indices stay distinct"
+    a = _gpu(ctx, x, bad.astype(np.int32))
+    b = _gpu(ctx, x, good)
+    assert np.array_equal(a, b)
+
+
+def test_nystrom_empty_inputs_are_noops(ctx):
+    import torch
+    Q = torch.zeros((0, 2, 16, 64), dtype=torch.bfloat16, device="cuda:0")
+    idx = torch.zeros((0, 4), dtype=torch.int32, device="cuda:0")
+    H = ctx.nystrom(Q, Q, Q, idx)
+    torch.cuda.synchronize()
+    assert H.shape == Q.shape
