@@ -462,6 +462,45 @@ def copy_reference(algo_bytes: int, steps: int, warmup: int) -> dict:
             "gbs": round(8 * n / (us * 1e-6) / 1e9, 1)}
 
 
+def stream_reference(tensor_bytes: int, steps: int, warmup: int) -> dict:
+    """The forward's byte pattern with no arithmetic: two tensors of `tensor_bytes` read and
+    one written per launch by the library's streaming reference kernel (one 16-byte chunk
+    of each buffer per thread), rotated over >= 1 GiB like the benchmark: the practical
+    bandwidth floor of one launch moving these bytes on this machine."""
+    import ctypes
+    import torch
+    from efficient_vision_transformer_amd import anchor_attn
+    lib = anchor_attn.load_library()
+    fn = lib.anchor_attn_stream_reference
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong,
+                   ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    nb = tensor_bytes // 16 * 16
+    R = max(1, -(-ROTATE_BYTES // (3 * nb)))
+    sets = [tuple(torch.full((nb // 2,), 3, dtype=torch.int16, device=dev) for _ in range(3))
+            for _ in range(R)]
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    call = lambda i: fn(sets[i % R][0].data_ptr(), sets[i % R][1].data_ptr(),
+                        sets[i % R][2].data_ptr(), nb, sp)
+    for i in range(warmup):
+        if call(i) != 0:
+            raise RuntimeError("stream reference launch failed")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    return {"bytes_per_launch": 3 * nb, "avg_duration_us": round(us, 3),
+            "gbs": round(3 * nb / (us * 1e-6) / 1e9, 1),
+            "kernel": "two buffers read, one written, one 16-byte chunk per thread"}
+
+
 def main():
     args = parse()
     if args.calibrate_copy_mib:
@@ -583,6 +622,9 @@ def main():
     ref = copy_reference(algo_bytes, min(args.steps, 200), min(args.warmup, 20))
     ref["frac_of_copy"] = round(gbs / ref["gbs"], 4) if ref["gbs"] > 0 else None
     out["copy_reference"] = ref
+    sref = stream_reference(algo_bytes // 3, min(args.steps, 200), min(args.warmup, 20))
+    sref["frac_of_stream"] = round(gbs / sref["gbs"], 4) if sref["gbs"] > 0 else None
+    out["stream_reference"] = sref
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     out["diagnostic"] = full_attention_gap(x, H)

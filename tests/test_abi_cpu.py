@@ -10,6 +10,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "anchor_attn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 PKG = os.path.join(ROOT, "efficient_vision_transformer_amd")
 
 
@@ -23,12 +25,13 @@ def lib():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"\b(anchor_attn_[a-z_]+)\s*\(", text)))
 
 
-def test_header_is_valid_c():
-    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+@pytest.mark.parametrize("header", HEADERS, ids=os.path.basename)
+def test_header_is_valid_c(header):
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", header],
                    check=True)
 
 
