@@ -14,8 +14,8 @@
 //               over all chunks, accumulated against V and against ones: F3 V and F3's row
 //               sums, unnormalised, per chunk.
 //   nys_solve   per slice: chunk sums -> F3 V; F2 in fp32 from the landmark rows; Z = F2^-1
-//               (F3 V) by Gauss-Jordan elimination with partial pivoting in LDS; Z stored as
-//               pass 2's W operands.
+//               (F3 V) by Gauss-Jordan elimination with partial pivoting, the augmented
+//               matrix spread over the waves' registers; Z stored as pass 2's W operands.
 //   pass 2      (split plan, per-slice anchors = the landmark keys): H = rowsoftmax(Q k^T c) Z.
 #include <algorithm>
 
