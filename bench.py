@@ -37,8 +37,8 @@ MEASURED_TRAFFIC = {
                                            "efficient_vision_transformer_amd/csrc/tile_ops.h",
                                            "efficient_vision_transformer_amd/csrc/device_common.h",
                                            "efficient_vision_transformer_amd/csrc/kernels.h"],
-                               "sha": "b68f3118c0b27f14", "read_bytes": 19474139,
-                               "write_bytes": 11014496},
+                               "sha": "3fd2041ff5db177e", "read_bytes": 19474503,
+                               "write_bytes": 10916934},
 }
 
 
@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--plan", default="auto", choices=["auto", "fused", "split"])
     ap.add_argument("--pass", dest="which", default="forward",
                     choices=["forward", "backward", "block", "linear", "nystrom"])
+    ap.add_argument("--head-dim", type=int, default=0,
+                    help="override the workload's head dim (32, 64 or 128)")
     ap.add_argument("--landmarks", type=int, default=0,
                     help="landmarks for --pass nystrom (default: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -516,6 +518,11 @@ def main():
 
     name = args.workload or HEADLINE
     w = WORKLOADS[name]
+    if args.head_dim:
+        # the workload's value structure at another head dim (d = 128 runs the split plan)
+        from efficient_vision_transformer_amd.inputs import Workload
+        w = Workload(**{**w.__dict__, "d": args.head_dim, "name": f"{w.name}_d{args.head_dim}"})
+        name = w.name
     dev = torch.device("cuda:0")
     x = make_inputs(w, with_k=True)
     ctx = AnchorAttention(dev, plan=args.plan)

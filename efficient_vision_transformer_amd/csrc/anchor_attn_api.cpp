@@ -93,7 +93,7 @@ anchor_attn_status_t check_shape(int B, int h, int n, int m, int d, anchor_attn_
   if (m == 0 || d == 0) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
   if (dtype != ANCHOR_ATTN_FP32 && dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   if (d != 32 && d != 64 && d != 128) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
-  // d = 128: the bf16 split plan of the forward only
+  // d = 128: the bf16 forward only (the fused and split plans)
   if (d == 128 && dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   if (m > 256) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   const long long slices = (long long)B * (long long)h;

@@ -28,11 +28,14 @@
 
 namespace aa {
 
-// LDS of one workgroup, sized for a workgroup that handles all D dims.
+// LDS of one workgroup, sized for a workgroup that handles DL of the D dims of V and H:
+// all of them, or half at d = 128, where every slice is shared by two workgroups (a whole
+// d = 128 slice's V rows would leave room for one workgroup per CU).
 template <int D, int MP, int NW>
 struct FusedLds {
-  static constexpr int AT = 2 * MP, KS = D / 32, DT = D / 16;
-  static constexpr int AS = tr_stride<32 * MP>(), VS = tr_stride<D>();
+  static constexpr int DL = (D == 128) ? D / 2 : D;
+  static constexpr int AT = 2 * MP, KS = D / 32, DT = DL / 16;
+  static constexpr int AS = tr_stride<32 * MP>(), VS = tr_stride<DL>();
   u32x4 u[AT][KS][kWave];                                   // U as left operands of S^T
   __attribute__((aligned(16))) __bf16 a[NW * 32 * AS];      // rows of A, this round
   __attribute__((aligned(16))) __bf16 v[NW * 32 * VS];      // rows of V, this round
@@ -56,6 +59,7 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
   constexpr int NDA = (TPW + DTW - 1) / DTW;   // anchor tiles per wave that need a Delta
   constexpr int AS = FusedLds<D, MP, NW>::AS, VS = tr_stride<DW>();
   static_assert(TILES % NW == 0 || NW % TILES == 0, "tiles split evenly over the waves");
+  static_assert(DW <= FusedLds<D, MP, NW>::DL, "the LDS holds this part's dims");
   const int head = slice % h;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -260,8 +264,9 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   __shared__ FusedLds<D, MP, NW> L;
   const int b = blockIdx.x;
   if (b < full) {
-    fused_part<D, D, MP, NW, ROUNDS, KEEP_A>(L, Q, U, V, H, vw, b, 0, h, n, m, c2);
-  } else if constexpr (D == 64) {
+    if constexpr (D != 128)   // at d = 128 every slice is shared (full == 0)
+      fused_part<D, D, MP, NW, ROUNDS, KEEP_A>(L, Q, U, V, H, vw, b, 0, h, n, m, c2);
+  } else if constexpr (D >= 64) {
     // Within each run of 16 shared workgroups, ids i and i + 8 take the two halves of one
     // slice: workgroups are dealt to the XCDs in turn, so both halves (which read the
     // same Q) usually sit on one XCD and the second read of Q hits its L2.  A last
@@ -281,29 +286,34 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   }
 }
 
-// Plans (n <= 1024, m <= 64):
+// Plans (n <= 1024, m <= 64; d = 128 and m <= 32: n <= 256):
 //   m <= 32: eight waves, A kept for up to two rounds (n <= 512), else recomputed;
-//   m <= 64: four waves, A kept for up to five rounds (n <= 640), else recomputed.
+//   m <= 64: four waves, A kept for up to five rounds (n <= 640; three rounds, n <= 384,
+//            at d = 128), else recomputed.
 // Both keep two workgroups per CU within the register and LDS budgets.  With d = 64 and
 // fewer than two slices per CU, 2 * CUs - slices slices are shared by two workgroups so
 // that every CU gets about one and a half slices' worth of loads, stores and products.
+// With d = 128 every slice is shared (each workgroup holds 64 dims of V in LDS).
 static bool fused_choose(const Geometry& g, int num_cus, FusedPlan* plan) {
-  if (g.d != 32 && g.d != 64) return false;
+  if (g.d != 32 && g.d != 64 && g.d != 128) return false;
   const int npairs = (g.n + 31) / 32;
   FusedPlan p{};
-  if (g.m_pad == 32 && npairs <= 32) {
+  // d = 128 with up to 32 anchors: one round only (more rounds do not fit eight waves'
+  // registers at two workgroups per CU); longer slices take the split plan
+  if (g.m_pad == 32 && npairs <= (g.d == 128 ? 8 : 32)) {
     p.waves = 8;
     p.pairs_per_wave = (npairs + 7) / 8;
     p.keep_a = p.pairs_per_wave <= 2;
   } else if (g.m_pad == 64 && npairs <= 32) {
     p.waves = 4;
     p.pairs_per_wave = (npairs + 3) / 4;
-    p.keep_a = p.pairs_per_wave <= 5;
+    p.keep_a = p.pairs_per_wave <= (g.d == 128 ? 3 : 5);   // d = 128: registers
   } else {
     return false;
   }
   p.shared = 0;
   if (g.d == 64) p.shared = std::min<long long>(g.slices, std::max<long long>(0, 2LL * num_cus - g.slices));
+  if (g.d == 128) p.shared = g.slices;
   if (plan) *plan = p;
   return true;
 }
@@ -330,13 +340,17 @@ static hipError_t dispatch(const Geometry& g, const FusedPlan& p, const void* Q,
   const int r = p.pairs_per_wave;
   if (g.m_pad == 32) {
     if (r == 1) return go<D, 1, 8, 1, true, 4>(g, p, Q, U, V, H, s);
-    if (r == 2) return go<D, 1, 8, 2, true, 2>(g, p, Q, U, V, H, s);
-    if (r <= 4) return go<D, 1, 8, 4, false, 2>(g, p, Q, U, V, H, s);
+    if constexpr (D != 128) {
+      if (r == 2) return go<D, 1, 8, 2, true, 2>(g, p, Q, U, V, H, s);
+      if (r <= 4) return go<D, 1, 8, 4, false, 2>(g, p, Q, U, V, H, s);
+    }
     return hipErrorInvalidValue;
   }
   if (r <= 2) return go<D, 2, 4, 2, true, 2>(g, p, Q, U, V, H, s);
   if (r <= 3) return go<D, 2, 4, 3, true, 2>(g, p, Q, U, V, H, s);
-  if (r <= 5) return go<D, 2, 4, 5, true, 2>(g, p, Q, U, V, H, s);
+  if constexpr (D != 128) {
+    if (r <= 5) return go<D, 2, 4, 5, true, 2>(g, p, Q, U, V, H, s);
+  }
   if (r <= 8) return go<D, 2, 4, 8, false, 2>(g, p, Q, U, V, H, s);
   return hipErrorInvalidValue;
 }
@@ -345,8 +359,10 @@ hipError_t launch_fused_bf16(const Geometry& g, const FusedPlan& p, const void* 
                              const void* V, void* H, hipStream_t s) {
   FusedPlan chk{};
   if (!fused_choose(g, 1, &chk) || chk.waves != p.waves || chk.pairs_per_wave != p.pairs_per_wave ||
-      chk.keep_a != p.keep_a || p.shared < 0 || p.shared > g.slices || (p.shared > 0 && g.d != 64))
+      chk.keep_a != p.keep_a || p.shared < 0 || p.shared > g.slices || (p.shared > 0 && g.d == 32) ||
+      (g.d == 128 && p.shared != g.slices))
     return hipErrorInvalidValue;
+  if (g.d == 128) return dispatch<128>(g, p, Q, U, V, H, s);
   if (g.d == 64) return dispatch<64>(g, p, Q, U, V, H, s);
   if (g.d == 32) return dispatch<32>(g, p, Q, U, V, H, s);
   return hipErrorInvalidValue;

@@ -85,8 +85,9 @@ anchor_attn_status_t anchor_attn_destroy(anchor_attn_ctx* ctx);
  *   Q, V, H : [B, h, n, d]  device, element type `dtype`
  *   U       : [h, m, d]     device, element type `dtype`
  * Domain: B, h, n >= 0 (B*h*n == 0 is a successful no-op); 1 <= m <= 256; d in {32, 64},
- * or d = 128 with dtype BF16 (run by the split plan only: PLAN_FUSED gives NOT_SUPPORTED);
- * other d, or d = 128 in FP32, give NOT_SUPPORTED.
+ * or d = 128 with dtype BF16 (the fused plan takes m <= 32 with n <= 256 and m <= 64 with
+ * n <= 1024; PLAN_FUSED gives NOT_SUPPORTED beyond that); other d, or d = 128 in FP32,
+ * give NOT_SUPPORTED.
  * m >= n is accepted (the result is still defined; the O(mn) saving needs m < n). */
 anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx,
                                          const void* Q, const void* U, const void* V, void* H,

@@ -1,5 +1,6 @@
-"""GPU parity of the forward at head dim d = 128 (bf16, split plan) against the fp64
-oracle, and the entry points that refuse d = 128.  Gate: relative Frobenius error <= 1e-2."""
+"""GPU parity of the forward at head dim d = 128 (bf16; the split plan, and the fused plan
+with every slice shared by two workgroups) against the fp64 oracle, and the entry points
+that refuse d = 128.  Gate: relative Frobenius error <= 1e-2."""
 import numpy as np
 import pytest
 
@@ -51,6 +52,54 @@ def test_d128_against_oracle(ctxs, dev, shape, plan):
     assert e <= TOL
 
 
+# (B, h, n, m, d) the fused plan takes at d = 128: one round of eight waves (m <= 32,
+# n <= 256), four waves with A kept (two and three rounds) or recomputed (up to eight),
+# one token, a ragged last pair, and the ViT-S/16 and ViT-B/16-384 shapes at d = 128
+FUSED_SHAPES = [(3, 2, 196, 30, 128), (2, 2, 256, 32, 128), (4, 2, 77, 9, 128),
+                (2, 3, 250, 50, 128), (1, 4, 333, 64, 128), (2, 2, 577, 33, 128),
+                (1, 2, 1024, 64, 128), (1, 1, 1, 1, 128), (64, 6, 196, 30, 128),
+                (8, 12, 576, 64, 128)]
+
+
+@pytest.mark.parametrize("shape", FUSED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_d128_fused_against_oracle(ctxs, dev, shape):
+    import torch
+    B, h, n, m, d = shape
+    x = random_case(1900 + n + m + B, B, h, n, m, d, dtype="bf16", q_scale=1.5)
+    print(f"  d=128 fused forward B={B} h={h} n={n} m={m}", flush=True)
+    desc = ctxs["fused"].describe(B, h, n, m, d, "bf16")
+    assert desc.startswith("fused") and f"(0 whole slices + {B * h} shared" in desc, desc
+    Q, U, V = to_device(x, dev)
+    H = ctxs["fused"].forward(Q, U, V)
+    torch.cuda.synchronize()
+    e = bf16_err(to_host(H), oracle.anchor_attn(x.Q, x.U, x.V))
+    print(f"  relative Frobenius error {e:.3e}", flush=True)
+    assert e <= TOL
+
+
+def test_d128_fused_is_auto_at_vit_shape(ctxs):
+    """384 slices at n = 196, m = 30: the automatic choice is the fused plan; 300 tokens
+    with 30 anchors (two rounds of eight waves) is left to the split plan."""
+    assert ctxs["auto"].describe(64, 6, 196, 30, 128, "bf16").startswith("fused")
+    assert ctxs["auto"].describe(64, 6, 300, 30, 128, "bf16").startswith("split")
+
+
+def test_d128_fused_strided_views_match_contiguous(ctxs, dev):
+    import torch
+    B, h, n, m, d = 2, 3, 190, 40, 128
+    x = random_case(79, B, h, n, m, d, dtype="bf16")
+    Q, U, V = to_device(x, dev)
+    packed = torch.empty((B, n, 2, h, d), dtype=Q.dtype, device=dev)
+    packed[:, :, 0] = Q.permute(0, 2, 1, 3)
+    packed[:, :, 1] = V.permute(0, 2, 1, 3)
+    out = torch.empty((B, n, h, d), dtype=Q.dtype, device=dev)
+    ctxs["fused"].forward(packed[:, :, 0].permute(0, 2, 1, 3), U, packed[:, :, 1].permute(0, 2, 1, 3),
+                          out=out.permute(0, 2, 1, 3))
+    Hc = ctxs["fused"].forward(Q, U, V)
+    torch.cuda.synchronize()
+    assert torch.equal(out.permute(0, 2, 1, 3), Hc)
+
+
 def test_d128_long_slices_sampled(ctxs, dev):
     """The long workload's value structure (1% sink tokens x 10) at d = 128, m = 256:
     two slices of 16384 tokens, sampled slice against the oracle."""
@@ -87,10 +136,11 @@ def test_d128_strided_views_match_contiguous(ctxs, dev):
 
 
 def test_d128_refusals(ctxs, dev):
-    """d = 128 runs only the bf16 split forward: the fused plan, fp32, the backward, the
-    linear attention and Nystrom attention refuse it (NOT_SUPPORTED)."""
+    """d = 128 runs only the bf16 forward: the fused plan beyond its limits (here 300 tokens
+    with 16 anchors), fp32, the backward, the linear attention and Nystrom attention refuse
+    it (NOT_SUPPORTED)."""
     import torch
-    x = random_case(78, 1, 2, 64, 16, 128, dtype="bf16")
+    x = random_case(78, 1, 2, 300, 16, 128, dtype="bf16")
     Q, U, V = to_device(x, dev)
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
         ctxs["fused"].forward(Q, U, V)
