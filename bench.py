@@ -1,7 +1,8 @@
 """Anchor-attention throughput on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--plan auto|fused|split]
-                [--pass forward|backward|block|linear] [--no-cpu-baseline]
+                [--pass forward|backward|block|linear|nystrom] [--head-dim 128]
+                [--no-cpu-baseline]
 
 One step = one forward of the whole hot path (logits, softmax, column sums and A^T V,
 normalisation, H = A W) over one batch of the workload; with --pass backward, one
