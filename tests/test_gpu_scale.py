@@ -45,8 +45,9 @@ def _check_slices(Q, U, V, H, dtype, picks, label):
         assert np.all(np.isfinite(got)) and e <= tol_for(dtype)
 
 
-@pytest.mark.parametrize("B,h,n,m,d", [(40, 1000, 1000, 30, 64),   # fused, 2.56e9 elements
-                                       (16, 16, 140000, 32, 64)])  # split, 2.29e9 elements
+@pytest.mark.parametrize("B,h,n,m,d", [(40, 1000, 1000, 30, 64),    # fused, 2.56e9 elements
+                                       (16, 16, 140000, 32, 64),   # split, 2.29e9 elements
+                                       (20, 1000, 1000, 64, 128)])  # fused, d = 128, 2.56e9
 def test_more_than_2_31_elements(ctx, B, h, n, m, d):
     import torch
     print(f"  bf16 B={B} h={h} n={n} m={m} d={d}: {ctx.describe(B, h, n, m, d, 'bf16')[:60]}",
