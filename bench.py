@@ -1,7 +1,7 @@
 """Anchor-attention throughput on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--plan auto|fused|split]
-                [--pass forward|backward|block|linear|nystrom] [--head-dim 128]
+                [--pass forward|backward|block|linear|nystrom] [--head-dim D] [--anchors M]
                 [--no-cpu-baseline]
 
 One step = one forward of the whole hot path (logits, softmax, column sums and A^T V,
@@ -68,6 +68,8 @@ def parse():
                     choices=["forward", "backward", "block", "linear", "nystrom"])
     ap.add_argument("--head-dim", type=int, default=0,
                     help="override the workload's head dim (32, 64 or 128)")
+    ap.add_argument("--anchors", type=int, default=0,
+                    help="override the workload's anchor count (up to 512)")
     ap.add_argument("--landmarks", type=int, default=0,
                     help="landmarks for --pass nystrom (default: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -519,10 +521,16 @@ def main():
 
     name = args.workload or HEADLINE
     w = WORKLOADS[name]
-    if args.head_dim:
-        # the workload's value structure at another head dim (d = 128 runs the split plan)
+    if args.head_dim or args.anchors:
+        # the workload's value structure at another head dim or anchor count
         from efficient_vision_transformer_amd.inputs import Workload
-        w = Workload(**{**w.__dict__, "d": args.head_dim, "name": f"{w.name}_d{args.head_dim}"})
+        over = {}
+        if args.head_dim:
+            over["d"] = args.head_dim
+        if args.anchors:
+            over["m"] = args.anchors
+        tag = "".join(f"_{k}{v}" for k, v in over.items())
+        w = Workload(**{**w.__dict__, **over, "name": f"{w.name}{tag}"})
         name = w.name
     dev = torch.device("cuda:0")
     x = make_inputs(w, with_k=True)

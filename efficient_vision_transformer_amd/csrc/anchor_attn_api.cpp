@@ -95,15 +95,17 @@ anchor_attn_status_t check_shape(int B, int h, int n, int m, int d, anchor_attn_
   if (d != 32 && d != 64 && d != 128) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   // d = 128: the bf16 forward only (the fused and split plans)
   if (d == 128 && dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
-  if (m > 256) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  if (m > 512) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  // more than 256 anchors: the bf16 split plan at d <= 64 only
+  if (m > 256 && (dtype != ANCHOR_ATTN_BF16 || d > 64)) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   const long long slices = (long long)B * (long long)h;
   *empty = (slices == 0 || n == 0);
   // Index limits: per-slice offsets are 64-bit, but grids and token indices are 32-bit.
   if (slices > (1LL << 24) || (long long)n > (1LL << 28)) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   g->B = B; g->h = h; g->n = n; g->m = m; g->d = d;
-  // anchors padded to a multiple of 32, or of 64 above 128 anchors (the split plan's
-  // anchor-split pass 1 divides the tiles among four waves)
-  g->m_pad = (m <= 128) ? (m + 31) / 32 * 32 : (m + 63) / 64 * 64;
+  // anchors padded to a multiple of 32, of 64 above 128 anchors and of 128 above 256 (the
+  // split plan's anchor-split pass 1 divides the tiles among four or eight waves)
+  g->m_pad = (m <= 128) ? (m + 31) / 32 * 32 : (m <= 256) ? (m + 63) / 64 * 64 : (m + 127) / 128 * 128;
   g->at = g->m_pad / 16;
   g->slices = slices;
   g->c2 = (float)(1.4426950408889634 / std::sqrt((double)d));

@@ -21,27 +21,29 @@
 namespace aa {
 
 // ---------------------------------------------------------------------------------------
-// Pass 1 for more than 128 anchors (AT = 12 or 16 tiles).  The four waves split the
-// anchors into groups of J = AT / 4 tiles.  Blocks of 128 tokens are staged through LDS:
+// Pass 1 for more than 128 anchors (AT = 12 or 16 tiles on four waves, 24 or 32 tiles on
+// eight).  The NW waves split the anchors into groups of J = AT / NW tiles.  Blocks of
+// 32 NW tokens are staged through LDS:
 // every wave loads one 32-token pair of Q (kept in its MFMA operand layout) and of V (kept
 // as rows); the next block's rows are in flight while the current block is computed.
 // For each pair, every wave forms S^T = U_group Q^T (lanes = tokens, registers = its
 // anchors), reduces the maximum and then the sum over its anchors in registers plus two
-// permlane swaps, and the four groups' partial maxima and sums of every token are
+// permlane swaps, and the NW groups' partial maxima and sums of every token are
 // combined through LDS.  The wave writes the pair's rows of A for its anchors to its own
 // LDS block and accumulates its (16-anchor, 16-dim) tiles of A^T V and Delta, reading
 // both operands (tokens on the contraction axis) with the transposing LDS read.
 // Partials leave in accumulator layout with dim tile dt holding dims 16dt .. 16dt + 15.
-template <int D, int AT>
-__global__ __launch_bounds__(4 * kWave, 2)
+template <int D, int AT, int NW = 4>
+__global__ __launch_bounds__(NW * kWave, 2)
 void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                  const __bf16* __restrict__ V, float* __restrict__ part,
                  float* __restrict__ dpart, View qw, View xw, int h, int n, int m, int chunks,
                  int chunk_len, float c2) {
-  constexpr int NW = 4, J = AT / NW, KS = D / 32, DT = D / 16;
+  constexpr int J = AT / NW, KS = D / 32, DT = D / 16;
   constexpr int AS = 80;                     // A row stride (16J + padding, bank-spread)
   constexpr int VS = tr_stride<D>();
-  static_assert(AT % NW == 0 && J >= 2 && J <= 4, "four anchor groups of 2 to 4 tiles");
+  static_assert(AT % NW == 0 && J >= 2 && J <= 4 && NW % 4 == 0,
+                "four or eight anchor groups of 2 to 4 tiles");
   const int slice = blockIdx.x / chunks;
   const int chunk = blockIdx.x - slice * chunks;
   const int head = slice % h;
@@ -55,8 +57,8 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   __shared__ u32x4 q_lds[NW][2][KS][kWave];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds[NW * 32 * VS];   // V rows, this block
   __shared__ __attribute__((aligned(16))) __bf16 a_lds[NW][32 * AS];    // A rows, per wave
-  __shared__ __attribute__((aligned(16))) float st_max[128][NW];        // per token, per group
-  __shared__ __attribute__((aligned(16))) float st_sum[128][NW];
+  __shared__ __attribute__((aligned(16))) float st_max[32 * NW][NW];    // per token, per group
+  __shared__ __attribute__((aligned(16))) float st_sum[32 * NW][NW];
 
   auto load_pair = [&](int blk, u32x4 (*qv)[KS], u32x4 (*vv)[KS]) {
 #pragma unroll
@@ -137,8 +139,15 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       float zp[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const f32x4 mg = *(const f32x4*)&st_max[32 * ps + 16 * tt + c][0];
-        const float mneg = -fmaxf(fmaxf(mg[0], mg[1]), fmaxf(mg[2], mg[3])) * c2;
+        const float* mrow = &st_max[32 * ps + 16 * tt + c][0];
+        f32x4 mg = *(const f32x4*)mrow;
+        float M = fmaxf(fmaxf(mg[0], mg[1]), fmaxf(mg[2], mg[3]));
+#pragma unroll
+        for (int q4 = 4; q4 < NW; q4 += 4) {
+          mg = *(const f32x4*)(mrow + q4);
+          M = fmaxf(M, fmaxf(fmaxf(mg[0], mg[1]), fmaxf(mg[2], mg[3])));
+        }
+        const float mneg = -M * c2;
         f32x4 zt = zero4();
 #pragma unroll
         for (int jl = 0; jl < J; ++jl) {
@@ -154,8 +163,13 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int tok = 32 * ps + 16 * tt + c;
-        const f32x4 zg = *(const f32x4*)&st_sum[tok][0];
-        const float Z = (zg[0] + zg[1]) + (zg[2] + zg[3]);
+        f32x4 zg = *(const f32x4*)&st_sum[tok][0];
+        float Z = (zg[0] + zg[1]) + (zg[2] + zg[3]);
+#pragma unroll
+        for (int q4 = 4; q4 < NW; q4 += 4) {   // groups summed in a fixed order
+          zg = *(const f32x4*)&st_sum[tok][q4];
+          Z += (zg[0] + zg[1]) + (zg[2] + zg[3]);
+        }
         const float inv = (blk + tok < t_end) ? __builtin_amdgcn_rcpf(Z) : 0.f;   // Z >= 1
         __bf16* arow = a_lds[w] + (16 * tt + c) * AS + 4 * g;
 #pragma unroll
@@ -419,18 +433,23 @@ void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpa
 // dense and long shapes; more slots cost registers and occupancy)
 constexpr int kPass2Ahead = 1;
 
+// Waves per pass-2 workgroup: eight from 384 anchors up (U and W fill 96-128 KB of LDS,
+// one workgroup per CU), else four.
+template <int AT>
+constexpr int pass2_waves() { return AT >= 24 ? 8 : kPass2Waves; }
+
 // Pass 2.  Each wave takes 16-token tiles.  Logits are formed transposed, S^T = U Q^T
 // (lanes = tokens, registers = anchors), so the softmax is an in-register reduction plus
 // two permlane swaps and the normalised A is directly the right operand of
 // H^T = W^T A^T.  U and W stay in LDS for the whole chunk.  Each wave keeps kPass2Ahead
 // of its Q tiles in flight (a register ring refilled as soon as a tile's logits are
 // formed); the first ones are requested before U and W are staged.
-template <int D, int AT>
-__global__ __launch_bounds__(kPass2Waves * kWave, 2)
+template <int D, int AT, int NW = pass2_waves<AT>()>
+__global__ __launch_bounds__(NW * kWave, 2)
 void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                 const u32x4* __restrict__ Wop, __bf16* __restrict__ H, View qw, View ow, int h,
                 int n, int m, int chunks, int chunk_len, float c2, int u_per_slice = 0) {
-  constexpr int NW = kPass2Waves, KS = D / 32, DT = D / 16, MP = AT / 2;
+  constexpr int KS = D / 32, DT = D / 16, MP = AT / 2;
   const int slice = blockIdx.x / chunks;
   const int chunk = blockIdx.x - slice * chunks;
   const int head = slice % h;
@@ -472,7 +491,8 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   for (int p = 0; p < PF; ++p) load_q(t_begin + 16 * w + step * p, q[p]);
   stage_store(ust, &u_lds[0][0][0]);
   stage_store(wst, &w_lds[0][0][0]);
-  constexpr int NPAD = pad_tiles(AT);
+  // above 256 anchors m is padded to a multiple of 128: up to eight padded tiles
+  constexpr int NPAD = AT > 16 ? 8 : pad_tiles(AT);
   f32x4 mask[NPAD];
   pad_mask_tiles<AT, NPAD>(g, m, mask);
   __syncthreads();
@@ -550,6 +570,10 @@ static void launch_pass1_t(const Geometry& geo, const SplitPlan& p, const void* 
     pass1x_bf16<D, AT / 2, kPass1Waves><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, stream>>>(
         (const __bf16*)Q, (const __bf16*)U, (const __bf16*)X, part, dpart, geo.vw.q, geo.vw.v,
         geo.h, geo.n, geo.m, p.chunks1, p.chunk_len1, geo.c2);
+  } else if constexpr (AT >= 24) {
+    pass1a_bf16<D, AT, 8><<<dim3((unsigned)g1), dim3(8 * kWave), 0, stream>>>(
+        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)X, part, dpart, geo.vw.q, geo.vw.v,
+        geo.h, geo.n, geo.m, p.chunks1, p.chunk_len1, geo.c2);
   } else {
     pass1a_bf16<D, AT><<<dim3((unsigned)g1), dim3(4 * kWave), 0, stream>>>(
         (const __bf16*)Q, (const __bf16*)U, (const __bf16*)X, part, dpart, geo.vw.q, geo.vw.v,
@@ -569,7 +593,7 @@ static hipError_t launch_split_bf16_t(const Geometry& geo, const SplitPlan& p, c
   finalize_bf16<D><<<dim3((unsigned)(geo.slices * AT)), dim3(256), 0, stream>>>(
       part, dpart, (__bf16*)Wop, p.chunks1, AT);
   const long long g2 = geo.slices * p.chunks2;
-  pass2_bf16<D, AT><<<dim3((unsigned)g2), dim3(kPass2Waves * kWave), 0, stream>>>(
+  pass2_bf16<D, AT><<<dim3((unsigned)g2), dim3(pass2_waves<AT>() * kWave), 0, stream>>>(
       (const __bf16*)Q, (const __bf16*)U, (const u32x4*)Wop, (__bf16*)H, geo.vw.q, geo.vw.o,
       geo.h, geo.n, geo.m, p.chunks2, p.chunk_len2, geo.c2);
   return hipGetLastError();
@@ -585,6 +609,13 @@ static hipError_t dispatch_at(const Geometry& g, const SplitPlan& p, const void*
     case 8: return launch_split_bf16_t<D, 8>(g, p, Q, U, V, H, ws, s);
     case 12: return launch_split_bf16_t<D, 12>(g, p, Q, U, V, H, ws, s);
     case 16: return launch_split_bf16_t<D, 16>(g, p, Q, U, V, H, ws, s);
+    case 24:
+    case 32:
+      if constexpr (D <= 64) {
+        return g.at == 24 ? launch_split_bf16_t<D, 24>(g, p, Q, U, V, H, ws, s)
+                          : launch_split_bf16_t<D, 32>(g, p, Q, U, V, H, ws, s);
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -653,7 +684,7 @@ hipError_t launch_nystrom_pass2_bf16(const Geometry& g, const SplitPlan& p, cons
   auto at = [&](auto D) -> hipError_t {
     constexpr int d = decltype(D)::value;
 #define AA_NYS2(AT)                                                                           \
-  pass2_bf16<d, AT><<<dim3((unsigned)g2), dim3(kPass2Waves * kWave), 0, s>>>(                 \
+  pass2_bf16<d, AT><<<dim3((unsigned)g2), dim3(pass2_waves<AT>() * kWave), 0, s>>>(           \
       (const __bf16*)Q, (const __bf16*)kt, (const u32x4*)Wop, (__bf16*)H, qw, ow, g.h, g.n, g.m, \
       p.chunks2, p.chunk_len2, g.c2, 1)
     switch (g.at) {

@@ -53,7 +53,7 @@ typedef enum {
 typedef enum {
     ANCHOR_ATTN_SUCCESS = 0,
     ANCHOR_ATTN_ERROR_INVALID_VALUE = 1,   /* null pointer, negative size, m or d == 0, overlap, misalignment */
-    ANCHOR_ATTN_ERROR_NOT_SUPPORTED = 2,   /* d not 32 or 64, m > 256, unknown dtype, plan not applicable */
+    ANCHOR_ATTN_ERROR_NOT_SUPPORTED = 2,   /* d, m or dtype outside the entry point's domain, plan not applicable */
     ANCHOR_ATTN_ERROR_OUT_OF_MEMORY = 3,   /* workspace allocation failed; the context stays usable */
     ANCHOR_ATTN_ERROR_HIP = 4              /* HIP runtime error (no device, launch failure) */
 } anchor_attn_status_t;
@@ -84,7 +84,8 @@ anchor_attn_status_t anchor_attn_destroy(anchor_attn_ctx* ctx);
  * and returns without waiting.
  *   Q, V, H : [B, h, n, d]  device, element type `dtype`
  *   U       : [h, m, d]     device, element type `dtype`
- * Domain: B, h, n >= 0 (B*h*n == 0 is a successful no-op); 1 <= m <= 256; d in {32, 64},
+ * Domain: B, h, n >= 0 (B*h*n == 0 is a successful no-op); 1 <= m <= 512 (more than 256
+ * anchors: dtype BF16 with d <= 64, run by the split plan); d in {32, 64},
  * or d = 128 with dtype BF16 (the fused plan takes m <= 32 with n <= 256 and m <= 64 with
  * n <= 1024; PLAN_FUSED gives NOT_SUPPORTED beyond that); other d, or d = 128 in FP32,
  * give NOT_SUPPORTED.

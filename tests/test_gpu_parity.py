@@ -269,7 +269,7 @@ def test_abi_rejects_bad_arguments(ctxs, dev):
     assert run(m=0) == 1
     assert run(n=-1) == 1
     assert run(d=48) == 2
-    assert run(m=257) == 2
+    assert run(m=513) == 2
     assert run(dt=5) == 2
     assert run(H=p(Q)) == 1            # output aliases an input
     assert run(V=p(V, 2)) == 1         # misaligned
