@@ -127,3 +127,14 @@ def test_forward_d128_graph(ctxs):
     H = torch.empty_like(Q)
     print("  forward d=128 graph", flush=True)
     _capture_and_replay(lambda: ctxs["auto"].forward(Q, U, V, out=H), [H])
+
+
+def test_forward_many_anchors_graph(ctxs):
+    """480 anchors (pass 1 and pass 2 on eight waves) captured."""
+    import torch
+    from efficient_vision_transformer_amd.inputs import random_case
+    x = random_case(6, 2, 2, 900, 480, 64, dtype="bf16")
+    Q, U, V = _conv(x.bits["Q"]), _conv(x.bits["U"]), _conv(x.bits["V"])
+    H = torch.empty_like(Q)
+    print("  forward m=480 graph", flush=True)
+    _capture_and_replay(lambda: ctxs["auto"].forward(Q, U, V, out=H), [H])
