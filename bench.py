@@ -41,6 +41,16 @@ MEASURED_TRAFFIC = {
                                "sha": "3fd2041ff5db177e", "read_bytes": 19474503,
                                "write_bytes": 10916934},
 }
+# the split plan's three kernels per step (pass 1, finalize, pass 2)
+_SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",
+                  "efficient_vision_transformer_amd/csrc/tile_ops.h",
+                  "efficient_vision_transformer_amd/csrc/device_common.h",
+                  "efficient_vision_transformer_amd/csrc/kernels.h",
+                  "efficient_vision_transformer_amd/csrc/pass2_layout.h"]
+MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "e6fbd966d5a6368e",
+                                             "read_bytes": 122357480, "write_bytes": 55179852}
+MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "e6fbd966d5a6368e",
+                                               "read_bytes": 249593259, "write_bytes": 107689644}
 
 
 def measured_traffic(workload: str, plan: str):

@@ -21,6 +21,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "pass2_layout.h"
 #include "tile_ops.h"
 
 namespace aa {
@@ -334,7 +335,7 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
 #pragma unroll
       for (int jj = 0; jj < CW; ++jj) {
         const int k = CW * w - MPAD + jj;
-        dst[wt_layout_index<D>(MP, a, k)] = (__bf16)((a < m) ? x[i][jj] / pvr[i] : 0.f);
+        dst[w2_layout_index(MP, a, k)] = (__bf16)((a < m) ? x[i][jj] / pvr[i] : 0.f);
       }
     }
   }

@@ -16,6 +16,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "pass2_layout.h"
 #include "tile_ops.h"
 
 namespace aa {
@@ -375,10 +376,8 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 
 // ---------------------------------------------------------------------------------------
 // Finalize: W = Delta^-1 (sum over chunks of P), chunk order fixed.  One workgroup per
-// (slice, 16-anchor tile).  Output layout = the left operand of pass 2's H^T = W^T A^T:
-// [slice][dt2][jj][lane'][slot] with lane' (c',g') holding dim out_dim(dt2, c') and
-// anchors {32jj + 4g' + slot (slot<4), 32jj + 16 + 4g' + slot - 4 (slot>=4)}.  Column c of
-// a partial's dim tile dt is dim 16dt + c.
+// (slice, 16-anchor tile).  Output layout = the left operand of pass 2's H^T = W^T A^T
+// (w2_layout_index, per slice).  Column c of a partial's dim tile dt is dim 16dt + c.
 template <int D>
 __global__ __launch_bounds__(256)
 void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpart,
@@ -415,16 +414,11 @@ void finalize_bf16(const float* __restrict__ part, const float* __restrict__ dpa
     }
   }
   const float rinv = (delta > 0.f) ? 1.f / delta : 0.f;
-  const int jj = anchor >> 5, half = (anchor >> 4) & 1, gg = (anchor >> 2) & 3;
-  const int slot = 4 * half + (anchor & 3);
+  __bf16* Ws = Wop + (size_t)slice * DT * MP * 64 * 8;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     const float wv = (delta > 0.f) ? p[dt] * rinv : 0.f;
-    const int dim = 16 * dt + c;
-    const int rem = dim % (D / 4);
-    const int dt2 = rem >> 2;
-    const int cc = 4 * (dim / (D / 4)) + (rem & 3);
-    Wop[((((size_t)slice * DT + dt2) * MP + jj) * 64 + 16 * gg + cc) * 8 + slot] = (__bf16)wv;
+    Ws[w2_layout_index(MP, anchor, 16 * dt + c)] = (__bf16)wv;
   }
 }
 
@@ -450,8 +444,19 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                 const u32x4* __restrict__ Wop, __bf16* __restrict__ H, View qw, View ow, int h,
                 int n, int m, int chunks, int chunk_len, float c2, int u_per_slice = 0) {
   constexpr int KS = D / 32, DT = D / 16, MP = AT / 2;
-  const int slice = blockIdx.x / chunks;
-  const int chunk = blockIdx.x - slice * chunks;
+  // Workgroups are dealt to the eight XCDs in turn (id b to XCD b % 8).  When the slices
+  // divide by eight, all chunks of a slice get ids on one XCD, so that its W^T operands are
+  // fetched into one L2 instead of eight.
+  const int b = blockIdx.x, slices = (int)gridDim.x / chunks;
+  int slice, chunk;
+  if ((slices & 7) == 0) {
+    const int k = b >> 3, ls = k / chunks;
+    slice = 8 * ls + (b & 7);
+    chunk = k - ls * chunks;
+  } else {
+    slice = b / chunks;
+    chunk = b - slice * chunks;
+  }
   const int head = slice % h;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -540,7 +545,8 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     bf16x8 abf[MP];
 #pragma unroll
     for (int jj = 0; jj < MP; ++jj) abf[jj] = pack_bf16(s[2 * jj] * inv, s[2 * jj + 1] * inv);
-    // a5: H^T = W^T A^T; lane (c,g) ends with token c, dims (D/4)g + 4dt2 + r.
+    // a5: H^T = W^T A^T; lane (c,g) ends with token c, dims out_dim_c(dt2, 4g + r), i.e.
+    // 32h + 8g .. + 7 in tiles 2h and 2h + 1.
     f32x4 hacc[DT];
 #pragma unroll
     for (int dt2 = 0; dt2 < DT; ++dt2) {
@@ -551,11 +557,11 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       hacc[dt2] = acc;
     }
     if (ok) {
-      __bf16* dst = H + ob + view_row(ow, row) + (D / 4) * g;
+      __bf16* dst = H + ob + view_row(ow, row) + 8 * g;
 #pragma unroll
-      for (int half = 0; half < DT / 2; ++half)
-        __builtin_nontemporal_store(as_u32x4(pack_bf16(hacc[2 * half], hacc[2 * half + 1])),
-                                    (u32x4*)(dst + 8 * half));
+      for (int hh = 0; hh < DT / 2; ++hh)
+        __builtin_nontemporal_store(as_u32x4(pack_bf16(hacc[2 * hh], hacc[2 * hh + 1])),
+                                    (u32x4*)(dst + 32 * hh));
     }
   }
   }

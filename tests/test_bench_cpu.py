@@ -24,3 +24,12 @@ def test_headline_traffic_record_matches_the_kernel_sources():
     t = bench.measured_traffic("vit_s16_224", "fused")
     assert t is not None, "kernel sources changed since the HBM counters were taken"
     assert 0.9 * 28924416 < t < 1.5 * 28924416
+
+
+def test_split_traffic_records_match_the_kernel_sources():
+    sys.path.insert(0, ROOT)
+    import bench
+    for wl, algo in (("dense_64x64", 100794368), ("long_16k_bf16", 201850880)):
+        t = bench.measured_traffic(wl, "split")
+        assert t is not None, f"{wl}: split kernel sources changed since the counters were taken"
+        assert algo < t < 2.5 * algo
