@@ -20,15 +20,16 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "pass2_layout.h"
 #include "tile_ops.h"
 
 namespace aa {
 
 // Anchor a, dim k of an m_pad x D matrix -> position in the "U layout" left operand of a
 // logits-like product (lane (c,g) of (tile j, chunk kk): anchor 16j + c, dims
-// 8*KS*g + 8kk .. + 7) and in the "W^T layout" left operand of an output-like product
-// ([dt2][jj][lane'][slot], lane' (c',g') holding dim out_dim(dt2, c') and anchors
-// {32jj + 4g' + slot, 32jj + 16 + 4g' + slot - 4}).
+// 8*KS*g + 8kk .. + 7); the "W^T layout" left operand of an output-like product is
+// w2_layout_index ([dt2][jj][lane'][slot], lane' (c',g') holding dim out_dim_c(dt2, c')
+// and anchors {32jj + 4g' + slot, 32jj + 16 + 4g' + slot - 4}).
 template <int D>
 __device__ __forceinline__ size_t u_layout_index(int AT, int a, int k) {
   constexpr int KS = D / 32;
@@ -96,7 +97,7 @@ void bwd_finalize(const float* __restrict__ partP, const float* __restrict__ par
     const int k = 16 * dt + c;
     wu[su + u_layout_index<D>(AT, anchor, k)] = (__bf16)p[dt];
     dpu[su + u_layout_index<D>(AT, anchor, k)] = (__bf16)q[dt];
-    dpw[sw + wt_layout_index<D>(MP, anchor, k)] = (__bf16)q[dt];
+    dpw[sw + w2_layout_index(MP, anchor, k)] = (__bf16)q[dt];
   }
 }
 
@@ -113,8 +114,8 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   constexpr int TILES = AT * DT, TPW = TILES / NW;
   constexpr int AS = tr_stride<32 * MP>(), VS = tr_stride<D>();
   static_assert(TILES % NW == 0, "tiles split evenly over the waves");
-  const int slice = blockIdx.x / chunks;
-  const int chunk = blockIdx.x - slice * chunks;
+  int slice, chunk;
+  slice_chunk_of(blockIdx.x, chunks, slice, chunk);   // a slice's chunks on one XCD
   const int head = slice % h;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -174,7 +175,7 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         const int a = idx / (D / 8), k = 8 * (idx - a * (D / 8));
         const bf16x8 v = as_bf16x8(utst.r[i]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ut[wt_layout_index<D>(MP, a, k + e)] = v[e];
+        for (int e = 0; e < 8; ++e) ut[w2_layout_index(MP, a, k + e)] = v[e];
       }
     }
   }
@@ -269,9 +270,10 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
           dsb[jj] = pack_bf16(d0, d1);
         }
         // dQ^T = c U^T dS^T and dV^T = dP^T A^T, two dim tiles at a time: lane (c,g) ends
-        // with token c, dims (D/4)g + 4dt2 + r'.
-        const size_t oq = dqb + view_row(bv.dq, row) + (D / 4) * g;
-        const size_t ov = dvb + view_row(bv.dv, row) + (D / 4) * g;
+        // with token c, dims 32hh + 8g .. + 7 (tiles 2hh and 2hh + 1), so each store
+        // instruction writes one contiguous 64-byte run per row.
+        const size_t oq = dqb + view_row(bv.dq, row) + 8 * g;
+        const size_t ov = dvb + view_row(bv.dv, row) + 8 * g;
 #pragma unroll
         for (int hh = 0; hh < DT / 2; ++hh) {
           f32x4 q0 = zero4(), q1 = zero4();
@@ -280,14 +282,14 @@ void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
             q0 = mfma_bf16(as_bf16x8(ut_lds[2 * hh][jj][lane]), dsb[jj], q0);
             q1 = mfma_bf16(as_bf16x8(ut_lds[2 * hh + 1][jj][lane]), dsb[jj], q1);
           }
-          if (ok) __builtin_nontemporal_store(as_u32x4(pack_bf16(q0 * cs, q1 * cs)), (u32x4*)(dQ + oq + 8 * hh));
+          if (ok) __builtin_nontemporal_store(as_u32x4(pack_bf16(q0 * cs, q1 * cs)), (u32x4*)(dQ + oq + 32 * hh));
           f32x4 v0 = zero4(), v1 = zero4();
 #pragma unroll
           for (int jj = 0; jj < MP; ++jj) {
             v0 = mfma_bf16(as_bf16x8(dpw_lds[2 * hh][jj][lane]), ab[jj], v0);
             v1 = mfma_bf16(as_bf16x8(dpw_lds[2 * hh + 1][jj][lane]), ab[jj], v1);
           }
-          if (ok) __builtin_nontemporal_store(as_u32x4(pack_bf16(v0, v1)), (u32x4*)(dV + ov + 8 * hh));
+          if (ok) __builtin_nontemporal_store(as_u32x4(pack_bf16(v0, v1)), (u32x4*)(dV + ov + 32 * hh));
         }
         // Rows of dS ([token][anchor], dsb[jj] holds anchors 32jj + 4g .. + 3 and
         // 32jj + 16 + 4g .. + 3).

@@ -1,5 +1,6 @@
-// pass2_layout.h -- the W^T operand layout that pass 2 of the split plan reads (written by
-// the forward's finalize and by the Nystrom solve).
+// pass2_layout.h -- the W^T operand layout that the split plan's output passes read
+// (forward pass 2, written by the forward's finalize and by the Nystrom solve; the
+// backward's token pass), and their workgroup-to-(slice, chunk) mapping.
 #pragma once
 #include "device_common.h"
 #include "tile_ops.h"
@@ -16,6 +17,22 @@ __device__ __forceinline__ size_t w2_layout_index(int MP, int a, int k) {
   const int q = k & 31, dt2 = 2 * (k >> 5) + ((q & 7) >> 2), cc = 4 * (q >> 3) + (q & 3);
   const int jj = a >> 5, half = (a >> 4) & 1, gg = (a >> 2) & 3;
   return ((((size_t)dt2 * MP + jj) * kWave) + 16 * gg + cc) * 8 + 4 * half + (a & 3);
+}
+
+// Workgroup b of a grid of slices x chunks -> (slice, chunk).  Workgroups are dealt to the
+// eight XCDs in turn (b to XCD b % 8); when the slices divide by eight, all chunks of a
+// slice get ids on one XCD, so the slice's operands staged by every chunk are fetched into
+// one L2 instead of eight.
+__device__ __forceinline__ void slice_chunk_of(int b, int chunks, int& slice, int& chunk) {
+  const int slices = (int)gridDim.x / chunks;
+  if ((slices & 7) == 0) {
+    const int k = b >> 3, ls = k / chunks;
+    slice = 8 * ls + (b & 7);
+    chunk = k - ls * chunks;
+  } else {
+    slice = b / chunks;
+    chunk = b - slice * chunks;
+  }
 }
 
 }  // namespace aa

@@ -444,19 +444,8 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                 const u32x4* __restrict__ Wop, __bf16* __restrict__ H, View qw, View ow, int h,
                 int n, int m, int chunks, int chunk_len, float c2, int u_per_slice = 0) {
   constexpr int KS = D / 32, DT = D / 16, MP = AT / 2;
-  // Workgroups are dealt to the eight XCDs in turn (id b to XCD b % 8).  When the slices
-  // divide by eight, all chunks of a slice get ids on one XCD, so that its W^T operands are
-  // fetched into one L2 instead of eight.
-  const int b = blockIdx.x, slices = (int)gridDim.x / chunks;
   int slice, chunk;
-  if ((slices & 7) == 0) {
-    const int k = b >> 3, ls = k / chunks;
-    slice = 8 * ls + (b & 7);
-    chunk = k - ls * chunks;
-  } else {
-    slice = b / chunks;
-    chunk = b - slice * chunks;
-  }
+  slice_chunk_of(blockIdx.x, chunks, slice, chunk);   // a slice's chunks on one XCD
   const int head = slice % h;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
