@@ -38,8 +38,8 @@ MEASURED_TRAFFIC = {
                                            "efficient_vision_transformer_amd/csrc/tile_ops.h",
                                            "efficient_vision_transformer_amd/csrc/device_common.h",
                                            "efficient_vision_transformer_amd/csrc/kernels.h"],
-                               "sha": "3fd2041ff5db177e", "read_bytes": 19474503,
-                               "write_bytes": 10916934},
+                               "sha": "f01cc7097ca16915", "read_bytes": 19474446,
+                               "write_bytes": 10950246},
 }
 # the split plan's three kernels per step (pass 1, finalize, pass 2)
 _SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",
@@ -47,10 +47,10 @@ _SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",
                   "efficient_vision_transformer_amd/csrc/device_common.h",
                   "efficient_vision_transformer_amd/csrc/kernels.h",
                   "efficient_vision_transformer_amd/csrc/pass2_layout.h"]
-MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "0805c8eac7cb1c41",
-                                             "read_bytes": 122376760, "write_bytes": 55165705}
-MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "0805c8eac7cb1c41",
-                                               "read_bytes": 249579410, "write_bytes": 107690886}
+MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "69f93d69814e1e83",
+                                             "read_bytes": 122357958, "write_bytes": 55167805}
+MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "69f93d69814e1e83",
+                                               "read_bytes": 249591257, "write_bytes": 107653684}
 
 
 def measured_traffic(workload: str, plan: str):

@@ -154,20 +154,4 @@ __device__ __forceinline__ void pad_mask_tiles(int g, int m, f32x4* mask) {
       mask[hh][r] = (16 * (AT - NPAD + hh) + 4 * g + r < m) ? 0.f : -INFINITY;
 }
 
-// Output dim of accumulator row i (= 4g + r) of a5 dim tile dt2: lane group g owns the
-// contiguous dims 4*DT*g .. 4*DT*g + 4*DT - 1, so each lane stores one run per token.
-__host__ __device__ constexpr int out_dim(int D, int dt2, int i) {
-  return (D / 4) * (i >> 2) + 4 * dt2 + (i & 3);
-}
-
-// (anchor a, dim k) -> element of one slice's block of pass 2's W^T operands
-// [dt2][jj][lane'][slot]: lane' (c', g') of [dt2][jj] holds dim out_dim(D, dt2, c') and
-// anchors 32jj + 4g' + slot (slot < 4) and 32jj + 16 + 4g' + slot - 4 (slot >= 4).
-template <int D>
-__device__ __forceinline__ size_t wt_layout_index(int MP, int a, int k) {
-  const int rem = k % (D / 4), dt2 = rem >> 2, cc = 4 * (k / (D / 4)) + (rem & 3);
-  const int jj = a >> 5, half = (a >> 4) & 1, gg = (a >> 2) & 3;
-  return ((((size_t)dt2 * MP + jj) * kWave) + 16 * gg + cc) * 8 + 4 * half + (a & 3);
-}
-
 }  // namespace aa

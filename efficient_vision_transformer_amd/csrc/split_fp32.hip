@@ -198,7 +198,8 @@ void pass1_fp32(const float* __restrict__ Q, const float* __restrict__ U,
 
 // Finalize (fp32): W = Delta^-1 sum_chunks P in chunk order; output is the left operand
 // of pass 2's H^T = W^T A^T per K step (j, r): [slice][dt2][j][r][lane'] with lane'
-// (c', g') holding W[16j + 4g' + r][out_dim(dt2, c')].
+// (c', g') holding W[16j + 4g' + r][(D/4)(c' / 4) + 4dt2 + c' % 4] (lane group g of the
+// output then holds the contiguous dims (D/4)g .. (D/4)g + D/4 - 1 of its token).
 template <int D>
 __global__ __launch_bounds__(256)
 void finalize_fp32(const float* __restrict__ part, const float* __restrict__ dpart,
