@@ -38,8 +38,8 @@ MEASURED_TRAFFIC = {
                                            "efficient_vision_transformer_amd/csrc/tile_ops.h",
                                            "efficient_vision_transformer_amd/csrc/device_common.h",
                                            "efficient_vision_transformer_amd/csrc/kernels.h"],
-                               "sha": "f01cc7097ca16915", "read_bytes": 19474446,
-                               "write_bytes": 10950246},
+                               "sha": "c059c519fcfc58a0", "read_bytes": 19474579,
+                               "write_bytes": 10941091},
 }
 # the split plan's three kernels per step (pass 1, finalize, pass 2)
 _SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",

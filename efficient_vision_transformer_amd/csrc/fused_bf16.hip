@@ -92,8 +92,11 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
   pad_mask<MP>(g, m, mask);
   __syncthreads();
   // With several rounds U's operands stay in registers instead of being read from LDS
-  // every round.
-  constexpr bool UREG = KEEP_A && ROUNDS > 2;
+  // every round.  At d = 128 those registers go to the kept A instead, and with more than
+  // three kept rounds the next pair's V is requested at the end of a round rather than a
+  // round ahead (registers again).
+  constexpr bool UREG = KEEP_A && ROUNDS > 2 && D != 128;
+  constexpr bool VAHEAD = !(D == 128 && KEEP_A && ROUNDS > 3);
   bf16x8 ureg[UREG ? AT : 1][KS];
   if constexpr (UREG) {
 #pragma unroll
@@ -118,12 +121,13 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
     if (pairs_here <= 0) break;
     const int p = r * NW + w;
     const bool more = (r + 1 < ROUNDS) && (p + NW < npairs);
-    u32x4 qn[2][KS], vn[2][KV];
+    u32x4 qn[2][KS], vn[VAHEAD ? 2 : 1][KV];
     if (more) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         load_rows_c<D, D>(Q, qb, qs, 32 * (p + NW) + 16 * tt + c, n, g, 0, qn[tt]);
-        load_rows_c<D, DW>(V, vb, vs, 32 * (p + NW) + 16 * tt + c, n, g, d0, vn[tt]);
+        if constexpr (VAHEAD)
+          load_rows_c<D, DW>(V, vb, vs, 32 * (p + NW) + 16 * tt + c, n, g, d0, vn[tt]);
       }
     }
     // Phase A: rows 32w .. 32w + 31 of the round's LDS blocks hold this wave's pair.
@@ -164,8 +168,12 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
       for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) qc[tt][kk] = qn[tt][kk];
+        if constexpr (VAHEAD) {
 #pragma unroll
-        for (int kk = 0; kk < KV; ++kk) vc[tt][kk] = vn[tt][kk];
+          for (int kk = 0; kk < KV; ++kk) vc[tt][kk] = vn[tt][kk];
+        } else {
+          load_rows_c<D, DW>(V, vb, vs, 32 * (p + NW) + 16 * tt + c, n, g, d0, vc[tt]);
+        }
       }
     }
   }
@@ -288,8 +296,7 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 
 // Plans (n <= 1024, m <= 64; d = 128 and m <= 32: n <= 256):
 //   m <= 32: eight waves, A kept for up to two rounds (n <= 512), else recomputed;
-//   m <= 64: four waves, A kept for up to five rounds (n <= 640; three rounds, n <= 384,
-//            at d = 128), else recomputed.
+//   m <= 64: four waves, A kept for up to five rounds (n <= 640), else recomputed.
 // Both keep two workgroups per CU within the register and LDS budgets.  With d = 64 and
 // fewer than two slices per CU, 2 * CUs - slices slices are shared by two workgroups so
 // that every CU gets about one and a half slices' worth of loads, stores and products.
@@ -307,7 +314,7 @@ static bool fused_choose(const Geometry& g, int num_cus, FusedPlan* plan) {
   } else if (g.m_pad == 64 && npairs <= 32) {
     p.waves = 4;
     p.pairs_per_wave = (npairs + 3) / 4;
-    p.keep_a = p.pairs_per_wave <= (g.d == 128 ? 3 : 5);   // d = 128: registers
+    p.keep_a = p.pairs_per_wave <= 5;
   } else {
     return false;
   }
@@ -348,9 +355,7 @@ static hipError_t dispatch(const Geometry& g, const FusedPlan& p, const void* Q,
   }
   if (r <= 2) return go<D, 2, 4, 2, true, 2>(g, p, Q, U, V, H, s);
   if (r <= 3) return go<D, 2, 4, 3, true, 2>(g, p, Q, U, V, H, s);
-  if constexpr (D != 128) {
-    if (r <= 5) return go<D, 2, 4, 5, true, 2>(g, p, Q, U, V, H, s);
-  }
+  if (r <= 5) return go<D, 2, 4, 5, true, 2>(g, p, Q, U, V, H, s);
   if (r <= 8) return go<D, 2, 4, 8, false, 2>(g, p, Q, U, V, H, s);
   return hipErrorInvalidValue;
 }
