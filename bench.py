@@ -38,8 +38,8 @@ MEASURED_TRAFFIC = {
                                            "efficient_vision_transformer_amd/csrc/tile_ops.h",
                                            "efficient_vision_transformer_amd/csrc/device_common.h",
                                            "efficient_vision_transformer_amd/csrc/kernels.h"],
-                               "sha": "c059c519fcfc58a0", "read_bytes": 19474579,
-                               "write_bytes": 10941091},
+                               "sha": "760f57594cd20770", "read_bytes": 19474638,
+                               "write_bytes": 11027404},
 }
 # the split plan's three kernels per step (pass 1, finalize, pass 2)
 _SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",

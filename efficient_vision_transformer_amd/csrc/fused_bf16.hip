@@ -295,7 +295,8 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 }
 
 // Plans (n <= 1024, m <= 64; d = 128 and m <= 32: n <= 256):
-//   m <= 32: eight waves, A kept for up to two rounds (n <= 512), else recomputed;
+//   m <= 32: eight waves, A kept for up to two rounds (n <= 512), else recomputed; at
+//            d = 128 four waves of up to two rounds, A kept;
 //   m <= 64: four waves, A kept for up to five rounds (n <= 640), else recomputed.
 // Both keep two workgroups per CU within the register and LDS budgets.  With d = 64 and
 // fewer than two slices per CU, 2 * CUs - slices slices are shared by two workgroups so
@@ -305,9 +306,13 @@ static bool fused_choose(const Geometry& g, int num_cus, FusedPlan* plan) {
   if (g.d != 32 && g.d != 64 && g.d != 128) return false;
   const int npairs = (g.n + 31) / 32;
   FusedPlan p{};
-  // d = 128 with up to 32 anchors: one round only (more rounds do not fit eight waves'
-  // registers at two workgroups per CU); longer slices take the split plan
-  if (g.m_pad == 32 && npairs <= (g.d == 128 ? 8 : 32)) {
+  // d = 128 with up to 32 anchors: n <= 256 (longer slices take the split plan)
+  if (g.m_pad == 32 && g.d == 128 && npairs <= 8) {
+    // four waves of up to two pairs: 45 KB of LDS, three workgroups per CU
+    p.waves = 4;
+    p.pairs_per_wave = (npairs + 3) / 4;
+    p.keep_a = true;
+  } else if (g.m_pad == 32 && npairs <= 32 && g.d != 128) {
     p.waves = 8;
     p.pairs_per_wave = (npairs + 7) / 8;
     p.keep_a = p.pairs_per_wave <= 2;
@@ -346,6 +351,10 @@ static hipError_t dispatch(const Geometry& g, const FusedPlan& p, const void* Q,
                            const void* V, void* H, hipStream_t s) {
   const int r = p.pairs_per_wave;
   if (g.m_pad == 32) {
+    if constexpr (D == 128) {
+      if (r <= 2) return go<D, 1, 4, 2, true, 3>(g, p, Q, U, V, H, s);
+      return hipErrorInvalidValue;
+    }
     if (r == 1) return go<D, 1, 8, 1, true, 4>(g, p, Q, U, V, H, s);
     if constexpr (D != 128) {
       if (r == 2) return go<D, 1, 8, 2, true, 2>(g, p, Q, U, V, H, s);
