@@ -54,8 +54,7 @@ def test_d128_against_oracle(ctxs, dev, shape, plan):
 
 # (B, h, n, m, d) the fused plan takes at d = 128: four waves of one or two rounds
 # (m <= 32, n <= 256), four waves with A kept (two, three and five rounds) or recomputed
-# (eight),
-# one token, a ragged last pair, and the ViT-S/16 and ViT-B/16-384 shapes at d = 128
+# (eight), one token, a ragged last pair, and the ViT-S/16 and ViT-B/16-384 shapes
 FUSED_SHAPES = [(3, 2, 196, 30, 128), (2, 2, 256, 32, 128), (4, 2, 77, 9, 128),
                 (2, 3, 250, 50, 128), (1, 4, 333, 64, 128), (2, 2, 577, 33, 128),
                 (1, 2, 1024, 64, 128), (1, 1, 1, 1, 128), (64, 6, 196, 30, 128),
