@@ -12,7 +12,9 @@ workload's B, n, h, m, d; with --pass linear, the ReLU kernel linear attention (
 page) on the workload's Q, K, V.  Inputs are resident in HBM:
 R copies of the batch (R * bytes >= 1 GiB, well beyond the 256 MB Infinity Cache) are
 cycled so every step reads cold HBM.  K steps are bracketed by events on the launch
-stream.  Prints one JSON line.
+stream.  Prints one JSON line; for the forward it carries `parity`, the output of the last
+timed launch against the fp64 oracle on sampled slices, and the run exits with status 1
+when that error is past the gate.
 """
 from __future__ import annotations
 
@@ -67,6 +69,62 @@ def measured_traffic(workload: str, plan: str):
     return rec["read_bytes"] + rec["write_bytes"]
 
 
+# Device-side delay queued just before the start event (GPU clock ticks of torch's spin
+# kernel; tens of microseconds to a few milliseconds depending on the counter's rate).
+LEAD_IN_CYCLES = 1_000_000
+
+
+def timed_steps(step, warmup: int, steps: int, stream, sets: int = 0) -> float:
+    """Average milliseconds per step on `stream`.
+
+    step(i) enqueues step i (callers rotate over `sets` buffer sets with i).  First every
+    set is touched once by an untimed step (so no timed step meets pages the device has
+    not mapped since their allocation); then warm-up steps 0 .. warmup - 1 run untimed and
+    the timed steps are warmup .. warmup + steps - 1, so with enough sets none of them
+    reuses a set still in the caches.  Both ends are bracketed by a device
+    synchronisation.  A spin kernel is queued right before the start event: while it runs,
+    the host enqueues the first timed launches, so the window holds the K launches back to
+    back rather than the host's latency to its first launch on an idle GPU."""
+    import torch
+    torch.cuda.synchronize()
+    for i in range(sets):
+        step(i)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(LEAD_IN_CYCLES)
+    e0.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def host_info() -> dict:
+    """Threads this process may use, nproc, the host's CPU count and its CPU model."""
+    import subprocess
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = int(subprocess.run(["nproc"], capture_output=True, text=True, check=True).stdout)
+    except (OSError, ValueError, subprocess.CalledProcessError):
+        nproc = None
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "nproc": nproc,
+            "cpu_count": os.cpu_count(), "cpu_model": model}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,8 +162,11 @@ def calibrate_copy(mib: int, reps: int = 5) -> None:
 
 
 def cpu_baseline(x, seconds: float) -> dict:
-    """The fp64 oracle as it stands, on this host's cores, over whole batches of the
-    same workload, repeated until `seconds` of wall clock have elapsed."""
+    """The fp64 oracle as it stands, on this host's cores: whole batches of the same
+    workload repeated until `seconds` of wall clock have elapsed, on the threads one GPU's
+    share of the host allows (all cores this process may use, at most 16); then once on a
+    single thread, over the whole batch when it has at most 2^30 multiply-adds per logits
+    product, else over its first four slices, extrapolated to the batch."""
     import numpy as np
     import oracle
     cores = oracle.default_threads()
@@ -118,9 +179,27 @@ def cpu_baseline(x, seconds: float) -> dict:
         if el >= seconds:
             break
     w = x.workload
-    return {"value": reps * w.B * w.n / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{reps} full batch(es) of {w.name} (B={w.B} h={w.h} n={w.n} m={w.m} d={w.d}) "
-                      f"in fp64, {el:.1f} s wall"}
+    whole = w.B * w.h * w.n * w.m * w.d <= (1 << 30)
+    if whole:
+        q1, v1, scale, what = Q, V, 1.0, "the whole batch"
+    else:
+        q1 = Q.reshape(w.B * w.h, w.n, w.d)[:4].reshape(1, 4, w.n, w.d)
+        v1 = V.reshape(w.B * w.h, w.n, w.d)[:4].reshape(1, 4, w.n, w.d)
+        u1 = np.stack([U[j % w.h] for j in range(4)])
+        scale, what = w.B * w.h / 4.0, f"4 of {w.B * w.h} slices, extrapolated"
+    t1 = time.perf_counter()
+    if whole:
+        oracle.anchor_attn(q1, U, v1, nthreads=1)
+    else:
+        oracle.anchor_attn(q1, u1, v1, nthreads=1)
+    el1 = (time.perf_counter() - t1) * scale
+    out = {"value": reps * w.B * w.n / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"{reps} full batch(es) of {w.name} (B={w.B} h={w.h} n={w.n} m={w.m} d={w.d}) "
+                     f"in fp64 on {cores} threads, {el:.1f} s wall",
+           "value_1thread": w.B * w.n / el1,
+           "sample_1thread": f"{what} on one thread, {el1:.2f} s per batch"}
+    out.update(host_info())
+    return out
 
 
 def cpu_baseline_backward(x, G, seconds: float) -> dict:
@@ -165,21 +244,12 @@ def bench_backward(args, ctx, x, dev, plan_desc) -> dict:
     R = max(1, -(-ROTATE_BYTES // algo_bytes))
     mk = lambda q, v, g: (q, v, g, (torch.empty_like(q), torch.empty_like(U), torch.empty_like(v)))
     sets = [mk(Q0, V0, G0)] + [mk(Q0.clone(), V0.clone(), G0.clone()) for _ in range(R - 1)]
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    for i in range(args.warmup):
+
+    def step(i):
         q, v, g, o = sets[i % R]
         ctx.backward(q, U, v, g, out=o, stream=stream)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        q, v, g, o = sets[i % R]
-        ctx.backward(q, U, v, g, out=o, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = timed_steps(step, args.warmup, args.steps, stream, R)
     gbs = algo_bytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -252,17 +322,7 @@ def bench_block(args, ctx, w, dev) -> dict:
     stream = torch.cuda.current_stream(dev)
     step = lambda i: ctx.block_forward(sets[i % R][0], t["Wqv"], t["bqv"], t["U"], t["Wo"],
                                        t["bo"], out=sets[i % R][1], stream=stream)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = timed_steps(step, args.warmup, args.steps, stream, R)
     gbs = algo_bytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     hbm_bound = algo_bytes / (HBM_PEAK_GBS * 1e9) >= flops / (BF16_PEAK_TFLOPS * 1e12)
@@ -306,17 +366,7 @@ def bench_linear(args, ctx, x, dev) -> dict:
         (Q0.clone(), K0.clone(), V0.clone(), torch.empty_like(Q0)) for _ in range(R - 1)]
     stream = torch.cuda.current_stream(dev)
     step = lambda i: ctx.relu_linear(*sets[i % R][:3], 100.0, 1.0, out=sets[i % R][3], stream=stream)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = timed_steps(step, args.warmup, args.steps, stream, R)
     gbs = algo_bytes / (ms * 1e-3) / 1e9
     out = {
         "metric": f"ReLU linear attention tokens/sec ({w.name} shape)",
@@ -382,17 +432,7 @@ def bench_nystrom(args, ctx, x, dev) -> dict:
         (Q0.clone(), K0.clone(), V0.clone(), torch.empty_like(Q0)) for _ in range(R - 1)]
     stream = torch.cuda.current_stream(dev)
     step = lambda i: ctx.nystrom(*sets[i % R][:3], idx, out=sets[i % R][3], stream=stream)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = timed_steps(step, args.warmup, args.steps, stream, R)
     gbs = algo_bytes / (ms * 1e-3) / 1e9
     out = {
         "metric": f"Nystrom attention tokens/sec ({w.name} shape, s={s} landmarks)",
@@ -429,6 +469,32 @@ def bench_nystrom(args, ctx, x, dev) -> dict:
     return out
 
 
+def timed_output_parity(x, H) -> dict:
+    """The output of the last timed launch against the fp64 oracle on a sample of whole
+    slices (first, last and seeded others): normwise max-relative error for fp32 (gate
+    1e-5), relative Frobenius error for bf16 (gate 1e-2), over the sample."""
+    import numpy as np
+    import oracle
+    w = x.workload
+    k = 4 if w.n > 8192 else 8
+    all_s = [(b, j) for b in range(w.B) for j in range(w.h)]
+    rng = np.random.default_rng(0)
+    pick = sorted({all_s[0], all_s[-1]} | {all_s[int(i)] for i in rng.integers(0, len(all_s), 3 * k)})[:k]
+    q = np.stack([x.Q[b, j] for b, j in pick])[None]
+    v = np.stack([x.V[b, j] for b, j in pick])[None]
+    u = np.stack([x.U[j] for _, j in pick])
+    ref = oracle.anchor_attn(q, u, v)[0]
+    got = np.stack([H[b, j] for b, j in pick])
+    if w.dtype == "fp32":
+        metric, gate = "normwise_max_relative", 1e-5
+        err = float(np.abs(got - ref).max() / np.abs(ref).max())
+    else:
+        metric, gate = "relative_frobenius", 1e-2
+        err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    return {"metric": metric, "error": err, "gate": gate, "ok": bool(err <= gate),
+            "slices": [list(p) for p in pick], "output": "last timed launch"}
+
+
 def full_attention_gap(x, H, slices=4) -> dict:
     """Report-only: relative Frobenius gap between softmax(QK^T/sqrt(d))V and H on a few
     slices (inputs exactly as stored)."""
@@ -460,19 +526,11 @@ def copy_reference(algo_bytes: int, steps: int, warmup: int) -> dict:
     pairs = [(torch.ones(n, dtype=torch.int32, device=dev), torch.empty(n, dtype=torch.int32, device=dev))
              for _ in range(R)]
     stream = torch.cuda.current_stream(dev)
-    for i in range(warmup):
+
+    def step(i):
         s, d = pairs[i % R]
         d.copy_(s)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(steps):
-        s, d = pairs[i % R]
-        d.copy_(s)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / steps * 1e3
+    us = timed_steps(step, warmup, steps, stream, R) * 1e3
     return {"bytes_per_launch": 8 * n, "avg_duration_us": round(us, 3),
             "gbs": round(8 * n / (us * 1e-6) / 1e9, 1)}
 
@@ -499,18 +557,14 @@ def stream_reference(tensor_bytes: int, steps: int, warmup: int) -> dict:
     sp = ctypes.c_void_p(stream.cuda_stream)
     call = lambda i: fn(sets[i % R][0].data_ptr(), sets[i % R][1].data_ptr(),
                         sets[i % R][2].data_ptr(), nb, sp)
-    for i in range(warmup):
+    bad = []
+
+    def step(i):
         if call(i) != 0:
-            raise RuntimeError("stream reference launch failed")
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(steps):
-        call(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / steps * 1e3
+            bad.append(i)
+    us = timed_steps(step, warmup, steps, stream, R) * 1e3
+    if bad:
+        raise RuntimeError(f"stream reference launch failed at step {bad[0]}")
     return {"bytes_per_launch": 3 * nb, "avg_duration_us": round(us, 3),
             "gbs": round(3 * nb / (us * 1e-6) / 1e9, 1),
             "kernel": "two buffers read, one written, one 16-byte chunk per thread"}
@@ -579,22 +633,27 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    for i in range(args.warmup):
-        q, v, h = sets[i % R]
-        ctx.forward(q, U, v, out=h, stream=stream)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        q, v, h = sets[i % R]
-        ctx.forward(q, U, v, out=h, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    # Each step is one anchor_attn_forward call through the C ABI with its arguments
+    # marshalled once up front (the binding's per-call Python checks stay out of the loop).
+    import ctypes
+    from efficient_vision_transformer_amd import anchor_attn
+    lib = anchor_attn.load_library()
+    sv = ctypes.c_void_p(stream.cuda_stream)
+    dcode = anchor_attn.BF16 if w.dtype == "bf16" else anchor_attn.FP32
+    calls = [(ctx._h, q.data_ptr(), U.data_ptr(), v.data_ptr(), hh.data_ptr(), w.B, w.h, w.n,
+              w.m, w.d, dcode, sv) for q, v, hh in sets]
+    bad = []
 
-    # correctness spot check of the first set against the recorded output (not timed)
-    H = sets[0][2].float().cpu().numpy().astype(np.float64)
+    def step(i):
+        rc = lib.anchor_attn_forward(*calls[i % R])
+        if rc != 0:
+            bad.append(rc)
+    ms = timed_steps(step, args.warmup, args.steps, stream, R)
+    if bad:
+        raise RuntimeError(f"anchor_attn_forward: {anchor_attn.status_string(bad[0])}")
+    # the output of the last timed launch, checked against the oracle below (not timed)
+    last = (args.warmup + args.steps - 1) % R
+    H = sets[last][2].float().cpu().numpy().astype(np.float64)
 
     tokens = w.B * w.n
     value = tokens / (ms * 1e-3)
@@ -654,8 +713,11 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds)
     out["diagnostic"] = full_attention_gap(x, H)
+    out["parity"] = timed_output_parity(x, H)
     ctx.close()
     print(json.dumps(out), flush=True)
+    if not out["parity"]["ok"]:
+        sys.exit(1)
 
 
 if __name__ == "__main__":

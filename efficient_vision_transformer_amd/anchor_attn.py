@@ -324,13 +324,32 @@ class AnchorAttention:
             pass
 
 
-_default: dict = {}
+_shared: dict = {}
+_shared_lock = threading.Lock()
+
+
+def shared_context(device, stream=None) -> AnchorAttention:
+    """The module's context for (device, stream): one per stream, because calls on one
+    context that run concurrently on different streams would share its workspace.  The
+    stream defaults to torch's current stream on `device`.  A context serves one host thread
+    at a time; the lock covers the lookup, callers on several threads and one stream must
+    serialise their calls themselves."""
+    import torch
+    dev = torch.device(device)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    key = (dev.index if dev.index is not None else torch.cuda.current_device(), stream.cuda_stream)
+    with _shared_lock:
+        ctx = _shared.get(key)
+        if ctx is None:
+            ctx = _shared[key] = AnchorAttention(dev)
+        return ctx
 
 
 def forward(Q, U, V, out=None, stream=None):
-    """H = A (Delta^-1 (A^T V)) with A = rowsoftmax(Q U^T / sqrt(d)), on Q's device."""
-    key = Q.device.index
-    ctx = _default.get(key)
-    if ctx is None:
-        ctx = _default[key] = AnchorAttention(Q.device)
-    return ctx.forward(Q, U, V, out=out, stream=stream)
+    """H = A (Delta^-1 (A^T V)) with A = rowsoftmax(Q U^T / sqrt(d)), on Q's device and
+    `stream` (default: torch's current stream), with that stream's shared context."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(Q.device)
+    return shared_context(Q.device, stream).forward(Q, U, V, out=out, stream=stream)

@@ -9,17 +9,14 @@ from __future__ import annotations
 
 import torch
 
-from .anchor_attn import AnchorAttention
-
-_ctx_by_device: dict = {}
+from .anchor_attn import AnchorAttention, shared_context
 
 
 def _context(device) -> AnchorAttention:
-    key = device.index
-    ctx = _ctx_by_device.get(key)
-    if ctx is None:
-        ctx = _ctx_by_device[key] = AnchorAttention(device)
-    return ctx
+    # one context per (device, current stream): the backward may run on another stream
+    # than the forward (autograd's own streams), and contexts must not share workspaces
+    # across streams
+    return shared_context(device, torch.cuda.current_stream(device))
 
 
 class AnchorAttentionFunction(torch.autograd.Function):

@@ -10,8 +10,11 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <vector>
 
 #include "kernels.h"
 
@@ -24,6 +27,12 @@ struct anchor_attn_ctx {
   aa::GemmCache* gemm = nullptr;    // block projections (created on first use)
   void* block_ws = nullptr;         // block: projected Q|V, H and the GEMM workspace
   size_t block_ws_bytes = 0;
+  // Workspaces replaced by larger ones.  They stay allocated until anchor_attn_destroy:
+  // a HIP graph captured before the growth still holds their addresses.
+  std::vector<void*> retired;
+  // Test hook (environment variable ANCHOR_ATTN_FAIL_ALLOC_ABOVE, read at create): device
+  // allocations of more than this many bytes fail as if the device were out of memory.
+  size_t fail_alloc_above = SIZE_MAX;
 };
 
 namespace {
@@ -194,22 +203,39 @@ const char* chosen_name(Chosen c) {
   return c == Chosen::Fused ? "fused" : (c == Chosen::Split ? "split" : "unsupported");
 }
 
-anchor_attn_status_t ensure_workspace(anchor_attn_ctx* ctx, size_t bytes) {
-  if (bytes <= ctx->workspace_bytes) return ANCHOR_ATTN_SUCCESS;
-  if (ctx->workspace) {
-    if (hipFree(ctx->workspace) != hipSuccess) return ANCHOR_ATTN_ERROR_HIP;
-    ctx->workspace = nullptr;
-    ctx->workspace_bytes = 0;
-  }
+// Allocates `bytes` of device memory for the context (honouring the test hook).
+anchor_attn_status_t device_alloc(anchor_attn_ctx* ctx, size_t bytes, void** out) {
+  *out = nullptr;
+  if (bytes > ctx->fail_alloc_above) return ANCHOR_ATTN_ERROR_OUT_OF_MEMORY;
   void* p = nullptr;
-  const hipError_t e = hipMalloc(&p, bytes);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();  // clear the sticky-free error state of this thread
+  if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();  // clear this thread's error state
     return ANCHOR_ATTN_ERROR_OUT_OF_MEMORY;
   }
-  ctx->workspace = p;
-  ctx->workspace_bytes = bytes;
+  *out = p;
   return ANCHOR_ATTN_SUCCESS;
+}
+
+// Grows a grow-only buffer to at least `bytes`.  The old buffer is retired, not freed (a
+// captured graph may still use it); on failure the buffer is left as it was.
+anchor_attn_status_t grow(anchor_attn_ctx* ctx, void** buf, size_t* have, size_t bytes) {
+  if (bytes <= *have) return ANCHOR_ATTN_SUCCESS;
+  try {
+    ctx->retired.reserve(ctx->retired.size() + 1);
+  } catch (...) {
+    return ANCHOR_ATTN_ERROR_OUT_OF_MEMORY;
+  }
+  void* p = nullptr;
+  const anchor_attn_status_t st = device_alloc(ctx, bytes, &p);
+  if (st != ANCHOR_ATTN_SUCCESS) return st;
+  if (*buf) ctx->retired.push_back(*buf);
+  *buf = p;
+  *have = bytes;
+  return ANCHOR_ATTN_SUCCESS;
+}
+
+anchor_attn_status_t ensure_workspace(anchor_attn_ctx* ctx, size_t bytes) {
+  return grow(ctx, &ctx->workspace, &ctx->workspace_bytes, bytes);
 }
 
 // Everything a forward of geometry g needs before it can be enqueued without failing: a
@@ -281,6 +307,11 @@ anchor_attn_status_t anchor_attn_create(anchor_attn_ctx** out) {
     if (!ctx) return ANCHOR_ATTN_ERROR_OUT_OF_MEMORY;
     ctx->device = dev;
     ctx->num_cus = cus > 0 ? cus : 256;
+    if (const char* lim = std::getenv("ANCHOR_ATTN_FAIL_ALLOC_ABOVE")) {
+      char* end = nullptr;
+      const unsigned long long v = std::strtoull(lim, &end, 10);
+      if (end && end != lim && *end == '\0') ctx->fail_alloc_above = (size_t)v;
+    }
     *out = ctx;
     return ANCHOR_ATTN_SUCCESS;
   } catch (...) {
@@ -291,10 +322,12 @@ anchor_attn_status_t anchor_attn_create(anchor_attn_ctx** out) {
 anchor_attn_status_t anchor_attn_destroy(anchor_attn_ctx* ctx) {
   if (!ctx) return ANCHOR_ATTN_SUCCESS;
   anchor_attn_status_t st = ANCHOR_ATTN_SUCCESS;
-  if (ctx->workspace || ctx->block_ws || ctx->gemm) {
+  if (ctx->workspace || ctx->block_ws || ctx->gemm || !ctx->retired.empty()) {
     DeviceGuard guard(ctx->device);
     if (ctx->workspace && hipFree(ctx->workspace) != hipSuccess) st = ANCHOR_ATTN_ERROR_HIP;
     if (ctx->block_ws && hipFree(ctx->block_ws) != hipSuccess) st = ANCHOR_ATTN_ERROR_HIP;
+    for (void* p : ctx->retired)
+      if (hipFree(p) != hipSuccess) st = ANCHOR_ATTN_ERROR_HIP;
     aa::gemm_cache_destroy(ctx->gemm);
   }
   delete ctx;
@@ -438,19 +471,8 @@ anchor_attn_status_t anchor_attn_block_forward(anchor_attn_ctx* ctx, const void*
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t qvb = al((size_t)T * 2 * C * es), hb = al((size_t)T * C * es);
     const size_t need = qvb + hb + aa::kGemmWorkspaceBytes;
-    if (need > ctx->block_ws_bytes) {
-      if (ctx->block_ws) {
-        if (hipFree(ctx->block_ws) != hipSuccess) return ANCHOR_ATTN_ERROR_HIP;
-        ctx->block_ws = nullptr;
-        ctx->block_ws_bytes = 0;
-      }
-      if (hipMalloc(&ctx->block_ws, need) != hipSuccess) {
-        (void)hipGetLastError();
-        ctx->block_ws = nullptr;
-        return ANCHOR_ATTN_ERROR_OUT_OF_MEMORY;
-      }
-      ctx->block_ws_bytes = need;
-    }
+    st = grow(ctx, &ctx->block_ws, &ctx->block_ws_bytes, need);
+    if (st != ANCHOR_ATTN_SUCCESS) return st;
     char* w = (char*)ctx->block_ws;
     void* QV = w;
     void* Hb = w + qvb;

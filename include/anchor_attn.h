@@ -23,12 +23,16 @@
  * owned by the caller, 16-byte aligned; H must not overlap Q, U or V.  The context owns
  * a grow-only device workspace used by long sequences: the first call that needs a
  * larger workspace allocates it (hipMalloc, which may synchronize); later calls of the
- * same or smaller size allocate nothing.  A context must not be used by two host
- * threads at once, and calls on one context that may run concurrently on different
- * streams share that workspace and race: give each stream its own context (contexts are
- * cheap; each owns only its workspaces).  Once an eager call of a shape has sized the
- * workspaces, calls of that shape allocate nothing, record no memset and can be captured
- * into a HIP graph.
+ * same or smaller size allocate nothing.  A workspace outgrown by a later call is kept
+ * (not freed) until anchor_attn_destroy, so a graph captured before the growth still
+ * replays on valid memory.  A context must not be used by two host threads at once, and
+ * calls on one context that may run concurrently on different streams share that
+ * workspace and race: give each stream its own context (contexts are cheap; each owns
+ * only its workspaces).  Once an eager call of a shape has sized the workspaces, calls of
+ * that shape allocate nothing, record no memset and can be captured into a HIP graph.
+ * Test hook: when the environment variable ANCHOR_ATTN_FAIL_ALLOC_ABOVE holds a decimal
+ * byte count at anchor_attn_create, that context's device allocations above it fail with
+ * ANCHOR_ATTN_ERROR_OUT_OF_MEMORY (as a full device would).
  *
  * Errors: every function returns a status; nothing is thrown, printed or aborted across
  * this boundary.  All arguments are validated before any work is enqueued, so on an

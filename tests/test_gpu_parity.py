@@ -68,28 +68,21 @@ def test_vit_workloads_full(ctxs, dev, name):
     assert max(per) <= 1e-2
 
 
-def _sampled_slices(w, k, seed=0):
-    rng = np.random.default_rng(seed)
-    all_s = [(b, j) for b in range(w.B) for j in range(w.h)]
-    pick = {all_s[0], all_s[-1]}
-    while len(pick) < min(k, len(all_s)):
-        pick.add(all_s[int(rng.integers(len(all_s)))])
-    return sorted(pick)
-
-
 @pytest.mark.parametrize("name", ["dense_64x64", "long_16k_bf16", "long_16k_fp32"])
-def test_large_workloads_sampled(ctxs, dev, name):
+def test_large_workloads_every_slice(ctxs, dev, name):
     """Full-size large workloads in the benchmarked launch configuration; the oracle
-    recomputes a sample of whole slices (first, last, random)."""
+    computes every slice (fp64, all host threads), and every slice meets the gate."""
     x = make_inputs(name, with_k=False)
     w = x.workload
     got = _run(ctxs["auto"], x, dev)
     assert np.all(np.isfinite(got))
-    for b, j in _sampled_slices(w, 4 if w.n > 8192 else 6):
-        _, _, _, ref = oracle.anchor_slice(x.Q[b, j], x.U[j], x.V[b, j])
-        e = err_for(w.dtype, got[b, j], ref)
-        print(f"  {name} slice ({b},{j}): {e:.3e}")
-        assert e <= tol_for(w.dtype)
+    ref = oracle.anchor_attn(x.Q, x.U, x.V)
+    e = err_for(w.dtype, got, ref)
+    print(f"  {name}: whole tensor {e:.3e}", flush=True)
+    assert e <= tol_for(w.dtype)
+    per = [err_for(w.dtype, got[b, j], ref[b, j]) for b in range(w.B) for j in range(w.h)]
+    print(f"  {name}: worst slice {max(per):.3e}", flush=True)
+    assert max(per) <= tol_for(w.dtype)
 
 
 # --- edge shapes and both plans -------------------------------------------------------------
@@ -179,7 +172,7 @@ def test_fused_shared_slices(ctxs, dev, bh, m):
     # every slice on its own: a mis-paired half would leave one slice far off
     for b in range(B):
         for hh in range(h):
-            assert err_for("bf16", got[b, hh], ref[b, hh]) <= 2e-2, (b, hh)
+            assert err_for("bf16", got[b, hh], ref[b, hh]) <= 1e-2, (b, hh)
 
 
 def test_fused_plan_rejects_what_it_cannot_run(ctxs, dev):
