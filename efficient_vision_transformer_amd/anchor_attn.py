@@ -41,6 +41,8 @@ def load_library():
         lib.anchor_attn_create.argtypes = [ctypes.POINTER(vp)]
         lib.anchor_attn_destroy.argtypes = [vp]
         lib.anchor_attn_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+        lib.anchor_attn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                    i32, i32, vp]
         llp = ctypes.POINTER(ctypes.c_longlong)
         lib.anchor_attn_forward_strided.argtypes = [vp, vp, llp, vp, vp, llp, vp, llp,
                                                     i32, i32, i32, i32, i32, i32, vp]
@@ -62,6 +64,7 @@ def load_library():
         lib.anchor_attn_status_string.argtypes = [i32]
         lib.anchor_attn_status_string.restype = ctypes.c_char_p
         for f in (lib.anchor_attn_create, lib.anchor_attn_destroy, lib.anchor_attn_forward,
+                  lib.anchor_attn_forward_noalloc,
                   lib.anchor_attn_forward_strided, lib.anchor_attn_block_forward,
                   lib.anchor_attn_relu_linear_forward, lib.anchor_attn_backward_strided,
                   lib.anchor_attn_backward, lib.anchor_attn_nystrom_forward,
@@ -163,6 +166,30 @@ class AnchorAttention:
         return out
 
     __call__ = forward
+
+    def forward_noalloc(self, Q, U, V, out, stream=None):
+        """forward() through anchor_attn_forward_noalloc: the split plan's partials live in
+        the library's fixed 64 MiB scratch on this GPU instead of this context's workspace,
+        so the call allocates nothing (``out`` must be given).  Contiguous tensors only.
+        Calls that may overlap on one GPU share that scratch and race."""
+        if Q.dim() != 4 or V.shape != Q.shape or U.dim() != 3 or out.shape != Q.shape:
+            raise ValueError(f"bad shapes Q{tuple(Q.shape)} U{tuple(U.shape)} V{tuple(V.shape)}")
+        B, h, n, d = Q.shape
+        if U.shape[0] != h or U.shape[2] != d:
+            raise ValueError(f"U must be [h={h}, m, d={d}], got {tuple(U.shape)}")
+        for name, t in (("Q", Q), ("U", U), ("V", V), ("out", out)):
+            if not t.is_cuda or t.device != self.device or t.dtype != Q.dtype:
+                raise ValueError(f"{name} must be a {Q.dtype} tensor on {self.device}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+        if stream is None:
+            import torch
+            stream = torch.cuda.current_stream(self.device)
+        _check(self._lib.anchor_attn_forward_noalloc(
+            self._h, Q.data_ptr(), U.data_ptr(), V.data_ptr(), out.data_ptr(), B, h, n,
+            U.shape[1], d, _dtype_code(Q), ctypes.c_void_p(stream.cuda_stream)),
+            "anchor_attn_forward_noalloc")
+        return out
 
     def relu_linear(self, Q, K, V, cmin: float = 100.0, qscale: float = 1.0, out=None,
                     stream=None):

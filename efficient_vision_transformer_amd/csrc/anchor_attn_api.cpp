@@ -249,10 +249,12 @@ anchor_attn_status_t prepare_forward(anchor_attn_ctx* ctx, const Geometry& g,
   return ANCHOR_ATTN_SUCCESS;
 }
 
-// Enqueues the forward (after prepare_forward succeeded for g).
-anchor_attn_status_t run_forward(anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t dtype,
-                                 const void* Q, const void* U, const void* V, void* H,
-                                 hipStream_t s) {
+// Enqueues the forward with the split plan's partials in `ws` (at least `ws_bytes`; unused
+// by the fused plan).
+anchor_attn_status_t run_forward_ws(anchor_attn_ctx* ctx, const Geometry& g,
+                                    anchor_attn_dtype_t dtype, const void* Q, const void* U,
+                                    const void* V, void* H, void* ws, size_t ws_bytes,
+                                    hipStream_t s) {
   FusedPlan fp{};
   const Chosen c = choose(ctx, g, dtype, &fp);
   hipError_t e;
@@ -260,9 +262,9 @@ anchor_attn_status_t run_forward(anchor_attn_ctx* ctx, const Geometry& g, anchor
     e = aa::launch_fused_bf16(g, fp, Q, U, V, H, s);
   } else if (c == Chosen::Split) {
     const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
-    if (ctx->workspace_bytes < p.workspace_bytes()) return ANCHOR_ATTN_ERROR_OUT_OF_MEMORY;
-    e = (dtype == ANCHOR_ATTN_BF16) ? aa::launch_split_bf16(g, p, Q, U, V, H, ctx->workspace, s)
-                                    : aa::launch_split_fp32(g, p, Q, U, V, H, ctx->workspace, s);
+    if (ws_bytes < p.workspace_bytes()) return ANCHOR_ATTN_ERROR_OUT_OF_MEMORY;
+    e = (dtype == ANCHOR_ATTN_BF16) ? aa::launch_split_bf16(g, p, Q, U, V, H, ws, s)
+                                    : aa::launch_split_fp32(g, p, Q, U, V, H, ws, s);
   } else {
     return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   }
@@ -273,6 +275,42 @@ anchor_attn_status_t run_forward(anchor_attn_ctx* ctx, const Geometry& g, anchor
   return ANCHOR_ATTN_SUCCESS;
 }
 
+// Enqueues the forward (after prepare_forward succeeded for g).
+anchor_attn_status_t run_forward(anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t dtype,
+                                 const void* Q, const void* U, const void* V, void* H,
+                                 hipStream_t s) {
+  return run_forward_ws(ctx, g, dtype, Q, U, V, H, ctx->workspace, ctx->workspace_bytes, s);
+}
+
+// ---- scratch of anchor_attn_forward_noalloc --------------------------------------------
+// The split plan's partials for callers that cannot allocate: a fixed array in device
+// memory, one copy per GPU the library runs on (held until the process ends).  In host
+// code `scratch` is only a handle for hipGetSymbolAddress; kernels receive the device
+// address that call returns for the current device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on device `dev`, looked up once per device with that
+// device current.
+anchor_attn_status_t scratch_on_device(int dev, void** out) {
+  *out = nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return ANCHOR_ATTN_ERROR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ANCHOR_ATTN_SUCCESS;
+}
 
 }  // namespace
 
@@ -415,6 +453,44 @@ anchor_attn_status_t anchor_attn_forward_strided(anchor_attn_ctx* ctx, const voi
     st = prepare_forward(ctx, g, dtype);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
     return run_forward(ctx, g, dtype, Q, U, V, H, (hipStream_t)stream);
+  } catch (...) {
+    return ANCHOR_ATTN_ERROR_HIP;
+  }
+}
+
+anchor_attn_status_t anchor_attn_forward_noalloc(anchor_attn_ctx* ctx, const void* Q,
+                                                 const void* U, const void* V, void* H, int B,
+                                                 int h, int n, int m, int d,
+                                                 anchor_attn_dtype_t dtype, void* stream) {
+  if (!ctx) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+  try {
+    Geometry g{};
+    bool empty = false;
+    anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype, &g, &empty);
+    if (st != ANCHOR_ATTN_SUCCESS) return st;
+    if (empty) return ANCHOR_ATTN_SUCCESS;
+    if (!Q || !U || !V || !H) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    if (((uintptr_t)Q | (uintptr_t)U | (uintptr_t)V | (uintptr_t)H) & 15u)
+      return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    const size_t es = (dtype == ANCHOR_ATTN_BF16) ? 2 : 4;
+    const size_t tb = (size_t)B * h * n * d * es, ub = (size_t)h * (size_t)m * (size_t)d * es;
+    if (overlaps(H, tb, Q, tb) || overlaps(H, tb, V, tb) || overlaps(H, tb, U, ub))
+      return ANCHOR_ATTN_ERROR_INVALID_VALUE;
+    FusedPlan fp{};
+    const Chosen c = choose(ctx, g, dtype, &fp);
+    if (c == Chosen::Unsupported) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+    // the split plan's partials must fit the fixed scratch
+    if (c == Chosen::Split && make_split_plan(g, dtype, ctx->num_cus).workspace_bytes() > kScratchBytes)
+      return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok) return ANCHOR_ATTN_ERROR_HIP;
+    void* ws = nullptr;
+    if (c == Chosen::Split) {
+      st = scratch_on_device(ctx->device, &ws);
+      if (st != ANCHOR_ATTN_SUCCESS) return st;
+    }
+    return run_forward_ws(ctx, g, dtype, Q, U, V, H, ws, ws ? kScratchBytes : 0,
+                          (hipStream_t)stream);
   } catch (...) {
     return ANCHOR_ATTN_ERROR_HIP;
   }

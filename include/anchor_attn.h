@@ -99,6 +99,23 @@ anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx,
                                          int B, int h, int n, int m, int d,
                                          anchor_attn_dtype_t dtype, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): anchor_attn_forward with the split
+ * plan's partials in a fixed scratch array of 64 MiB in device memory that the library
+ * holds on every GPU it runs on until the process ends, instead of the context's
+ * workspace.  It calls no allocating routine; the context only supplies its device, CU
+ * count and plan setting.  Arguments, layouts, domain and errors as anchor_attn_forward
+ * (contiguous tensors), plus: a shape whose split-plan partials exceed 64 MiB returns
+ * ANCHOR_ATTN_ERROR_NOT_SUPPORTED with nothing enqueued (32 slices of 16384 tokens with
+ * 256 anchors at d = 64 need ~35 MiB).  All calls on one GPU share its scratch, which
+ * keeps the last call's contents (every call writes each partial before reading it, so
+ * nothing needs clearing): calls that may overlap on one GPU (other streams, other
+ * threads, other contexts) race and must be serialised by the caller. */
+anchor_attn_status_t anchor_attn_forward_noalloc(anchor_attn_ctx* ctx,
+                                                 const void* Q, const void* U, const void* V,
+                                                 void* H, int B, int h, int n, int m, int d,
+                                                 anchor_attn_dtype_t dtype, void* stream);
+
 /* The same forward on strided views, so that Q and V can be read where a fused projection
  * left them (for example the two halves of a packed [B, n, 2, h, d] or [B, n, 3, h, d]
  * tensor) and H written straight into a [B, n, h, d] layout for the output projection

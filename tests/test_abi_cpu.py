@@ -59,6 +59,8 @@ def test_null_arguments(lib):
     assert lib.anchor_attn_destroy(None) == 0
     assert lib.anchor_attn_set_plan(None, 0) == 1
     assert lib.anchor_attn_forward(None, None, None, None, None, 1, 1, 1, 1, 32, 0, None) == 1
+    assert lib.anchor_attn_forward_noalloc(None, None, None, None, None, 1, 1, 1, 1, 32, 0,
+                                           None) == 1
     assert lib.anchor_attn_forward_strided(None, None, None, None, None, None, None, None,
                                            1, 1, 1, 1, 32, 0, None) == 1
     assert lib.anchor_attn_relu_linear_forward(None, None, None, None, None, None, None, None,

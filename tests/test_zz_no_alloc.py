@@ -1,0 +1,124 @@
+"""anchor_attn_forward_noalloc through the C ABI against anchor_attn_forward: the same
+results (bit for bit: the same kernels with the partials in the library's fixed scratch
+instead of the context's workspace), within the gates against the fp64 oracle, on two
+calls in a row with the second smaller, in the split plan (bf16 and fp32) and the fused
+plan; on a context whose every device allocation fails; and the refusal of partials
+beyond the scratch's 64 MiB."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from efficient_vision_transformer_amd.inputs import random_case
+
+from gpu_util import err_for, tol_for, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from efficient_vision_transformer_amd import anchor_attn
+    lib = anchor_attn.load_library()
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    lib.anchor_attn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                i32, vp]
+    lib.anchor_attn_forward_noalloc.restype = i32
+    return lib
+
+
+def _call(lib, fn, ctx, x, Q, U, V, H):
+    import torch
+    w = x.workload
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    code = 1 if w.dtype == "bf16" else 0
+    return getattr(lib, fn)(ctx._h, Q.data_ptr(), U.data_ptr(), V.data_ptr(), H.data_ptr(),
+                            w.B, w.h, w.n, w.m, w.d, code, stream)
+
+
+# (plan, first shape, second smaller shape) with shapes (B, h, n, m, d, dtype)
+SEQUENCES = [
+    ("split", (2, 4, 4096, 128, 64, "bf16"), (1, 2, 1000, 30, 64, "bf16")),
+    ("split", (2, 16, 16384, 256, 64, "bf16"), (1, 3, 5000, 200, 32, "bf16")),
+    ("split", (1, 4, 6000, 256, 64, "fp32"), (2, 2, 700, 64, 32, "fp32")),
+    ("auto", (32, 12, 576, 64, 64, "bf16"), (16, 12, 196, 30, 64, "bf16")),
+    ("auto", (1, 2, 3000, 100, 128, "bf16"), (1, 1, 250, 30, 128, "bf16")),
+]
+
+
+@pytest.mark.parametrize("plan,first,second", SEQUENCES,
+                         ids=["-".join(map(str, a + b)) for _, a, b in SEQUENCES])
+def test_noalloc_matches_forward(lib, plan, first, second):
+    import torch
+    from efficient_vision_transformer_amd import AnchorAttention
+    dev = torch.device("cuda:0")
+    ctx = AnchorAttention(dev, plan=plan)
+    for k, (B, h, n, m, d, dtype) in enumerate((first, second)):
+        x = random_case(400 + 7 * k + n + m, B, h, n, m, d, dtype=dtype, q_scale=1.5)
+        print(f"  call {k}: {ctx.describe(B, h, n, m, d, dtype)}", flush=True)
+        Q, U, V = to_device(x, dev)
+        H0 = torch.full_like(Q, float("nan"))
+        H1 = torch.full_like(Q, float("nan"))
+        assert _call(lib, "anchor_attn_forward_noalloc", ctx, x, Q, U, V, H1) == 0
+        assert _call(lib, "anchor_attn_forward", ctx, x, Q, U, V, H0) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(H1.view(torch.int16 if dtype == "bf16" else torch.int32),
+                           H0.view(torch.int16 if dtype == "bf16" else torch.int32)), k
+        got = to_host(H1)
+        if n > 8192:   # two whole slices
+            ref = oracle.anchor_attn(x.Q[:1, :2], x.U[:2], x.V[:1, :2])
+            got = got[:1, :2]
+        else:
+            ref = oracle.anchor_attn(x.Q, x.U, x.V)
+        e = err_for(dtype, got, ref)
+        print(f"  call {k}: error against the oracle {e:.3e}", flush=True)
+        assert e <= tol_for(dtype)
+    ctx.close()
+
+
+def test_noalloc_on_a_context_that_cannot_allocate(lib, monkeypatch):
+    """Every device allocation of this context fails (test hook), yet split-plan calls
+    through the no-allocation entry point run, while the ordinary forward reports
+    OUT_OF_MEMORY."""
+    import torch
+    from efficient_vision_transformer_amd import AnchorAttention
+    dev = torch.device("cuda:0")
+    monkeypatch.setenv("ANCHOR_ATTN_FAIL_ALLOC_ABOVE", "0")
+    ctx = AnchorAttention(dev, plan="split")
+    monkeypatch.delenv("ANCHOR_ATTN_FAIL_ALLOC_ABOVE")
+    for k, shape in enumerate(((1, 4, 3000, 64, 64), (1, 2, 500, 16, 32))):
+        x = random_case(500 + k, *shape, dtype="bf16")
+        Q, U, V = to_device(x, dev)
+        H = torch.full_like(Q, 7.0)
+        assert _call(lib, "anchor_attn_forward", ctx, x, Q, U, V, H) == 3   # OUT_OF_MEMORY
+        torch.cuda.synchronize()
+        assert torch.all(H == 7.0)
+        if k == 0:
+            assert _call(lib, "anchor_attn_forward_noalloc", ctx, x, Q, U, V, H) == 0
+        else:   # through the Python binding
+            ctx.forward_noalloc(Q, U, V, out=H)
+        torch.cuda.synchronize()
+        assert err_for("bf16", to_host(H), oracle.anchor_attn(x.Q, x.U, x.V)) <= 1e-2
+    ctx.close()
+
+
+def test_noalloc_refuses_partials_beyond_the_scratch(lib):
+    """512 anchors over 32 slices of 16384 tokens need more than 64 MiB of partials:
+    NOT_SUPPORTED, nothing enqueued (the output keeps its contents)."""
+    import torch
+    from efficient_vision_transformer_amd import AnchorAttention
+    dev = torch.device("cuda:0")
+    ctx = AnchorAttention(dev, plan="split")
+    desc = ctx.describe(2, 16, 16384, 512, 64, "bf16")
+    print(f"  {desc}", flush=True)
+    assert int(desc.split("workspace=")[1].split(";")[0]) > (64 << 20)
+    x = random_case(600, 2, 16, 16384, 512, 64, dtype="bf16")
+    Q, U, V = to_device(x, dev)
+    H = torch.full_like(Q, 7.0)
+    assert _call(lib, "anchor_attn_forward_noalloc", ctx, x, Q, U, V, H) == 2   # NOT_SUPPORTED
+    torch.cuda.synchronize()
+    assert torch.all(H == 7.0)
+    ctx.close()
