@@ -12,7 +12,8 @@ import os
 import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libanchor_attn.so")
+# ANCHOR_ATTN_LIBRARY names another build of the library (the host sanitizer test's)
+_LIB_PATH = os.environ.get("ANCHOR_ATTN_LIBRARY") or os.path.join(_HERE, "libanchor_attn.so")
 
 FP32, BF16 = 0, 1
 PLAN_AUTO, PLAN_FUSED, PLAN_SPLIT = 0, 1, 2

@@ -94,13 +94,25 @@ bool view_injective(const aa::View& w, int B, int h, int n, int d) {
   return true;
 }
 
+// The int a caller passed for an enum parameter, read without loading it as the enum type
+// (a C caller may pass any int; in C++ a value outside the enumerators' range must not be
+// loaded as the enum).
+template <typename E>
+int raw(const E* p) {
+  static_assert(sizeof(E) == sizeof(int), "int-sized enum");
+  int v;
+  std::memcpy(&v, p, sizeof v);
+  return v;
+}
+
 // Argument checks shared by forward and describe.  Returns SUCCESS and fills *g, or the
 // error.  *empty is set when there is no work (B*h*n == 0).
-anchor_attn_status_t check_shape(int B, int h, int n, int m, int d, anchor_attn_dtype_t dtype,
+anchor_attn_status_t check_shape(int B, int h, int n, int m, int d, int dtype_raw,
                                  Geometry* g, bool* empty) {
   if (B < 0 || h < 0 || n < 0 || m < 0 || d < 0) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
   if (m == 0 || d == 0) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
-  if (dtype != ANCHOR_ATTN_FP32 && dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  if (dtype_raw != ANCHOR_ATTN_FP32 && dtype_raw != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  const anchor_attn_dtype_t dtype = (anchor_attn_dtype_t)dtype_raw;
   if (d != 32 && d != 64 && d != 128) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   // d = 128: the bf16 forward only (the fused and split plans)
   if (d == 128 && dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
@@ -317,7 +329,7 @@ anchor_attn_status_t scratch_on_device(int dev, void** out) {
 extern "C" {
 
 const char* anchor_attn_status_string(anchor_attn_status_t s) {
-  switch (s) {
+  switch (raw(&s)) {
     case ANCHOR_ATTN_SUCCESS: return "ANCHOR_ATTN_SUCCESS";
     case ANCHOR_ATTN_ERROR_INVALID_VALUE: return "ANCHOR_ATTN_ERROR_INVALID_VALUE";
     case ANCHOR_ATTN_ERROR_NOT_SUPPORTED: return "ANCHOR_ATTN_ERROR_NOT_SUPPORTED";
@@ -374,8 +386,8 @@ anchor_attn_status_t anchor_attn_destroy(anchor_attn_ctx* ctx) {
 
 anchor_attn_status_t anchor_attn_set_plan(anchor_attn_ctx* ctx, anchor_attn_plan_t plan) {
   if (!ctx) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
-  if (plan != ANCHOR_ATTN_PLAN_AUTO && plan != ANCHOR_ATTN_PLAN_FUSED &&
-      plan != ANCHOR_ATTN_PLAN_SPLIT)
+  const int pr = raw(&plan);
+  if (pr != ANCHOR_ATTN_PLAN_AUTO && pr != ANCHOR_ATTN_PLAN_FUSED && pr != ANCHOR_ATTN_PLAN_SPLIT)
     return ANCHOR_ATTN_ERROR_INVALID_VALUE;
   ctx->plan = plan;
   return ANCHOR_ATTN_SUCCESS;
@@ -388,7 +400,7 @@ anchor_attn_status_t anchor_attn_describe_plan(anchor_attn_ctx* ctx, int B, int 
   try {
     Geometry g{};
     bool empty = false;
-    anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype, &g, &empty);
+    anchor_attn_status_t st = check_shape(B, h, n, m, d, raw(&dtype), &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
     if (empty) {
       std::snprintf(buf, (size_t)len, "empty: no work");
@@ -421,18 +433,19 @@ anchor_attn_status_t anchor_attn_describe_plan(anchor_attn_ctx* ctx, int B, int 
   }
 }
 
-anchor_attn_status_t anchor_attn_forward_strided(anchor_attn_ctx* ctx, const void* Q,
+static anchor_attn_status_t forward_strided_impl(anchor_attn_ctx* ctx, const void* Q,
                                                  const long long* q_strides, const void* U,
                                                  const void* V, const long long* v_strides,
                                                  void* H, const long long* h_strides, int B,
                                                  int h, int n, int m, int d,
-                                                 anchor_attn_dtype_t dtype, void* stream) {
+                                                 int dtype_raw, void* stream) {
   if (!ctx) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
   try {
     Geometry g{};
     bool empty = false;
-    anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype, &g, &empty);
+    anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype_raw, &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
+    const anchor_attn_dtype_t dtype = (anchor_attn_dtype_t)dtype_raw;
     const size_t es = (dtype == ANCHOR_ATTN_BF16) ? 2 : 4;
     if (!take_view(q_strides, es, &g.vw.q) || !take_view(v_strides, es, &g.vw.v) ||
         !take_view(h_strides, es, &g.vw.o))
@@ -458,6 +471,16 @@ anchor_attn_status_t anchor_attn_forward_strided(anchor_attn_ctx* ctx, const voi
   }
 }
 
+anchor_attn_status_t anchor_attn_forward_strided(anchor_attn_ctx* ctx, const void* Q,
+                                                 const long long* q_strides, const void* U,
+                                                 const void* V, const long long* v_strides,
+                                                 void* H, const long long* h_strides, int B,
+                                                 int h, int n, int m, int d,
+                                                 anchor_attn_dtype_t dtype, void* stream) {
+  return forward_strided_impl(ctx, Q, q_strides, U, V, v_strides, H, h_strides, B, h, n, m, d,
+                              raw(&dtype), stream);
+}
+
 anchor_attn_status_t anchor_attn_forward_noalloc(anchor_attn_ctx* ctx, const void* Q,
                                                  const void* U, const void* V, void* H, int B,
                                                  int h, int n, int m, int d,
@@ -466,7 +489,7 @@ anchor_attn_status_t anchor_attn_forward_noalloc(anchor_attn_ctx* ctx, const voi
   try {
     Geometry g{};
     bool empty = false;
-    anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype, &g, &empty);
+    anchor_attn_status_t st = check_shape(B, h, n, m, d, raw(&dtype), &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
     if (empty) return ANCHOR_ATTN_SUCCESS;
     if (!Q || !U || !V || !H) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
@@ -499,8 +522,8 @@ anchor_attn_status_t anchor_attn_forward_noalloc(anchor_attn_ctx* ctx, const voi
 anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx, const void* Q, const void* U,
                                          const void* V, void* H, int B, int h, int n, int m,
                                          int d, anchor_attn_dtype_t dtype, void* stream) {
-  return anchor_attn_forward_strided(ctx, Q, nullptr, U, V, nullptr, H, nullptr, B, h, n, m, d,
-                                     dtype, stream);
+  return forward_strided_impl(ctx, Q, nullptr, U, V, nullptr, H, nullptr, B, h, n, m, d,
+                              raw(&dtype), stream);
 }
 
 anchor_attn_status_t anchor_attn_block_forward(anchor_attn_ctx* ctx, const void* X, const void* Wqv,
@@ -512,7 +535,7 @@ anchor_attn_status_t anchor_attn_block_forward(anchor_attn_ctx* ctx, const void*
   try {
     Geometry g{};
     bool empty = false;
-    anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype, &g, &empty);
+    anchor_attn_status_t st = check_shape(B, h, n, m, d, raw(&dtype), &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
     if (dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
     const long long C = (long long)h * d, T = (long long)B * n;
@@ -579,7 +602,7 @@ anchor_attn_status_t anchor_attn_relu_linear_forward(
   try {
     Geometry g{};
     bool empty = false;
-    anchor_attn_status_t st = check_shape(B, h, n, 1, d, dtype, &g, &empty);
+    anchor_attn_status_t st = check_shape(B, h, n, 1, d, raw(&dtype), &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
     if (d > 64) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
     if (!(cmin > 0.f) || !std::isfinite(cmin) || !(qscale > 0.f) || !std::isfinite(qscale))
@@ -638,7 +661,7 @@ anchor_attn_status_t anchor_attn_nystrom_forward(anchor_attn_ctx* ctx, const voi
     if (s < 1 || s > n) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
     Geometry g{};
     bool empty = false;
-    anchor_attn_status_t st = check_shape(B, h, n, s, d, dtype, &g, &empty);
+    anchor_attn_status_t st = check_shape(B, h, n, s, d, raw(&dtype), &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
     if (dtype != ANCHOR_ATTN_BF16 || s > 128 || d > 64) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
     if (!Q || !K || !V || !idx || !H) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
@@ -675,17 +698,18 @@ anchor_attn_status_t anchor_attn_nystrom_forward(anchor_attn_ctx* ctx, const voi
   }
 }
 
-anchor_attn_status_t anchor_attn_backward_strided(
+static anchor_attn_status_t backward_strided_impl(
     anchor_attn_ctx* ctx, const void* Q, const long long* q_strides, const void* U, const void* V,
     const long long* v_strides, const void* dH, const long long* dh_strides, void* dQ,
     const long long* dq_strides, void* dU, void* dV, const long long* dv_strides, int B, int h,
-    int n, int m, int d, anchor_attn_dtype_t dtype, void* stream) {
+    int n, int m, int d, int dtype_raw, void* stream) {
   if (!ctx) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
   try {
     Geometry g{};
     bool empty = false;
-    anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype, &g, &empty);
+    anchor_attn_status_t st = check_shape(B, h, n, m, d, dtype_raw, &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
+    const anchor_attn_dtype_t dtype = (anchor_attn_dtype_t)dtype_raw;
     const Chosen plan = choose_backward(ctx, g, dtype);
     if (plan == Chosen::Unsupported) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
     const size_t es = 2;
@@ -765,12 +789,21 @@ anchor_attn_status_t anchor_attn_backward_strided(
   }
 }
 
+anchor_attn_status_t anchor_attn_backward_strided(
+    anchor_attn_ctx* ctx, const void* Q, const long long* q_strides, const void* U, const void* V,
+    const long long* v_strides, const void* dH, const long long* dh_strides, void* dQ,
+    const long long* dq_strides, void* dU, void* dV, const long long* dv_strides, int B, int h,
+    int n, int m, int d, anchor_attn_dtype_t dtype, void* stream) {
+  return backward_strided_impl(ctx, Q, q_strides, U, V, v_strides, dH, dh_strides, dQ,
+                               dq_strides, dU, dV, dv_strides, B, h, n, m, d, raw(&dtype), stream);
+}
+
 anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx, const void* Q, const void* U,
                                           const void* V, const void* dH, void* dQ, void* dU,
                                           void* dV, int B, int h, int n, int m, int d,
                                           anchor_attn_dtype_t dtype, void* stream) {
-  return anchor_attn_backward_strided(ctx, Q, nullptr, U, V, nullptr, dH, nullptr, dQ, nullptr,
-                                      dU, dV, nullptr, B, h, n, m, d, dtype, stream);
+  return backward_strided_impl(ctx, Q, nullptr, U, V, nullptr, dH, nullptr, dQ, nullptr, dU, dV,
+                               nullptr, B, h, n, m, d, raw(&dtype), stream);
 }
 
 }  // extern "C"

@@ -35,7 +35,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "anchor_oracle.c")
-_LIB = os.path.join(_HERE, "libanchor_oracle.so")
+_DEFAULT_LIB = os.path.join(_HERE, "libanchor_oracle.so")
+# ANCHOR_ORACLE_LIB names another build of anchor_oracle.c to load (the sanitizer test's)
+_LIB = os.environ.get("ANCHOR_ORACLE_LIB") or _DEFAULT_LIB
 _lib = None
 
 _DBL = ctypes.POINTER(ctypes.c_double)
@@ -45,13 +47,13 @@ _L = ctypes.c_long
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (fp64, no fused contraction, no fast-math)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
+    if force or not os.path.exists(_DEFAULT_LIB):
+        tmp = _DEFAULT_LIB + ".tmp"
         cmd = ["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
                "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, _DEFAULT_LIB)
+    return _DEFAULT_LIB
 
 
 def _load():
