@@ -40,8 +40,8 @@ MEASURED_TRAFFIC = {
                                            "efficient_vision_transformer_amd/csrc/tile_ops.h",
                                            "efficient_vision_transformer_amd/csrc/device_common.h",
                                            "efficient_vision_transformer_amd/csrc/kernels.h"],
-                               "sha": "760f57594cd20770", "read_bytes": 19474638,
-                               "write_bytes": 11027404},
+                               "sha": "db26e82bc99be324", "read_bytes": 19473802,
+                               "write_bytes": 11033778},
 }
 # the split plan's three kernels per step (pass 1, finalize, pass 2)
 _SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",
@@ -49,10 +49,10 @@ _SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",
                   "efficient_vision_transformer_amd/csrc/device_common.h",
                   "efficient_vision_transformer_amd/csrc/kernels.h",
                   "efficient_vision_transformer_amd/csrc/pass2_layout.h"]
-MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "69f93d69814e1e83",
-                                             "read_bytes": 122357958, "write_bytes": 55167805}
-MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "69f93d69814e1e83",
-                                               "read_bytes": 249591257, "write_bytes": 107653684}
+MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "3cce8cf693703ddd",
+                                             "read_bytes": 122357958, "write_bytes": 55151127}
+MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "3cce8cf693703ddd",
+                                               "read_bytes": 249587291, "write_bytes": 107702073}
 
 
 def measured_traffic(workload: str, plan: str):
@@ -331,7 +331,10 @@ def bench_block(args, ctx, w, dev) -> dict:
             {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
              "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4)})
     roof.update({"traffic": None,
-                 "kernel": "whole block (hipBLASLt projection, the layer, hipBLASLt projection)",
+                 "kernel": "whole block (Q|V projection fused into the layer's kernel, hipBLASLt "
+                           "output projection)" if (w.m <= 32 and w.n <= 256 and w.d <= 64 and
+                                                   args.plan != "split")
+                 else "whole block (hipBLASLt projection, the layer, hipBLASLt projection)",
                  "per_launch": {"algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
                                 "avg_duration_us": round(ms * 1e3, 3)}})
     out = {

@@ -559,16 +559,22 @@ anchor_attn_status_t anchor_attn_block_forward(anchor_attn_ctx* ctx, const void*
     g.vw.v = g.vw.q;
     g.vw.o = aa::View{(long long)n * C, d, C};
 
+    // The Q|V projection fused in front of the layer (one kernel writes H) unless the split
+    // plan is forced or the shape is outside that kernel's limits; otherwise the projection
+    // runs through hipBLASLt and the layer reads it in place.
+    const bool fuse = ctx->plan != ANCHOR_ATTN_PLAN_SPLIT && aa::block_fused_supported(g);
     DeviceGuard guard(ctx->device);
     if (!guard.ok) return ANCHOR_ATTN_ERROR_HIP;
     if (!ctx->gemm && !(ctx->gemm = aa::gemm_cache_create())) return ANCHOR_ATTN_ERROR_HIP;
-    if (!aa::gemm_prepare(ctx->gemm, T, (int)C, (int)(2 * C), bqv != nullptr) ||
+    if ((!fuse && !aa::gemm_prepare(ctx->gemm, T, (int)C, (int)(2 * C), bqv != nullptr)) ||
         !aa::gemm_prepare(ctx->gemm, T, (int)C, (int)C, bo != nullptr))
       return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
-    st = prepare_forward(ctx, g, dtype);
-    if (st != ANCHOR_ATTN_SUCCESS) return st;
+    if (!fuse) {
+      st = prepare_forward(ctx, g, dtype);
+      if (st != ANCHOR_ATTN_SUCCESS) return st;
+    }
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-    const size_t qvb = al((size_t)T * 2 * C * es), hb = al((size_t)T * C * es);
+    const size_t qvb = fuse ? 0 : al((size_t)T * 2 * C * es), hb = al((size_t)T * C * es);
     const size_t need = qvb + hb + aa::kGemmWorkspaceBytes;
     st = grow(ctx, &ctx->block_ws, &ctx->block_ws_bytes, need);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
@@ -577,12 +583,19 @@ anchor_attn_status_t anchor_attn_block_forward(anchor_attn_ctx* ctx, const void*
     void* Hb = w + qvb;
     void* gws = w + qvb + hb;
     hipStream_t s = (hipStream_t)stream;
-    if (aa::gemm_run(ctx->gemm, X, Wqv, bqv, QV, T, (int)C, (int)(2 * C), gws, s) != hipSuccess) {
-      (void)hipGetLastError();
-      return ANCHOR_ATTN_ERROR_HIP;
+    if (fuse) {
+      if (aa::launch_block_fused_bf16(g, X, Wqv, bqv, U, Hb, s) != hipSuccess) {
+        (void)hipGetLastError();
+        return ANCHOR_ATTN_ERROR_HIP;
+      }
+    } else {
+      if (aa::gemm_run(ctx->gemm, X, Wqv, bqv, QV, T, (int)C, (int)(2 * C), gws, s) != hipSuccess) {
+        (void)hipGetLastError();
+        return ANCHOR_ATTN_ERROR_HIP;
+      }
+      st = run_forward(ctx, g, dtype, QV, U, (const char*)QV + C * es, Hb, s);
+      if (st != ANCHOR_ATTN_SUCCESS) return st;
     }
-    st = run_forward(ctx, g, dtype, QV, U, (const char*)QV + C * es, Hb, s);
-    if (st != ANCHOR_ATTN_SUCCESS) return st;
     if (aa::gemm_run(ctx->gemm, Hb, Wo, bo, Y, T, (int)C, (int)C, gws, s) != hipSuccess) {
       (void)hipGetLastError();
       return ANCHOR_ATTN_ERROR_HIP;

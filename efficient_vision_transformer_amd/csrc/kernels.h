@@ -97,6 +97,13 @@ void gemm_cache_destroy(GemmCache* c);
 bool gemm_prepare(GemmCache* c, long long T, int K, int N, bool bias);
 hipError_t gemm_run(GemmCache* c, const void* X, const void* W, const void* bias, void* D,
                     long long T, int K, int N, void* ws, hipStream_t stream);
+// The attention block with the Q|V projection fused in front of the layer (bf16): one
+// workgroup per slice projects X [B, n, C] with its head's columns of Wqv [C, 2C] (+ bqv,
+// may be null) and writes H [B, n, C] (head-major columns).  d = 32 or 64 with A kept in
+// registers, one round of eight waves: m <= 32 and n <= 256.
+bool block_fused_supported(const Geometry& g);
+hipError_t launch_block_fused_bf16(const Geometry& g, const void* X, const void* Wqv,
+                                   const void* bqv, const void* U, void* H, hipStream_t stream);
 // ReLU kernel linear attention, one workgroup per slice (bf16, d = 32 or 64): out =
 // phi(Q) (phi(K)^T V) / max(phi(Q) phi(K)^T 1, cmin) on strided views.
 hipError_t launch_relu_linear_bf16(const Geometry& g, const void* Q, const View& qw, const void* K,

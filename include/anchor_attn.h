@@ -147,10 +147,13 @@ anchor_attn_status_t anchor_attn_forward_strided(anchor_attn_ctx* ctx,
  *   H       = anchor attention of every (batch, head) slice with U [h, m, d]
  *   Y       = H Wo + bo         H [B, n, C] with head-major columns, Wo [C, C], bo [C]
  * All row-major bf16 device arrays; fp32 accumulation; Q, V and H are rounded to bf16
- * between the steps.  bqv and bo may be NULL (no bias).  The two projections run through
- * hipBLASLt, the attention through the kernels of anchor_attn_forward_strided reading the
- * projection in place.  The context keeps a second workspace for the projection, H and
- * hipBLASLt (grown on demand; growth synchronizes).  The first call of a new shape also
+ * between the steps.  bqv and bo may be NULL (no bias).  With d <= 64, m <= 32 and n <= 256
+ * (a ViT-S/16 block, say) and any plan but PLAN_SPLIT, one kernel per (batch, head) slice
+ * projects that slice's Q and V from X on the matrix cores and runs the attention on them
+ * (no Q|V tensor in memory); otherwise the Q|V projection runs through hipBLASLt and the
+ * attention through the kernels of anchor_attn_forward_strided reading the projection in
+ * place.  The output projection runs through hipBLASLt.  The context keeps a second
+ * workspace for the projection, H and hipBLASLt (grown on demand; growth synchronizes).  The first call of a new shape also
  * times hipBLASLt's candidate algorithms on the call's own operands and synchronizes the
  * stream; later calls of that shape only enqueue.  Y must not overlap any input.
  * Domain: dtype BF16 (else NOT_SUPPORTED); B, n, h >= 0 (no tokens: a no-op); m and d as
