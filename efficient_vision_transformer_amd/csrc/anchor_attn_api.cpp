@@ -199,10 +199,11 @@ Chosen choose(const anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t
   }
 }
 
-// The backward (bf16, m <= 128): one workgroup per slice when that plan applies, else the
-// split passes; the context's plan setting is honoured as for the forward.
+// The backward (bf16; m <= 256 at d <= 64, m <= 128 at d = 128): one workgroup per slice
+// when that plan applies, else the split passes; the context's plan setting is honoured as
+// for the forward.
 Chosen choose_backward(const anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t dtype) {
-  if (dtype != ANCHOR_ATTN_BF16 || g.at > 8 || g.d > 64) return Chosen::Unsupported;
+  if (dtype != ANCHOR_ATTN_BF16 || !aa::bwd_split_supported(g)) return Chosen::Unsupported;
   const bool fused_ok = aa::bwd_fused_supported(g);
   switch (ctx->plan) {
     case ANCHOR_ATTN_PLAN_FUSED: return fused_ok ? Chosen::Fused : Chosen::Unsupported;

@@ -298,7 +298,8 @@ void fused_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 //   m <= 32: eight waves, A kept for up to two rounds (n <= 512), else recomputed; at
 //            d = 128 four waves of up to two rounds, A kept;
 //   m <= 64: four waves, A kept for up to five rounds (n <= 640), else recomputed.
-// Both keep two workgroups per CU within the register and LDS budgets.  With d = 64 and
+// Registers and LDS allow two workgroups per CU (three for the d = 128, m <= 32 plan:
+// 45 KB of LDS, four waves).  With d = 64 and
 // fewer than two slices per CU, 2 * CUs - slices slices are shared by two workgroups so
 // that every CU gets about one and a half slices' worth of loads, stores and products.
 // With d = 128 every slice is shared (each workgroup holds 64 dims of V in LDS).

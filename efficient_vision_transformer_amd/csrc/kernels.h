@@ -64,6 +64,7 @@ struct BackwardBuffers {
   void* wu;       // W, logits-layout operands     [slice][AT][KS][64] x 16 B
   void* dpu;      // dP, logits-layout operands    [slice][AT][KS][64] x 16 B
   void* dpw;      // dP^T, output-layout operands  [slice][DT][MP][64] x 16 B
+                  // (row-major dP [slice][m_pad][d] beyond 128 anchors or at d = 128)
   float* dd;      // dDelta                        [slice][16 AT]
   float* partU;   // partials of dS^T Q            [slice][chunk][AT][DT][256]
 };
@@ -73,6 +74,8 @@ struct BwdViews {
 };
 // Zeroes `bytes` (a multiple of 4) with a fill kernel (safe under stream capture).
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
+// Domain of the split backward: up to 256 anchors at d = 32 or 64, up to 128 at d = 128.
+bool bwd_split_supported(const Geometry& g);
 hipError_t launch_backward_bf16(const Geometry& g, const SplitPlan& p, const BackwardBuffers& wb,
                                 const BwdViews& bv, const void* Q, const void* U, const void* V,
                                 const void* G, void* dQ, void* dU, void* dV, hipStream_t stream);

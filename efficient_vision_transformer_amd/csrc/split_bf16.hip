@@ -640,6 +640,7 @@ hipError_t launch_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* 
   };
   if (g.d == 64) return at(std::integral_constant<int, 64>{});
   if (g.d == 32) return at(std::integral_constant<int, 32>{});
+  if (g.d == 128) return at(std::integral_constant<int, 128>{});
   return hipErrorInvalidValue;
 }
 

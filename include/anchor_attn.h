@@ -64,9 +64,9 @@ typedef enum {
 
 /* Plans: how a call is mapped onto kernels.  AUTO picks per shape.  FUSED computes a
  * (batch, head) slice in one kernel without workspace (short sequences, n <= 1024,
- * m <= 64, bf16 only): one workgroup per slice, or, when there are fewer than two slices
- * per CU and d = 64, two workgroups for some slices, each writing one half of the output
- * dims.  SPLIT
+ * m <= 64, bf16 only): one workgroup per slice, or two workgroups for a slice, each writing one half of
+ * the output dims: at d = 64 for some slices when there are fewer than two slices per CU,
+ * at d = 128 for every slice.  SPLIT
  * splits the tokens of a slice over workgroups: pass 1 writes per-chunk partial column
  * sums and A^T V, a finalize kernel reduces them in a fixed order into
  * Delta^-1 A^T V, and pass 2 recomputes A and writes H. */
@@ -223,9 +223,9 @@ anchor_attn_status_t anchor_attn_nystrom_forward(anchor_attn_ctx* ctx, const voi
  * Accumulation is fp32; results are rounded to bf16.  dQ, dU and dV are written in full
  * (dU is zero when B*h*n == 0); they must not overlap each other or any input.  The
  * context's workspace grows as for the split plan (the first call of a larger shape may
- * synchronize).  Domain: as anchor_attn_forward with dtype BF16, m <= 128 and d in
- * {32, 64}; other dtypes, larger m or d = 128 return NOT_SUPPORTED.  Errors as anchor_attn_forward: nothing is
- * enqueued and no output is touched. */
+ * synchronize).  Domain: as anchor_attn_forward with dtype BF16 and either d in {32, 64}
+ * with m <= 256 or d = 128 with m <= 128; other dtypes and larger m return NOT_SUPPORTED.
+ * Errors as anchor_attn_forward: nothing is enqueued and no output is touched. */
 anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx,
                                           const void* Q, const void* U, const void* V,
                                           const void* dH, void* dQ, void* dU, void* dV,

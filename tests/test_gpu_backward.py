@@ -158,9 +158,14 @@ def test_backward_rejects_what_it_cannot_run(ctxs, dev):
     with pytest.raises(RuntimeError, match="status 2"):
         ctx.backward(Q, U, V, V.clone())
     Qb = torch.zeros((1, 1, 40, 32), dtype=torch.bfloat16, device=dev)
-    Ub = torch.zeros((1, 129, 32), dtype=torch.bfloat16, device=dev)
+    Ub = torch.zeros((1, 257, 32), dtype=torch.bfloat16, device=dev)
     with pytest.raises(RuntimeError, match="status 2"):
         ctx.backward(Qb, Ub, Qb.clone(), Qb.clone())
+    # d = 128 takes up to 128 anchors
+    Q8 = torch.zeros((1, 1, 40, 128), dtype=torch.bfloat16, device=dev)
+    U8 = torch.zeros((1, 129, 128), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(RuntimeError, match="status 2"):
+        ctx.backward(Q8, U8, Q8.clone(), Q8.clone())
     # the one-workgroup-per-slice plan, forced, rejects m > 64 and n > 1024
     Ub = torch.zeros((1, 65, 32), dtype=torch.bfloat16, device=dev)
     with pytest.raises(RuntimeError, match="status 2"):

@@ -85,7 +85,8 @@ def test_d128_fused_against_oracle(ctxs, dev, shape):
 
 def test_d128_fused_is_auto_at_vit_shape(ctxs):
     """384 slices at n = 196, m = 30: the automatic choice is the fused plan; 300 tokens
-    with 30 anchors (two rounds of eight waves) is left to the split plan."""
+    with 30 anchors (ten pairs of rows, beyond the fused plan's two rounds of four waves) is
+    left to the split plan."""
     assert ctxs["auto"].describe(64, 6, 196, 30, 128, "bf16").startswith("fused")
     assert ctxs["auto"].describe(64, 6, 300, 30, 128, "bf16").startswith("split")
 
