@@ -39,19 +39,19 @@ MEASURED_TRAFFIC = {
     ("vit_s16_224", "fused"): {"sources": ["efficient_vision_transformer_amd/csrc/fused_bf16.hip",
                                            "efficient_vision_transformer_amd/csrc/tile_ops.h",
                                            "efficient_vision_transformer_amd/csrc/device_common.h",
-                                           "efficient_vision_transformer_amd/csrc/kernels.h"],
-                               "sha": "2a53b3794334645d", "read_bytes": 19473768,
+                                           "efficient_vision_transformer_amd/csrc/geometry.h"],
+                               "sha": "c22e73ce4b2d268e", "read_bytes": 19473768,
                                "write_bytes": 11024565},
 }
 # the split plan's three kernels per step (pass 1, finalize, pass 2)
 _SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",
                   "efficient_vision_transformer_amd/csrc/tile_ops.h",
                   "efficient_vision_transformer_amd/csrc/device_common.h",
-                  "efficient_vision_transformer_amd/csrc/kernels.h",
+                  "efficient_vision_transformer_amd/csrc/geometry.h",
                   "efficient_vision_transformer_amd/csrc/pass2_layout.h"]
-MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "516b003b02f859e2",
+MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "ae24a7b1029a2e91",
                                              "read_bytes": 122349464, "write_bytes": 55155380}
-MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "516b003b02f859e2",
+MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "ae24a7b1029a2e91",
                                                "read_bytes": 249575241, "write_bytes": 107663991}
 
 
@@ -235,11 +235,13 @@ def bench_backward(args, ctx, x, dev, plan_desc) -> dict:
     import torch
     from efficient_vision_transformer_amd.inputs import make_upstream_grad
     w = x.workload
-    if w.dtype != "bf16":
-        raise SystemExit("the backward runs in bf16 only")
     G, gbits = make_upstream_grad(x, w.seed + 1)
-    up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
-    Q0, U, V0, G0 = up(x.bits["Q"]), up(x.bits["U"]), up(x.bits["V"]), up(gbits)
+    if w.dtype == "bf16":
+        up = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+        Q0, U, V0, G0 = up(x.bits["Q"]), up(x.bits["U"]), up(x.bits["V"]), up(gbits)
+    else:
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+        Q0, U, V0, G0 = up(x.Q), up(x.U), up(x.V), up(G)
     algo_bytes, flops = backward_bytes_flops(w)
     R = max(1, -(-ROTATE_BYTES // algo_bytes))
     mk = lambda q, v, g: (q, v, g, (torch.empty_like(q), torch.empty_like(U), torch.empty_like(v)))
@@ -253,15 +255,19 @@ def bench_backward(args, ctx, x, dev, plan_desc) -> dict:
     gbs = algo_bytes / (ms * 1e-3) / 1e9
     tflops = flops / (ms * 1e-3) / 1e12
     # the bound is whichever floor is higher: the bytes at HBM peak or the flops at the
-    # dense bf16 MFMA peak (the long and dense workloads' many anchors make it the latter)
-    if flops / (BF16_PEAK_TFLOPS * 1e12) > algo_bytes / (HBM_PEAK_GBS * 1e9):
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    # dense MFMA peak of the dtype (the long and dense workloads' many anchors, and fp32,
+    # make it the latter)
+    peak_tf = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+    if flops / (peak_tf * 1e12) > algo_bytes / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_tf,
+                "unit": "TFLOP/s", "frac": round(tflops / peak_tf, 4), "traffic": None}
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
     roof.update({
-            "kernel": "whole backward (pass1 x2 + finalize + tokens + dU reduction)",
+            "kernel": ("whole backward (pass1 x2 + finalize + tokens + dU reduction)"
+                       if w.dtype == "bf16" else
+                       "whole backward (pass1 x2 + finalize + tokens + dS^T Q + dU reduction)"),
             "per_launch": {"algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
                            "avg_duration_us": round(ms * 1e3, 3)}})
     out = {

@@ -289,9 +289,9 @@ class AnchorAttention:
 
     def backward(self, Q, U, V, dH, out=None, stream=None):
         """Gradients for dL/dH = dH: returns (dQ [B,h,n,d], dU [h,m,d] summed over the
-        batch, dV [B,h,n,d]), bf16, enqueued on ``stream``; no synchronisation.  Q, V, dH
-        (and dQ, dV in ``out``) may be strided views whose d values per token are
-        contiguous; U and dU are contiguous.  ``out`` may give (dQ, dU, dV) to write into."""
+        batch, dV [B,h,n,d]) in the inputs' dtype (bf16 or fp32), enqueued on ``stream``; no
+        synchronisation.  Q, V, dH (and dQ, dV in ``out``) may be strided views whose d
+        values per token are contiguous; U and dU are contiguous.  ``out`` may give (dQ, dU, dV) to write into."""
         import torch
         if Q.dim() != 4 or V.shape != Q.shape or dH.shape != Q.shape or U.dim() != 3:
             raise ValueError(f"bad shapes Q{tuple(Q.shape)} U{tuple(U.shape)} V{tuple(V.shape)} "

@@ -2,8 +2,9 @@
 (the learnable anchors) and V receive gradients in an ordinary training step.
 
 Both directions run in the HIP library through the C ABI (anchor_attn_forward and
-anchor_attn_backward); this module only hands tensors over.  bf16, m <= 128 for the
-backward (the library's domain); U's gradient is summed over the batch.
+anchor_attn_backward); this module only hands tensors over.  The backward's domain is
+the library's: bf16 with m <= 256 (m <= 128 at d = 128), fp32 with m <= 256 and d = 32 or
+64; U's gradient is summed over the batch.
 """
 from __future__ import annotations
 

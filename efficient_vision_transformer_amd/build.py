@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libanchor_attn.so")
 SOURCES = ["anchor_attn_api.cpp", "split_bf16.hip", "split_fp32.hip", "fused_bf16.hip",
            "backward_bf16.hip", "backward_fused_bf16.hip", "block_gemm.cpp",
-           "linear_bf16.hip", "nystrom_bf16.hip", "stream_reference.hip", "block_fused_bf16.hip"]
+           "linear_bf16.hip", "nystrom_bf16.hip", "stream_reference.hip", "block_fused_bf16.hip",
+           "backward_fp32.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

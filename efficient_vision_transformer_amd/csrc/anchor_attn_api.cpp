@@ -203,6 +203,11 @@ Chosen choose(const anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t
 // when that plan applies, else the split passes; the context's plan setting is honoured as
 // for the forward.
 Chosen choose_backward(const anchor_attn_ctx* ctx, const Geometry& g, anchor_attn_dtype_t dtype) {
+  if (dtype == ANCHOR_ATTN_FP32) {
+    // fp32: the split passes only (m <= 256, d = 32 or 64)
+    if (!aa::bwd_fp32_supported(g) || ctx->plan == ANCHOR_ATTN_PLAN_FUSED) return Chosen::Unsupported;
+    return Chosen::Split;
+  }
   if (dtype != ANCHOR_ATTN_BF16 || !aa::bwd_split_supported(g)) return Chosen::Unsupported;
   const bool fused_ok = aa::bwd_fused_supported(g);
   switch (ctx->plan) {
@@ -726,7 +731,7 @@ static anchor_attn_status_t backward_strided_impl(
     const anchor_attn_dtype_t dtype = (anchor_attn_dtype_t)dtype_raw;
     const Chosen plan = choose_backward(ctx, g, dtype);
     if (plan == Chosen::Unsupported) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
-    const size_t es = 2;
+    const size_t es = (dtype == ANCHOR_ATTN_FP32) ? 4 : 2;
     aa::BwdViews bv{g.vw.q, g.vw.q, g.vw.q, g.vw.q, g.vw.q};
     if (!take_view(q_strides, es, &bv.q) || !take_view(v_strides, es, &bv.v) ||
         !take_view(dh_strides, es, &bv.g) || !take_view(dq_strides, es, &bv.dq) ||
@@ -773,6 +778,26 @@ static anchor_attn_status_t backward_strided_impl(
       st = ensure_workspace(ctx, al((size_t)g.slices * g.m_pad * g.d * sizeof(float)));
       if (st != ANCHOR_ATTN_SUCCESS) return st;
       e = aa::launch_backward_fused_bf16(g, bv, Q, U, V, dH, dQ, dU, dV, (float*)ctx->workspace, s);
+    } else if (dtype == ANCHOR_ATTN_FP32) {
+      const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
+      const size_t part = al((size_t)g.slices * p.chunks1 * g.m_pad * g.d * sizeof(float));
+      const size_t dpart = al((size_t)g.slices * p.chunks1 * g.m_pad * sizeof(float));
+      const size_t rows = al((size_t)g.slices * g.m_pad * g.d * sizeof(float));
+      const size_t ddb = al((size_t)g.slices * g.m_pad * sizeof(float));
+      const size_t dsb = al((size_t)g.slices * (size_t)g.n * g.m_pad * sizeof(float));
+      st = ensure_workspace(ctx, 3 * part + dpart + 2 * rows + ddb + dsb);
+      if (st != ANCHOR_ATTN_SUCCESS) return st;
+      char* w = (char*)ctx->workspace;
+      aa::BackwardBuffersF32 wb{};
+      wb.partP = (float*)w; w += part;
+      wb.partG = (float*)w; w += part;
+      wb.partU = (float*)w; w += part;
+      wb.dpart = (float*)w; w += dpart;
+      wb.wrm = (float*)w; w += rows;
+      wb.dprm = (float*)w; w += rows;
+      wb.dd = (float*)w; w += ddb;
+      wb.ds = (float*)w;
+      e = aa::launch_backward_fp32(g, p, wb, bv, Q, U, V, dH, dQ, dU, dV, s);
     } else {
       const SplitPlan p = make_split_plan(g, dtype, ctx->num_cus);
       const size_t part = al((size_t)g.slices * p.chunks1 * g.m_pad * g.d * sizeof(float));

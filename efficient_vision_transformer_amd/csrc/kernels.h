@@ -3,50 +3,9 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "geometry.h"
+
 namespace aa {
-
-// Element strides (batch, head, token) of a [B, h, n, d] view whose d values per token are
-// contiguous; the contiguous layout is (h*n*d, n*d, d).  Strides are non-negative
-// multiples of 16 bytes, so every row is a whole number of 16-byte vectors.
-struct View {
-  long long sb, sh, st;
-};
-// The views of one forward call: Q and V (inputs) and H (output).
-struct Views {
-  View q, v, o;
-};
-
-// Problem geometry of one call.  Q, V, H: [B, h, n, d] views; U: [h, m, d] contiguous.
-struct Geometry {
-  int B, h, n, m, d;
-  int m_pad;          // m rounded up to a multiple of 32
-  int at;             // anchor tiles of 16: m_pad / 16
-  long long slices;   // B * h
-  float c2;           // log2(e) / sqrt(d): logits are kept in base-2 units
-  Views vw;           // strides of Q, V, H (contiguous unless the caller gives others)
-};
-
-// Split plan: pass 1 over chunks1 chunks of chunk_len1 tokens per slice writes
-// partials; finalize reduces them; pass 2 over chunks2 chunks writes H.
-struct SplitPlan {
-  int chunks1, chunk_len1;
-  int chunks2, chunk_len2;
-  size_t part_bytes, dpart_bytes, w_bytes;   // workspace sections
-  size_t workspace_bytes() const { return part_bytes + dpart_bytes + w_bytes; }
-};
-
-// Fused plan: one workgroup per slice, everything on chip.
-struct FusedPlan {
-  int waves;          // waves per workgroup
-  int pairs_per_wave; // 32-token pairs handled by each wave
-  bool keep_a;        // A kept in registers (else recomputed from Q for the output)
-  long long shared;   // slices handled by two workgroups (one per half of the output dims)
-};
-
-constexpr int kPass1Waves = 4;    // pass 1 block = 4 pairs = 128 tokens
-constexpr int kPass1Block = 128;
-constexpr int kPass2Waves = 4;    // pass 2 block = 4 tiles = 64 tokens
-constexpr int kPass2Block = 64;
 
 hipError_t launch_split_bf16(const Geometry& g, const SplitPlan& p, const void* Q,
                              const void* U, const void* V, void* H, void* workspace,
@@ -79,6 +38,26 @@ bool bwd_split_supported(const Geometry& g);
 hipError_t launch_backward_bf16(const Geometry& g, const SplitPlan& p, const BackwardBuffers& wb,
                                 const BwdViews& bv, const void* Q, const void* U, const void* V,
                                 const void* G, void* dQ, void* dU, void* dV, hipStream_t stream);
+// fp32 split pass 1 alone on (Q, U, X), partials as launch_pass1_bf16's.
+hipError_t launch_pass1_fp32(const Geometry& g, const SplitPlan& p, const void* Q, const void* U,
+                             const void* X, float* part, float* dpart, hipStream_t stream);
+// Workspace sections of the fp32 backward (see backward_fp32.hip).
+struct BackwardBuffersF32 {
+  float* partP;   // pass-1 partials of A^T V      [slice][chunk][AT][DT][256]
+  float* partG;   // pass-1 partials of A^T dH     [slice][chunk][AT][DT][256]
+  float* dpart;   // pass-1 partials of Delta      [slice][chunk][16 AT]
+  float* wrm;     // W, row-major                  [slice][m_pad][d]
+  float* dprm;    // dP, row-major                 [slice][m_pad][d]
+  float* dd;      // dDelta                        [slice][m_pad]
+  float* ds;      // dS rows                       [slice][n][m_pad]
+  float* partU;   // partials of dS^T Q            [slice][chunk][AT][DT][256]
+};
+// Domain of the fp32 backward: d = 32 or 64, up to 256 anchors.
+bool bwd_fp32_supported(const Geometry& g);
+hipError_t launch_backward_fp32(const Geometry& g, const SplitPlan& p,
+                                const BackwardBuffersF32& wb, const BwdViews& bv, const void* Q,
+                                const void* U, const void* V, const void* G, void* dQ, void* dU,
+                                void* dV, hipStream_t stream);
 // dU = (1/sqrt(d)) x the sum over batch and chunks of per-(slice, chunk) partial tiles
 // [slice][chunk][AT][DT][256] of dS^T Q.
 hipError_t launch_du_reduce_bf16(const Geometry& g, const float* partU, int chunks, void* dU,

@@ -6,6 +6,8 @@
 // (AnchorFormer, Pith verdict page: referee summary, Eq. (11) in the Eq. (12) order).
 // Every product runs on v_mfma_f32_16x16x4_f32 (full fp32 products, fp32 accumulate);
 // there is no reduced-precision step anywhere on this path.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -408,6 +410,32 @@ hipError_t launch_split_fp32(const Geometry& g, const SplitPlan& p, const void* 
                              const void* V, void* H, void* ws, hipStream_t stream) {
   if (g.d == 64) return dispatch_at<64>(g, p, Q, U, V, H, ws, stream);
   if (g.d == 32) return dispatch_at<32>(g, p, Q, U, V, H, ws, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_pass1_fp32(const Geometry& g, const SplitPlan& p, const void* Q, const void* U,
+                             const void* X, float* part, float* dpart, hipStream_t s) {
+  const long long g1 = g.slices * p.chunks1;
+  auto at = [&](auto D) -> hipError_t {
+    constexpr int d = decltype(D)::value;
+#define AA_P1F(AT)                                                                           \
+  pass1_fp32<d, AT, (AT % 4 == 0) ? 4 : 2><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, s>>>( \
+      (const float*)Q, (const float*)U, (const float*)X, part, dpart, g.vw.q, g.vw.v, g.h, g.n, \
+      g.m, p.chunks1, p.chunk_len1, g.c2)
+    switch (g.at) {
+      case 2: AA_P1F(2); break;
+      case 4: AA_P1F(4); break;
+      case 6: AA_P1F(6); break;
+      case 8: AA_P1F(8); break;
+      case 12: AA_P1F(12); break;
+      case 16: AA_P1F(16); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef AA_P1F
+    return hipGetLastError();
+  };
+  if (g.d == 64) return at(std::integral_constant<int, 64>{});
+  if (g.d == 32) return at(std::integral_constant<int, 32>{});
   return hipErrorInvalidValue;
 }
 

@@ -217,14 +217,18 @@ anchor_attn_status_t anchor_attn_nystrom_forward(anchor_attn_ctx* ctx, const voi
  * abstract: the anchors are learnable, so the layer is trained through; the Pith verdict
  * page's Eq. (11) in the Eq. (12) order is the function differentiated), on `stream`,
  * without waiting:
- *   Q, V, dH, dQ, dV : [B, h, n, d]  device, bf16
- *   U, dU            : [h, m, d]     device, bf16; dU is summed over the batch (U is
+ *   Q, V, dH, dQ, dV : [B, h, n, d]  device, bf16 or fp32 (dtype)
+ *   U, dU            : [h, m, d]     device, same dtype; dU is summed over the batch (U is
  *                                    shared by every batch element)
- * Accumulation is fp32; results are rounded to bf16.  dQ, dU and dV are written in full
+ * Accumulation is fp32; bf16 results are rounded from it.  The fp32 path keeps every
+ * operand in fp32 (full fp32 matrix-core products) and holds the n x m_pad matrix dS in
+ * the workspace (4 bytes per element).  dQ, dU and dV are written in full
  * (dU is zero when B*h*n == 0); they must not overlap each other or any input.  The
  * context's workspace grows as for the split plan (the first call of a larger shape may
- * synchronize).  Domain: as anchor_attn_forward with dtype BF16 and either d in {32, 64}
- * with m <= 256 or d = 128 with m <= 128; other dtypes and larger m return NOT_SUPPORTED.
+ * synchronize).  Domain: as anchor_attn_forward, with dtype BF16 and either d in {32, 64}
+ * with m <= 256 or d = 128 with m <= 128, or dtype FP32 with d in {32, 64} and m <= 256
+ * (split plan only: a context whose plan is FUSED returns NOT_SUPPORTED for fp32); larger
+ * m returns NOT_SUPPORTED.
  * Errors as anchor_attn_forward: nothing is enqueued and no output is touched. */
 anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx,
                                           const void* Q, const void* U, const void* V,

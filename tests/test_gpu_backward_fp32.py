@@ -1,0 +1,180 @@
+"""GPU parity of the fp32 backward (fp32 inputs, every product and accumulation in fp32)
+against the fp64 oracle's gradients, element by element, on seeded inputs.
+
+Gate: normwise max-relative error max|g - g_ref| / max|g_ref| <= 1e-5 for each of dQ, dU
+and dV, the fp32 gate of the forward.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from efficient_vision_transformer_amd.inputs import make_inputs, make_upstream_grad, random_case
+
+from gpu_util import FP32_TOL, fp32_err, to_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ctxs(dev):
+    from efficient_vision_transformer_amd import AnchorAttention
+    out = {p: AnchorAttention(dev, plan=p) for p in ("auto", "split", "fused")}
+    yield out
+    for c in out.values():
+        c.close()
+
+
+def _grads(ctx, dev, x, gseed):
+    import torch
+    w = x.workload
+    print(f"  fp32 backward {w.name} B={w.B} h={w.h} n={w.n} m={w.m} d={w.d} gseed={gseed}",
+          flush=True)
+    G, _ = make_upstream_grad(x, gseed)
+    Q, U, V = to_device(x, dev)
+    dH = torch.from_numpy(np.ascontiguousarray(G)).to(dev)
+    dQ, dU, dV = ctx.backward(Q, U, V, dH)
+    torch.cuda.synchronize()
+    assert dQ.dtype == torch.float32 and dU.dtype == torch.float32
+    return (to_host(dQ), to_host(dU), to_host(dV)), G
+
+
+def _check_all(got, ref, label, tol=FP32_TOL):
+    errs = [fp32_err(gv, rv) for gv, rv in zip(got, ref)]
+    print(f"  {label}: max-relative dQ {errs[0]:.3e} dU {errs[1]:.3e} dV {errs[2]:.3e}",
+          flush=True)
+    for name, e in zip(("dQ", "dU", "dV"), errs):
+        assert e <= tol, f"{label} {name}: {e:.3e} > {tol}"
+
+
+# (B, h, n, m, d): every anchor-tile count (2 .. 16 tiles of 16), padded tiles, ragged
+# token counts (two tokens, a partial 16-token tile, several chunks per slice)
+SHAPES = [
+    (1, 1, 64, 8, 32),
+    (1, 1, 2, 5, 64),
+    (2, 3, 77, 30, 64),
+    (1, 2, 300, 64, 32),
+    (2, 1, 257, 100, 64),
+    (1, 2, 129, 128, 64),
+    (1, 1, 500, 150, 32),
+    (1, 2, 1000, 256, 64),
+    (2, 2, 3000, 200, 64),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda v: "x".join(map(str, v)))
+def test_backward_fp32_shapes(ctxs, dev, shape):
+    B, h, n, m, d = shape
+    x = random_case(27000 + n + m, B, h, n, m, d, "fp32")
+    got, G = _grads(ctxs["auto"], dev, x, 28000 + n)
+    ref = oracle.anchor_backward(x.Q, x.U, x.V, G)
+    _check_all(got, ref, "x".join(map(str, shape)))
+
+
+def test_backward_fp32_one_token(ctxs, dev):
+    """One token: H = V, so dV = dH and dQ, dU vanish up to rounding."""
+    x = random_case(27050, 1, 2, 1, 40, 64, "fp32")
+    got, G = _grads(ctxs["auto"], dev, x, 27051)
+    assert fp32_err(got[2], G) <= FP32_TOL
+    scale = np.abs(G).max()
+    print(f"  max|dQ| {np.abs(got[0]).max():.2e} max|dU| {np.abs(got[1]).max():.2e}", flush=True)
+    assert np.abs(got[0]).max() <= 1e-5 * scale and np.abs(got[1]).max() <= 1e-5 * scale
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "long_16k_fp32"])
+def test_backward_fp32_workloads_full(ctxs, dev, name):
+    """The tiny workload (B = 1, h = 1, n = 64, m = 8, d = 32) and the long-sequence one
+    (B = 2, h = 16, n = 16384, m = 256, d = 64, 1% sink tokens), every gradient element
+    against the oracle."""
+    x = make_inputs(name)
+    got, G = _grads(ctxs["auto"], dev, x, 29000)
+    ref = oracle.anchor_backward(x.Q, x.U, x.V, G)
+    _check_all(got, ref, name)
+
+
+def test_backward_fp32_deterministic_bitwise(ctxs, dev):
+    import torch
+    x = random_case(27100, 2, 3, 700, 200, 64, "fp32")
+    G, _ = make_upstream_grad(x, 27101)
+    Q, U, V = to_device(x, dev)
+    dH = torch.from_numpy(np.ascontiguousarray(G)).to(dev)
+    first = [t.clone() for t in ctxs["auto"].backward(Q, U, V, dH)]
+    second = ctxs["auto"].backward(Q, U, V, dH)
+    torch.cuda.synchronize()
+    for a, b in zip(first, second):
+        assert torch.equal(a, b)
+
+
+def test_backward_fp32_plans(ctxs, dev):
+    """fp32 takes the split passes under AUTO and SPLIT; the one-workgroup-per-slice plan is
+    bf16 only, so a context forced to it refuses fp32."""
+    import torch
+    x = random_case(27200, 1, 2, 100, 20, 32, "fp32")
+    Q, U, V = to_device(x, dev)
+    assert ctxs["auto"].describe(1, 2, 100, 20, 32, "fp32").endswith("backward: split")
+    a = ctxs["auto"].backward(Q, U, V, Q.clone())
+    b = ctxs["split"].backward(Q, U, V, Q.clone())
+    torch.cuda.synchronize()
+    for p_, q_ in zip(a, b):
+        assert torch.equal(p_, q_)
+    with pytest.raises(RuntimeError, match="status 2"):
+        ctxs["fused"].backward(Q, U, V, Q.clone())
+    U2 = torch.zeros((2, 257, 32), dtype=torch.float32, device=dev)
+    with pytest.raises(RuntimeError, match="status 2"):
+        ctxs["auto"].backward(Q, U2, V, Q.clone())
+    Q8 = torch.zeros((1, 1, 10, 128), dtype=torch.float32, device=dev)
+    U8 = torch.zeros((1, 4, 128), dtype=torch.float32, device=dev)
+    with pytest.raises(RuntimeError, match="status 2"):
+        ctxs["auto"].backward(Q8, U8, Q8.clone(), Q8.clone())
+
+
+def test_backward_fp32_strided_views(ctxs, dev):
+    """Q and V read from a packed [B, n, 3, h, d] fp32 tensor and dQ, dV written into padded
+    buffers whose gaps stay untouched; equal bit for bit to the contiguous call."""
+    import torch
+    B, h, n, m, d = 2, 3, 190, 40, 64
+    x = random_case(27300, B, h, n, m, d, "fp32")
+    G, _ = make_upstream_grad(x, 27301)
+    qkv = torch.from_numpy(np.ascontiguousarray(np.stack(
+        [x.Q.transpose(0, 2, 1, 3), x.Q.transpose(0, 2, 1, 3), x.V.transpose(0, 2, 1, 3)],
+        axis=2))).to(dev)
+    Qv, Vv = qkv[:, :, 0].permute(0, 2, 1, 3), qkv[:, :, 2].permute(0, 2, 1, 3)
+    dHv = torch.from_numpy(np.ascontiguousarray(G.transpose(0, 2, 1, 3))).to(dev).permute(0, 2, 1, 3)
+    U = torch.from_numpy(np.ascontiguousarray(x.U)).to(dev)
+    bufs = [torch.full((B, n, h, d + 4), 5.0, dtype=torch.float32, device=dev) for _ in range(2)]
+    dQv, dVv = (b_[..., :d].permute(0, 2, 1, 3) for b_ in bufs)
+    dU = torch.empty_like(U)
+    print("  strided fp32 backward", flush=True)
+    ctxs["auto"].backward(Qv, U, Vv, dHv, out=(dQv, dU, dVv))
+    torch.cuda.synchronize()
+    for b_ in bufs:
+        assert torch.all(b_[..., d:] == 5.0).item(), "writes outside the output views"
+    Q, U_, V = to_device(x, dev)
+    cq, cu, cv = ctxs["auto"].backward(Q, U_, V, torch.from_numpy(np.ascontiguousarray(G)).to(dev))
+    torch.cuda.synchronize()
+    for a, b_ in ((dQv, cq), (dU, cu), (dVv, cv)):
+        assert torch.equal(a.contiguous(), b_)
+    ref = oracle.anchor_backward(x.Q, x.U, x.V, G)
+    _check_all((to_host(cq), to_host(cu), to_host(cv)), ref, "strided fp32")
+
+
+def test_autograd_fp32_matches_oracle():
+    """A loss on fp32 H back-propagates through the fp32 backward into Q, U and V."""
+    import torch
+    from efficient_vision_transformer_amd import anchor_attention
+    x = random_case(27400, 2, 3, 196, 30, 64, "fp32")
+    Q, U, V = (torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0").requires_grad_(True)
+               for a in (x.Q, x.U, x.V))
+    Wl = np.random.default_rng(5).standard_normal(x.Q.shape).astype(np.float32)
+    W = torch.from_numpy(Wl).to("cuda:0")
+    H = anchor_attention(Q, U, V)
+    (H * W).sum().backward()
+    torch.cuda.synchronize()
+    refs = oracle.anchor_backward(x.Q, x.U, x.V, Wl.astype(np.float64))
+    _check_all(tuple(to_host(t.grad) for t in (Q, U, V)), refs, "autograd fp32")
