@@ -696,16 +696,15 @@ anchor_attn_status_t anchor_attn_nystrom_forward(anchor_attn_ctx* ctx, const voi
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     const size_t rows = al((size_t)g.slices * s * d * 2);
     const size_t cmax = al((size_t)g.slices * p.chunks1 * g.m_pad * sizeof(float));
-    st = ensure_workspace(ctx, p.workspace_bytes() + 2 * rows + cmax);
+    st = ensure_workspace(ctx, p.workspace_bytes() + rows + cmax);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
     char* ws = (char*)ctx->workspace;
     aa::NystromBuffers nb{};
     nb.part = (float*)ws;
     nb.dpart = (float*)(ws + p.part_bytes);
     nb.wop = (__bf16*)(ws + p.part_bytes + p.dpart_bytes);
-    nb.qt = (__bf16*)(ws + p.workspace_bytes());
-    nb.kt = (__bf16*)(ws + p.workspace_bytes() + rows);
-    nb.cmax = (float*)(ws + p.workspace_bytes() + 2 * rows);
+    nb.kt = (__bf16*)(ws + p.workspace_bytes());
+    nb.cmax = (float*)(ws + p.workspace_bytes() + rows);
     const hipError_t e = aa::launch_nystrom_bf16(g, p, Q, K, V, idx, H, nb, (hipStream_t)stream);
     if (e != hipSuccess) {
       (void)hipGetLastError();

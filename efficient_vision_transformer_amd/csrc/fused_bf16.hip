@@ -120,7 +120,10 @@ __device__ __forceinline__ void fused_part(FusedLds<D, MP, NW>& L, const __bf16*
     const int pairs_here = min(NW, npairs - r * NW);  // uniform over the workgroup
     if (pairs_here <= 0) break;
     const int p = r * NW + w;
-    const bool more = (r + 1 < ROUNDS) && (p + NW < npairs);
+    // The next round's rows are requested unconditionally (rows past the slice read its
+    // last row; a pair past the end is never used): a load under a branch would make the
+    // wait for this round's rows at the join an unconditional vmcnt(0).
+    const bool more = r + 1 < ROUNDS;
     u32x4 qn[2][KS], vn[VAHEAD ? 2 : 1][KV];
     if (more) {
 #pragma unroll

@@ -114,17 +114,16 @@ struct NystromBuffers {
   float* part;    // pass-1 partials of F3 V (unnormalised)  [slice][chunk][AT][DT][256]
   float* dpart;   // pass-1 partials of F3's row sums        [slice][chunk][16 AT]
   __bf16* wop;    // Z = F2^-1 F3 V as pass-2 W operands      [slice][DT][MP][64][8]
-  __bf16* qt;     // landmark rows of Q                       [slice][s][d]
-  __bf16* kt;     // landmark rows of K                       [slice][s][d]
+  __bf16* kt;     // landmark rows of K (written by the solve) [slice][s][d]
   float* cmax;    // per-chunk landmark maxima of q.k         [slice][chunk][16 AT]
 };
 hipError_t launch_nystrom_bf16(const Geometry& g, const SplitPlan& p, const void* Q, const void* K,
                                const void* V, const int* idx, void* H, const NystromBuffers& nb,
                                hipStream_t stream);
 hipError_t launch_nystrom_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* K,
-                                     const View& kw, const void* qt, const void* V,
-                                     const View& vw, float* part, float* dpart,
-                                     const float* cmax, hipStream_t s);
+                                     const View& kw, const void* Q, const View& qw,
+                                     const int* idx, const void* V, const View& vw, float* part,
+                                     float* dpart, float* cmax, hipStream_t s);
 hipError_t launch_nystrom_pass2_bf16(const Geometry& g, const SplitPlan& p, const void* Q,
                                      const View& qw, const void* kt, const void* Wop, void* H,
                                      const View& ow, hipStream_t s);

@@ -6,16 +6,17 @@
 // (batch, head) slice, with c = 1/sqrt(d):
 //   F1 = rowsoftmax(Q k^T c) (n x s),  F2 = rowsoftmax(q k^T c) (s x s),
 //   F3 = rowsoftmax(q K^T c) (s x n),  H = F1 (F2^-1 (F3 V)).
-// Four launches:
-//   nys_max     per (slice, token chunk): each landmark's largest logit q_a . k_t over the
-//               chunk (MFMA, tokens in lanes); the chunk-0 workgroup of each slice also
-//               copies the landmark rows of Q and K (token indices per batch element).
-//   pass 1      (split plan, landmark mode): exp(c q_a . k_t - c M_a) with M_a the maximum
-//               over all chunks, accumulated against V and against ones: F3 V and F3's row
-//               sums, unnormalised, per chunk.
-//   nys_solve   per slice: chunk sums -> F3 V; F2 in fp32 from the landmark rows; Z = F2^-1
-//               (F3 V) by Gauss-Jordan elimination with partial pivoting, the augmented
-//               matrix spread over the waves' registers; Z stored as pass 2's W operands.
+// Three launches:
+//   pass 1      (split plan, landmark mode): the landmark query rows (gathered from Q
+//               through the indices) as anchors, the keys K streamed as the tokens; per
+//               chunk, each landmark's largest logit q_a . k_t over the chunk (a first
+//               sweep), then exp(c q_a . k_t - c M_a) accumulated against V and against
+//               ones: F3 V and F3's row sums, unnormalised, with the chunk maxima M_a.
+//   nys_solve   per slice: the chunks rescaled to each landmark's overall maximum and
+//               summed -> F3 V; F2 in fp32 from the landmark rows (gathered through the
+//               indices; the key rows are also written out for pass 2); Z = F2^-1 (F3 V) by
+//               Gauss-Jordan elimination with partial pivoting; Z stored as pass 2's W
+//               operands.
 //   pass 2      (split plan, per-slice anchors = the landmark keys): H = rowsoftmax(Q k^T c) Z.
 #include <algorithm>
 
@@ -26,89 +27,92 @@
 
 namespace aa {
 
-// Per (slice, chunk): cmax[slice][chunk][a] = max over the chunk's tokens t of q_a . k_t
-// (raw logits, fp32 accumulation of bf16 products in the same MFMA order as pass 1's, so
-// pass 1's exponents are never positive), with the landmark query rows q_a read from Q
-// through the indices.  The slice's chunk-0 workgroup also writes the landmark rows of Q
-// and K (qt, kt) for the later launches.  Four waves; each takes 16-token tiles with the
-// next tile's rows in flight.  Entries of padded landmarks (a >= m) repeat landmark m - 1.
-// Q and K contiguous [B, h, n, d]; landmark indices clamped to [0, n).
-template <int D, int AT>
-__global__ __launch_bounds__(256)
-void nys_max(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
-             const int* __restrict__ idx, __bf16* __restrict__ qt, __bf16* __restrict__ kt,
-             float* __restrict__ cmax, View kw, int h, int n, int m, int chunks, int chunk_len) {
-  constexpr int KS = D / 32, NW = 4, CH = D / 8;
-  const int slice = blockIdx.x / chunks;
-  const int chunk = blockIdx.x - slice * chunks;
-  const int b = slice / h;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 15, g = lane >> 4;
-  const size_t kb = view_base(kw, slice, h);
-  const int t_begin = chunk * chunk_len;
-  const int t_end = min(n, t_begin + chunk_len);
-  const int* ib = idx + (size_t)b * m;
-  auto token = [&](int a) { return min(max(ib[a], 0), n - 1); };
+// Landmark rows of Q and K for one slice into LDS (row stride RS, rows >= m zero), the
+// key rows also to kt ([slice][m][d], pass 2's anchors).  T threads; Q and K contiguous
+// [B, h, n, d] (view vw); indices clamped to [0, n).
+template <int D, int MPAD, int T, int RS>
+__device__ __forceinline__ void nys_landmark_rows(const __bf16* __restrict__ Q,
+                                                  const __bf16* __restrict__ K, const View& vw,
+                                                  const int* __restrict__ idx, int slice, int h,
+                                                  int n, int m, int tid, __bf16* ql, __bf16* kl,
+                                                  __bf16* __restrict__ kt) {
+  constexpr int CH = D / 8, N = MPAD * CH;
+  const size_t base = view_base(vw, slice, h);
+  const int* ib = idx + (size_t)(slice / h) * m;
+  auto src = [&](int i) {
+    const int a = i / CH, k8 = i - a * CH;
+    const int tok = min(max(ib[min(a, m - 1)], 0), n - 1);
+    return base + (size_t)((long long)tok * vw.st) + 8 * k8;
+  };
+  Stage<N, T> qst, kst;
+  stage_load(qst, [&](int i) { return (i < m * CH) ? *(const u32x4*)(Q + src(i)) : u32x4{0u, 0u, 0u, 0u}; });
+  stage_load(kst, [&](int i) { return (i < m * CH) ? *(const u32x4*)(K + src(i)) : u32x4{0u, 0u, 0u, 0u}; });
+#pragma unroll
+  for (int i = 0; i < Stage<N, T>::kPer; ++i) {
+    const int e = tid + i * T;
+    if (N % T == 0 || e < N) {
+      const int a = e / CH, k8 = e - a * CH;
+      *(u32x4*)(ql + a * RS + 8 * k8) = qst.r[i];
+      *(u32x4*)(kl + a * RS + 8 * k8) = kst.r[i];
+      if (a < m) *(u32x4*)(kt + ((size_t)slice * m + a) * D + 8 * k8) = kst.r[i];
+    }
+  }
+}
 
-  __shared__ u32x4 u_lds[AT][KS][kWave];
-  __shared__ float red[NW][16 * AT];
-  Stage<AT * KS * kWave, NW * kWave> ust;
-  stage_load(ust, [&](int i) {
-    const int j = i / (KS * kWave), kk = (i / kWave) % KS, l = i & 63;
-    const int a = min(16 * j + (l & 15), m - 1);
-    return *(const u32x4*)(Q + kb + (size_t)token(a) * D + 8 * KS * (l >> 4) + 8 * kk);
-  });
-  if (chunk == 0) {
-    const size_t ob = (size_t)slice * m * D;
-    for (int i = threadIdx.x; i < m * CH; i += NW * kWave) {
-      const int a = i / CH, ch = i - a * CH;
-      const size_t src = kb + (size_t)token(a) * D + 8 * ch;
-      const u32x4 vq = *(const u32x4*)(Q + src), vk = *(const u32x4*)(K + src);
-      *(u32x4*)(qt + ob + (size_t)a * D + 8 * ch) = vq;
-      *(u32x4*)(kt + ob + (size_t)a * D + 8 * ch) = vk;
+// F3 V (unnormalised) and F3's row sums from the chunk partials: chunk c's weights are
+// relative to its own maxima M_c (cmax), so each chunk is scaled by exp(c (M_c - M)) with M
+// the landmark's overall maximum, and the chunks are added in chunk order.  Partial
+// element f of a chunk: tile f / 256 = (jt, dt), slot r * 64 + l, i.e. landmark
+// 16 jt + 4 (l / 16) + r, dim 16 dt + l % 16.  Results go to Mx[a * LD + MPAD + k] and
+// zl[a].  T threads; Ml and facl are LDS scratch (MPAD and 2 x MPAD floats).
+template <int D, int AT, int T, int LD>
+__device__ __forceinline__ void nys_rhs(const float* __restrict__ part,
+                                        const float* __restrict__ dpart,
+                                        const float* __restrict__ cmax, int slice, int chunks,
+                                        int m, float c2, int tid, float* Mx, float* zl,
+                                        float* Ml, float (*facl)[16 * AT]) {
+  constexpr int MPAD = 16 * AT, DT = D / 16, EPT = (MPAD * D + T - 1) / T;
+  const float* cm = cmax + (size_t)slice * chunks * MPAD;
+  if (tid < MPAD) {
+    float M = -INFINITY;
+    for (int ch = 0; ch < chunks; ++ch) M = fmaxf(M, cm[(size_t)ch * MPAD + tid]);
+    Ml[tid] = M;
+  }
+  float acc[EPT], z = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
+  for (int ch = 0; ch < chunks; ++ch) {
+    const size_t sc = (size_t)slice * chunks + ch;
+    const float* src = part + sc * MPAD * D;
+    float v[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int f = tid + e * T;
+      v[e] = (f < MPAD * D) ? src[f] : 0.f;
+    }
+    const float dz = (tid < MPAD) ? dpart[sc * MPAD + tid] : 0.f;
+    const float cmv = (tid < MPAD) ? cm[(size_t)ch * MPAD + tid] : 0.f;
+    __syncthreads();   // Ml written; the previous use of this facl buffer is over
+    if (tid < MPAD) facl[ch & 1][tid] = (tid < m) ? exp2_fast((cmv - Ml[tid]) * c2) : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int f = tid + e * T, slot = f & 255, l = slot & 63;
+      const int a = 16 * ((f >> 8) / DT) + 4 * (l >> 4) + (slot >> 6);
+      if (f < MPAD * D) acc[e] = fmaf(facl[ch & 1][a], v[e], acc[e]);
+    }
+    if (tid < MPAD) z = fmaf(facl[ch & 1][tid], dz, z);
+  }
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int f = tid + e * T;
+    if (f < MPAD * D) {
+      const int tile = f >> 8, slot = f & 255, jt = tile / DT, dt = tile - jt * DT;
+      const int l = slot & 63, a = 16 * jt + 4 * (l >> 4) + (slot >> 6), k = 16 * dt + (l & 15);
+      Mx[a * LD + MPAD + k] = acc[e];
     }
   }
-  u32x4 kr[KS];
-  load_rows<D>(K, kb, kw.st, t_begin + 16 * w + c, n, g, kr);
-  stage_store(ust, &u_lds[0][0][0]);
-  __syncthreads();
-
-  float mx[AT][4];
-#pragma unroll
-  for (int j = 0; j < AT; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mx[j][r] = -INFINITY;
-  for (int t0 = t_begin + 16 * w; t0 < t_end; t0 += 16 * NW) {
-    u32x4 kn[KS];
-    load_rows<D>(K, kb, kw.st, t0 + 16 * NW + c, n, g, kn);   // rows clamped to the slice
-    const bool ok = t0 + c < t_end;
-#pragma unroll
-    for (int j = 0; j < AT; ++j) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(kr[kk]), acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx[j][r] = ok ? fmaxf(mx[j][r], acc[r]) : mx[j][r];
-    }
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) kr[kk] = kn[kk];
-  }
-  // lane (c, g) holds landmarks 16j + 4g + r over its tokens; reduce over the 16 lanes c
-#pragma unroll
-  for (int j = 0; j < AT; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = row16_max(mx[j][r]);
-      if (c == 0) red[w][16 * j + 4 * g + r] = v;
-    }
-  __syncthreads();
-  if ((int)threadIdx.x < 16 * AT) {
-    float M = red[0][threadIdx.x];
-#pragma unroll
-    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, red[ww][threadIdx.x]);
-    cmax[((size_t)slice * chunks + chunk) * 16 * AT + threadIdx.x] = M;
-  }
+  if (tid < MPAD) zl[tid] = z;
 }
 
 // Per slice: F3 V from the chunk partials, F2 from the landmark rows, Z = F2^-1 (F3 V) by
@@ -129,9 +133,11 @@ constexpr int nys_solve_waves() { return (16 * AT + D) / nys_solve_cw<D, AT>(); 
 template <int D, int AT>
 __global__ __launch_bounds__((nys_solve_waves<D, AT>() * kWave), 1)
 void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
-               const __bf16* __restrict__ qt, const __bf16* __restrict__ kt,
-               __bf16* __restrict__ Wop, int m, int chunks, float c2) {
-  constexpr int MPAD = 16 * AT, DT = D / 16, MP = AT / 2, NC = MPAD + D, LD = NC + 1;
+               const float* __restrict__ cmax, const __bf16* __restrict__ Q,
+               const __bf16* __restrict__ K, View vw, const int* __restrict__ idx,
+               __bf16* __restrict__ kt, __bf16* __restrict__ Wop, int h, int n, int m,
+               int chunks, float c2) {
+  constexpr int MPAD = 16 * AT, MP = AT / 2, NC = MPAD + D, LD = NC + 1;
   constexpr int NG = nys_solve_waves<D, AT>(), T = NG * kWave, RPL = (MPAD + 63) / 64;
   constexpr int CW = nys_solve_cw<D, AT>();
   static_assert(MPAD % CW == 0 && D % CW == 0, "column groups of CW");
@@ -148,57 +154,9 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
   __shared__ int pbuf[2];
   __shared__ float pvbuf[2];
 
-  // landmark rows (rows >= m zero)
-  {
-    const u32x4* qs = (const u32x4*)(qt + (size_t)slice * m * D);
-    const u32x4* ks = (const u32x4*)(kt + (size_t)slice * m * D);
-    Stage<MPAD * D / 8, T> qst, kst;
-    stage_load(qst, [&](int i) { return (i < m * D / 8) ? qs[i] : u32x4{0u, 0u, 0u, 0u}; });
-    stage_load(kst, [&](int i) { return (i < m * D / 8) ? ks[i] : u32x4{0u, 0u, 0u, 0u}; });
-#pragma unroll
-    for (int i = 0; i < Stage<MPAD * D / 8, T>::kPer; ++i) {
-      const int c = tid + i * T;
-      if ((MPAD * D / 8) % T == 0 || c < MPAD * D / 8) {
-        const int a = c / (D / 8), k8 = c - a * (D / 8);
-        *(u32x4*)(ql + a * RS + 8 * k8) = qst.r[i];
-        *(u32x4*)(kl + a * RS + 8 * k8) = kst.r[i];
-      }
-    }
-  }
-  // chunk sums in chunk order into the right-hand side columns (element f of a chunk's
-  // partial block: tile f / 256 = (jt, dt), slot r * 64 + l); every load of a chunk is in
-  // flight at once
-  {
-    constexpr int EPT = (MPAD * D + T - 1) / T;
-    float acc[EPT], z = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
-#pragma unroll 2
-    for (int ch = 0; ch < chunks; ++ch) {
-      const size_t sc = (size_t)slice * chunks + ch;
-      const float* src = part + sc * MPAD * D;
-      float v[EPT];
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const int f = tid + e * T;
-        v[e] = (f < MPAD * D) ? src[f] : 0.f;
-      }
-      const float dz = (tid < MPAD) ? dpart[sc * MPAD + tid] : 0.f;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) acc[e] += v[e];
-      z += dz;
-    }
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int f = tid + e * T;
-      if (f < MPAD * D) {
-        const int tile = f >> 8, slot = f & 255, jt = tile / DT, dt = tile - jt * DT;
-        const int l = slot & 63, a = 16 * jt + 4 * (l >> 4) + (slot >> 6), k = 16 * dt + (l & 15);
-        Mx[a * LD + MPAD + k] = acc[e];
-      }
-    }
-    if (tid < MPAD) zl[tid] = z;
-  }
+  __shared__ float Ml[MPAD], facl[2][MPAD];
+  nys_landmark_rows<D, MPAD, T, RS>(Q, K, vw, idx, slice, h, n, m, tid, ql, kl, kt);
+  nys_rhs<D, AT, T, LD>(part, dpart, cmax, slice, chunks, m, c2, tid, Mx, zl, Ml, facl);
   // F2 logits (fp32 sums of the bf16 products), identity rows and zero columns for padding
   for (int e = tid; e < MPAD * MPAD; e += T) {
     const int a = e / MPAD, l = e - a * MPAD;
@@ -341,30 +299,206 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
   }
 }
 
+// The same solve for up to 32 landmarks in one wave per slice, with no workgroup barrier:
+// the elimination's per-step exchange (pivot search, pivot row, multipliers) stays inside
+// the wave.  Lane l holds row l % MPAD of the augmented matrix [F2 | F3 V] and the CPL
+// consecutive columns of group l / MPAD (MPAD = 16 or 32: four or two groups).
+//   set-up: landmark rows of Q and K into LDS; F2's logits on the MFMA (fp32 sums of the
+//           bf16 products); F3 V from the chunk partials in chunk order; the row softmax
+//           of F2 one row per lane; the matrix into the lanes' registers;
+//   step k: the wave's largest |x[k]| among unused rows of the group holding column k
+//           (smallest row on ties), the pivot row published through LDS by its lanes and
+//           read back by every lane of the same group, the lane's own column-k value from
+//           the lane holding it, and x -= (x[k] / pivot) * pivot row on every row but the
+//           pivot's.  Unknown k is the pivot row's right-hand side over its pivot.
+template <int D, int AT>
+__global__ __launch_bounds__(kWave)
+void nys_solve1(const float* __restrict__ part, const float* __restrict__ dpart,
+                const float* __restrict__ cmax, const __bf16* __restrict__ Q,
+                const __bf16* __restrict__ K, View vw, const int* __restrict__ idx,
+                __bf16* __restrict__ kt, __bf16* __restrict__ Wop, int h, int n, int m,
+                int chunks, float c2) {
+  constexpr int MPAD = 16 * AT, NC = MPAD + D, G = kWave / MPAD, CPL = NC / G;
+  constexpr int KS = D / 32, MP = AT / 2, LD = NC + 1, RS = D + 8;
+  static_assert(MPAD <= 32 && NC % G == 0 && CPL % 4 == 0, "one wave, whole column groups");
+  const int slice = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int c = lane & 15, g = lane >> 4;
+  const int row = lane % MPAD, grp = lane / MPAD;
+  __shared__ float Mx[MPAD * LD];
+  __shared__ __attribute__((aligned(16))) __bf16 ql[MPAD * RS], kl[MPAD * RS];
+  __shared__ float zl[MPAD];
+  __shared__ __attribute__((aligned(16))) float prow[2][G][CPL];   // by step parity
+  __shared__ float Ml[MPAD], facl[2][MPAD];
+  nys_landmark_rows<D, MPAD, kWave, RS>(Q, K, vw, idx, slice, h, n, m, lane, ql, kl, kt);
+  nys_rhs<D, AT, kWave, LD>(part, dpart, cmax, slice, chunks, m, c2, lane, Mx, zl, Ml, facl);
+  __syncthreads();   // one wave: orders the LDS writes above before the reads below
+  // F2 logits q_a . k_l on the MFMA: tile (ti, tj), lane (c,g) ends with a = 16ti + 4g + r,
+  // l = 16tj + c; padded rows become identity rows, padded columns zero
+#pragma unroll
+  for (int ti = 0; ti < AT; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < AT; ++tj) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const bf16x8 x = as_bf16x8(*(const u32x4*)(ql + (16 * ti + c) * RS + 8 * KS * g + 8 * kk));
+        const bf16x8 y = as_bf16x8(*(const u32x4*)(kl + (16 * tj + c) * RS + 8 * KS * g + 8 * kk));
+        acc = mfma_bf16(x, y, acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int a = 16 * ti + 4 * g + r, l = 16 * tj + c;
+        Mx[a * LD + l] = (a < m && l < m) ? acc[r] : ((a == l) ? 1.f : 0.f);
+      }
+    }
+  __syncthreads();
+  // row softmax of F2 over the m landmark keys (lane a: row a), F3 V = P / z; rows of
+  // padded landmarks keep their identity row and a zero right-hand side
+  if (lane < m) {
+    float* rw = Mx + lane * LD;
+    float mx = -INFINITY;
+    for (int l = 0; l < m; ++l) mx = fmaxf(mx, rw[l]);
+    float z = 0.f;
+    for (int l = 0; l < m; ++l) {
+      const float e = exp2_fast((rw[l] - mx) * c2);
+      rw[l] = e;
+      z += e;
+    }
+    const float iz = 1.f / z;
+    for (int l = 0; l < m; ++l) rw[l] *= iz;
+    const float izl = 1.f / zl[lane];   // z >= 1: each landmark's largest weight is exp(0)
+    for (int k = 0; k < D; ++k) rw[MPAD + k] *= izl;
+  } else if (lane < MPAD) {
+    float* rw = Mx + lane * LD;
+    for (int k = 0; k < D; ++k) rw[MPAD + k] = 0.f;
+  }
+  __syncthreads();
+
+  float x[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) x[j] = Mx[row * LD + grp * CPL + j];
+  bool used = false;
+  int var = 0;
+  float pvr = 1.f;
+  // Step k's elimination (multiplier f for this lane's row, pivot row pr) is applied at
+  // the start of step k + 1: first to column k + 1 alone, whose pivot-row value prk comes
+  // by readlane, so that step k + 1's pivot search can start at once; then to the other
+  // columns with the pivot row read back from LDS a whole step earlier.
+  float fprev = 0.f, prk = 0.f;
+  f32x4 pr[CPL / 4];
+#pragma unroll
+  for (int j = 0; j < CPL / 4; ++j) pr[j] = zero4();
+  // fully unrolled, so that column k is a fixed register in every step
+#pragma clang loop unroll(full)
+  for (int k = 0; k < MPAD; ++k) {
+    const int gk = k / CPL, kr = k % CPL;   // column k: register kr of group gk
+    if (grp == gk) x[kr] = fmaf(-fprev, prk, x[kr]);
+    const bool cand = grp == gk && !used;
+    const float v = cand ? fabsf(x[kr]) : -1.f;
+    // maximum over the MPAD lanes of each group (other groups' lanes hold -1)
+    float best = row16_max(v);
+    if constexpr (MPAD >= 32) best = xor16_max(best);
+    // no candidate equals the maximum only when the column holds NaN: then the first
+    // unused row (the output is non-finite, and every unknown still gets its row)
+    const unsigned long long bal = __ballot(cand && v == best);
+    const unsigned long long any = __ballot(cand);
+    const int lp = (int)__builtin_ctzll(bal ? bal : any);
+    const int p = lp - gk * MPAD;
+    const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[kr]), lp));
+    // this lane's row in column k, from the lane of group gk that holds it
+    float xk;
+    if constexpr (G == 2) {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[kr]), __float_as_uint(x[kr]), false, false);
+      xk = grp == gk ? x[kr] : __uint_as_float(sw[0]);
+    } else {
+      xk = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (row + gk * MPAD), __float_as_int(x[kr])));
+    }
+    float ipv = __builtin_amdgcn_rcpf(pv);
+    ipv = ipv * fmaf(-pv, ipv, 2.f);   // one Newton step
+    const bool piv = row == p;
+    const float f = piv ? 0.f : xk * ipv;
+    if (piv) {   // every column group's copy of the pivot row
+      used = true;
+      var = k;
+      pvr = pv;
+    }
+    // step k - 1 on the remaining columns
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+      if (j != kr) x[j] = fmaf(-fprev, pr[j / 4][j % 4], x[j]);
+    if (grp != gk) x[kr] = fmaf(-fprev, pr[kr / 4][kr % 4], x[kr]);
+    // step k's pivot row (complete through step k - 1), one copy per column group; the
+    // barrier (one wave: a wait and a compiler fence) makes the pivot lanes' writes
+    // visible to the other lanes, and with the two buffers also orders the previous
+    // step's reads before the next writes (measured: as fast as fetching the row with
+    // ds_bpermute, and either exchange takes over half of the step)
+    const int b = k & 1;
+    if (piv) {
+#pragma unroll
+      for (int j = 0; j < CPL; j += 4)
+        *(f32x4*)&prow[b][grp][j] = f32x4{x[j], x[j + 1], x[j + 2], x[j + 3]};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < CPL; j += 4) pr[j / 4] = *(const f32x4*)&prow[b][grp][j];
+    if (k + 1 < MPAD) {
+      const int gk1 = (k + 1) / CPL, kr1 = (k + 1) % CPL;
+      prk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[kr1]), lp + (gk1 - gk) * MPAD));
+    }
+    fprev = f;
+  }
+  // the last step on every column
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) x[j] = fmaf(-fprev, pr[j / 4][j % 4], x[j]);
+  // Z[var][k] = right-hand side over the pivot: through LDS (row var of Mx), then out as
+  // pass 2's W operands in 16-byte pieces
+  const float ipr = (var < m) ? 1.f / pvr : 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int col = grp * CPL + j;
+    if (col >= MPAD) Mx[var * LD + col] = x[j] * ipr;
+  }
+  __syncthreads();
+  u32x4* dst = (u32x4*)(Wop + (size_t)slice * MPAD * D);
+#pragma unroll
+  for (int i = 0; i < MPAD * D / (8 * kWave); ++i) {
+    // piece q = lane + 64 i of [dt2][jj][lane'][8]: lane' (c', g') holds dim
+    // out_dim_c(dt2, c') and anchors 32jj + 4g' + s (s < 4), 32jj + 16 + 4g' + s - 4
+    const int q = lane + kWave * i, lq = q & 63, jj = (q >> 6) % MP, dt2 = (q >> 6) / MP;
+    const int k = out_dim_c(dt2, lq & 15), a0 = 32 * jj + 4 * (lq >> 4);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = Mx[(a0 + (e < 4 ? e : 12 + e)) * LD + MPAD + k];
+    dst[q] = as_u32x4(pack_bf16(f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]}));
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 template <int D, int AT>
-static void launch_nys_kernels_t(const Geometry& g, const SplitPlan& p, const NystromBuffers& nb,
-                                 const void* Q, const void* K, const int* idx, hipStream_t s,
-                                 bool solve) {
-  if (!solve) {
-    nys_max<D, AT><<<dim3((unsigned)(g.slices * p.chunks1)), dim3(256), 0, s>>>(
-        (const __bf16*)Q, (const __bf16*)K, idx, nb.qt, nb.kt, nb.cmax, g.vw.q, g.h, g.n, g.m,
-        p.chunks1, p.chunk_len1);
+static void launch_nys_solve_t(const Geometry& g, const SplitPlan& p, const NystromBuffers& nb,
+                               const void* Q, const void* K, const int* idx, hipStream_t s) {
+  if constexpr (16 * AT <= 32) {
+    // one wave per slice up to 32 landmarks (at 64, with 64 dependent steps over 128
+    // columns per lane, the ViT-B/16-shape step took 153 us with it against 122 us)
+    nys_solve1<D, AT><<<dim3((unsigned)g.slices), dim3(kWave), 0, s>>>(
+        nb.part, nb.dpart, nb.cmax, (const __bf16*)Q, (const __bf16*)K, g.vw.q, idx, nb.kt,
+        nb.wop, g.h, g.n, g.m, p.chunks1, g.c2);
   } else {
     nys_solve<D, AT><<<dim3((unsigned)g.slices), dim3(nys_solve_waves<D, AT>() * kWave), 0, s>>>(
-        nb.part, nb.dpart, nb.qt, nb.kt, nb.wop, g.m, p.chunks1, g.c2);
+        nb.part, nb.dpart, nb.cmax, (const __bf16*)Q, (const __bf16*)K, g.vw.q, idx, nb.kt,
+        nb.wop, g.h, g.n, g.m, p.chunks1, g.c2);
   }
 }
 
 template <int D>
-static hipError_t launch_nys_t(const Geometry& g, const SplitPlan& p, const NystromBuffers& nb,
-                               const void* Q, const void* K, const int* idx, hipStream_t s,
-                               bool solve) {
+static hipError_t launch_nys_solve(const Geometry& g, const SplitPlan& p, const NystromBuffers& nb,
+                                   const void* Q, const void* K, const int* idx, hipStream_t s) {
   switch (g.at) {
-    case 2: launch_nys_kernels_t<D, 2>(g, p, nb, Q, K, idx, s, solve); break;
-    case 4: launch_nys_kernels_t<D, 4>(g, p, nb, Q, K, idx, s, solve); break;
-    case 6: launch_nys_kernels_t<D, 6>(g, p, nb, Q, K, idx, s, solve); break;
-    case 8: launch_nys_kernels_t<D, 8>(g, p, nb, Q, K, idx, s, solve); break;
+    case 2: launch_nys_solve_t<D, 2>(g, p, nb, Q, K, idx, s); break;
+    case 4: launch_nys_solve_t<D, 4>(g, p, nb, Q, K, idx, s); break;
+    case 6: launch_nys_solve_t<D, 6>(g, p, nb, Q, K, idx, s); break;
+    case 8: launch_nys_solve_t<D, 8>(g, p, nb, Q, K, idx, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -374,16 +508,12 @@ hipError_t launch_nystrom_bf16(const Geometry& g, const SplitPlan& p, const void
                                const void* V, const int* idx, void* H, const NystromBuffers& nb,
                                hipStream_t stream) {
   if (g.d != 32 && g.d != 64) return hipErrorInvalidValue;
-  auto step = [&](bool solve) {
-    return g.d == 64 ? launch_nys_t<64>(g, p, nb, Q, K, idx, stream, solve)
-                     : launch_nys_t<32>(g, p, nb, Q, K, idx, stream, solve);
-  };
-  hipError_t e;
-  if ((e = step(false)) != hipSuccess) return e;
-  e = launch_nystrom_pass1_bf16(g, p, K, g.vw.q, nb.qt, V, g.vw.v, nb.part, nb.dpart, nb.cmax,
-                                stream);
+  hipError_t e = launch_nystrom_pass1_bf16(g, p, K, g.vw.q, Q, g.vw.q, idx, V, g.vw.v, nb.part,
+                                           nb.dpart, nb.cmax, stream);
   if (e != hipSuccess) return e;
-  if ((e = step(true)) != hipSuccess) return e;
+  e = g.d == 64 ? launch_nys_solve<64>(g, p, nb, Q, K, idx, stream)
+                : launch_nys_solve<32>(g, p, nb, Q, K, idx, stream);
+  if (e != hipSuccess) return e;
   return launch_nystrom_pass2_bf16(g, p, Q, g.vw.q, nb.kt, nb.wop, H, g.vw.o, stream);
 }
 

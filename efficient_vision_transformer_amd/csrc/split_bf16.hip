@@ -224,16 +224,19 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 // contraction axis) from the row copies with the transposing LDS read.  Partials leave in
 // accumulator layout with dim tile dt holding dims 16dt .. 16dt + 15.
 //
-// NYS (Nystrom attention, landmark pass): U holds per-slice landmark query rows, Q the
-// keys, and the weights are exp(c q.k - c M) with M the landmark's maximum over all tokens
-// (from the per-chunk maxima in cmax) instead of a softmax over anchors; phase B then
-// accumulates F3 V and the row sums of F3 unnormalised.
+// NYS (Nystrom attention, landmark pass): the anchors are the slice's landmark query rows,
+// gathered from U (the queries, view uw) through the landmark indices lidx ([B][m]); Q
+// holds the keys; and the weights are exp(c q.k - c M_a) with M_a landmark a's largest
+// logit over this chunk's tokens (a first sweep over the chunk finds it, and it is written
+// to cmax for the solve, which rescales the chunks to the overall maximum) instead of a
+// softmax over anchors; phase B then accumulates F3 V and the row sums of F3 unnormalised.
 template <int D, int MP, int NW, bool NYS = false>
 __global__ __launch_bounds__(NW * kWave, 2)
 void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                  const __bf16* __restrict__ V, float* __restrict__ part,
                  float* __restrict__ dpart, View qw, View xw, int h, int n, int m, int chunks,
-                 int chunk_len, float c2, const float* __restrict__ cmax = nullptr) {
+                 int chunk_len, float c2, float* __restrict__ cmax = nullptr,
+                 const int* __restrict__ lidx = nullptr, View uw = View{0, 0, 0}) {
   constexpr int KS = D / 32, DT = D / 16, AT = 2 * MP;
   constexpr int TILES = AT * DT, TPW = (TILES + NW - 1) / NW;
   constexpr int NDA = (TPW + DT - 1) / DT;   // anchor tiles per wave needing a Delta
@@ -258,49 +261,94 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   constexpr int UCH = AT * KS * kWave;
   constexpr int UPT = (UCH + NW * kWave - 1) / (NW * kWave);
   u32x4 ust[UPT];
-  const __bf16* Uh = U + (size_t)(NYS ? slice : head) * m * D;
+  // anchor a's row: U[head][a] (NYS: the query row of landmark token lidx[b][a])
+  auto urow = [&](int a) -> const __bf16* {
+    if constexpr (NYS) {
+      const int tok = min(max(lidx[(size_t)(slice / h) * m + a], 0), n - 1);
+      return U + view_base(uw, slice, h) + (size_t)((long long)tok * uw.st);
+    } else {
+      return U + ((size_t)head * m + a) * D;
+    }
+  };
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     const int idx = threadIdx.x + i * NW * kWave;
     if (idx < UCH) {
       const int j = idx / (KS * kWave), kk = (idx / kWave) % KS, l = idx & 63;
       const int a = min(16 * j + (l & 15), m - 1);   // padded anchors are masked
-      ust[i] = *(const u32x4*)(Uh + (size_t)a * D + 8 * KS * (l >> 4) + 8 * kk);
+      ust[i] = *(const u32x4*)(urow(a) + 8 * KS * (l >> 4) + 8 * kk);
     }
   }
-  u32x4 qc[2][KS], vc[2][KS];
+  // Rows of the wave's pair in each round; rows past the chunk read its last row (their
+  // weights are zeroed), so every load is unconditional and the waits are exact counts.
+  // Two register sets alternate between rounds: the next round's rows are requested at
+  // the start of a round and first waited for at the start of the next one.
+  auto load_pair = [&](int p, u32x4 (*qv)[KS], u32x4 (*vv)[KS]) {
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    load_rows<D>(Q, qb, qw.st, t_begin + 32 * w + 16 * tt + c, n, g, qc[tt]);
-    load_rows<D>(V, xb, xw.st, t_begin + 32 * w + 16 * tt + c, n, g, vc[tt]);
-  }
+    for (int tt = 0; tt < 2; ++tt) {
+      const int row = min(t_begin + 32 * p + 16 * tt + c, t_end - 1);
+      load_rows<D>(Q, qb, qw.st, row, n, g, qv[tt]);
+      load_rows<D>(V, xb, xw.st, row, n, g, vv[tt]);
+    }
+  };
+  u32x4 qa[2][KS], va[2][KS], qz[2][KS], vz[2][KS];
+  load_pair(w, qa, va);
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     const int idx = threadIdx.x + i * NW * kWave;
     if (idx < UCH) (&u_lds[0][0][0])[idx] = ust[i];
   }
-  // NYS: mneg[a] = -c2 * (landmark a's maximum over the chunks' maxima), 0 for padding
-  __shared__ __attribute__((aligned(16))) float mneg[NYS ? 16 * AT : 4];
-  if constexpr (NYS) {
-    static_assert(16 * AT <= NW * kWave, "one landmark per thread");
-    const int a = threadIdx.x;
-    if (a < 16 * AT) {
-      const float* src = cmax + (size_t)slice * chunks * 16 * AT + a;
-      float M = -INFINITY;
-      for (int ch0 = 0; ch0 < chunks; ch0 += 8) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = src[(size_t)min(ch0 + u, chunks - 1) * 16 * AT];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) M = fmaxf(M, v[u]);
-      }
-      mneg[a] = (a < m) ? -M * c2 : 0.f;
-    }
-  }
   const bf16x8 ones = splat_bf16(1.f);
   f32x4 mask[2];
   pad_mask<MP>(g, m, mask);
+  // NYS: mneg[a] = -c2 * (landmark a's largest logit over this chunk's tokens), 0 for
+  // padding; the logits are formed exactly as tile_exp forms them below, so no exponent
+  // there is positive
+  __shared__ __attribute__((aligned(16))) float mneg[NYS ? 16 * AT : 4];
+  __shared__ float cred[NYS ? NW : 1][NYS ? 16 * AT : 1];
   __syncthreads();
+  if constexpr (NYS) {
+    static_assert(16 * AT <= NW * kWave, "one landmark per thread");
+    f32x4 mx[AT];
+#pragma unroll
+    for (int j = 0; j < AT; ++j) mx[j] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    for (int p = w; p < npairs; p += NW) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int row = t_begin + 32 * p + 16 * tt + c;
+        u32x4 kr[KS];
+        load_rows<D>(Q, qb, qw.st, min(row, t_end - 1), n, g, kr);
+        const bool ok = row < t_end;
+#pragma unroll
+        for (int j = 0; j < AT; ++j) {
+          f32x4 acc = (j >= AT - 2) ? mask[j - (AT - 2)] : zero4();
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(kr[kk]), acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx[j][r] = ok ? fmaxf(mx[j][r], acc[r]) : mx[j][r];
+        }
+      }
+    }
+    // lane (c, g) holds landmarks 16j + 4g + r over its tokens: reduce over the lanes c,
+    // then over the waves
+#pragma unroll
+    for (int j = 0; j < AT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = row16_max(mx[j][r]);
+        if (c == 0) cred[w][16 * j + 4 * g + r] = v;
+      }
+    __syncthreads();
+    const int a = threadIdx.x;
+    if (a < 16 * AT) {
+      float M = cred[0][a];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, cred[ww][a]);
+      mneg[a] = (a < m) ? -M * c2 : 0.f;
+      cmax[((size_t)slice * chunks + chunk) * 16 * AT + a] = M;
+    }
+    __syncthreads();
+  }
 
   // Wave w owns the contiguous tiles w*TPW .. w*TPW + TPW - 1 (tile t: anchor tile t / DT,
   // dim tile t % DT); the Delta of anchor tile ja is accumulated with its dim tile 0.
@@ -311,18 +359,10 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   for (int k = 0; k < NDA; ++k) dacc[k] = zero4();
 
   const int rounds = (npairs + NW - 1) / NW;
-  for (int r = 0; r < rounds; ++r) {
+  auto round = [&](int r, u32x4 (*qc)[KS], u32x4 (*vc)[KS], u32x4 (*qn)[KS], u32x4 (*vn)[KS]) {
     const int pairs_here = min(NW, npairs - r * NW);  // uniform over the workgroup
     const int p = r * NW + w;
-    const bool more = p + NW < npairs;
-    u32x4 qn[2][KS], vn[2][KS];
-    if (more) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        load_rows<D>(Q, qb, qw.st, t_begin + 32 * (p + NW) + 16 * tt + c, n, g, qn[tt]);
-        load_rows<D>(V, xb, xw.st, t_begin + 32 * (p + NW) + 16 * tt + c, n, g, vn[tt]);
-      }
-    }
+    load_pair(p + NW, qn, vn);
     // Phase A: rows 32w .. 32w + 31 of the round's LDS blocks hold this wave's pair.
     if (p < npairs) {
 #pragma unroll
@@ -349,12 +389,10 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     __syncthreads();
     accumulate_tiles<TPW, DT, AS, VS>(a_lds, v_lds, w * TPW, pairs_here, c, g, ones, pacc, dacc);
     __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) { qc[tt][kk] = qn[tt][kk]; vc[tt][kk] = vn[tt][kk]; }
-    }
+  };
+  for (int r = 0; r < rounds; r += 2) {
+    round(r, qa, va, qz, vz);
+    if (r + 1 < rounds) round(r + 1, qz, vz, qa, va);
   }
 
   // Partials: [slice][chunk][jt][dt][r][lane] holds P[16jt + 4g + r][16dt + c];
@@ -645,19 +683,20 @@ hipError_t launch_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* 
 }
 
 // Nystrom attention: pass 1 in landmark mode (the keys K streamed as the tokens, the
-// per-slice landmark query rows qt as the anchors, cmax the per-chunk landmark maxima) and
-// pass 2 with the per-slice landmark key rows kt as the anchors.
+// landmark query rows gathered from Q through idx as the anchors, the per-chunk landmark
+// maxima written to cmax) and pass 2 with the per-slice landmark key rows kt as the
+// anchors.
 hipError_t launch_nystrom_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* K,
-                                     const View& kw, const void* qt, const void* V,
-                                     const View& vw, float* part, float* dpart,
-                                     const float* cmax, hipStream_t s) {
+                                     const View& kw, const void* Q, const View& qw,
+                                     const int* idx, const void* V, const View& vw, float* part,
+                                     float* dpart, float* cmax, hipStream_t s) {
   const long long g1 = g.slices * p.chunks1;
   auto at = [&](auto D) -> hipError_t {
     constexpr int d = decltype(D)::value;
 #define AA_NYS1(MP)                                                                          \
   pass1x_bf16<d, MP, kPass1Waves, true><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, s>>>( \
-      (const __bf16*)K, (const __bf16*)qt, (const __bf16*)V, part, dpart, kw, vw, g.h, g.n, g.m, \
-      p.chunks1, p.chunk_len1, g.c2, cmax)
+      (const __bf16*)K, (const __bf16*)Q, (const __bf16*)V, part, dpart, kw, vw, g.h, g.n, g.m, \
+      p.chunks1, p.chunk_len1, g.c2, cmax, idx, qw)
     switch (g.at) {
       case 2: AA_NYS1(1); break;
       case 4: AA_NYS1(2); break;

@@ -153,10 +153,6 @@ def test_backward_empty_inputs(ctx, dev):
 def test_backward_rejects_what_it_cannot_run(ctxs, dev):
     import torch
     ctx = ctxs["auto"]
-    x = random_case(7200, 1, 1, 40, 16, 32, "fp32")
-    Q, U, V = to_device(x, dev)
-    with pytest.raises(RuntimeError, match="status 2"):
-        ctx.backward(Q, U, V, V.clone())
     Qb = torch.zeros((1, 1, 40, 32), dtype=torch.bfloat16, device=dev)
     Ub = torch.zeros((1, 257, 32), dtype=torch.bfloat16, device=dev)
     with pytest.raises(RuntimeError, match="status 2"):

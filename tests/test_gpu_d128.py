@@ -143,9 +143,10 @@ def test_d128_strided_views_match_contiguous(ctxs, dev):
 
 
 def test_d128_refusals(ctxs, dev):
-    """d = 128 runs only the bf16 forward: the fused plan beyond its limits (here 300 tokens
-    with 16 anchors), fp32, the backward, the linear attention and Nystrom attention refuse
-    it (NOT_SUPPORTED)."""
+    """d = 128 runs the bf16 forward and the bf16 backward (up to 128 anchors): the fused
+    plan beyond its limits (here 300 tokens with 16 anchors), fp32, the fp32 backward, the
+    bf16 backward above 128 anchors, the linear attention and Nystrom attention refuse it
+    (NOT_SUPPORTED)."""
     import torch
     x = random_case(78, 1, 2, 300, 16, 128, dtype="bf16")
     Q, U, V = to_device(x, dev)
@@ -154,7 +155,10 @@ def test_d128_refusals(ctxs, dev):
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
         ctxs["auto"].forward(Q.float(), U.float(), V.float())
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
-        ctxs["auto"].backward(Q, U, V, torch.ones_like(Q))
+        ctxs["auto"].backward(Q.float(), U.float(), V.float(), torch.ones_like(Q.float()))
+    U129 = torch.zeros((2, 129, 128), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
+        ctxs["auto"].backward(Q, U129, V, torch.ones_like(Q))
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
         ctxs["auto"].relu_linear(Q, Q, V)
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
