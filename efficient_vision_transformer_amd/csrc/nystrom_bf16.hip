@@ -27,6 +27,21 @@
 
 namespace aa {
 
+// A double from lane `lane` of the wave (two 32-bit lane reads), and a double's halves
+// swapped between lanes l and l ^ 32.
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, lane);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ double swap32_f64(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)b, (unsigned)b, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(b >> 32), (unsigned)(b >> 32), false, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi[0] << 32) | lo[0]));
+}
+
 // Landmark rows of Q and K for one slice into LDS (row stride RS, rows >= m zero), the
 // key rows also to kt ([slice][m][d], pass 2's anchors).  T threads; Q and K contiguous
 // [B, h, n, d] (view vw); indices clamped to [0, n).
@@ -150,9 +165,9 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
   constexpr int RS = D + 8;
   __shared__ __attribute__((aligned(16))) __bf16 ql[MPAD * RS], kl[MPAD * RS];
   __shared__ float zl[MPAD];
-  __shared__ float fbuf[2][MPAD];
+  __shared__ double fbuf[2][MPAD];
   __shared__ int pbuf[2];
-  __shared__ float pvbuf[2];
+  __shared__ double pvbuf[2];
 
   __shared__ float Ml[MPAD], facl[2][MPAD];
   nys_landmark_rows<D, MPAD, T, RS>(Q, K, vw, idx, slice, h, n, m, tid, ql, kl, kt);
@@ -207,7 +222,10 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
   }
   __syncthreads();
 
-  float x[RPL][CW];
+  // the elimination in fp64: with a sink token among the landmarks F2's condition number
+  // reaches 1e14, beyond what fp32 can invert, while H (in which Z's huge components
+  // cancel) stays well defined
+  double x[RPL][CW];
   bool used[RPL];
   int var[RPL];
 #pragma unroll
@@ -216,21 +234,21 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
     used[i] = r >= MPAD;   // lanes past the padded system never pivot
     var[i] = 0;
 #pragma unroll
-    for (int jj = 0; jj < CW; ++jj) x[i][jj] = (r < MPAD) ? Mx[r * LD + CW * w + jj] : 0.f;
+    for (int jj = 0; jj < CW; ++jj) x[i][jj] = (r < MPAD) ? (double)Mx[r * LD + CW * w + jj] : 0.0;
   }
 
   // Step col: the wave owning column col picks the pivot among the unused rows (largest
-  // |value|, smallest row on ties: wave maximum with DPP and permlane swaps, the row from a
-  // ballot) and publishes the column, the pivot row and its value through LDS; after one
-  // barrier every wave still holding columns >= col takes the pivot row from that lane of
-  // its own registers (readlane) and subtracts (x_r[col] / pivot) times it from every other
-  // row.  The pivot row is left unscaled (its own factor is zero); unknown col is its
-  // right-hand side over the pivot, divided out at the end.  Steps run in groups of CW
-  // (the column group W, uniform), unrolled within a group so that register indices are
-  // static.
-  float pvr[RPL];
+  // |value| as a float, smallest row on ties: wave maximum with DPP and permlane swaps, the
+  // row from a ballot; a column holding NaN takes its first unused row) and publishes the
+  // column, the pivot row and its value through LDS; after one barrier every wave still
+  // holding columns >= col takes the pivot row from that lane of its own registers
+  // (readlane) and subtracts (x_r[col] / pivot) times it from every other row.  The pivot
+  // row is left unscaled (its own factor is zero); unknown col is its right-hand side over
+  // the pivot, divided out at the end.  Steps run in groups of CW (the column group W,
+  // uniform), unrolled within a group so that register indices are static.
+  double pvr[RPL];
 #pragma unroll
-  for (int i = 0; i < RPL; ++i) pvr[i] = 1.f;
+  for (int i = 0; i < RPL; ++i) pvr[i] = 1.0;
   for (int W = 0; W < MPAD / CW; ++W) {
 #pragma unroll
   for (int jc = 0; jc < CW; ++jc) {
@@ -239,16 +257,19 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
       float v[RPL], best = -1.f;
 #pragma unroll
       for (int i = 0; i < RPL; ++i) {
-        v[i] = used[i] ? -1.f : fabsf(x[i][jc]);
+        v[i] = used[i] ? -1.f : (float)fabs(x[i][jc]);
         best = fmaxf(best, v[i]);
       }
       best = xor32_max(xor16_max(row16_max(best)));
-      int bi = MPAD;
+      int bi = MPAD, bu = MPAD;
 #pragma unroll
       for (int i = RPL - 1; i >= 0; --i) {
-        const unsigned long long bal = __ballot(v[i] == best);
+        const unsigned long long bal = __ballot(!used[i] && v[i] == best);
+        const unsigned long long un = __ballot(!used[i]);
         if (bal) bi = 64 * i + __builtin_ctzll(bal);
+        if (un) bu = 64 * i + __builtin_ctzll(un);
       }
+      if (bi == MPAD) bi = bu;
 #pragma unroll
       for (int i = 0; i < RPL; ++i) {
         const int r = lane + 64 * i;
@@ -260,26 +281,25 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
     __syncthreads();
     if (CW * w + CW - 1 < col) continue;   // this wave's columns are all eliminated
     const int p = __builtin_amdgcn_readfirstlane(pbuf[b]);
-    const float pv = pvbuf[b];
-    float ipv = __builtin_amdgcn_rcpf(pv);
-    ipv = ipv * fmaf(-pv, ipv, 2.f);   // one Newton step
+    const double pv = pvbuf[b];
+    const double ipv = 1.0 / pv;
     const int ip = p >> 6, lp = p & 63;
-    float f[RPL];
+    double f[RPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
       const int r = lane + 64 * i;
       const bool piv = (r == p);
       if (piv) { used[i] = true; var[i] = col; pvr[i] = pv; }
-      f[i] = (piv || r >= MPAD) ? 0.f : fbuf[b][r] * ipv;
+      f[i] = (piv || r >= MPAD) ? 0.0 : fbuf[b][r] * ipv;
     }
 #pragma unroll
     for (int jj = 0; jj < CW; ++jj) {
-      float xv = x[0][jj];
+      double xv = x[0][jj];
 #pragma unroll
       for (int i = 1; i < RPL; ++i) xv = (ip == i) ? x[i][jj] : xv;
-      const float pr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xv), lp));
+      const double pr = readlane_f64(xv, lp);
 #pragma unroll
-      for (int i = 0; i < RPL; ++i) x[i][jj] = fmaf(-f[i], pr, x[i][jj]);
+      for (int i = 0; i < RPL; ++i) x[i][jj] = fma(-f[i], pr, x[i][jj]);
     }
   }
   }
@@ -293,7 +313,7 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
 #pragma unroll
       for (int jj = 0; jj < CW; ++jj) {
         const int k = CW * w - MPAD + jj;
-        dst[w2_layout_index(MP, a, k)] = (__bf16)((a < m) ? x[i][jj] / pvr[i] : 0.f);
+        dst[w2_layout_index(MP, a, k)] = (__bf16)(float)((a < m) ? x[i][jj] / pvr[i] : 0.0);
       }
     }
   }
@@ -328,7 +348,7 @@ void nys_solve1(const float* __restrict__ part, const float* __restrict__ dpart,
   __shared__ float Mx[MPAD * LD];
   __shared__ __attribute__((aligned(16))) __bf16 ql[MPAD * RS], kl[MPAD * RS];
   __shared__ float zl[MPAD];
-  __shared__ __attribute__((aligned(16))) float prow[2][G][CPL];   // by step parity
+  __shared__ __attribute__((aligned(16))) double prow[2][G][CPL];   // by step parity
   __shared__ float Ml[MPAD], facl[2][MPAD];
   nys_landmark_rows<D, MPAD, kWave, RS>(Q, K, vw, idx, slice, h, n, m, lane, ql, kl, kt);
   nys_rhs<D, AT, kWave, LD>(part, dpart, cmax, slice, chunks, m, c2, lane, Mx, zl, Ml, facl);
@@ -375,27 +395,28 @@ void nys_solve1(const float* __restrict__ part, const float* __restrict__ dpart,
   }
   __syncthreads();
 
-  float x[CPL];
+  // the elimination in fp64 (see nys_solve)
+  double x[CPL];
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) x[j] = Mx[row * LD + grp * CPL + j];
+  for (int j = 0; j < CPL; ++j) x[j] = (double)Mx[row * LD + grp * CPL + j];
   bool used = false;
   int var = 0;
-  float pvr = 1.f;
+  double pvr = 1.0;
   // Step k's elimination (multiplier f for this lane's row, pivot row pr) is applied at
   // the start of step k + 1: first to column k + 1 alone, whose pivot-row value prk comes
   // by readlane, so that step k + 1's pivot search can start at once; then to the other
   // columns with the pivot row read back from LDS a whole step earlier.
-  float fprev = 0.f, prk = 0.f;
-  f32x4 pr[CPL / 4];
+  double fprev = 0.0, prk = 0.0;
+  double pr[CPL];
 #pragma unroll
-  for (int j = 0; j < CPL / 4; ++j) pr[j] = zero4();
+  for (int j = 0; j < CPL; ++j) pr[j] = 0.0;
   // fully unrolled, so that column k is a fixed register in every step
 #pragma clang loop unroll(full)
   for (int k = 0; k < MPAD; ++k) {
     const int gk = k / CPL, kr = k % CPL;   // column k: register kr of group gk
-    if (grp == gk) x[kr] = fmaf(-fprev, prk, x[kr]);
+    if (grp == gk) x[kr] = fma(-fprev, prk, x[kr]);
     const bool cand = grp == gk && !used;
-    const float v = cand ? fabsf(x[kr]) : -1.f;
+    const float v = cand ? (float)fabs(x[kr]) : -1.f;
     // maximum over the MPAD lanes of each group (other groups' lanes hold -1)
     float best = row16_max(v);
     if constexpr (MPAD >= 32) best = xor16_max(best);
@@ -405,19 +426,16 @@ void nys_solve1(const float* __restrict__ part, const float* __restrict__ dpart,
     const unsigned long long any = __ballot(cand);
     const int lp = (int)__builtin_ctzll(bal ? bal : any);
     const int p = lp - gk * MPAD;
-    const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[kr]), lp));
+    const double pv = readlane_f64(x[kr], lp);
     // this lane's row in column k, from the lane of group gk that holds it
-    float xk;
-    if constexpr (G == 2) {
-      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[kr]), __float_as_uint(x[kr]), false, false);
-      xk = grp == gk ? x[kr] : __uint_as_float(sw[0]);
-    } else {
-      xk = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (row + gk * MPAD), __float_as_int(x[kr])));
-    }
-    float ipv = __builtin_amdgcn_rcpf(pv);
-    ipv = ipv * fmaf(-pv, ipv, 2.f);   // one Newton step
+    // (the exchange runs on every lane, outside any branch: a lane exchange under a
+    // divergent branch reads inactive lanes)
+    static_assert(G == 2, "two column groups");
+    const double other = swap32_f64(x[kr]);
+    const double xk = grp == gk ? x[kr] : other;
+    const double ipv = 1.0 / pv;
     const bool piv = row == p;
-    const float f = piv ? 0.f : xk * ipv;
+    const double f = piv ? 0.0 : xk * ipv;
     if (piv) {   // every column group's copy of the pivot row
       used = true;
       var = k;
@@ -426,8 +444,8 @@ void nys_solve1(const float* __restrict__ part, const float* __restrict__ dpart,
     // step k - 1 on the remaining columns
 #pragma unroll
     for (int j = 0; j < CPL; ++j)
-      if (j != kr) x[j] = fmaf(-fprev, pr[j / 4][j % 4], x[j]);
-    if (grp != gk) x[kr] = fmaf(-fprev, pr[kr / 4][kr % 4], x[kr]);
+      if (j != kr) x[j] = fma(-fprev, pr[j], x[j]);
+    if (grp != gk) x[kr] = fma(-fprev, pr[kr], x[kr]);
     // step k's pivot row (complete through step k - 1), one copy per column group; the
     // barrier (one wave: a wait and a compiler fence) makes the pivot lanes' writes
     // visible to the other lanes, and with the two buffers also orders the previous
@@ -436,28 +454,27 @@ void nys_solve1(const float* __restrict__ part, const float* __restrict__ dpart,
     const int b = k & 1;
     if (piv) {
 #pragma unroll
-      for (int j = 0; j < CPL; j += 4)
-        *(f32x4*)&prow[b][grp][j] = f32x4{x[j], x[j + 1], x[j + 2], x[j + 3]};
+      for (int j = 0; j < CPL; ++j) prow[b][grp][j] = x[j];
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < CPL; j += 4) pr[j / 4] = *(const f32x4*)&prow[b][grp][j];
+    for (int j = 0; j < CPL; ++j) pr[j] = prow[b][grp][j];
     if (k + 1 < MPAD) {
       const int gk1 = (k + 1) / CPL, kr1 = (k + 1) % CPL;
-      prk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[kr1]), lp + (gk1 - gk) * MPAD));
+      prk = readlane_f64(x[kr1], lp + (gk1 - gk) * MPAD);
     }
     fprev = f;
   }
   // the last step on every column
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) x[j] = fmaf(-fprev, pr[j / 4][j % 4], x[j]);
+  for (int j = 0; j < CPL; ++j) x[j] = fma(-fprev, pr[j], x[j]);
   // Z[var][k] = right-hand side over the pivot: through LDS (row var of Mx), then out as
   // pass 2's W operands in 16-byte pieces
-  const float ipr = (var < m) ? 1.f / pvr : 0.f;
+  const double ipr = (var < m) ? 1.0 / pvr : 0.0;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int col = grp * CPL + j;
-    if (col >= MPAD) Mx[var * LD + col] = x[j] * ipr;
+    if (col >= MPAD) Mx[var * LD + col] = (float)(x[j] * ipr);
   }
   __syncthreads();
   u32x4* dst = (u32x4*)(Wop + (size_t)slice * MPAD * D);

@@ -200,9 +200,10 @@ anchor_attn_status_t anchor_attn_relu_linear_forward(anchor_attn_ctx* ctx,
  * each batch element (shared by its heads; the page picks them by farthest-point
  * sampling, which is the caller's business here).  Indices are expected distinct and in
  * [0, n); out-of-range values are clamped to that range.  Repeated indices make F2
- * singular and the output non-finite.  bf16 in and out, fp32 accumulation; F2 and the
- * solve in fp32 (Gauss-Jordan with partial pivoting), F1, F3 and Z = F2^-1 F3 V rounded
- * to bf16 as matrix-core operands.  Uses the context's workspace (grown on demand;
+ * singular and the output non-finite.  bf16 in and out, fp32 accumulation; F2 in fp32
+ * and its solve in fp64 (Gauss-Jordan with partial pivoting: F2's condition number reaches
+ * 1e14 when a sink token is among the landmarks), F1, F3 and Z = F2^-1 F3 V rounded to
+ * bf16 as matrix-core operands.  Uses the context's workspace (grown on demand;
  * growth synchronizes).
  * Domain: dtype BF16 (else NOT_SUPPORTED), d in {32, 64} and 1 <= s <= 128 (else
  * NOT_SUPPORTED), s <= n (else INVALID_VALUE); B, h, n >= 0 with no tokens a no-op.  All

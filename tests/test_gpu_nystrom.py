@@ -117,6 +117,37 @@ def test_nystrom_sink_tokens_report(ctx):
     assert e <= NYS_TOL
 
 
+def test_nystrom_sink_token_landmarks(ctx):
+    """A sink token (x10) among the landmarks: its F2 row and column are nearly one-hot, so
+    F2's condition number reaches 1e9-1e14 (checked here in fp64), beyond what an fp32
+    elimination can invert; Z then has huge components that cancel in F1 Z, and H stays
+    well defined (fp64 solvers agree on it to 1e-5).  The elimination runs in fp64: the
+    output must be finite and within the bf16 gate in every slice."""
+    x, idx = _case("long_16k_bf16", {"n": 4096}, 64, seed=0)
+    w = x.workload
+    norms = np.linalg.norm(x.Q[:, 0], axis=-1)
+    for b in range(w.B):
+        sinks = set(np.where(norms[b] > 3 * np.median(norms[b]))[0].tolist())
+        assert sinks & set(idx[b].tolist()), "the case must hold a sink landmark"
+    conds = []
+    for b in range(w.B):
+        for j in range(w.h):
+            q, k = x.Q[b, j, idx[b]].astype(np.float64), x.K[b, j, idx[b]].astype(np.float64)
+            S = q @ k.T / np.sqrt(w.d)
+            F2 = np.exp(S - S.max(1, keepdims=True))
+            conds.append(np.linalg.cond(F2 / F2.sum(1, keepdims=True)))
+    print(f"  cond(F2): median {np.median(conds):.1e}, max {max(conds):.1e}", flush=True)
+    assert max(conds) > 1e12
+    got = _gpu(ctx, x, idx)
+    ref = oracle.nystrom_attn(x.Q, x.K, x.V, idx)
+    assert np.isfinite(got).all()
+    e = bf16_err(got, ref)
+    worst = max(bf16_err(got[b, j], ref[b, j]) for b in range(w.B) for j in range(w.h))
+    print(f"  sink landmarks: relative Frobenius error {e:.3e}, worst slice {worst:.3e}",
+          flush=True)
+    assert worst <= NYS_TOL
+
+
 def test_nystrom_rejects_what_it_cannot_run(ctx):
     import torch
     x, idx = _case("vit_s16_224", {"B": 1, "h": 1, "n": 20}, 4, seed=9)
