@@ -186,8 +186,11 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     const int p = r * NW + w;
     const int ri = KEEP ? r : 0;
     TileRows<D> nxt[KEEP ? 1 : 2];
-    const bool more = !KEEP && (p + NW < npairs);
-    if (more) {
+    // the next round's rows, unconditionally (rows past the slice read its last row; a
+    // pair past the end is never used): a load under a branch would make the wait for
+    // this round's rows at the join a wait for everything
+    constexpr bool more = !KEEP;
+    if constexpr (more) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) load_tile_rows<D>(Q, V, G, sr, 32 * (p + NW) + 16 * tt + c, n, g, nxt[tt]);
     }
@@ -211,10 +214,8 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     accumulate_tiles<TPW, DT, AS, VS, false>(L.a, L.g, w * TPW, pairs_here, c, g, ones, gacc, dummy);
     __syncthreads();
     if constexpr (!KEEP) {
-      if (more) {
-        rows[0][0] = nxt[0];
-        rows[0][1] = nxt[1];
-      }
+      rows[0][0] = nxt[0];
+      rows[0][1] = nxt[1];
     }
   }
 
@@ -275,8 +276,11 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     const int p = r * NW + w;
     const int ri = KEEP ? r : 0;
     TileRows<D> nxt[KEEP ? 1 : 2];
-    const bool more = !KEEP && (p + NW < npairs);
-    if (more) {
+    // the next round's rows, unconditionally (rows past the slice read its last row; a
+    // pair past the end is never used): a load under a branch would make the wait for
+    // this round's rows at the join a wait for everything
+    constexpr bool more = !KEEP;
+    if constexpr (more) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) load_tile_rows<D>(Q, V, G, sr, 32 * (p + NW) + 16 * tt + c, n, g, nxt[tt]);
     }
@@ -364,10 +368,8 @@ void bwd_fused(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     accumulate_tiles<TPW, DT, AS, VS, false>(L.a, L.v, w * TPW, pairs_here, c, g, ones, uacc, dummy);
     __syncthreads();
     if constexpr (!KEEP) {
-      if (more) {
-        rows[0][0] = nxt[0];
-        rows[0][1] = nxt[1];
-      }
+      rows[0][0] = nxt[0];
+      rows[0][1] = nxt[1];
     }
   }
 

@@ -67,14 +67,15 @@ __device__ __forceinline__ void lin_reduce(LinLds<D, NW, DW>& L, const __bf16* _
   for (int r = 0; r < rounds; ++r) {
     const int pairs_here = min(NW, npairs - r * NW);  // uniform over the workgroup
     const int p = r * NW + w;
-    const bool more = p + NW < npairs;
+    // the next round's rows, requested unconditionally (rows past the range read its last
+    // row and are never used): a load under a branch would turn the wait for this round's
+    // rows at the join into a wait for everything
     u32x4 kn[2][KS], vn[2][KV];
-    if (more) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        load_rows_c<D, D>(K, kb, ks, t0 + 32 * (p + NW) + 16 * tt + c, n, g, 0, kn[tt]);
-        load_rows_c<D, DW>(V, vb, vs, t0 + 32 * (p + NW) + 16 * tt + c, n, g, d0, vn[tt]);
-      }
+    for (int tt = 0; tt < 2; ++tt) {
+      const int row = min(t0 + 32 * (p + NW) + 16 * tt + c, t1 - 1);
+      load_rows_c<D, D>(K, kb, ks, row, n, g, 0, kn[tt]);
+      load_rows_c<D, DW>(V, vb, vs, row, n, g, d0, vn[tt]);
     }
     if (p < npairs) {
 #pragma unroll
@@ -94,14 +95,12 @@ __device__ __forceinline__ void lin_reduce(LinLds<D, NW, DW>& L, const __bf16* _
     __syncthreads();
     accumulate_tiles<TPW, DTW, KSTR, VS, true>(L.k, L.v, w * TPW, pairs_here, c, g, ones, pacc, dacc);
     __syncthreads();
-    if (more) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) kc[tt][kk] = kn[tt][kk];
+      for (int kk = 0; kk < KS; ++kk) kc[tt][kk] = kn[tt][kk];
 #pragma unroll
-        for (int kk = 0; kk < KV; ++kk) vc[tt][kk] = vn[tt][kk];
-      }
+      for (int kk = 0; kk < KV; ++kk) vc[tt][kk] = vn[tt][kk];
     }
   }
 }
@@ -147,12 +146,10 @@ __device__ __forceinline__ void lin_apply(const u32x4 (*sop)[D / 32][kWave], con
     for (int tt = 0; tt < 2; ++tt) load_rows_c<D, D>(Q, qb, qs, t0 + 32 * w + 16 * tt + c, n, g, 0, qc[tt]);
   }
   for (int p = w; p < npairs; p += NW) {
-    const bool more = p + NW < npairs;
-    u32x4 qn[2][KS];
-    if (more) {
+    u32x4 qn[2][KS];   // next pair's rows, unconditionally (see lin_reduce)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) load_rows_c<D, D>(Q, qb, qs, t0 + 32 * (p + NW) + 16 * tt + c, n, g, 0, qn[tt]);
-    }
+    for (int tt = 0; tt < 2; ++tt)
+      load_rows_c<D, D>(Q, qb, qs, min(t0 + 32 * (p + NW) + 16 * tt + c, t1 - 1), n, g, 0, qn[tt]);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int row = t0 + 32 * p + 16 * tt + c;
@@ -182,12 +179,10 @@ __device__ __forceinline__ void lin_apply(const u32x4 (*sop)[D / 32][kWave], con
                                       (u32x4*)(dst + 32 * hh));
       }
     }
-    if (more) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) qc[tt][kk] = qn[tt][kk];
-    }
+      for (int kk = 0; kk < KS; ++kk) qc[tt][kk] = qn[tt][kk];
   }
 }
 

@@ -298,9 +298,9 @@ void pass2_fp32(const float* __restrict__ Q, const float* __restrict__ U,
   __syncthreads();
 
   // Software pipeline: the next tile's Q rows are requested before this tile is computed.
-  // Rows past the chunk read the slice's last row (clamped) and are not stored.
+  // Rows past the chunk read its last row (clamped) and are not stored.
   auto load_q = [&](int t0, f32x4* q) {
-    const size_t off = qb + view_row(qw, min(t0 + c, n - 1)) + (D / 4) * g;
+    const size_t off = qb + view_row(qw, min(t0 + c, t_end - 1)) + (D / 4) * g;
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq) q[kq] = __builtin_nontemporal_load((const f32x4*)(Q + off + 4 * kq));
   };
@@ -309,9 +309,8 @@ void pass2_fp32(const float* __restrict__ Q, const float* __restrict__ U,
   for (int t0 = t_begin + 16 * w; t0 < t_end; t0 += 16 * NW) {
     const int row = t0 + c;
     const bool ok = row < t_end;
-    f32x4 qn[KQ];
-    const bool more = t0 + 16 * NW < t_end;
-    if (more) load_q(t0 + 16 * NW, qn);
+    f32x4 qn[KQ];   // the next tile's rows, unconditionally (clamped; unused past the end)
+    load_q(t0 + 16 * NW, qn);
     f32x4 s[AT];
 #pragma unroll
     for (int j = 0; j < AT; ++j) {
@@ -363,10 +362,8 @@ void pass2_fp32(const float* __restrict__ Q, const float* __restrict__ U,
 #pragma unroll
       for (int dt2 = 0; dt2 < DT; ++dt2) __builtin_nontemporal_store(hacc[dt2], (f32x4*)(dst + 4 * dt2));
     }
-    if (more) {
 #pragma unroll
-      for (int kq = 0; kq < KQ; ++kq) q[kq] = qn[kq];
-    }
+    for (int kq = 0; kq < KQ; ++kq) q[kq] = qn[kq];
   }
 }
 
