@@ -803,7 +803,7 @@ static anchor_attn_status_t backward_strided_impl(
       const size_t dpart = al((size_t)g.slices * p.chunks1 * g.m_pad * sizeof(float));
       const size_t ops = al((size_t)g.slices * g.m_pad * g.d * es);
       const size_t ddb = al((size_t)g.slices * g.m_pad * sizeof(float));
-      st = ensure_workspace(ctx, 3 * part + dpart + 3 * ops + ddb);
+      st = ensure_workspace(ctx, 3 * part + dpart + 2 * ops + ddb);
       if (st != ANCHOR_ATTN_SUCCESS) return st;
       char* w = (char*)ctx->workspace;
       aa::BackwardBuffers wb{};
@@ -812,8 +812,7 @@ static anchor_attn_status_t backward_strided_impl(
       wb.partU = (float*)w; w += part;
       wb.dpart = (float*)w; w += dpart;
       wb.wu = w; w += ops;
-      wb.dpu = w; w += ops;
-      wb.dpw = w; w += ops;
+      wb.dprm = w; w += ops;
       wb.dd = (float*)w;
       e = aa::launch_backward_bf16(g, p, wb, bv, Q, U, V, dH, dQ, dU, dV, s);
     }

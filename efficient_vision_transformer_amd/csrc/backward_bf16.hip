@@ -8,10 +8,10 @@
 //   dQ = c dS U,   dV = A dP,   dU = c sum over the batch of dS^T Q.
 // Kernels (on top of the split plan's pass 1, run on (Q, U, V) and on (Q, U, G)):
 //   bwd_finalize (per slice x 16 anchors): chunk sums of P, dW and Delta in chunk order;
-//     W, dP and dDelta as ready-made MFMA operands;
-//   bwd_tokens (per slice x token chunk, rounds of one 32-token pair per wave): A
+//     W as logits-layout MFMA operands, dP as a row-major [anchor][dim] block, dDelta;
+//   bwd_tokens_rm (per slice x token chunk, one 16-token tile per wave per round): A
 //     recomputed; dA^T = dDelta + W G^T + dP V^T on the MFMA (lanes = tokens); dS in
-//     registers; dQ^T = c U^T dS^T and dV^T = dP^T A^T written out; the pair's rows of dS
+//     registers; dQ^T = c U^T dS^T and dV^T = dP^T A^T written out; the round's rows of dS
 //     and Q go to LDS and every wave accumulates its tiles of dS^T Q (transposing LDS
 //     reads) into per-chunk partials of dU;
 //   du_reduce (per head x 16 anchors x 16 dims): dU = c x (partials summed over batch and
@@ -27,9 +27,7 @@ namespace aa {
 
 // Anchor a, dim k of an m_pad x D matrix -> position in the "U layout" left operand of a
 // logits-like product (lane (c,g) of (tile j, chunk kk): anchor 16j + c, dims
-// 8*KS*g + 8kk .. + 7); the "W^T layout" left operand of an output-like product is
-// w2_layout_index ([dt2][jj][lane'][slot], lane' (c',g') holding dim out_dim_c(dt2, c')
-// and anchors {32jj + 4g' + slot, 32jj + 16 + 4g' + slot - 4}).
+// 8*KS*g + 8kk .. + 7).
 template <int D>
 __device__ __forceinline__ size_t u_layout_index(int AT, int a, int k) {
   constexpr int KS = D / 32;
@@ -37,16 +35,12 @@ __device__ __forceinline__ size_t u_layout_index(int AT, int a, int k) {
   return ((((size_t)j * KS + (rem >> 3)) * kWave) + 16 * gg + cc) * 8 + (rem & 7);
 }
 
-// Token pass with row-major U and dP (bwd_tokens_rm): beyond 128 anchors, and at d = 128.
-constexpr bool bwd_rows_plan(int d, int at) { return at > 8 || d > 64; }
-
 // ---------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256)
 void bwd_finalize(const float* __restrict__ partP, const float* __restrict__ partG,
                   const float* __restrict__ dpart, __bf16* __restrict__ wu,
-                  __bf16* __restrict__ dpu, __bf16* __restrict__ dpw, float* __restrict__ dd,
-                  int chunks, int AT, int dp_rows) {
+                  __bf16* __restrict__ dprm, float* __restrict__ dd, int chunks, int AT) {
   constexpr int DT = D / 16, KS = D / 32;
   const int MP = AT / 2;
   const int slice = blockIdx.x / AT;
@@ -94,238 +88,12 @@ void bwd_finalize(const float* __restrict__ partP, const float* __restrict__ par
   dot = row16_sum(dot);            // over the 16 lanes c: all D dims of the anchor
   if (c == 0) dd[(size_t)slice * (16 * AT) + anchor] = -dot * rinv;
   const size_t su = (size_t)slice * AT * KS * kWave * 8;
-  const size_t sw = (size_t)slice * DT * MP * kWave * 8;
+  const size_t sr = (size_t)slice * 16 * AT * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     const int k = 16 * dt + c;
     wu[su + u_layout_index<D>(AT, anchor, k)] = (__bf16)p[dt];
-    if (dp_rows) {
-      dpw[sw + (size_t)anchor * D + k] = (__bf16)q[dt];   // row-major [anchor][dim]
-    } else {
-      dpu[su + u_layout_index<D>(AT, anchor, k)] = (__bf16)q[dt];
-      dpw[sw + w2_layout_index(MP, anchor, k)] = (__bf16)q[dt];
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------------------
-template <int D, int MP>
-__global__ __launch_bounds__(4 * kWave, 1)
-void bwd_tokens(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
-                const __bf16* __restrict__ V, const __bf16* __restrict__ G,
-                const u32x4* __restrict__ wu, const u32x4* __restrict__ dpu,
-                const u32x4* __restrict__ dpw, const float* __restrict__ dd,
-                __bf16* __restrict__ dQ, __bf16* __restrict__ dV, float* __restrict__ partU,
-                BwdViews bv, int h, int n, int m, int chunks, int chunk_len, float c2, float cs) {
-  constexpr int NW = 4, KS = D / 32, DT = D / 16, AT = 2 * MP;
-  constexpr int TILES = AT * DT, TPW = TILES / NW;
-  constexpr int AS = tr_stride<32 * MP>(), VS = tr_stride<D>();
-  static_assert(TILES % NW == 0, "tiles split evenly over the waves");
-  int slice, chunk;
-  slice_chunk_of(blockIdx.x, chunks, slice, chunk);   // a slice's chunks on one XCD
-  const int head = slice % h;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 15, g = lane >> 4;
-  const size_t qb = view_base(bv.q, slice, h), vb = view_base(bv.v, slice, h);
-  const size_t gb = view_base(bv.g, slice, h);
-  const size_t dqb = view_base(bv.dq, slice, h), dvb = view_base(bv.dv, slice, h);
-  const int t_begin = chunk * chunk_len;
-  const int t_end = min(n, t_begin + chunk_len);
-  const int npairs = (t_end - t_begin + 31) >> 5;
-
-  __shared__ u32x4 u_lds[AT][KS][kWave];     // U, logits layout
-  __shared__ u32x4 wu_lds[AT][KS][kWave];    // W, logits layout
-  __shared__ u32x4 dpu_lds[AT][KS][kWave];   // dP, logits layout
-  __shared__ u32x4 dpw_lds[DT][MP][kWave];   // dP^T, output layout
-  __shared__ u32x4 ut_lds[DT][MP][kWave];    // U^T, output layout
-  __shared__ __attribute__((aligned(16))) float dd_lds[16 * AT];
-  __shared__ __attribute__((aligned(16))) __bf16 s_rows[NW * 32 * AS];   // rows of dS
-  __shared__ __attribute__((aligned(16))) __bf16 q_rows[NW * 32 * VS];   // rows of Q
-
-  // Stage the slice's operands: every load is issued before the first LDS write.
-  constexpr int T = NW * kWave, UCH = AT * KS * kWave, UTC = 16 * AT * D / 8;
-  static_assert(16 * AT <= T, "one Delta-gradient value per thread");
-  const __bf16* Uh = U + (size_t)head * m * D;
-  const size_t so = (size_t)slice * UCH;
-  Stage<UCH, T> ust, wust, dpust;
-  stage_load(ust, [&](int idx) {
-    const int j = idx / (KS * kWave), kk = (idx / kWave) % KS, l = idx & 63;
-    const int a = 16 * j + (l & 15);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + 8 * KS * (l >> 4) + 8 * kk);
-    return v;
-  });
-  stage_load(wust, [&](int idx) { return wu[so + idx]; });
-  stage_load(dpust, [&](int idx) { return dpu[so + idx]; });
-  Stage<DT * MP * kWave, T> dpwst;
-  stage_load(dpwst, [&](int idx) { return dpw[(size_t)slice * DT * MP * kWave + idx]; });
-  // rows of U (padded anchors zero) as chunks of 8 dims: chunk i = anchor i / (D/8)
-  Stage<UTC, T> utst;
-  stage_load(utst, [&](int idx) {
-    const int a = idx / (D / 8), k = 8 * (idx - a * (D / 8));
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (a < m) v = *(const u32x4*)(Uh + (size_t)a * D + k);
-    return v;
-  });
-  const float ddv = ((int)threadIdx.x < 16 * AT) ? dd[(size_t)slice * 16 * AT + threadIdx.x] : 0.f;
-  stage_store(ust, &u_lds[0][0][0]);
-  stage_store(wust, &wu_lds[0][0][0]);
-  stage_store(dpust, &dpu_lds[0][0][0]);
-  stage_store(dpwst, &dpw_lds[0][0][0]);
-  {
-    __bf16* ut = (__bf16*)&ut_lds[0][0][0];
-#pragma unroll
-    for (int i = 0; i < Stage<UTC, T>::kPer; ++i) {
-      const int idx = (int)threadIdx.x + i * T;
-      if (UTC % T == 0 || idx < UTC) {
-        const int a = idx / (D / 8), k = 8 * (idx - a * (D / 8));
-        const bf16x8 v = as_bf16x8(utst.r[i]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ut[w2_layout_index(MP, a, k + e)] = v[e];
-      }
-    }
-  }
-  if ((int)threadIdx.x < 16 * AT) dd_lds[threadIdx.x] = ddv;
-  f32x4 mask[2];
-  pad_mask<MP>(g, m, mask);
-  const bf16x8 ones = splat_bf16(1.f);
-  __syncthreads();
-
-  f32x4 pacc[TPW], dummy[1];
-#pragma unroll
-  for (int k = 0; k < TPW; ++k) pacc[k] = zero4();
-  dummy[0] = zero4();
-
-  const int rounds = (npairs + NW - 1) / NW;
-  for (int r = 0; r < rounds; ++r) {
-    const int pairs_here = min(NW, npairs - r * NW);  // uniform over the workgroup
-    const int p = r * NW + w;
-    if (p < npairs) {
-#pragma unroll 1
-      for (int tt = 0; tt < 2; ++tt) {
-        // The LDS operands are loop-invariant; keeping the compiler from hoisting all of
-        // them into registers (which spills at m = 128) costs only LDS reads.
-        asm volatile("" ::: "memory");
-        const int row = t_begin + 32 * p + 16 * tt + c;
-        const bool ok = row < t_end;
-        u32x4 qv[KS], vv[KS], gv[KS];
-        load_rows<D>(Q, qb, bv.q.st, row, n, g, qv);
-        load_rows<D>(V, vb, bv.v.st, row, n, g, vv);
-        load_rows<D>(G, gb, bv.g.st, row, n, g, gv);
-        // A (normalised, rounded to bf16) in the transposed layout: ab[jj] lane (c,g) holds
-        // token c, anchors 32jj + 4g .. + 3 (slots 0-3) and 32jj + 16 + 4g .. + 3 (4-7).
-        bf16x8 ab[MP];
-        {
-          f32x4 s[AT];
-#pragma unroll
-          for (int j = 0; j < AT; ++j) {
-            f32x4 acc = (j >= AT - 2) ? mask[j - (AT - 2)] : zero4();
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(qv[kk]), acc);
-            s[j] = acc;
-          }
-          float mx = s[0][0];
-#pragma unroll
-          for (int j = 0; j < AT; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) mx = fmaxf(mx, s[j][q]);
-          mx = xor32_max(xor16_max(mx));
-          const float mneg = -mx * c2;
-          f32x4 zt = zero4();
-#pragma unroll
-          for (int j = 0; j < AT; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) s[j][q] = exp2_fast(fmaf(s[j][q], c2, mneg));
-            zt += s[j];
-          }
-          const float z = xor32_sum(xor16_sum((zt[0] + zt[1]) + (zt[2] + zt[3])));
-          const float inv = ok ? 1.f / z : 0.f;
-#pragma unroll
-          for (int jj = 0; jj < MP; ++jj) ab[jj] = pack_bf16(s[2 * jj] * inv, s[2 * jj + 1] * inv);
-        }
-        // Rows of Q ([token][dim]) for the dU tiles.
-        __bf16* qrow = q_rows + (32 * w + 16 * tt + c) * VS + 8 * KS * g;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) *(u32x4*)(qrow + 8 * kk) = qv[kk];
-        // dA^T = dDelta + W G^T + dP V^T, then dS = A * (dA - rowsum(A * dA)), with the
-        // bf16 A that also feeds dV.
-        f32x4 da[AT];
-        float rs = 0.f;
-#pragma unroll
-        for (int j = 0; j < AT; ++j) {
-          f32x4 acc = *(const f32x4*)&dd_lds[16 * j + 4 * g];
-#pragma unroll
-          for (int kk = 0; kk < KS; ++kk) {
-            acc = mfma_bf16(as_bf16x8(wu_lds[j][kk][lane]), as_bf16x8(gv[kk]), acc);
-            acc = mfma_bf16(as_bf16x8(dpu_lds[j][kk][lane]), as_bf16x8(vv[kk]), acc);
-          }
-          da[j] = acc;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) rs = fmaf((float)ab[j >> 1][4 * (j & 1) + q], acc[q], rs);
-        }
-        rs = xor32_sum(xor16_sum(rs));
-        bf16x8 dsb[MP];
-#pragma unroll
-        for (int jj = 0; jj < MP; ++jj) {
-          f32x4 d0, d1;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            d0[q] = (float)ab[jj][q] * (da[2 * jj][q] - rs);
-            d1[q] = (float)ab[jj][4 + q] * (da[2 * jj + 1][q] - rs);
-          }
-          dsb[jj] = pack_bf16(d0, d1);
-        }
-        // dQ^T = c U^T dS^T and dV^T = dP^T A^T, two dim tiles at a time: lane (c,g) ends
-        // with token c, dims 32hh + 8g .. + 7 (tiles 2hh and 2hh + 1), so each store
-        // instruction writes one contiguous 64-byte run per row.
-        const size_t oq = dqb + view_row(bv.dq, row) + 8 * g;
-        const size_t ov = dvb + view_row(bv.dv, row) + 8 * g;
-#pragma unroll
-        for (int hh = 0; hh < DT / 2; ++hh) {
-          f32x4 q0 = zero4(), q1 = zero4();
-#pragma unroll
-          for (int jj = 0; jj < MP; ++jj) {
-            q0 = mfma_bf16(as_bf16x8(ut_lds[2 * hh][jj][lane]), dsb[jj], q0);
-            q1 = mfma_bf16(as_bf16x8(ut_lds[2 * hh + 1][jj][lane]), dsb[jj], q1);
-          }
-          if (ok) __builtin_nontemporal_store(as_u32x4(pack_bf16(q0 * cs, q1 * cs)), (u32x4*)(dQ + oq + 32 * hh));
-          f32x4 v0 = zero4(), v1 = zero4();
-#pragma unroll
-          for (int jj = 0; jj < MP; ++jj) {
-            v0 = mfma_bf16(as_bf16x8(dpw_lds[2 * hh][jj][lane]), ab[jj], v0);
-            v1 = mfma_bf16(as_bf16x8(dpw_lds[2 * hh + 1][jj][lane]), ab[jj], v1);
-          }
-          if (ok) __builtin_nontemporal_store(as_u32x4(pack_bf16(v0, v1)), (u32x4*)(dV + ov + 32 * hh));
-        }
-        // Rows of dS ([token][anchor], dsb[jj] holds anchors 32jj + 4g .. + 3 and
-        // 32jj + 16 + 4g .. + 3).
-        __bf16* srow = s_rows + (32 * w + 16 * tt + c) * AS + 4 * g;
-#pragma unroll
-        for (int jj = 0; jj < MP; ++jj) {
-          const u32x4 v = as_u32x4(dsb[jj]);
-          *(u32x2*)(srow + 32 * jj) = u32x2{v[0], v[1]};
-          *(u32x2*)(srow + 32 * jj + 16) = u32x2{v[2], v[3]};
-        }
-      }
-    }
-    __syncthreads();
-    // dS^T Q over the round's pairs, this wave's (16-anchor, 16-dim) tiles.
-    accumulate_tiles<TPW, DT, AS, VS, false>(s_rows, q_rows, w * TPW, pairs_here, c, g, ones,
-                                             pacc, dummy);
-    __syncthreads();
-  }
-
-  // dU partials: [slice][chunk][jt][dt][r][lane] holds sum over the chunk's tokens of
-  // dS[token][16jt + 4g + r] Q[token][16dt + c].
-  const size_t sc = (size_t)slice * chunks + chunk;
-#pragma unroll
-  for (int k = 0; k < TPW; ++k) {
-    const int t = w * TPW + k;
-    const int ja = t / DT, dt = t - (t / DT) * DT;
-    float* dst = partU + ((sc * AT + ja) * DT + dt) * 256;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q * 64 + lane] = pacc[k][q];
+    dprm[sr + (size_t)anchor * D + k] = (__bf16)q[dt];   // row-major [anchor][dim]
   }
 }
 
@@ -344,11 +112,13 @@ __device__ __forceinline__ bf16x8 rows_operand_out(const __bf16* blk, int stride
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Token pass for wide slices: up to 256 anchors at d = 32 or 64, up to 128 at d = 128.
-// Same products as bwd_tokens, with the LDS budget of one workgroup per CU: U and dP are
-// kept once, as row-major [anchor][dim] blocks, and serve both as the logits-layout left
+// Token pass: up to 256 anchors at d = 32 or 64, up to 128 at d = 128.  U and dP are kept
+// once in LDS, as row-major [anchor][dim] blocks, and serve both as the logits-layout left
 // operands (16-byte row reads) and as the output-layout ones (transposing reads); W stays
-// in its logits layout.  Each of the four waves takes one 16-token tile per round, so a
+// in its logits layout.  (An earlier pass kept five operand blocks, U, W and dP in the
+// logits layout and U^T, dP^T in the output layout, which could not grow past 128 anchors
+// and, without the row prefetch, was slower at every size.)  Each of the four waves takes
+// one 16-token tile per round, so a
 // round's rows of dS and Q for the dU tiles cover 64 tokens.  The next round's rows of Q,
 // V and dH are requested before the current round is computed.
 template <int D, int AT>
@@ -551,7 +321,8 @@ void bwd_tokens_rm(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     }
   }
 
-  // dU partials: [slice][chunk][jt][dt][r][lane] as in bwd_tokens
+  // dU partials: [slice][chunk][jt][dt][r][lane] holds the sum over the chunk's tokens of
+  // dS[token][16jt + 4g + r] Q[token][16dt + c] (the layout du_reduce reads)
   const size_t sc = (size_t)slice * chunks + chunk;
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
@@ -644,21 +415,12 @@ static hipError_t go_bwd(const Geometry& g, const SplitPlan& p, const BackwardBu
   if (e != hipSuccess) return e;
   e = launch_pass1_bf16(gg, p, Q, U, G, wb.partG, wb.dpart, s);
   if (e != hipSuccess) return e;
-  constexpr bool ROWS = bwd_rows_plan(D, AT);
   bwd_finalize<D><<<dim3((unsigned)(g.slices * AT)), dim3(256), 0, s>>>(
-      wb.partP, wb.partG, wb.dpart, (__bf16*)wb.wu, (__bf16*)wb.dpu, (__bf16*)wb.dpw, wb.dd,
-      p.chunks1, AT, ROWS ? 1 : 0);
-  if constexpr (ROWS) {
-    bwd_tokens_rm<D, AT><<<dim3((unsigned)(g.slices * p.chunks1)), dim3(4 * kWave), 0, s>>>(
-        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (const __bf16*)G,
-        (const u32x4*)wb.wu, (const __bf16*)wb.dpw, wb.dd, (__bf16*)dQ, (__bf16*)dV, wb.partU,
-        bv, g.h, g.n, g.m, p.chunks1, p.chunk_len1, g.c2, cs);
-  } else {
-    bwd_tokens<D, MP><<<dim3((unsigned)(g.slices * p.chunks1)), dim3(4 * kWave), 0, s>>>(
-        (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (const __bf16*)G,
-        (const u32x4*)wb.wu, (const u32x4*)wb.dpu, (const u32x4*)wb.dpw, wb.dd, (__bf16*)dQ,
-        (__bf16*)dV, wb.partU, bv, g.h, g.n, g.m, p.chunks1, p.chunk_len1, g.c2, cs);
-  }
+      wb.partP, wb.partG, wb.dpart, (__bf16*)wb.wu, (__bf16*)wb.dprm, wb.dd, p.chunks1, AT);
+  bwd_tokens_rm<D, AT><<<dim3((unsigned)(g.slices * p.chunks1)), dim3(4 * kWave), 0, s>>>(
+      (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (const __bf16*)G,
+      (const u32x4*)wb.wu, (const __bf16*)wb.dprm, wb.dd, (__bf16*)dQ, (__bf16*)dV, wb.partU,
+      bv, g.h, g.n, g.m, p.chunks1, p.chunk_len1, g.c2, cs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_du_reduce_bf16(g, wb.partU, p.chunks1, dU, s);

@@ -21,9 +21,7 @@ struct BackwardBuffers {
   float* partG;   // pass-1 partials of A^T dH     [slice][chunk][AT][DT][256]
   float* dpart;   // pass-1 partials of Delta      [slice][chunk][16 AT]
   void* wu;       // W, logits-layout operands     [slice][AT][KS][64] x 16 B
-  void* dpu;      // dP, logits-layout operands    [slice][AT][KS][64] x 16 B
-  void* dpw;      // dP^T, output-layout operands  [slice][DT][MP][64] x 16 B
-                  // (row-major dP [slice][m_pad][d] beyond 128 anchors or at d = 128)
+  void* dprm;     // dP, row-major bf16            [slice][m_pad][d]
   float* dd;      // dDelta                        [slice][16 AT]
   float* partU;   // partials of dS^T Q            [slice][chunk][AT][DT][256]
 };
