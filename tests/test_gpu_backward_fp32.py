@@ -178,3 +178,57 @@ def test_autograd_fp32_matches_oracle():
     torch.cuda.synchronize()
     refs = oracle.anchor_backward(x.Q, x.U, x.V, Wl.astype(np.float64))
     _check_all(tuple(to_host(t.grad) for t in (Q, U, V)), refs, "autograd fp32")
+
+
+def test_backward_fp32_empty(ctxs, dev):
+    """No tokens (n = 0) or no batch (B = 0): dU is written as zeros."""
+    import torch
+    for B, n in ((1, 0), (0, 50)):
+        Q = torch.zeros((B, 2, n, 32), dtype=torch.float32, device=dev)
+        U = torch.ones((2, 20, 32), dtype=torch.float32, device=dev)
+        dU = torch.full_like(U, 3.0)
+        dQ, dV = torch.empty_like(Q), torch.empty_like(Q)
+        ctxs["auto"].backward(Q, U, Q.clone(), Q.clone(), out=(dQ, dU, dV))
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(dU).item() == 0
+
+
+def test_backward_fp32_one_anchor(ctxs, dev):
+    """m = 1: A is all ones and W is the token mean of V, so H is that mean in every row:
+    dQ = dU = 0 and every row of dV is the token mean of dH (the closed form the oracle
+    is pinned to)."""
+    x = random_case(27500, 2, 2, 300, 1, 64, "fp32")
+    got, G = _grads(ctxs["auto"], dev, x, 27501)
+    mean = np.broadcast_to(G.mean(axis=2, keepdims=True), G.shape)
+    assert fp32_err(got[2], mean) <= FP32_TOL
+    assert np.abs(got[0]).max() <= 1e-6 * np.abs(G).max()
+    assert np.abs(got[1]).max() <= 1e-6 * np.abs(G).max()
+
+
+def test_backward_fp32_dead_anchor(ctxs, dev):
+    """A dead anchor (its softmax column exactly zero: Delta = 0, W row = 0) contributes
+    nothing: its dU row is exactly zero and dQ, dV equal the call without it to rounding."""
+    import math
+    import torch
+    B, h, n, m, d, dead = 1, 2, 300, 150, 64, 77
+    rng = np.random.default_rng(27600)
+    Q = rng.standard_normal((B, h, n, d))
+    Q[..., 0] = 5.0 + np.abs(Q[..., 0])
+    U = rng.standard_normal((h, m, d))
+    U[:, dead, :] = 0.0
+    U[:, dead, 0] = -2000.0 * math.sqrt(d)
+    V = rng.standard_normal((B, h, n, d))
+    G = rng.standard_normal((B, h, n, d))
+    vals = {k: a.astype(np.float32) for k, a in (("Q", Q), ("U", U), ("V", V), ("G", G))}
+    Qd, Ud, Vd, Gd = (torch.from_numpy(np.ascontiguousarray(vals[k])).to(dev) for k in ("Q", "U", "V", "G"))
+    dQ, dU, dV = ctxs["auto"].backward(Qd, Ud, Vd, Gd)
+    keep = [a for a in range(m) if a != dead]
+    Uk = torch.from_numpy(np.ascontiguousarray(vals["U"][:, keep])).to(dev)
+    dQ2, dU2, dV2 = ctxs["auto"].backward(Qd, Uk, Vd, Gd)
+    torch.cuda.synchronize()
+    ref = oracle.anchor_backward(*(vals[k].astype(np.float64) for k in ("Q", "U", "V", "G")))
+    got = (to_host(dQ), to_host(dU), to_host(dV))
+    _check_all(got, ref, "fp32 dead anchor")
+    assert np.abs(got[1][:, dead]).max() == 0.0
+    for a, b in ((got[0], to_host(dQ2)), (got[1][:, keep], to_host(dU2)), (got[2], to_host(dV2))):
+        assert fp32_err(a, b) <= FP32_TOL
