@@ -40,8 +40,8 @@ MEASURED_TRAFFIC = {
                                            "efficient_vision_transformer_amd/csrc/tile_ops.h",
                                            "efficient_vision_transformer_amd/csrc/device_common.h",
                                            "efficient_vision_transformer_amd/csrc/geometry.h"],
-                               "sha": "a34e392a809d81e0", "read_bytes": 19471751,
-                               "write_bytes": 10898927},
+                               "sha": "84710bd8b22f54c8", "read_bytes": 19471753,
+                               "write_bytes": 10890544},
 }
 # the split plan's three kernels per step (pass 1, finalize, pass 2)
 _SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",
@@ -49,10 +49,10 @@ _SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",
                   "efficient_vision_transformer_amd/csrc/device_common.h",
                   "efficient_vision_transformer_amd/csrc/geometry.h",
                   "efficient_vision_transformer_amd/csrc/pass2_layout.h"]
-MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "399542a0c55a91c8",
-                                             "read_bytes": 122721580, "write_bytes": 55298832}
-MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "399542a0c55a91c8",
-                                               "read_bytes": 249720130, "write_bytes": 107486768}
+MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "11de7818e01488f5",
+                                             "read_bytes": 122528405, "write_bytes": 55173812}
+MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "11de7818e01488f5",
+                                               "read_bytes": 251131513, "write_bytes": 109760032}
 
 
 def measured_traffic(workload: str, plan: str):

@@ -159,6 +159,8 @@ SplitPlan make_split_plan(const Geometry& g, anchor_attn_dtype_t dtype, int num_
   p.part_bytes = al((size_t)g.slices * p.chunks1 * g.m_pad * g.d * sizeof(float));
   p.dpart_bytes = al((size_t)g.slices * p.chunks1 * g.m_pad * sizeof(float));
   p.w_bytes = al((size_t)g.slices * g.m_pad * g.d * es);
+  // each token's log-sum-exp, passed from pass 1 to pass 2 above 128 anchors (bf16)
+  p.lse_bytes = (dtype == ANCHOR_ATTN_BF16 && g.at > 8) ? al((size_t)g.slices * n * sizeof(float)) : 0;
   return p;
 }
 

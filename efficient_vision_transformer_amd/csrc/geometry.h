@@ -27,12 +27,13 @@ struct Geometry {
 };
 
 // Split plan: pass 1 over chunks1 chunks of chunk_len1 tokens per slice writes
-// partials; finalize reduces them; pass 2 over chunks2 chunks writes H.
+// partials (and each token's log-sum-exp); finalize reduces them; pass 2 over chunks2
+// chunks writes H.
 struct SplitPlan {
   int chunks1, chunk_len1;
   int chunks2, chunk_len2;
-  size_t part_bytes, dpart_bytes, w_bytes;   // workspace sections
-  size_t workspace_bytes() const { return part_bytes + dpart_bytes + w_bytes; }
+  size_t part_bytes, dpart_bytes, w_bytes, lse_bytes;   // workspace sections, in order
+  size_t workspace_bytes() const { return part_bytes + dpart_bytes + w_bytes + lse_bytes; }
 };
 
 // Fused plan: one workgroup per slice, everything on chip.

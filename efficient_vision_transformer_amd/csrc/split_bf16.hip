@@ -39,7 +39,7 @@ __global__ __launch_bounds__(NW * kWave, 2)
 void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                  const __bf16* __restrict__ V, float* __restrict__ part,
                  float* __restrict__ dpart, View qw, View xw, int h, int n, int m, int chunks,
-                 int chunk_len, float c2) {
+                 int chunk_len, float c2, float* __restrict__ lse) {
   constexpr int J = AT / NW, KS = D / 32, DT = D / 16;
   constexpr int AS = 80;                     // A row stride (16J + padding, bank-spread)
   constexpr int VS = tr_stride<D>();
@@ -137,7 +137,7 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         if (g == 0) st_max[32 * ps + 16 * tt + c][w] = mx;
       }
       __syncthreads();
-      float zp[2];
+      float zp[2], mneg2[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const float* mrow = &st_max[32 * ps + 16 * tt + c][0];
@@ -149,6 +149,7 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
           M = fmaxf(M, fmaxf(fmaxf(mg[0], mg[1]), fmaxf(mg[2], mg[3])));
         }
         const float mneg = -M * c2;
+        mneg2[tt] = mneg;
         f32x4 zt = zero4();
 #pragma unroll
         for (int jl = 0; jl < J; ++jl) {
@@ -172,6 +173,9 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
           Z += (zg[0] + zg[1]) + (zg[2] + zg[3]);
         }
         const float inv = (blk + tok < t_end) ? __builtin_amdgcn_rcpf(Z) : 0.f;   // Z >= 1
+        // the token's log-sum-exp (base 2) for pass 2: every group holds it, group 0 writes
+        if (lse && w == 0 && g == 0 && blk + tok < t_end)
+          lse[(size_t)slice * n + blk + tok] = __builtin_amdgcn_logf(Z) - mneg2[tt];
         __bf16* arow = a_lds[w] + (16 * tt + c) * AS + 4 * g;
 #pragma unroll
         for (int jl = 0; jl < J; ++jl) {
@@ -476,11 +480,12 @@ constexpr int pass2_waves() { return AT >= 24 ? 8 : kPass2Waves; }
 // H^T = W^T A^T.  U and W stay in LDS for the whole chunk.  Each wave keeps kPass2Ahead
 // of its Q tiles in flight (a register ring refilled as soon as a tile's logits are
 // formed); the first ones are requested before U and W are staged.
-template <int D, int AT, int NW = pass2_waves<AT>()>
+template <int D, int AT, bool LSE, int NW = pass2_waves<AT>()>
 __global__ __launch_bounds__(NW * kWave, 2)
 void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                 const u32x4* __restrict__ Wop, __bf16* __restrict__ H, View qw, View ow, int h,
-                int n, int m, int chunks, int chunk_len, float c2, int u_per_slice = 0) {
+                int n, int m, int chunks, int chunk_len, float c2, int u_per_slice,
+                const float* __restrict__ lse) {
   constexpr int KS = D / 32, DT = D / 16, MP = AT / 2;
   int slice, chunk;
   slice_chunk_of(blockIdx.x, chunks, slice, chunk);   // a slice's chunks on one XCD
@@ -511,16 +516,21 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 
   // Tiles past the chunk read the slice's last row (clamped) and are not stored; loads
   // are unconditional so the wait before each tile is an exact count.
-  auto load_q = [&](int t0, u32x4* q) {
-    const size_t off = qb + view_row(qw, min(t0 + c, n - 1)) + 8 * KS * g;
+  // LSE: the token's log-sum-exp from pass 1 comes with its Q row.
+  const float* lse_s = LSE ? lse + (size_t)slice * n : nullptr;
+  auto load_q = [&](int t0, u32x4* q, float& L) {
+    const int row = min(t0 + c, n - 1);
+    const size_t off = qb + view_row(qw, row) + 8 * KS * g;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) q[kk] = __builtin_nontemporal_load((const u32x4*)(Q + off + 8 * kk));
+    if constexpr (LSE) L = __builtin_nontemporal_load(lse_s + row);
   };
   // Wave w takes the tiles t_begin + 16w + step*i; tile i lives in ring slot i % PF.
   constexpr int PF = kPass2Ahead, step = 16 * NW;
   u32x4 q[PF][KS];
+  float lq[PF];
 #pragma unroll
-  for (int p = 0; p < PF; ++p) load_q(t_begin + 16 * w + step * p, q[p]);
+  for (int p = 0; p < PF; ++p) load_q(t_begin + 16 * w + step * p, q[p], lq[p]);
   stage_store(ust, &u_lds[0][0][0]);
   stage_store(wst, &w_lds[0][0][0]);
   // above 256 anchors m is padded to a multiple of 128: up to eight padded tiles
@@ -548,30 +558,43 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(q[p][kk]), acc);
       s[j] = acc;
     }
-    // the slot is free: request the wave's tile PF steps ahead into it
-    load_q(t0 + step * PF, q[p]);
-    // a2
-    float mx = s[0][0];
-#pragma unroll
-    for (int j = 0; j < AT; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[j][r]);
-    mx = xor32_max(xor16_max(mx));
-    const float mneg = -mx * c2;
-    float z = 0.f;
-#pragma unroll
-    for (int j = 0; j < AT; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = exp2_fast(fmaf(s[j][r], c2, mneg));
-        s[j][r] = e;
-        z += e;
-      }
-    z = xor32_sum(xor16_sum(z));
-    const float inv = __builtin_amdgcn_rcpf(z);   // z >= 1 (the maximum adds 1)
     bf16x8 abf[MP];
+    if constexpr (LSE) {
+      // a2 with the token's log-sum-exp L from pass 1: A = exp2(c2 s - L), already
+      // normalised (padded anchors start from -inf and give 0)
+      const float nl = -lq[p];
+      load_q(t0 + step * PF, q[p], lq[p]);   // the slot is free: the tile PF steps ahead
 #pragma unroll
-    for (int jj = 0; jj < MP; ++jj) abf[jj] = pack_bf16(s[2 * jj] * inv, s[2 * jj + 1] * inv);
+      for (int j = 0; j < AT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[j][r] = exp2_fast(fmaf(s[j][r], c2, nl));
+#pragma unroll
+      for (int jj = 0; jj < MP; ++jj) abf[jj] = pack_bf16(s[2 * jj], s[2 * jj + 1]);
+    } else {
+      // the slot is free: request the wave's tile PF steps ahead into it
+      load_q(t0 + step * PF, q[p], lq[p]);
+      // a2
+      float mx = s[0][0];
+#pragma unroll
+      for (int j = 0; j < AT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[j][r]);
+      mx = xor32_max(xor16_max(mx));
+      const float mneg = -mx * c2;
+      float z = 0.f;
+#pragma unroll
+      for (int j = 0; j < AT; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = exp2_fast(fmaf(s[j][r], c2, mneg));
+          s[j][r] = e;
+          z += e;
+        }
+      z = xor32_sum(xor16_sum(z));
+      const float inv = __builtin_amdgcn_rcpf(z);   // z >= 1 (the maximum adds 1)
+#pragma unroll
+      for (int jj = 0; jj < MP; ++jj) abf[jj] = pack_bf16(s[2 * jj] * inv, s[2 * jj + 1] * inv);
+    }
     // a5: H^T = W^T A^T; lane (c,g) ends with token c, dims out_dim_c(dt2, 4g + r), i.e.
     // 32h + 8g .. + 7 in tiles 2h and 2h + 1.
     f32x4 hacc[DT];
@@ -595,9 +618,12 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 }
 
 // ---------------------------------------------------------------------------------------
+// Pass 1 above 128 anchors also writes each token's log-sum-exp in base 2 to lse
+// ([slice][n], when lse is not null) for pass 2.
 template <int D, int AT>
 static void launch_pass1_t(const Geometry& geo, const SplitPlan& p, const void* Q, const void* U,
-                           const void* X, float* part, float* dpart, hipStream_t stream) {
+                           const void* X, float* part, float* dpart, float* lse,
+                           hipStream_t stream) {
   const long long g1 = geo.slices * p.chunks1;
   if constexpr (AT <= 8) {
     pass1x_bf16<D, AT / 2, kPass1Waves><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, stream>>>(
@@ -606,11 +632,11 @@ static void launch_pass1_t(const Geometry& geo, const SplitPlan& p, const void* 
   } else if constexpr (AT >= 24) {
     pass1a_bf16<D, AT, 8><<<dim3((unsigned)g1), dim3(8 * kWave), 0, stream>>>(
         (const __bf16*)Q, (const __bf16*)U, (const __bf16*)X, part, dpart, geo.vw.q, geo.vw.v,
-        geo.h, geo.n, geo.m, p.chunks1, p.chunk_len1, geo.c2);
+        geo.h, geo.n, geo.m, p.chunks1, p.chunk_len1, geo.c2, lse);
   } else {
     pass1a_bf16<D, AT><<<dim3((unsigned)g1), dim3(4 * kWave), 0, stream>>>(
         (const __bf16*)Q, (const __bf16*)U, (const __bf16*)X, part, dpart, geo.vw.q, geo.vw.v,
-        geo.h, geo.n, geo.m, p.chunks1, p.chunk_len1, geo.c2);
+        geo.h, geo.n, geo.m, p.chunks1, p.chunk_len1, geo.c2, lse);
   }
 }
 
@@ -622,13 +648,17 @@ static hipError_t launch_split_bf16_t(const Geometry& geo, const SplitPlan& p, c
   float* part = (float*)wsb;
   float* dpart = (float*)(wsb + p.part_bytes);
   void* Wop = (void*)(wsb + p.part_bytes + p.dpart_bytes);
-  launch_pass1_t<D, AT>(geo, p, Q, U, V, part, dpart, stream);
+  // above 128 anchors pass 2 takes each token's log-sum-exp from pass 1 instead of forming
+  // the softmax again (measured: the long workload 2 us faster, 128 anchors 1 us slower)
+  constexpr bool kLse = AT > 8;
+  float* lse = kLse ? (float*)(wsb + p.part_bytes + p.dpart_bytes + p.w_bytes) : nullptr;
+  launch_pass1_t<D, AT>(geo, p, Q, U, V, part, dpart, lse, stream);
   finalize_bf16<D><<<dim3((unsigned)(geo.slices * AT)), dim3(256), 0, stream>>>(
       part, dpart, (__bf16*)Wop, p.chunks1, AT);
   const long long g2 = geo.slices * p.chunks2;
-  pass2_bf16<D, AT><<<dim3((unsigned)g2), dim3(pass2_waves<AT>() * kWave), 0, stream>>>(
+  pass2_bf16<D, AT, kLse><<<dim3((unsigned)g2), dim3(pass2_waves<AT>() * kWave), 0, stream>>>(
       (const __bf16*)Q, (const __bf16*)U, (const u32x4*)Wop, (__bf16*)H, geo.vw.q, geo.vw.o,
-      geo.h, geo.n, geo.m, p.chunks2, p.chunk_len2, geo.c2);
+      geo.h, geo.n, geo.m, p.chunks2, p.chunk_len2, geo.c2, 0, lse);
   return hipGetLastError();
 }
 
@@ -666,12 +696,12 @@ hipError_t launch_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* 
   auto at = [&](auto D) -> hipError_t {
     constexpr int d = decltype(D)::value;
     switch (g.at) {
-      case 2: launch_pass1_t<d, 2>(g, p, Q, U, X, part, dpart, s); break;
-      case 4: launch_pass1_t<d, 4>(g, p, Q, U, X, part, dpart, s); break;
-      case 6: launch_pass1_t<d, 6>(g, p, Q, U, X, part, dpart, s); break;
-      case 8: launch_pass1_t<d, 8>(g, p, Q, U, X, part, dpart, s); break;
-      case 12: launch_pass1_t<d, 12>(g, p, Q, U, X, part, dpart, s); break;
-      case 16: launch_pass1_t<d, 16>(g, p, Q, U, X, part, dpart, s); break;
+      case 2: launch_pass1_t<d, 2>(g, p, Q, U, X, part, dpart, nullptr, s); break;
+      case 4: launch_pass1_t<d, 4>(g, p, Q, U, X, part, dpart, nullptr, s); break;
+      case 6: launch_pass1_t<d, 6>(g, p, Q, U, X, part, dpart, nullptr, s); break;
+      case 8: launch_pass1_t<d, 8>(g, p, Q, U, X, part, dpart, nullptr, s); break;
+      case 12: launch_pass1_t<d, 12>(g, p, Q, U, X, part, dpart, nullptr, s); break;
+      case 16: launch_pass1_t<d, 16>(g, p, Q, U, X, part, dpart, nullptr, s); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -719,9 +749,9 @@ hipError_t launch_nystrom_pass2_bf16(const Geometry& g, const SplitPlan& p, cons
   auto at = [&](auto D) -> hipError_t {
     constexpr int d = decltype(D)::value;
 #define AA_NYS2(AT)                                                                           \
-  pass2_bf16<d, AT><<<dim3((unsigned)g2), dim3(pass2_waves<AT>() * kWave), 0, s>>>(           \
+  pass2_bf16<d, AT, false><<<dim3((unsigned)g2), dim3(pass2_waves<AT>() * kWave), 0, s>>>(    \
       (const __bf16*)Q, (const __bf16*)kt, (const u32x4*)Wop, (__bf16*)H, qw, ow, g.h, g.n, g.m, \
-      p.chunks2, p.chunk_len2, g.c2, 1)
+      p.chunks2, p.chunk_len2, g.c2, 1, nullptr)
     switch (g.at) {
       case 2: AA_NYS2(2); break;
       case 4: AA_NYS2(4); break;
