@@ -88,25 +88,36 @@ __device__ __forceinline__ void nys_rhs(const float* __restrict__ part,
                                         float* Ml, float (*facl)[16 * AT]) {
   constexpr int MPAD = 16 * AT, DT = D / 16, EPT = (MPAD * D + T - 1) / T;
   const float* cm = cmax + (size_t)slice * chunks * MPAD;
-  if (tid < MPAD) {
+  // a chunk's partials (indices clamped, so the loads are unconditional)
+  const int tc = min(tid, MPAD - 1);
+  auto load_chunk = [&](int ch, float* v, float& dz, float& cmv) {
+    const size_t sc = (size_t)slice * chunks + min(ch, chunks - 1);
+    const float* src = part + sc * MPAD * D;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) v[e] = src[min(tid + e * T, MPAD * D - 1)];
+    dz = dpart[sc * MPAD + tc];
+    cmv = cm[(sc - (size_t)slice * chunks) * MPAD + tc];
+  };
+  float v[EPT], dz, cmv;
+  load_chunk(0, v, dz, cmv);
+  {  // each landmark's overall maximum, four chunks' maxima in flight at a time
     float M = -INFINITY;
-    for (int ch = 0; ch < chunks; ++ch) M = fmaxf(M, cm[(size_t)ch * MPAD + tid]);
-    Ml[tid] = M;
+    for (int ch = 0; ch < chunks; ch += 4) {
+      float mc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mc[i] = cm[(size_t)min(ch + i, chunks - 1) * MPAD + tc];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) M = fmaxf(M, mc[i]);
+    }
+    if (tid < MPAD) Ml[tid] = M;
   }
   float acc[EPT], z = 0.f;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
   for (int ch = 0; ch < chunks; ++ch) {
-    const size_t sc = (size_t)slice * chunks + ch;
-    const float* src = part + sc * MPAD * D;
-    float v[EPT];
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int f = tid + e * T;
-      v[e] = (f < MPAD * D) ? src[f] : 0.f;
-    }
-    const float dz = (tid < MPAD) ? dpart[sc * MPAD + tid] : 0.f;
-    const float cmv = (tid < MPAD) ? cm[(size_t)ch * MPAD + tid] : 0.f;
+    // the next chunk's partials are requested before this chunk is used
+    float vn[EPT], dzn, cmvn;
+    load_chunk(ch + 1, vn, dzn, cmvn);
     __syncthreads();   // Ml written; the previous use of this facl buffer is over
     if (tid < MPAD) facl[ch & 1][tid] = (tid < m) ? exp2_fast((cmv - Ml[tid]) * c2) : 0.f;
     __syncthreads();
@@ -117,6 +128,10 @@ __device__ __forceinline__ void nys_rhs(const float* __restrict__ part,
       if (f < MPAD * D) acc[e] = fmaf(facl[ch & 1][a], v[e], acc[e]);
     }
     if (tid < MPAD) z = fmaf(facl[ch & 1][tid], dz, z);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) v[e] = vn[e];
+    dz = dzn;
+    cmv = cmvn;
   }
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
@@ -282,7 +297,9 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
     if (CW * w + CW - 1 < col) continue;   // this wave's columns are all eliminated
     const int p = __builtin_amdgcn_readfirstlane(pbuf[b]);
     const double pv = pvbuf[b];
-    const double ipv = 1.0 / pv;
+    // 1 / pv: the hardware reciprocal refined by one Newton step
+    double ipv = __builtin_amdgcn_rcp(pv);
+    ipv = fma(ipv, fma(-pv, ipv, 1.0), ipv);
     const int ip = p >> 6, lp = p & 63;
     double f[RPL];
 #pragma unroll
@@ -353,52 +370,59 @@ void nys_solve1(const float* __restrict__ part, const float* __restrict__ dpart,
   nys_landmark_rows<D, MPAD, kWave, RS>(Q, K, vw, idx, slice, h, n, m, lane, ql, kl, kt);
   nys_rhs<D, AT, kWave, LD>(part, dpart, cmax, slice, chunks, m, c2, lane, Mx, zl, Ml, facl);
   __syncthreads();   // one wave: orders the LDS writes above before the reads below
-  // F2 logits q_a . k_l on the MFMA: tile (ti, tj), lane (c,g) ends with a = 16ti + 4g + r,
-  // l = 16tj + c; padded rows become identity rows, padded columns zero
+  // F2 = rowsoftmax(q k^T c) in registers: logits q_a . k_l on the MFMA, tile (ti, tj),
+  // lane (c,g) ends with a = 16ti + 4g + r, l = 16tj + c; each row's maximum and sum over
+  // its m columns across the 16 lanes c (DPP); padded rows become identity rows
+  {
+    f32x4 f2[AT][AT];
 #pragma unroll
-  for (int ti = 0; ti < AT; ++ti)
+    for (int ti = 0; ti < AT; ++ti)
 #pragma unroll
-    for (int tj = 0; tj < AT; ++tj) {
-      f32x4 acc = zero4();
+      for (int tj = 0; tj < AT; ++tj) {
+        f32x4 acc = zero4();
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const bf16x8 x = as_bf16x8(*(const u32x4*)(ql + (16 * ti + c) * RS + 8 * KS * g + 8 * kk));
-        const bf16x8 y = as_bf16x8(*(const u32x4*)(kl + (16 * tj + c) * RS + 8 * KS * g + 8 * kk));
-        acc = mfma_bf16(x, y, acc);
+        for (int kk = 0; kk < KS; ++kk) {
+          const bf16x8 x = as_bf16x8(*(const u32x4*)(ql + (16 * ti + c) * RS + 8 * KS * g + 8 * kk));
+          const bf16x8 y = as_bf16x8(*(const u32x4*)(kl + (16 * tj + c) * RS + 8 * KS * g + 8 * kk));
+          acc = mfma_bf16(x, y, acc);
+        }
+        f2[ti][tj] = acc;
       }
+#pragma unroll
+    for (int ti = 0; ti < AT; ++ti)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int a = 16 * ti + 4 * g + r, l = 16 * tj + c;
-        Mx[a * LD + l] = (a < m && l < m) ? acc[r] : ((a == l) ? 1.f : 0.f);
+        const int a = 16 * ti + 4 * g + r;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tj = 0; tj < AT; ++tj) mx = (16 * tj + c < m) ? fmaxf(mx, f2[ti][tj][r]) : mx;
+        mx = row16_max(mx);
+        float e[AT], z = 0.f;
+#pragma unroll
+        for (int tj = 0; tj < AT; ++tj) {
+          e[tj] = (16 * tj + c < m) ? exp2_fast((f2[ti][tj][r] - mx) * c2) : 0.f;
+          z += e[tj];
+        }
+        const float iz = 1.f / row16_sum(z);
+#pragma unroll
+        for (int tj = 0; tj < AT; ++tj) {
+          const int l = 16 * tj + c;
+          Mx[a * LD + l] = (a < m) ? e[tj] * iz : ((a == l) ? 1.f : 0.f);
+        }
       }
-    }
-  __syncthreads();
-  // row softmax of F2 over the m landmark keys (lane a: row a), F3 V = P / z; rows of
-  // padded landmarks keep their identity row and a zero right-hand side
-  if (lane < m) {
-    float* rw = Mx + lane * LD;
-    float mx = -INFINITY;
-    for (int l = 0; l < m; ++l) mx = fmaxf(mx, rw[l]);
-    float z = 0.f;
-    for (int l = 0; l < m; ++l) {
-      const float e = exp2_fast((rw[l] - mx) * c2);
-      rw[l] = e;
-      z += e;
-    }
-    const float iz = 1.f / z;
-    for (int l = 0; l < m; ++l) rw[l] *= iz;
-    const float izl = 1.f / zl[lane];   // z >= 1: each landmark's largest weight is exp(0)
-    for (int k = 0; k < D; ++k) rw[MPAD + k] *= izl;
-  } else if (lane < MPAD) {
-    float* rw = Mx + lane * LD;
-    for (int k = 0; k < D; ++k) rw[MPAD + k] = 0.f;
   }
   __syncthreads();
 
   // the elimination in fp64 (see nys_solve)
+  // the right-hand side is F3 V over F3's row sums (zero for padded landmark rows)
+  const float izl = (row < m) ? 1.f / zl[row] : 0.f;   // zl >= 1: each landmark's largest weight is exp(0)
   double x[CPL];
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) x[j] = (double)Mx[row * LD + grp * CPL + j];
+  for (int j = 0; j < CPL; ++j) {
+    const int col = grp * CPL + j;
+    const float xv = Mx[row * LD + col];
+    x[j] = (double)(col >= MPAD ? xv * izl : xv);
+  }
   bool used = false;
   int var = 0;
   double pvr = 1.0;
@@ -433,7 +457,9 @@ void nys_solve1(const float* __restrict__ part, const float* __restrict__ dpart,
     static_assert(G == 2, "two column groups");
     const double other = swap32_f64(x[kr]);
     const double xk = grp == gk ? x[kr] : other;
-    const double ipv = 1.0 / pv;
+    // 1 / pv: the hardware reciprocal refined by one Newton step
+    double ipv = __builtin_amdgcn_rcp(pv);
+    ipv = fma(ipv, fma(-pv, ipv, 1.0), ipv);
     const bool piv = row == p;
     const double f = piv ? 0.0 : xk * ipv;
     if (piv) {   // every column group's copy of the pivot row
