@@ -625,7 +625,6 @@ anchor_attn_status_t anchor_attn_relu_linear_forward(
     bool empty = false;
     anchor_attn_status_t st = check_shape(B, h, n, 1, d, raw(&dtype), &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
-    if (d > 64) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
     if (!(cmin > 0.f) || !std::isfinite(cmin) || !(qscale > 0.f) || !std::isfinite(qscale))
       return ANCHOR_ATTN_ERROR_INVALID_VALUE;
     if (dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;

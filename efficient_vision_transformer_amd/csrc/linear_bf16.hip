@@ -231,19 +231,21 @@ __device__ __forceinline__ void lin_fused_part(LinLds<D, NW, DW>& L, const __bf1
 // Workgroups 0 .. full - 1 take slices 0 .. full - 1 whole; with d = 64 the remaining
 // slices are shared by two workgroups, one per half of the output dims (both compute z
 // and read all of Q and K; each reads half of V and writes half of the output), so that a
-// grid with between one and two slices per CU gives every CU about the same work.  Ids
-// i and i + 8 of each run of 16 shared workgroups take the two halves of one slice (the
-// same XCD, so the second reads of Q and K can hit its L2).
+// grid with between one and two slices per CU gives every CU about the same work.  At
+// d = 128 every slice is shared (full == 0): a whole slice's S tiles, V rows and S
+// operands would take more registers and LDS than one workgroup has.  Ids i and i + 8 of
+// each run of 16 shared workgroups take the two halves of one slice (the same XCD, so the
+// second reads of Q and K can hit its L2).
 template <int D, int NW>
 __global__ __launch_bounds__(NW * kWave, 2)
 void relu_linear_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                       const __bf16* __restrict__ V, __bf16* __restrict__ O, View qw, View kw,
                       View vw, View ow, int h, int n, float cmin, int full) {
-  __shared__ LinLds<D, NW, D> L;
+  __shared__ LinLds<D, NW, D == 128 ? D / 2 : D> L;
   const int b = blockIdx.x;
   if (b < full) {
-    lin_fused_part<D, NW, D>(L, Q, K, V, O, qw, kw, vw, ow, b, 0, h, n, cmin);
-  } else if constexpr (D == 64) {
+    if constexpr (D != 128) lin_fused_part<D, NW, D>(L, Q, K, V, O, qw, kw, vw, ow, b, 0, h, n, cmin);
+  } else if constexpr (D >= 64) {
     const int k = b - full;
     const int nsh = (int)(gridDim.x - full);
     int sl, hf;
@@ -254,23 +256,27 @@ void relu_linear_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       sl = k >> 1;
       hf = k & 1;
     }
-    static_assert(sizeof(LinLds<D, NW, D / 2>) <= sizeof(LinLds<D, NW, D>), "half fits");
+    static_assert(sizeof(LinLds<D, NW, D / 2>) <= sizeof(L), "half fits");
     lin_fused_part<D, NW, D / 2>(*reinterpret_cast<LinLds<D, NW, D / 2>*>(&L), Q, K, V, O, qw, kw,
                                  vw, ow, full + sl, hf * (D / 2), h, n, cmin);
   }
 }
 
-// Split plan, pass 1: per (slice, chunk) partial S tiles [slice][chunk][t][4][64] and z
-// [slice][chunk][D].
+// Split plan, pass 1: per (slice, chunk) partial S tiles [slice][chunk][t][4][64] (tile t:
+// input-dim tile t / DT, output-dim tile t % DT) and z [slice][chunk][D].  At d = 128 two
+// workgroups take each chunk, one per half of the output dims (a whole chunk's tiles would
+// take more registers and LDS than one workgroup has); the first of them writes z.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * kWave, 2)
 void relu_linear_pass1(const __bf16* __restrict__ K, const __bf16* __restrict__ V, View kw,
                        View vw, float* __restrict__ part, float* __restrict__ zpart, int h,
                        int n, int chunks, int chunk_len) {
-  using L_t = LinLds<D, NW>;
-  constexpr int DT = D / 16, TILES = DT * DT, TPW = TILES / NW;
+  constexpr int HALVES = D == 128 ? 2 : 1, DW = D / HALVES;
+  using L_t = LinLds<D, NW, DW>;
+  constexpr int DT = D / 16, DTW = DW / 16, TILES = DT * DT, TPW = DT * DTW / NW;
   __shared__ L_t L;
-  const int slice = blockIdx.x / chunks, chunk = blockIdx.x - slice * chunks;
+  const int hf = blockIdx.x % HALVES, bc = blockIdx.x / HALVES;
+  const int slice = bc / chunks, chunk = bc - slice * chunks;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
@@ -278,17 +284,18 @@ void relu_linear_pass1(const __bf16* __restrict__ K, const __bf16* __restrict__ 
   f32x4 pacc[TPW], dacc[TPW];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) { pacc[k] = zero4(); dacc[k] = zero4(); }
-  lin_reduce<D, NW, D>(L, K, V, view_base(kw, slice, h), kw.st, view_base(vw, slice, h), vw.st,
-                       t0, t1, n, 0, pacc, dacc);
+  lin_reduce<D, NW, DW>(L, K, V, view_base(kw, slice, h), kw.st, view_base(vw, slice, h), vw.st,
+                        t0, t1, n, hf * DW, pacc, dacc);
   const size_t sc = (size_t)slice * chunks + chunk;
 #pragma unroll
   for (int k = 0; k < TPW; ++k) {
-    const int t = w * TPW + k, ja = t / DT, dt = t - (t / DT) * DT;
+    const int tl = w * TPW + k, ja = tl / DTW, dt = hf * DTW + tl - (tl / DTW) * DTW;
+    const int t = ja * DT + dt;
     float* dst = part + (sc * TILES + t) * 256;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       dst[r * 64 + lane] = pacc[k][r];
-      if (dt == 0 && c == 0) zpart[sc * D + 16 * ja + 4 * g + r] = dacc[k / DT][r];
+      if (dt == 0 && c == 0) zpart[sc * D + 16 * ja + 4 * g + r] = dacc[k / DTW][r];
     }
   }
 }
@@ -334,23 +341,27 @@ void relu_linear_finalize(const float* __restrict__ part, const float* __restric
   }
 }
 
-// Split plan, pass 2: per (slice, chunk), the slice's operands to LDS, then phase 3.
+// Split plan, pass 2: per (slice, chunk), the slice's operands to LDS, then phase 3.  At
+// d = 128 two workgroups take each chunk, one per half of the output dims (operand blocks
+// dt2 of that half; the whole would spill registers).
 template <int D, int NW>
-__global__ __launch_bounds__(NW * kWave, 4)
+__global__ __launch_bounds__(NW * kWave, D == 128 ? 2 : 4)
 void relu_linear_pass2(const __bf16* __restrict__ Q, __bf16* __restrict__ O, View qw, View ow,
                        const u32x4* __restrict__ sops, const float* __restrict__ zs, int h, int n,
                        int chunks, int chunk_len, float cmin) {
-  constexpr int DT = D / 16, KS = D / 32;
-  __shared__ u32x4 s_lds[DT][KS][kWave];
+  constexpr int HALVES = D == 128 ? 2 : 1, DW = D / HALVES;
+  constexpr int DT = D / 16, DTW = DW / 16, KS = D / 32;
+  __shared__ u32x4 s_lds[DTW][KS][kWave];
   __shared__ __attribute__((aligned(16))) float z_lds[D];
-  const int slice = blockIdx.x / chunks, chunk = blockIdx.x - slice * chunks;
-  const u32x4* src = sops + (size_t)slice * DT * KS * kWave;
-  for (int i = threadIdx.x; i < DT * KS * kWave; i += NW * kWave) (&s_lds[0][0][0])[i] = src[i];
+  const int hf = blockIdx.x % HALVES, bc = blockIdx.x / HALVES;
+  const int slice = bc / chunks, chunk = bc - slice * chunks;
+  const u32x4* src = sops + ((size_t)slice * DT + hf * DTW) * KS * kWave;
+  for (int i = threadIdx.x; i < DTW * KS * kWave; i += NW * kWave) (&s_lds[0][0][0])[i] = src[i];
   for (int i = threadIdx.x; i < D; i += NW * kWave) z_lds[i] = zs[(size_t)slice * D + i];
   __syncthreads();
   const int t0 = chunk * chunk_len, t1 = min(n, t0 + chunk_len);
-  lin_apply<D, NW>(s_lds, z_lds, Q, view_base(qw, slice, h), qw.st, O, view_base(ow, slice, h), ow,
-                   t0, t1, n, cmin);
+  lin_apply<D, NW, DW>(s_lds, z_lds, Q, view_base(qw, slice, h), qw.st, O, view_base(ow, slice, h),
+                       ow, t0, t1, n, cmin, nullptr, hf * DW);
 }
 
 hipError_t launch_relu_linear_bf16(const Geometry& g, const void* Q, const View& qw, const void* K,
@@ -358,7 +369,9 @@ hipError_t launch_relu_linear_bf16(const Geometry& g, const void* Q, const View&
                                    const View& ow, float cmin, int num_cus, hipStream_t s) {
   constexpr int NW = 4;
   const long long shared =
-      (g.d == 64) ? std::min<long long>(g.slices, std::max<long long>(0, 2LL * num_cus - g.slices)) : 0;
+      (g.d == 128) ? g.slices
+      : (g.d == 64) ? std::min<long long>(g.slices, std::max<long long>(0, 2LL * num_cus - g.slices))
+                    : 0;
   const long long full = g.slices - shared, grid = full + 2 * shared;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 gr((unsigned)grid), block(NW * kWave);
@@ -366,6 +379,10 @@ hipError_t launch_relu_linear_bf16(const Geometry& g, const void* Q, const View&
     relu_linear_bf16<64, NW><<<gr, block, 0, s>>>((const __bf16*)Q, (const __bf16*)K,
                                                   (const __bf16*)V, (__bf16*)O, qw, kw, vw, ow,
                                                   g.h, g.n, cmin, (int)full);
+  else if (g.d == 128)
+    relu_linear_bf16<128, NW><<<gr, block, 0, s>>>((const __bf16*)Q, (const __bf16*)K,
+                                                   (const __bf16*)V, (__bf16*)O, qw, kw, vw, ow,
+                                                   g.h, g.n, cmin, (int)full);
   else if (g.d == 32)
     relu_linear_bf16<32, NW><<<gr, block, 0, s>>>((const __bf16*)Q, (const __bf16*)K,
                                                   (const __bf16*)V, (__bf16*)O, qw, kw, vw, ow,
@@ -387,13 +404,13 @@ static hipError_t lin_split_t(const Geometry& g, const LinearSplitPlan& p, const
   __bf16* sops = (__bf16*)(w + p.part_bytes + p.zpart_bytes);
   float* zs = (float*)(w + p.part_bytes + p.zpart_bytes + p.sop_bytes);
   const long long g1 = g.slices * p.chunks1, g2 = g.slices * p.chunks2;
-  if (g1 > 0x7fffffffLL || g2 > 0x7fffffffLL) return hipErrorInvalidValue;
-  relu_linear_pass1<D, NW><<<dim3((unsigned)g1), dim3(NW * kWave), 0, s>>>(
+  if (2 * g1 > 0x7fffffffLL || 2 * g2 > 0x7fffffffLL) return hipErrorInvalidValue;
+  relu_linear_pass1<D, NW><<<dim3((unsigned)(g1 * (D == 128 ? 2 : 1))), dim3(NW * kWave), 0, s>>>(
       (const __bf16*)K, (const __bf16*)V, kw, vw, part, zpart, g.h, g.n, p.chunks1, p.chunk_len1);
   constexpr int GROUPS = ((D / 16) * (D / 16) + 3) / 4;
   relu_linear_finalize<D><<<dim3((unsigned)(g.slices * GROUPS)), dim3(256), 0, s>>>(
       part, zpart, sops, zs, p.chunks1);
-  relu_linear_pass2<D, NW><<<dim3((unsigned)g2), dim3(NW * kWave), 0, s>>>(
+  relu_linear_pass2<D, NW><<<dim3((unsigned)(g2 * (D == 128 ? 2 : 1))), dim3(NW * kWave), 0, s>>>(
       (const __bf16*)Q, (__bf16*)O, qw, ow, (const u32x4*)sops, zs, g.h, g.n, p.chunks2,
       p.chunk_len2, cmin);
   return hipGetLastError();
@@ -405,6 +422,7 @@ hipError_t launch_relu_linear_split_bf16(const Geometry& g, const LinearSplitPla
                                          float cmin, void* ws, hipStream_t s) {
   if (g.d == 64) return lin_split_t<64>(g, p, Q, qw, K, kw, V, vw, O, ow, cmin, ws, s);
   if (g.d == 32) return lin_split_t<32>(g, p, Q, qw, K, kw, V, vw, O, ow, cmin, ws, s);
+  if (g.d == 128) return lin_split_t<128>(g, p, Q, qw, K, kw, V, vw, O, ow, cmin, ws, s);
   return hipErrorInvalidValue;
 }
 

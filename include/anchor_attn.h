@@ -174,10 +174,11 @@ anchor_attn_status_t anchor_attn_block_forward(anchor_attn_ctx* ctx,
  * qscale stands for 1/s, the page's learnable scale; since phi(a q) = a phi(q) it only
  * moves the clamp.  bf16 in and out, fp32 accumulation (phi(K)^T V rounded to bf16 as a
  * matrix-core operand).  With enough slices one workgroup per slice (Q, K, V read once,
- * O written once); with fewer than half a slice per CU, or under PLAN_SPLIT, the tokens of
- * a slice are split over workgroups (partial sums in the context's workspace, reduced in
- * a fixed order).
- * Domain: dtype BF16 (else NOT_SUPPORTED), d in {32, 64}, B, h, n >= 0 (no tokens: a
+ * O written once; at d = 128 two workgroups per slice, one per half of the output dims,
+ * each reading all of Q and K); with fewer than half a slice per CU, or under PLAN_SPLIT,
+ * the tokens of a slice are split over workgroups (partial sums in the context's workspace,
+ * reduced in a fixed order).
+ * Domain: dtype BF16 (else NOT_SUPPORTED), d in {32, 64, 128}, B, h, n >= 0 (no tokens: a
  * no-op), cmin > 0 and qscale > 0 finite (else INVALID_VALUE); views as for
  * anchor_attn_forward_strided (O's rows distinct, O's span disjoint from the inputs').
  * Errors: nothing is enqueued. */

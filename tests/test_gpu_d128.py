@@ -143,9 +143,9 @@ def test_d128_strided_views_match_contiguous(ctxs, dev):
 
 
 def test_d128_refusals(ctxs, dev):
-    """d = 128 runs the bf16 forward and the bf16 backward (up to 128 anchors): the fused
-    plan beyond its limits (here 300 tokens with 16 anchors), fp32, the fp32 backward, the
-    bf16 backward above 128 anchors, the linear attention and Nystrom attention refuse it
+    """d = 128 runs the bf16 forward, the bf16 backward (up to 128 anchors) and the linear
+    attention: the fused plan beyond its limits (here 300 tokens with 16 anchors), fp32, the
+    fp32 backward, the bf16 backward above 128 anchors and Nystrom attention refuse it
     (NOT_SUPPORTED)."""
     import torch
     x = random_case(78, 1, 2, 300, 16, 128, dtype="bf16")
@@ -159,7 +159,5 @@ def test_d128_refusals(ctxs, dev):
     U129 = torch.zeros((2, 129, 128), dtype=torch.bfloat16, device=dev)
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
         ctxs["auto"].backward(Q, U129, V, torch.ones_like(Q))
-    with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
-        ctxs["auto"].relu_linear(Q, Q, V)
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
         ctxs["auto"].nystrom(Q, Q, V, torch.zeros((1, 4), dtype=torch.int32, device=dev))

@@ -49,8 +49,12 @@ def _run(ctx, x, cmin=100.0, qscale=1.0):
     return e
 
 
+# (B, h, n, d): the ViT-S/16 shape, ragged and single-token slices, long slices; at
+# d = 128 every slice is shared by two workgroups (one per half of the output dims) in the
+# one-kernel plan, and pass 1 and pass 2 of the split plan run in halves as well
 SHAPES = [(64, 6, 196, 64), (2, 3, 77, 32), (1, 1, 1, 64), (1, 2, 33, 32), (2, 2, 1000, 64),
-          (1, 4, 4096, 64)]
+          (1, 4, 4096, 64), (8, 6, 196, 128), (2, 3, 77, 128), (1, 1, 1, 128),
+          (1, 2, 2051, 128)]
 
 
 @pytest.mark.parametrize("plan", ["split", "fused"])
@@ -84,6 +88,28 @@ def test_relu_linear_clamp_and_scale(ctx, cmin, qscale):
     """Clamp inactive (cmin tiny), mostly binding (cmin large) and moved by the scale."""
     x = make_inputs("vit_s16_224", seed=4100, shape={"B": 4})
     assert _run(ctx, x, cmin, qscale) <= LIN_TOL
+
+
+def test_relu_linear_d128_plans_agree_long(ctxs):
+    """A long d = 128 slice pair (n = 16384) through both plans, against each other and the
+    oracle."""
+    import torch
+    x = make_inputs("long_16k_bf16", shape={"B": 1, "h": 2, "d": 128})
+    outs = {}
+    for plan in ("split", "fused"):
+        O = ctxs[plan].relu_linear(_conv(x.bits["Q"]), _conv(x.bits["K"]), _conv(x.bits["V"]))
+        torch.cuda.synchronize()
+        outs[plan] = O.float().cpu().numpy().astype(np.float64)
+    ref = oracle.relu_linear_attn(x.Q, x.K, x.V)
+    for plan, got in outs.items():
+        e = bf16_err(got, ref)
+        print(f"  long d=128 {plan}: relative Frobenius error {e:.3e}", flush=True)
+        assert e <= LIN_TOL
+        # each output half comes from its own workgroup: a mis-paired half would leave one
+        # half far off while the whole tensor passes
+        for hf in range(2):
+            assert bf16_err(got[..., 64 * hf:64 * hf + 64], ref[..., 64 * hf:64 * hf + 64]) <= LIN_TOL
+    assert bf16_err(outs["split"], outs["fused"]) <= LIN_TOL
 
 
 def test_relu_linear_packed_views(ctx):
