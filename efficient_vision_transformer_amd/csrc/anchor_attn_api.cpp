@@ -683,7 +683,8 @@ anchor_attn_status_t anchor_attn_nystrom_forward(anchor_attn_ctx* ctx, const voi
     bool empty = false;
     anchor_attn_status_t st = check_shape(B, h, n, s, d, raw(&dtype), &g, &empty);
     if (st != ANCHOR_ATTN_SUCCESS) return st;
-    if (dtype != ANCHOR_ATTN_BF16 || s > 128 || d > 64) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+    if (dtype != ANCHOR_ATTN_BF16 || s > 128 || (d == 128 && s > 96))
+      return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
     if (!Q || !K || !V || !idx || !H) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
     if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)H) & 15u) return ANCHOR_ATTN_ERROR_INVALID_VALUE;
     if ((uintptr_t)idx & 3u) return ANCHOR_ATTN_ERROR_INVALID_VALUE;

@@ -521,7 +521,7 @@ void nys_solve1(const float* __restrict__ part, const float* __restrict__ dpart,
 template <int D, int AT>
 static void launch_nys_solve_t(const Geometry& g, const SplitPlan& p, const NystromBuffers& nb,
                                const void* Q, const void* K, const int* idx, hipStream_t s) {
-  if constexpr (16 * AT <= 32) {
+  if constexpr (16 * AT <= 32 && D <= 64) {
     // one wave per slice up to 32 landmarks (at 64, with 64 dependent steps over 128
     // columns per lane, the ViT-B/16-shape step took 153 us with it against 122 us)
     nys_solve1<D, AT><<<dim3((unsigned)g.slices), dim3(kWave), 0, s>>>(
@@ -541,7 +541,9 @@ static hipError_t launch_nys_solve(const Geometry& g, const SplitPlan& p, const 
     case 2: launch_nys_solve_t<D, 2>(g, p, nb, Q, K, idx, s); break;
     case 4: launch_nys_solve_t<D, 4>(g, p, nb, Q, K, idx, s); break;
     case 6: launch_nys_solve_t<D, 6>(g, p, nb, Q, K, idx, s); break;
-    case 8: launch_nys_solve_t<D, 8>(g, p, nb, Q, K, idx, s); break;
+    case 8:
+      if constexpr (D <= 64) { launch_nys_solve_t<D, 8>(g, p, nb, Q, K, idx, s); break; }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -550,12 +552,14 @@ static hipError_t launch_nys_solve(const Geometry& g, const SplitPlan& p, const 
 hipError_t launch_nystrom_bf16(const Geometry& g, const SplitPlan& p, const void* Q, const void* K,
                                const void* V, const int* idx, void* H, const NystromBuffers& nb,
                                hipStream_t stream) {
-  if (g.d != 32 && g.d != 64) return hipErrorInvalidValue;
+  // d = 128 up to 96 landmarks (the solve's set-up matrix would outgrow LDS above)
+  if (g.d != 32 && g.d != 64 && !(g.d == 128 && g.at <= 6)) return hipErrorInvalidValue;
   hipError_t e = launch_nystrom_pass1_bf16(g, p, K, g.vw.q, Q, g.vw.q, idx, V, g.vw.v, nb.part,
                                            nb.dpart, nb.cmax, stream);
   if (e != hipSuccess) return e;
-  e = g.d == 64 ? launch_nys_solve<64>(g, p, nb, Q, K, idx, stream)
-                : launch_nys_solve<32>(g, p, nb, Q, K, idx, stream);
+  e = g.d == 64    ? launch_nys_solve<64>(g, p, nb, Q, K, idx, stream)
+      : g.d == 128 ? launch_nys_solve<128>(g, p, nb, Q, K, idx, stream)
+                   : launch_nys_solve<32>(g, p, nb, Q, K, idx, stream);
   if (e != hipSuccess) return e;
   return launch_nystrom_pass2_bf16(g, p, Q, g.vw.q, nb.kt, nb.wop, H, g.vw.o, stream);
 }

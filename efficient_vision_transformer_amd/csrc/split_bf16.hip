@@ -731,7 +731,9 @@ hipError_t launch_nystrom_pass1_bf16(const Geometry& g, const SplitPlan& p, cons
       case 2: AA_NYS1(1); break;
       case 4: AA_NYS1(2); break;
       case 6: AA_NYS1(3); break;
-      case 8: AA_NYS1(4); break;
+      case 8:
+        if constexpr (d <= 64) { AA_NYS1(4); break; }
+        return hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
 #undef AA_NYS1
@@ -739,6 +741,7 @@ hipError_t launch_nystrom_pass1_bf16(const Geometry& g, const SplitPlan& p, cons
   };
   if (g.d == 64) return at(std::integral_constant<int, 64>{});
   if (g.d == 32) return at(std::integral_constant<int, 32>{});
+  if (g.d == 128) return at(std::integral_constant<int, 128>{});   // up to 96 landmarks
   return hipErrorInvalidValue;
 }
 
@@ -756,7 +759,9 @@ hipError_t launch_nystrom_pass2_bf16(const Geometry& g, const SplitPlan& p, cons
       case 2: AA_NYS2(2); break;
       case 4: AA_NYS2(4); break;
       case 6: AA_NYS2(6); break;
-      case 8: AA_NYS2(8); break;
+      case 8:
+        if constexpr (d <= 64) { AA_NYS2(8); break; }
+        return hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
 #undef AA_NYS2
@@ -764,6 +769,7 @@ hipError_t launch_nystrom_pass2_bf16(const Geometry& g, const SplitPlan& p, cons
   };
   if (g.d == 64) return at(std::integral_constant<int, 64>{});
   if (g.d == 32) return at(std::integral_constant<int, 32>{});
+  if (g.d == 128) return at(std::integral_constant<int, 128>{});   // up to 96 landmarks
   return hipErrorInvalidValue;
 }
 

@@ -206,8 +206,8 @@ anchor_attn_status_t anchor_attn_relu_linear_forward(anchor_attn_ctx* ctx,
  * 1e14 when a sink token is among the landmarks), F1, F3 and Z = F2^-1 F3 V rounded to
  * bf16 as matrix-core operands.  Uses the context's workspace (grown on demand;
  * growth synchronizes).
- * Domain: dtype BF16 (else NOT_SUPPORTED), d in {32, 64} and 1 <= s <= 128 (else
- * NOT_SUPPORTED), s <= n (else INVALID_VALUE); B, h, n >= 0 with no tokens a no-op.  All
+ * Domain: dtype BF16 (else NOT_SUPPORTED), d in {32, 64} with 1 <= s <= 128, or d = 128
+ * with 1 <= s <= 96 (else NOT_SUPPORTED), s <= n (else INVALID_VALUE); B, h, n >= 0 with no tokens a no-op.  All
  * pointers 16-byte aligned (idx 4-byte); H must not overlap Q, K, V or idx.
  * Errors: nothing is enqueued. */
 anchor_attn_status_t anchor_attn_nystrom_forward(anchor_attn_ctx* ctx, const void* Q,

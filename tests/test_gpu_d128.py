@@ -143,10 +143,10 @@ def test_d128_strided_views_match_contiguous(ctxs, dev):
 
 
 def test_d128_refusals(ctxs, dev):
-    """d = 128 runs the bf16 forward, the bf16 backward (up to 128 anchors) and the linear
-    attention: the fused plan beyond its limits (here 300 tokens with 16 anchors), fp32, the
-    fp32 backward, the bf16 backward above 128 anchors and Nystrom attention refuse it
-    (NOT_SUPPORTED)."""
+    """d = 128 runs the bf16 forward, the bf16 backward (up to 128 anchors), the linear
+    attention and Nystrom attention (up to 96 landmarks): the fused plan beyond its limits
+    (here 300 tokens with 16 anchors), fp32, the fp32 backward, the bf16 backward above 128
+    anchors and Nystrom attention above 96 landmarks refuse it (NOT_SUPPORTED)."""
     import torch
     x = random_case(78, 1, 2, 300, 16, 128, dtype="bf16")
     Q, U, V = to_device(x, dev)
@@ -160,4 +160,4 @@ def test_d128_refusals(ctxs, dev):
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
         ctxs["auto"].backward(Q, U129, V, torch.ones_like(Q))
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
-        ctxs["auto"].nystrom(Q, Q, V, torch.zeros((1, 4), dtype=torch.int32, device=dev))
+        ctxs["auto"].nystrom(Q, Q, V, torch.arange(97, dtype=torch.int32, device=dev)[None, :])

@@ -54,6 +54,13 @@ CASES = [
     ("vit_s16_224", {"B": 1, "h": 1, "n": 1}, 1),             # one token
     ("vit_s16_224", {"B": 3, "h": 1, "n": 1000, "d": 32}, 17),
     ("vit_s16_224", {"B": 1, "h": 2, "n": 16384}, 64),        # many token chunks
+    ("vit_b16_384", {"B": 1, "d": 128}, 64),                  # d = 128, most landmarks
+    ("vit_s16_224", {"B": 2, "h": 3, "n": 77, "d": 128}, 5),  # d = 128, ragged tiles
+    ("vit_s16_224", {"B": 1, "h": 1, "n": 1, "d": 128}, 1),
+    ("vit_s16_224", {"B": 1, "h": 2, "n": 4099, "d": 128}, 33),
+    ("long_16k_bf16", {"B": 1, "h": 4, "n": 4096, "d": 128}, 64),  # sinks: cond(F2) ~ 3e10
+    ("dense_64x64", {"B": 1, "h": 2, "d": 128}, 96),          # d = 128, most landmarks
+    ("vit_s16_224", {"B": 2, "h": 2, "n": 333, "d": 128}, 71),
 ]
 
 
@@ -71,9 +78,10 @@ def test_nystrom_against_oracle(ctx, case):
     assert e <= NYS_TOL
 
 
-def test_nystrom_every_token_a_landmark_is_full_attention(ctx):
+@pytest.mark.parametrize("d", [64, 128])
+def test_nystrom_every_token_a_landmark_is_full_attention(ctx, d):
     """s = n in a shuffled order: the Nystrom product is exactly softmax(Q K^T c) V."""
-    x = make_inputs("vit_s16_224", shape={"B": 1, "h": 2, "n": 48})
+    x = make_inputs("vit_s16_224", shape={"B": 1, "h": 2, "n": 48, "d": d})
     idx = np.random.default_rng(5).permutation(48).astype(np.int32)[None, :]
     got = _gpu(ctx, x, idx)
     for j in range(2):
@@ -156,8 +164,12 @@ def test_nystrom_rejects_what_it_cannot_run(ctx):
         ctx.nystrom(Q, K, V, torch.zeros((1, 21), dtype=torch.int32, device="cuda:0"))
     x2, _ = _case("vit_s16_224", {"B": 1, "h": 1, "n": 200}, 4, seed=9)
     Q2, K2, V2 = (_conv(x2.bits[k]) for k in ("Q", "K", "V"))
-    with pytest.raises(RuntimeError):   # s > 128
+    with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):   # s > 128
         ctx.nystrom(Q2, K2, V2, torch.arange(129, dtype=torch.int32, device="cuda:0")[None, :])
+    x3, _ = _case("vit_s16_224", {"B": 1, "h": 1, "n": 200, "d": 128}, 4, seed=9)
+    Q3, K3, V3 = (_conv(x3.bits[k]) for k in ("Q", "K", "V"))
+    with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):   # s > 96 at d = 128
+        ctx.nystrom(Q3, K3, V3, torch.arange(97, dtype=torch.int32, device="cuda:0")[None, :])
     with pytest.raises(RuntimeError):   # fp32 is not built
         ctx.nystrom(Q.float(), K.float(), V.float(), torch.from_numpy(idx).to("cuda:0"))
 
