@@ -114,8 +114,8 @@ anchor_attn_status_t check_shape(int B, int h, int n, int m, int d, int dtype_ra
   if (dtype_raw != ANCHOR_ATTN_FP32 && dtype_raw != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   const anchor_attn_dtype_t dtype = (anchor_attn_dtype_t)dtype_raw;
   if (d != 32 && d != 64 && d != 128) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
-  // d = 128: the bf16 forward only (the fused and split plans)
-  if (d == 128 && dtype != ANCHOR_ATTN_BF16) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
+  // d = 128 in fp32: the split plan's forward up to 128 anchors
+  if (d == 128 && dtype != ANCHOR_ATTN_BF16 && m > 128) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   if (m > 512) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;
   // more than 256 anchors: the bf16 split plan at d <= 64 only
   if (m > 256 && (dtype != ANCHOR_ATTN_BF16 || d > 64)) return ANCHOR_ATTN_ERROR_NOT_SUPPORTED;

@@ -397,8 +397,11 @@ static hipError_t dispatch_at(const Geometry& g, const SplitPlan& p, const void*
     case 4: return launch_split_fp32_t<D, 4>(g, p, Q, U, V, H, ws, s);
     case 6: return launch_split_fp32_t<D, 6>(g, p, Q, U, V, H, ws, s);
     case 8: return launch_split_fp32_t<D, 8>(g, p, Q, U, V, H, ws, s);
-    case 12: return launch_split_fp32_t<D, 12>(g, p, Q, U, V, H, ws, s);
-    case 16: return launch_split_fp32_t<D, 16>(g, p, Q, U, V, H, ws, s);
+    // at d = 128, U and W in fp32 outgrow pass 2's LDS above 128 anchors
+    case 12: if constexpr (D <= 64) return launch_split_fp32_t<D, 12>(g, p, Q, U, V, H, ws, s);
+             return hipErrorInvalidValue;
+    case 16: if constexpr (D <= 64) return launch_split_fp32_t<D, 16>(g, p, Q, U, V, H, ws, s);
+             return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -407,6 +410,7 @@ hipError_t launch_split_fp32(const Geometry& g, const SplitPlan& p, const void* 
                              const void* V, void* H, void* ws, hipStream_t stream) {
   if (g.d == 64) return dispatch_at<64>(g, p, Q, U, V, H, ws, stream);
   if (g.d == 32) return dispatch_at<32>(g, p, Q, U, V, H, ws, stream);
+  if (g.d == 128) return dispatch_at<128>(g, p, Q, U, V, H, ws, stream);   // m <= 128
   return hipErrorInvalidValue;
 }
 

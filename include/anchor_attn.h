@@ -91,8 +91,8 @@ anchor_attn_status_t anchor_attn_destroy(anchor_attn_ctx* ctx);
  * Domain: B, h, n >= 0 (B*h*n == 0 is a successful no-op); 1 <= m <= 512 (more than 256
  * anchors: dtype BF16 with d <= 64, run by the split plan); d in {32, 64},
  * or d = 128 with dtype BF16 (the fused plan takes m <= 32 with n <= 256 and m <= 64 with
- * n <= 1024; PLAN_FUSED gives NOT_SUPPORTED beyond that); other d, or d = 128 in FP32,
- * give NOT_SUPPORTED.
+ * n <= 1024; PLAN_FUSED gives NOT_SUPPORTED beyond that) or with dtype FP32 and m <= 128
+ * (the split plan); other d, or d = 128 in FP32 above 128 anchors, give NOT_SUPPORTED.
  * m >= n is accepted (the result is still defined; the O(mn) saving needs m < n). */
 anchor_attn_status_t anchor_attn_forward(anchor_attn_ctx* ctx,
                                          const void* Q, const void* U, const void* V, void* H,

@@ -1,13 +1,14 @@
-"""GPU parity of the forward at head dim d = 128 (bf16; the split plan, and the fused plan
-with every slice shared by two workgroups) against the fp64 oracle, and the entry points
-that refuse d = 128.  Gate: relative Frobenius error <= 1e-2."""
+"""GPU parity of the forward at head dim d = 128 (bf16: the split plan, and the fused plan
+with every slice shared by two workgroups; fp32: the split plan up to 128 anchors) against
+the fp64 oracle, and the entry points that refuse d = 128.  Gates: relative Frobenius error
+<= 1e-2 in bf16, normwise max-relative error <= 1e-5 in fp32."""
 import numpy as np
 import pytest
 
 import oracle
 from efficient_vision_transformer_amd.inputs import make_inputs, random_case
 
-from gpu_util import bf16_err, to_device, to_host
+from gpu_util import bf16_err, fp32_err, to_device, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +51,27 @@ def test_d128_against_oracle(ctxs, dev, shape, plan):
     e = bf16_err(to_host(H), oracle.anchor_attn(x.Q, x.U, x.V))
     print(f"  relative Frobenius error {e:.3e}", flush=True)
     assert e <= TOL
+
+
+# fp32 at d = 128: every anchor padding up to 128 anchors, ragged token counts, one token,
+# m > n
+FP32_SHAPES = [(2, 3, 300, 30, 128), (4, 2, 77, 9, 128), (1, 2, 2051, 64, 128),
+               (1, 1, 1, 1, 128), (2, 2, 1000, 90, 128), (1, 2, 4096, 128, 128),
+               (1, 1, 40, 100, 128)]
+
+
+@pytest.mark.parametrize("shape", FP32_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_d128_fp32_against_oracle(ctxs, dev, shape):
+    import torch
+    B, h, n, m, d = shape
+    x = random_case(700 + n + m, B, h, n, m, d, dtype="fp32", q_scale=1.5)
+    print(f"  d=128 fp32 forward B={B} h={h} n={n} m={m}", flush=True)
+    Q, U, V = to_device(x, dev)
+    H = ctxs["auto"].forward(Q, U, V)
+    torch.cuda.synchronize()
+    e = fp32_err(to_host(H), oracle.anchor_attn(x.Q, x.U, x.V))
+    print(f"  normwise max-relative error {e:.3e}", flush=True)
+    assert e <= 1e-5
 
 
 # (B, h, n, m, d) the fused plan takes at d = 128: four waves of one or two rounds
@@ -143,17 +165,19 @@ def test_d128_strided_views_match_contiguous(ctxs, dev):
 
 
 def test_d128_refusals(ctxs, dev):
-    """d = 128 runs the bf16 forward, the bf16 backward (up to 128 anchors), the linear
-    attention and Nystrom attention (up to 96 landmarks): the fused plan beyond its limits
-    (here 300 tokens with 16 anchors), fp32, the fp32 backward, the bf16 backward above 128
-    anchors and Nystrom attention above 96 landmarks refuse it (NOT_SUPPORTED)."""
+    """d = 128 runs the bf16 forward, the fp32 forward (up to 128 anchors), the bf16
+    backward (up to 128 anchors), the linear attention and Nystrom attention (up to 96
+    landmarks): the fused plan beyond its limits (here 300 tokens with 16 anchors), the fp32
+    forward above 128 anchors, the fp32 backward, the bf16 backward above 128 anchors and
+    Nystrom attention above 96 landmarks refuse it (NOT_SUPPORTED)."""
     import torch
     x = random_case(78, 1, 2, 300, 16, 128, dtype="bf16")
     Q, U, V = to_device(x, dev)
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
         ctxs["fused"].forward(Q, U, V)
+    U130 = torch.zeros((2, 130, 128), dtype=torch.float32, device=dev)
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
-        ctxs["auto"].forward(Q.float(), U.float(), V.float())
+        ctxs["auto"].forward(Q.float(), U130, V.float())
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
         ctxs["auto"].backward(Q.float(), U.float(), V.float(), torch.ones_like(Q.float()))
     U129 = torch.zeros((2, 129, 128), dtype=torch.bfloat16, device=dev)
