@@ -49,10 +49,10 @@ _SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",
                   "efficient_vision_transformer_amd/csrc/device_common.h",
                   "efficient_vision_transformer_amd/csrc/geometry.h",
                   "efficient_vision_transformer_amd/csrc/pass2_layout.h"]
-MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "bf3889fbeb293899",
-                                             "read_bytes": 122650687, "write_bytes": 55199403}
-MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "bf3889fbeb293899",
-                                               "read_bytes": 251175136, "write_bytes": 109666318}
+MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "ab6e42bd162c1589",
+                                             "read_bytes": 120737826, "write_bytes": 54908292}
+MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "ab6e42bd162c1589",
+                                               "read_bytes": 244456867, "write_bytes": 111976512}
 
 
 def measured_traffic(workload: str, plan: str):

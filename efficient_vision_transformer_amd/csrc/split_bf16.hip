@@ -474,13 +474,21 @@ constexpr int kPass2Ahead = 1;
 template <int AT>
 constexpr int pass2_waves() { return AT >= 24 ? 8 : kPass2Waves; }
 
-// Pass 2.  Each wave takes 16-token tiles.  Logits are formed transposed, S^T = U Q^T
-// (lanes = tokens, registers = anchors), so the softmax is an in-register reduction plus
-// two permlane swaps and the normalised A is directly the right operand of
-// H^T = W^T A^T.  U and W stay in LDS for the whole chunk.  Each wave keeps kPass2Ahead
-// of its Q tiles in flight (a register ring refilled as soon as a tile's logits are
-// formed); the first ones are requested before U and W are staged.
-template <int D, int AT, bool LSE, int NW = pass2_waves<AT>()>
+// Tiles per pass-2 step: above 128 anchors (up to 256, d <= 64) two 16-token tiles share
+// every U and W operand read from LDS.  At 128 anchors that was not faster (dense 56.7 us
+// against 58.6 at three waves per SIMD and 57.3 when held to four); at d = 128 or beyond
+// 256 anchors the second tile's registers would spill.
+template <int D, int AT>
+constexpr int pass2_tiles() { return (D <= 64 && AT > 8 && AT <= 16) ? 2 : 1; }
+
+// Pass 2.  Each wave takes steps of TT consecutive 16-token tiles.  Logits are formed
+// transposed, S^T = U Q^T (lanes = tokens, registers = anchors), so the softmax is an
+// in-register reduction plus two permlane swaps and the normalised A is directly the right
+// operand of H^T = W^T A^T.  U and W stay in LDS for the whole chunk; each operand read
+// from it serves the step's TT tiles.  Each wave keeps kPass2Ahead of its steps' Q rows in
+// flight (a register ring refilled as soon as a step's logits are formed); the first ones
+// are requested before U and W are staged.
+template <int D, int AT, bool LSE, int NW = pass2_waves<AT>(), int TT = pass2_tiles<D, AT>()>
 __global__ __launch_bounds__(NW * kWave, 2)
 void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                 const u32x4* __restrict__ Wop, __bf16* __restrict__ H, View qw, View ow, int h,
@@ -514,23 +522,27 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   Stage<DT * MP * kWave, NW * kWave> wst;
   stage_load(wst, [&](int idx) { return Ws[idx]; });
 
-  // Tiles past the chunk read the slice's last row (clamped) and are not stored; loads
-  // are unconditional so the wait before each tile is an exact count.
+  // Tiles past the chunk read the chunk's last row (clamped) and are not stored; loads
+  // are unconditional so the wait before each step is an exact count.
   // LSE: the token's log-sum-exp from pass 1 comes with its Q row.
   const float* lse_s = LSE ? lse + (size_t)slice * n : nullptr;
-  auto load_q = [&](int t0, u32x4* q, float& L) {
-    const int row = min(t0 + c, n - 1);
-    const size_t off = qb + view_row(qw, row) + 8 * KS * g;
+  auto load_q = [&](int t0, u32x4 (*q)[KS], float* L) {
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) q[kk] = __builtin_nontemporal_load((const u32x4*)(Q + off + 8 * kk));
-    if constexpr (LSE) L = __builtin_nontemporal_load(lse_s + row);
+    for (int tt = 0; tt < TT; ++tt) {
+      const int row = min(t0 + 16 * tt + c, t_end - 1);
+      const size_t off = qb + view_row(qw, row) + 8 * KS * g;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        q[tt][kk] = __builtin_nontemporal_load((const u32x4*)(Q + off + 8 * kk));
+      if constexpr (LSE) L[tt] = __builtin_nontemporal_load(lse_s + row);
+    }
   };
-  // Wave w takes the tiles t_begin + 16w + step*i; tile i lives in ring slot i % PF.
-  constexpr int PF = kPass2Ahead, step = 16 * NW;
-  u32x4 q[PF][KS];
-  float lq[PF];
+  // Wave w takes the steps t_begin + 16 TT w + step*i; step i lives in ring slot i % PF.
+  constexpr int PF = kPass2Ahead, step = 16 * TT * NW;
+  u32x4 q[PF][TT][KS];
+  float lq[PF][TT];
 #pragma unroll
-  for (int p = 0; p < PF; ++p) load_q(t_begin + 16 * w + step * p, q[p], lq[p]);
+  for (int p = 0; p < PF; ++p) load_q(t_begin + 16 * TT * w + step * p, q[p], lq[p]);
   stage_store(ust, &u_lds[0][0][0]);
   stage_store(wst, &w_lds[0][0][0]);
   // above 256 anchors m is padded to a multiple of 128: up to eight padded tiles
@@ -539,79 +551,97 @@ void pass2_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   pad_mask_tiles<AT, NPAD>(g, m, mask);
   __syncthreads();
 
-  for (int tb = t_begin + 16 * w; tb < t_end; tb += step * PF) {
+  for (int tb = t_begin + 16 * TT * w; tb < t_end; tb += step * PF) {
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
     const int t0 = tb + step * p;
     if (t0 >= t_end) break;   // uniform per wave
-    const int row = t0 + c;
-    const bool ok = row < t_end;
-    // a1 (transposed): s[j] lane (c,g): token c, anchors 16j + 4g + r.
-    f32x4 s[AT];
+    // a1 (transposed): s[tt][j] lane (c,g): token t0 + 16tt + c, anchors 16j + 4g + r.
+    f32x4 s[TT][AT];
 #pragma unroll
     for (int j = 0; j < AT; ++j) {
       // keeps the LDS operand loads of later tiles from being hoisted (register budget)
       if (AT >= 8 && j % 4 == 0) asm volatile("" ::: "memory");
       // padded anchors (>= m) lie in the last NPAD tiles and start from -inf
-      f32x4 acc = (j >= AT - NPAD) ? mask[j - (AT - NPAD)] : zero4();
+      const f32x4 a0 = (j >= AT - NPAD) ? mask[j - (AT - NPAD)] : zero4();
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) acc = mfma_bf16(as_bf16x8(u_lds[j][kk][lane]), as_bf16x8(q[p][kk]), acc);
-      s[j] = acc;
+      for (int tt = 0; tt < TT; ++tt) s[tt][j] = a0;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const bf16x8 u = as_bf16x8(u_lds[j][kk][lane]);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) s[tt][j] = mfma_bf16(u, as_bf16x8(q[p][tt][kk]), s[tt][j]);
+      }
     }
-    bf16x8 abf[MP];
+    bf16x8 abf[TT][MP];
+    float nl[TT];
     if constexpr (LSE) {
-      // a2 with the token's log-sum-exp L from pass 1: A = exp2(c2 s - L), already
-      // normalised (padded anchors start from -inf and give 0)
-      const float nl = -lq[p];
-      load_q(t0 + step * PF, q[p], lq[p]);   // the slot is free: the tile PF steps ahead
 #pragma unroll
-      for (int j = 0; j < AT; ++j)
+      for (int tt = 0; tt < TT; ++tt) nl[tt] = -lq[p][tt];
+    }
+    // the slot is free: request the wave's step PF steps ahead into it
+    load_q(t0 + step * PF, q[p], lq[p]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[j][r] = exp2_fast(fmaf(s[j][r], c2, nl));
+    for (int tt = 0; tt < TT; ++tt) {
+      if constexpr (LSE) {
+        // a2 with the token's log-sum-exp L from pass 1: A = exp2(c2 s - L), already
+        // normalised (padded anchors start from -inf and give 0)
 #pragma unroll
-      for (int jj = 0; jj < MP; ++jj) abf[jj] = pack_bf16(s[2 * jj], s[2 * jj + 1]);
-    } else {
-      // the slot is free: request the wave's tile PF steps ahead into it
-      load_q(t0 + step * PF, q[p], lq[p]);
-      // a2
-      float mx = s[0][0];
+        for (int j = 0; j < AT; ++j)
 #pragma unroll
-      for (int j = 0; j < AT; ++j)
+          for (int r = 0; r < 4; ++r) s[tt][j][r] = exp2_fast(fmaf(s[tt][j][r], c2, nl[tt]));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[j][r]);
-      mx = xor32_max(xor16_max(mx));
-      const float mneg = -mx * c2;
-      float z = 0.f;
+        for (int jj = 0; jj < MP; ++jj) abf[tt][jj] = pack_bf16(s[tt][2 * jj], s[tt][2 * jj + 1]);
+      } else {
+        // a2
+        float mx = s[tt][0][0];
 #pragma unroll
-      for (int j = 0; j < AT; ++j)
+        for (int j = 0; j < AT; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = exp2_fast(fmaf(s[j][r], c2, mneg));
-          s[j][r] = e;
-          z += e;
-        }
-      z = xor32_sum(xor16_sum(z));
-      const float inv = __builtin_amdgcn_rcpf(z);   // z >= 1 (the maximum adds 1)
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[tt][j][r]);
+        mx = xor32_max(xor16_max(mx));
+        const float mneg = -mx * c2;
+        float z = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < MP; ++jj) abf[jj] = pack_bf16(s[2 * jj] * inv, s[2 * jj + 1] * inv);
+        for (int j = 0; j < AT; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = exp2_fast(fmaf(s[tt][j][r], c2, mneg));
+            s[tt][j][r] = e;
+            z += e;
+          }
+        z = xor32_sum(xor16_sum(z));
+        const float inv = __builtin_amdgcn_rcpf(z);   // z >= 1 (the maximum adds 1)
+#pragma unroll
+        for (int jj = 0; jj < MP; ++jj)
+          abf[tt][jj] = pack_bf16(s[tt][2 * jj] * inv, s[tt][2 * jj + 1] * inv);
+      }
     }
     // a5: H^T = W^T A^T; lane (c,g) ends with token c, dims out_dim_c(dt2, 4g + r), i.e.
     // 32h + 8g .. + 7 in tiles 2h and 2h + 1.
-    f32x4 hacc[DT];
+    f32x4 hacc[TT][DT];
 #pragma unroll
     for (int dt2 = 0; dt2 < DT; ++dt2) {
       if (AT >= 8) asm volatile("" ::: "memory");
-      f32x4 acc = zero4();
 #pragma unroll
-      for (int jj = 0; jj < MP; ++jj) acc = mfma_bf16(as_bf16x8(w_lds[dt2][jj][lane]), abf[jj], acc);
-      hacc[dt2] = acc;
+      for (int tt = 0; tt < TT; ++tt) hacc[tt][dt2] = zero4();
+#pragma unroll
+      for (int jj = 0; jj < MP; ++jj) {
+        const bf16x8 wv = as_bf16x8(w_lds[dt2][jj][lane]);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) hacc[tt][dt2] = mfma_bf16(wv, abf[tt][jj], hacc[tt][dt2]);
+      }
     }
-    if (ok) {
-      __bf16* dst = H + ob + view_row(ow, row) + 8 * g;
 #pragma unroll
-      for (int hh = 0; hh < DT / 2; ++hh)
-        __builtin_nontemporal_store(as_u32x4(pack_bf16(hacc[2 * hh], hacc[2 * hh + 1])),
-                                    (u32x4*)(dst + 32 * hh));
+    for (int tt = 0; tt < TT; ++tt) {
+      const int row = t0 + 16 * tt + c;
+      if (row < t_end) {
+        __bf16* dst = H + ob + view_row(ow, row) + 8 * g;
+#pragma unroll
+        for (int hh = 0; hh < DT / 2; ++hh)
+          __builtin_nontemporal_store(as_u32x4(pack_bf16(hacc[tt][2 * hh], hacc[tt][2 * hh + 1])),
+                                      (u32x4*)(dst + 32 * hh));
+      }
     }
   }
   }
