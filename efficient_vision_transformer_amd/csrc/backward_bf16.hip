@@ -192,7 +192,7 @@ void bwd_tokens_rm(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   const int rounds = (t_end - t_begin + TOK - 1) / TOK;
   u32x4 qv[KS], vv[KS], gv[KS];
   {
-    const int row = t_begin + 16 * w + c;
+    const int row = min(t_begin + 16 * w + c, t_end - 1);
     load_rows<D>(Q, qb, bv.q.st, row, n, g, qv);
     load_rows<D>(V, vb, bv.v.st, row, n, g, vv);
     load_rows<D>(G, gb, bv.g.st, row, n, g, gv);
@@ -202,11 +202,13 @@ void bwd_tokens_rm(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   for (int r = 0; r < rounds; ++r) {
     const int row = t_begin + TOK * r + 16 * w + c;
     const bool ok = row < t_end;
-    // next round's rows (clamped to the slice's last row past its end)
+    // next round's rows (past the chunk: its last row, which is cached, rather than the
+    // next chunk's rows)
     u32x4 nq[KS], nv[KS], ng[KS];
-    load_rows<D>(Q, qb, bv.q.st, row + TOK, n, g, nq);
-    load_rows<D>(V, vb, bv.v.st, row + TOK, n, g, nv);
-    load_rows<D>(G, gb, bv.g.st, row + TOK, n, g, ng);
+    const int nrow = min(row + TOK, t_end - 1);
+    load_rows<D>(Q, qb, bv.q.st, nrow, n, g, nq);
+    load_rows<D>(V, vb, bv.v.st, nrow, n, g, nv);
+    load_rows<D>(G, gb, bv.g.st, nrow, n, g, ng);
     asm volatile("" ::: "memory");   // LDS operands are re-read each round, not hoisted
     // A (normalised, bf16): ab[jj] lane (c,g) holds token c, anchors 32jj + 4g .. + 3
     // (slots 0-3) and 32jj + 16 + 4g .. + 3 (slots 4-7).
