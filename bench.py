@@ -463,7 +463,7 @@ def bench_nystrom(args, ctx, x, dev) -> dict:
         "achieved_tflops": round(flops / (ms * 1e-3) / 1e12, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "the whole step (five launches)",
+                     "kernel": "the whole step (three launches)",
                      "per_launch": {"algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
                                     "avg_duration_us": round(ms * 1e3, 3)}},
     }
