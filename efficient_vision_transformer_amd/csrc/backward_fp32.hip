@@ -399,14 +399,17 @@ static hipError_t dispatch_bwd_fp32(const Geometry& g, const SplitPlan& p,
     case 4: return go_bwd_fp32<D, 4>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
     case 6: return go_bwd_fp32<D, 6>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
     case 8: return go_bwd_fp32<D, 8>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
-    case 12: return go_bwd_fp32<D, 12>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
-    case 16: return go_bwd_fp32<D, 16>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
+    // at d = 128 the U and dP blocks of the token pass take the LDS up to 128 anchors
+    case 12: if constexpr (D <= 64) return go_bwd_fp32<D, 12>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
+             return hipErrorInvalidValue;
+    case 16: if constexpr (D <= 64) return go_bwd_fp32<D, 16>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
+             return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
 bool bwd_fp32_supported(const Geometry& g) {
-  return (g.d == 32 || g.d == 64) && g.at <= 16;
+  return ((g.d == 32 || g.d == 64) && g.at <= 16) || (g.d == 128 && g.at <= 8);
 }
 
 hipError_t launch_backward_fp32(const Geometry& g, const SplitPlan& p,
@@ -415,6 +418,7 @@ hipError_t launch_backward_fp32(const Geometry& g, const SplitPlan& p,
                                 void* dV, hipStream_t s) {
   if (!bwd_fp32_supported(g)) return hipErrorInvalidValue;
   if (g.d == 64) return dispatch_bwd_fp32<64>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
+  if (g.d == 128) return dispatch_bwd_fp32<128>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
   return dispatch_bwd_fp32<32>(g, p, wb, bv, Q, U, V, G, dQ, dU, dV, s);
 }
 

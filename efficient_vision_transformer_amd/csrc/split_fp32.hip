@@ -428,8 +428,12 @@ hipError_t launch_pass1_fp32(const Geometry& g, const SplitPlan& p, const void* 
       case 4: AA_P1F(4); break;
       case 6: AA_P1F(6); break;
       case 8: AA_P1F(8); break;
-      case 12: AA_P1F(12); break;
-      case 16: AA_P1F(16); break;
+      case 12:
+        if constexpr (d <= 64) { AA_P1F(12); break; }
+        return hipErrorInvalidValue;
+      case 16:
+        if constexpr (d <= 64) { AA_P1F(16); break; }
+        return hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
 #undef AA_P1F
@@ -437,6 +441,7 @@ hipError_t launch_pass1_fp32(const Geometry& g, const SplitPlan& p, const void* 
   };
   if (g.d == 64) return at(std::integral_constant<int, 64>{});
   if (g.d == 32) return at(std::integral_constant<int, 32>{});
+  if (g.d == 128) return at(std::integral_constant<int, 128>{});   // up to 128 anchors
   return hipErrorInvalidValue;
 }
 

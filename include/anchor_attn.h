@@ -228,9 +228,9 @@ anchor_attn_status_t anchor_attn_nystrom_forward(anchor_attn_ctx* ctx, const voi
  * (dU is zero when B*h*n == 0); they must not overlap each other or any input.  The
  * context's workspace grows as for the split plan (the first call of a larger shape may
  * synchronize).  Domain: as anchor_attn_forward, with dtype BF16 and either d in {32, 64}
- * with m <= 256 or d = 128 with m <= 128, or dtype FP32 with d in {32, 64} and m <= 256
- * (split plan only: a context whose plan is FUSED returns NOT_SUPPORTED for fp32); larger
- * m returns NOT_SUPPORTED.
+ * with m <= 256 or d = 128 with m <= 128, or dtype FP32 with d in {32, 64} and m <= 256 or
+ * d = 128 and m <= 128 (split plan only: a context whose plan is FUSED returns
+ * NOT_SUPPORTED for fp32); larger m returns NOT_SUPPORTED.
  * Errors as anchor_attn_forward: nothing is enqueued and no output is touched. */
 anchor_attn_status_t anchor_attn_backward(anchor_attn_ctx* ctx,
                                           const void* Q, const void* U, const void* V,

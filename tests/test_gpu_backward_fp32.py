@@ -65,6 +65,10 @@ SHAPES = [
     (1, 1, 500, 150, 32),
     (1, 2, 1000, 256, 64),
     (2, 2, 3000, 200, 64),
+    (2, 2, 77, 9, 128),       # d = 128: 32, 64, 96 and 128 padded anchors
+    (1, 2, 300, 64, 128),
+    (1, 1, 1000, 90, 128),
+    (1, 2, 2051, 128, 128),
 ]
 
 
@@ -129,8 +133,8 @@ def test_backward_fp32_plans(ctxs, dev):
     with pytest.raises(RuntimeError, match="status 2"):
         ctxs["auto"].backward(Q, U2, V, Q.clone())
     Q8 = torch.zeros((1, 1, 10, 128), dtype=torch.float32, device=dev)
-    U8 = torch.zeros((1, 4, 128), dtype=torch.float32, device=dev)
-    with pytest.raises(RuntimeError, match="status 2"):
+    U8 = torch.zeros((1, 129, 128), dtype=torch.float32, device=dev)
+    with pytest.raises(RuntimeError, match="status 2"):   # d = 128 above 128 anchors
         ctxs["auto"].backward(Q8, U8, Q8.clone(), Q8.clone())
 
 

@@ -165,11 +165,11 @@ def test_d128_strided_views_match_contiguous(ctxs, dev):
 
 
 def test_d128_refusals(ctxs, dev):
-    """d = 128 runs the bf16 forward, the fp32 forward (up to 128 anchors), the bf16
-    backward (up to 128 anchors), the linear attention and Nystrom attention (up to 96
-    landmarks): the fused plan beyond its limits (here 300 tokens with 16 anchors), the fp32
-    forward above 128 anchors, the fp32 backward, the bf16 backward above 128 anchors and
-    Nystrom attention above 96 landmarks refuse it (NOT_SUPPORTED)."""
+    """d = 128 runs the bf16 and fp32 forwards and backwards (fp32 and the backward up to 128
+    anchors), the linear attention and Nystrom attention (up to 96 landmarks): the fused
+    plan beyond its limits (here 300 tokens with 16 anchors), the fp32 forward and either
+    backward above 128 anchors and Nystrom attention above 96 landmarks refuse it
+    (NOT_SUPPORTED)."""
     import torch
     x = random_case(78, 1, 2, 300, 16, 128, dtype="bf16")
     Q, U, V = to_device(x, dev)
@@ -179,7 +179,7 @@ def test_d128_refusals(ctxs, dev):
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
         ctxs["auto"].forward(Q.float(), U130, V.float())
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
-        ctxs["auto"].backward(Q.float(), U.float(), V.float(), torch.ones_like(Q.float()))
+        ctxs["auto"].backward(Q.float(), U130, V.float(), torch.ones_like(Q.float()))
     U129 = torch.zeros((2, 129, 128), dtype=torch.bfloat16, device=dev)
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
         ctxs["auto"].backward(Q, U129, V, torch.ones_like(Q))
