@@ -138,8 +138,11 @@ anchor_attn_status_t check_shape(int B, int h, int n, int m, int d, int dtype_ra
 SplitPlan make_split_plan(const Geometry& g, anchor_attn_dtype_t dtype, int num_cus) {
   SplitPlan p{};
   const int n = g.n;
-  // Pass 1: aim for ~2 workgroups per CU, chunks a multiple of the 128-token block.
-  const long long want1 = 2LL * num_cus;
+  // Pass 1: chunks a multiple of the 128-token block; about one workgroup per CU for the
+  // token-split bf16 pass 1 (up to 128 anchors: fewer, longer chunks halve the partials
+  // and measured faster), about two for the anchor-split one and for fp32.
+  const bool one_per_cu = dtype == ANCHOR_ATTN_BF16 && g.at <= 8;
+  const long long want1 = (one_per_cu ? 1LL : 2LL) * num_cus;
   int max_chunks1 = (n + aa::kPass1Block - 1) / aa::kPass1Block;
   int c1 = (int)std::min<long long>(max_chunks1, std::max<long long>(1, (want1 + g.slices - 1) / g.slices));
   int len1 = (n + c1 - 1) / c1;
