@@ -149,8 +149,12 @@ SplitPlan make_split_plan(const Geometry& g, anchor_attn_dtype_t dtype, int num_
   len1 = (len1 + aa::kPass1Block - 1) / aa::kPass1Block * aa::kPass1Block;
   p.chunk_len1 = len1;
   p.chunks1 = (n + len1 - 1) / len1;
-  // Pass 2: ~4 workgroups per CU, chunks a multiple of the 64-token block.
-  const long long want2 = 4LL * num_cus;
+  // Pass 2: chunks a multiple of the 64-token block; about four workgroups per CU, two for
+  // the bf16 pass 2 with two 16-token tiles per step (129 to 256 anchors; long step 141.9
+  // -> 139.5 us, while two made the dense step slower, 52.7 -> 53.9 us, and eight were
+  // slower at both).
+  const bool two_tile_pass2 = dtype == ANCHOR_ATTN_BF16 && g.d <= 64 && g.at > 8 && g.at <= 16;
+  const long long want2 = (two_tile_pass2 ? 2LL : 4LL) * num_cus;
   int max_chunks2 = (n + aa::kPass2Block - 1) / aa::kPass2Block;
   int c2 = (int)std::min<long long>(max_chunks2, std::max<long long>(1, (want2 + g.slices - 1) / g.slices));
   int len2 = (n + c2 - 1) / c2;
@@ -170,7 +174,8 @@ SplitPlan make_split_plan(const Geometry& g, anchor_attn_dtype_t dtype, int num_
 enum class Chosen { Fused, Split, Unsupported };
 
 // Linear attention split plan: chunks of whole 128-token blocks (four waves x one
-// 32-token pair), about two pass-1 and four pass-2 workgroups per CU.
+// 32-token pair), about one pass-1 workgroup per CU (half the partials of two: dense
+// 41.7 -> 39.5 us, long 71.9 -> 69.0 us) and four pass-2 workgroups per CU.
 aa::LinearSplitPlan make_linear_plan(const Geometry& g, int num_cus) {
   aa::LinearSplitPlan p{};
   const int n = g.n, blk = 128;
@@ -182,7 +187,7 @@ aa::LinearSplitPlan make_linear_plan(const Geometry& g, int num_cus) {
     *len = l;
     *chunks = (n + l - 1) / l;
   };
-  chunking(2LL * num_cus, &p.chunks1, &p.chunk_len1);
+  chunking(1LL * num_cus, &p.chunks1, &p.chunk_len1);
   chunking(4LL * num_cus, &p.chunks2, &p.chunk_len2);
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   p.part_bytes = al((size_t)g.slices * p.chunks1 * g.d * g.d * sizeof(float));
