@@ -140,8 +140,10 @@ SplitPlan make_split_plan(const Geometry& g, anchor_attn_dtype_t dtype, int num_
   const int n = g.n;
   // Pass 1: chunks a multiple of the 128-token block; about one workgroup per CU for the
   // token-split bf16 pass 1 (up to 128 anchors: fewer, longer chunks halve the partials
-  // and measured faster), about two for the anchor-split one and for fp32.
-  const bool one_per_cu = dtype == ANCHOR_ATTN_BF16 && g.at <= 8;
+  // and measured faster) and for the eight-wave anchor-split one above 256 anchors (one
+  // fits a CU), about two for the four-wave anchor-split one and for fp32 (one was slower
+  // for both: long bf16 147.6 -> 165.9 us, long fp32 716 -> 755 us).
+  const bool one_per_cu = dtype == ANCHOR_ATTN_BF16 && (g.at <= 8 || g.at >= 24);
   const long long want1 = (one_per_cu ? 1LL : 2LL) * num_cus;
   int max_chunks1 = (n + aa::kPass1Block - 1) / aa::kPass1Block;
   int c1 = (int)std::min<long long>(max_chunks1, std::max<long long>(1, (want1 + g.slices - 1) / g.slices));
@@ -152,9 +154,10 @@ SplitPlan make_split_plan(const Geometry& g, anchor_attn_dtype_t dtype, int num_
   // Pass 2: chunks a multiple of the 64-token block; about four workgroups per CU, two for
   // the bf16 pass 2 with two 16-token tiles per step (129 to 256 anchors; long step 141.9
   // -> 139.5 us, while two made the dense step slower, 52.7 -> 53.9 us, and eight were
-  // slower at both).
+  // slower at both), one for the eight-wave pass 2 above 256 anchors (one fits a CU).
   const bool two_tile_pass2 = dtype == ANCHOR_ATTN_BF16 && g.d <= 64 && g.at > 8 && g.at <= 16;
-  const long long want2 = (two_tile_pass2 ? 2LL : 4LL) * num_cus;
+  const bool wide_pass2 = dtype == ANCHOR_ATTN_BF16 && g.at >= 24;
+  const long long want2 = (wide_pass2 ? 1LL : two_tile_pass2 ? 2LL : 4LL) * num_cus;
   int max_chunks2 = (n + aa::kPass2Block - 1) / aa::kPass2Block;
   int c2 = (int)std::min<long long>(max_chunks2, std::max<long long>(1, (want2 + g.slices - 1) / g.slices));
   int len2 = (n + c2 - 1) / c2;

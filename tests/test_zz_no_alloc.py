@@ -106,16 +106,16 @@ def test_noalloc_on_a_context_that_cannot_allocate(lib, monkeypatch):
 
 
 def test_noalloc_refuses_partials_beyond_the_scratch(lib):
-    """512 anchors over 32 slices of 16384 tokens need more than 64 MiB of partials:
+    """512 anchors over 600 slices (one chunk each) need more than 64 MiB of partials:
     NOT_SUPPORTED, nothing enqueued (the output keeps its contents)."""
     import torch
     from efficient_vision_transformer_amd import AnchorAttention
     dev = torch.device("cuda:0")
     ctx = AnchorAttention(dev, plan="split")
-    desc = ctx.describe(2, 16, 16384, 512, 64, "bf16")
+    desc = ctx.describe(50, 12, 128, 512, 64, "bf16")
     print(f"  {desc}", flush=True)
     assert int(desc.split("workspace=")[1].split(";")[0]) > (64 << 20)
-    x = random_case(600, 2, 16, 16384, 512, 64, dtype="bf16")
+    x = random_case(600, 50, 12, 128, 512, 64, dtype="bf16")
     Q, U, V = to_device(x, dev)
     H = torch.full_like(Q, 7.0)
     assert _call(lib, "anchor_attn_forward_noalloc", ctx, x, Q, U, V, H) == 2   # NOT_SUPPORTED
