@@ -49,11 +49,11 @@ _SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",
                   "efficient_vision_transformer_amd/csrc/device_common.h",
                   "efficient_vision_transformer_amd/csrc/geometry.h",
                   "efficient_vision_transformer_amd/csrc/pass2_layout.h",
-                  "efficient_vision_transformer_amd/csrc/anchor_attn_api.cpp"]   # the chunking
-MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "6c77b3a795ff9f58",
-                                             "read_bytes": 111442589, "write_bytes": 46431682}
-MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "6c77b3a795ff9f58",
-                                               "read_bytes": 244299476, "write_bytes": 111264215}
+                  "efficient_vision_transformer_amd/csrc/split_plan.h"]   # the chunking
+MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "7878fe12befeb8c7",
+                                             "read_bytes": 111434160, "write_bytes": 46541494}
+MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "7878fe12befeb8c7",
+                                               "read_bytes": 244303122, "write_bytes": 111411934}
 
 
 def measured_traffic(workload: str, plan: str):

@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "kernels.h"
+#include "split_plan.h"
 
 struct anchor_attn_ctx {
   int device = 0;
@@ -136,42 +137,7 @@ anchor_attn_status_t check_shape(int B, int h, int n, int m, int d, int dtype_ra
 }
 
 SplitPlan make_split_plan(const Geometry& g, anchor_attn_dtype_t dtype, int num_cus) {
-  SplitPlan p{};
-  const int n = g.n;
-  // Pass 1: chunks a multiple of the 128-token block; about one workgroup per CU for the
-  // token-split bf16 pass 1 (up to 128 anchors: fewer, longer chunks halve the partials
-  // and measured faster) and for the eight-wave anchor-split one above 256 anchors (one
-  // fits a CU), about two for the four-wave anchor-split one and for fp32 (one was slower
-  // for both: long bf16 147.6 -> 165.9 us, long fp32 716 -> 755 us).
-  const bool one_per_cu = dtype == ANCHOR_ATTN_BF16 && (g.at <= 8 || g.at >= 24);
-  const long long want1 = (one_per_cu ? 1LL : 2LL) * num_cus;
-  int max_chunks1 = (n + aa::kPass1Block - 1) / aa::kPass1Block;
-  int c1 = (int)std::min<long long>(max_chunks1, std::max<long long>(1, (want1 + g.slices - 1) / g.slices));
-  int len1 = (n + c1 - 1) / c1;
-  len1 = (len1 + aa::kPass1Block - 1) / aa::kPass1Block * aa::kPass1Block;
-  p.chunk_len1 = len1;
-  p.chunks1 = (n + len1 - 1) / len1;
-  // Pass 2: chunks a multiple of the 64-token block; about four workgroups per CU, two for
-  // the bf16 pass 2 with two 16-token tiles per step (129 to 256 anchors; long step 141.9
-  // -> 139.5 us, while two made the dense step slower, 52.7 -> 53.9 us, and eight were
-  // slower at both), one for the eight-wave pass 2 above 256 anchors (one fits a CU).
-  const bool two_tile_pass2 = dtype == ANCHOR_ATTN_BF16 && g.d <= 64 && g.at > 8 && g.at <= 16;
-  const bool wide_pass2 = dtype == ANCHOR_ATTN_BF16 && g.at >= 24;
-  const long long want2 = (wide_pass2 ? 1LL : two_tile_pass2 ? 2LL : 4LL) * num_cus;
-  int max_chunks2 = (n + aa::kPass2Block - 1) / aa::kPass2Block;
-  int c2 = (int)std::min<long long>(max_chunks2, std::max<long long>(1, (want2 + g.slices - 1) / g.slices));
-  int len2 = (n + c2 - 1) / c2;
-  len2 = (len2 + aa::kPass2Block - 1) / aa::kPass2Block * aa::kPass2Block;
-  p.chunk_len2 = len2;
-  p.chunks2 = (n + len2 - 1) / len2;
-  const size_t es = (dtype == ANCHOR_ATTN_BF16) ? 2 : 4;
-  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  p.part_bytes = al((size_t)g.slices * p.chunks1 * g.m_pad * g.d * sizeof(float));
-  p.dpart_bytes = al((size_t)g.slices * p.chunks1 * g.m_pad * sizeof(float));
-  p.w_bytes = al((size_t)g.slices * g.m_pad * g.d * es);
-  // each token's log-sum-exp, passed from pass 1 to pass 2 above 128 anchors (bf16)
-  p.lse_bytes = (dtype == ANCHOR_ATTN_BF16 && g.at > 8) ? al((size_t)g.slices * n * sizeof(float)) : 0;
-  return p;
+  return aa::split_plan(g, dtype == ANCHOR_ATTN_BF16, num_cus);
 }
 
 enum class Chosen { Fused, Split, Unsupported };
@@ -827,6 +793,7 @@ static anchor_attn_status_t backward_strided_impl(
       wb.wu = w; w += ops;
       wb.dprm = w; w += ops;
       wb.dd = (float*)w;
+      aa::token_pass_chunks(g, p, ctx->num_cus, &wb.chunks_t, &wb.chunk_len_t);
       e = aa::launch_backward_bf16(g, p, wb, bv, Q, U, V, dH, dQ, dU, dV, s);
     }
     if (e != hipSuccess) {

@@ -419,13 +419,13 @@ static hipError_t go_bwd(const Geometry& g, const SplitPlan& p, const BackwardBu
   if (e != hipSuccess) return e;
   bwd_finalize<D><<<dim3((unsigned)(g.slices * AT)), dim3(256), 0, s>>>(
       wb.partP, wb.partG, wb.dpart, (__bf16*)wb.wu, (__bf16*)wb.dprm, wb.dd, p.chunks1, AT);
-  bwd_tokens_rm<D, AT><<<dim3((unsigned)(g.slices * p.chunks1)), dim3(4 * kWave), 0, s>>>(
+  bwd_tokens_rm<D, AT><<<dim3((unsigned)(g.slices * wb.chunks_t)), dim3(4 * kWave), 0, s>>>(
       (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (const __bf16*)G,
       (const u32x4*)wb.wu, (const __bf16*)wb.dprm, wb.dd, (__bf16*)dQ, (__bf16*)dV, wb.partU,
-      bv, g.h, g.n, g.m, p.chunks1, p.chunk_len1, g.c2, cs);
+      bv, g.h, g.n, g.m, wb.chunks_t, wb.chunk_len_t, g.c2, cs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_du_reduce_bf16(g, wb.partU, p.chunks1, dU, s);
+  return launch_du_reduce_bf16(g, wb.partU, wb.chunks_t, dU, s);
 }
 
 template <int D>

@@ -23,7 +23,8 @@ struct BackwardBuffers {
   void* wu;       // W, logits-layout operands     [slice][AT][KS][64] x 16 B
   void* dprm;     // dP, row-major bf16            [slice][m_pad][d]
   float* dd;      // dDelta                        [slice][16 AT]
-  float* partU;   // partials of dS^T Q            [slice][chunk][AT][DT][256]
+  float* partU;   // partials of dS^T Q            [slice][chunk_t][AT][DT][256]
+  int chunks_t, chunk_len_t;   // the token pass's chunks (at most pass 1's)
 };
 // Views of the backward's tensors: Q, V, dH (inputs) and dQ, dV (outputs).
 struct BwdViews {
