@@ -144,7 +144,8 @@ enum class Chosen { Fused, Split, Unsupported };
 
 // Linear attention split plan: chunks of whole 128-token blocks (four waves x one
 // 32-token pair), about one pass-1 workgroup per CU (half the partials of two: dense
-// 41.7 -> 39.5 us, long 71.9 -> 69.0 us) and four pass-2 workgroups per CU.
+// 41.7 -> 39.5 us, long 71.9 -> 69.0 us) and sixteen pass-2 workgroups per CU (against
+// four: dense 39.4 -> 36.9 us, long 69.4 -> 63.8 us; eight gave 37.0 and 68.1).
 aa::LinearSplitPlan make_linear_plan(const Geometry& g, int num_cus) {
   aa::LinearSplitPlan p{};
   const int n = g.n, blk = 128;
@@ -157,7 +158,7 @@ aa::LinearSplitPlan make_linear_plan(const Geometry& g, int num_cus) {
     *chunks = (n + l - 1) / l;
   };
   chunking(1LL * num_cus, &p.chunks1, &p.chunk_len1);
-  chunking(4LL * num_cus, &p.chunks2, &p.chunk_len2);
+  chunking(16LL * num_cus, &p.chunks2, &p.chunk_len2);
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   p.part_bytes = al((size_t)g.slices * p.chunks1 * g.d * g.d * sizeof(float));
   p.zpart_bytes = al((size_t)g.slices * p.chunks1 * g.d * sizeof(float));

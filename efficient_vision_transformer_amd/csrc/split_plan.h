@@ -30,9 +30,11 @@ inline SplitPlan split_plan(const Geometry& g, bool bf16, int num_cus) {
   // Pass 2: chunks a multiple of the 64-token block; about four workgroups per CU, two for
   // the bf16 pass 2 with two 16-token tiles per step (129 to 256 anchors; long step 141.9
   // -> 139.5 us, while two made the dense step slower, 52.7 -> 53.9 us, and eight were
-  // slower at both), one for the eight-wave pass 2 above 256 anchors (one fits a CU).
+  // slower at both), one for the eight-wave passes 2 whose U and W fill the LDS (one fits a
+  // CU): bf16 above 256 anchors, fp32 with more than 80 KB of them (long fp32 708 -> 695
+  // us).
   const bool two_tile_pass2 = bf16 && g.d <= 64 && g.at > 8 && g.at <= 16;
-  const bool wide_pass2 = bf16 && g.at >= 24;
+  const bool wide_pass2 = bf16 ? g.at >= 24 : (long long)g.at * g.d * 128 > 80 * 1024;
   const long long want2 = (wide_pass2 ? 1LL : two_tile_pass2 ? 2LL : 4LL) * num_cus;
   int max_chunks2 = (n + kPass2Block - 1) / kPass2Block;
   int c2 = (int)std::min<long long>(max_chunks2, std::max<long long>(1, (want2 + g.slices - 1) / g.slices));
