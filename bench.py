@@ -50,10 +50,10 @@ _SPLIT_SOURCES = ["efficient_vision_transformer_amd/csrc/split_bf16.hip",
                   "efficient_vision_transformer_amd/csrc/geometry.h",
                   "efficient_vision_transformer_amd/csrc/pass2_layout.h",
                   "efficient_vision_transformer_amd/csrc/split_plan.h"]   # the chunking
-MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "1edfd2d0425d4ddd",
-                                             "read_bytes": 111424909, "write_bytes": 46756527}
-MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "1edfd2d0425d4ddd",
-                                               "read_bytes": 244302749, "write_bytes": 111171671}
+MEASURED_TRAFFIC[("dense_64x64", "split")] = {"sources": _SPLIT_SOURCES, "sha": "379fa99f948d2665",
+                                             "read_bytes": 111428694, "write_bytes": 46509977}
+MEASURED_TRAFFIC[("long_16k_bf16", "split")] = {"sources": _SPLIT_SOURCES, "sha": "379fa99f948d2665",
+                                               "read_bytes": 244294440, "write_bytes": 111205929}
 
 
 def measured_traffic(workload: str, plan: str):

@@ -413,9 +413,15 @@ static hipError_t go_bwd(const Geometry& g, const SplitPlan& p, const BackwardBu
   gv.vw.q = gg.vw.q = bv.q;
   gv.vw.v = bv.v;
   gg.vw.v = bv.g;
-  hipError_t e = launch_pass1_bf16(gv, p, Q, U, V, wb.partP, wb.dpart, s);
-  if (e != hipSuccess) return e;
-  e = launch_pass1_bf16(gg, p, Q, U, G, wb.partG, wb.dpart, s);
+  hipError_t e;
+  if constexpr (D <= 64) {
+    // one pass 1 for both: Q read and A formed once (at d = 128 its registers would spill)
+    e = launch_pass1_dual_bf16(gv, p, Q, U, V, bv.v, G, bv.g, wb.partP, wb.partG, wb.dpart, s);
+  } else {
+    e = launch_pass1_bf16(gv, p, Q, U, V, wb.partP, wb.dpart, s);
+    if (e != hipSuccess) return e;
+    e = launch_pass1_bf16(gg, p, Q, U, G, wb.partG, wb.dpart, s);
+  }
   if (e != hipSuccess) return e;
   bwd_finalize<D><<<dim3((unsigned)(g.slices * AT)), dim3(256), 0, s>>>(
       wb.partP, wb.partG, wb.dpart, (__bf16*)wb.wu, (__bf16*)wb.dprm, wb.dd, p.chunks1, AT);

@@ -15,6 +15,12 @@ hipError_t launch_split_bf16(const Geometry& g, const SplitPlan& p, const void* 
 // X = dH).
 hipError_t launch_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* Q, const void* U,
                              const void* X, float* part, float* dpart, hipStream_t stream);
+// The backward's pass 1 on V (view vw) and on G (view gw) in one launch, up to 256 anchors
+// at d <= 64: A formed once, A^T V and Delta into part / dpart, A^T G into partG.
+hipError_t launch_pass1_dual_bf16(const Geometry& g, const SplitPlan& p, const void* Q,
+                                  const void* U, const void* V, const View& vw, const void* G,
+                                  const View& gw, float* part, float* partG, float* dpart,
+                                  hipStream_t s);
 // Workspace sections of the backward (see bwd_finalize / bwd_tokens).
 struct BackwardBuffers {
   float* partP;   // pass-1 partials of A^T V      [slice][chunk][AT][DT][256]

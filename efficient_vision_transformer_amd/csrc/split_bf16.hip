@@ -34,12 +34,16 @@ namespace aa {
 // LDS block and accumulates its (16-anchor, 16-dim) tiles of A^T V and Delta, reading
 // both operands (tokens on the contraction axis) with the transposing LDS read.
 // Partials leave in accumulator layout with dim tile dt holding dims 16dt .. 16dt + 15.
-template <int D, int AT, int NW = 4>
-__global__ __launch_bounds__(NW * kWave, 2)
+// DUAL (the backward): G ([token][dim], view gw) is staged beside V and A^T G accumulated
+// into partG from the same A (no Delta), so Q is read and A formed once for both.
+template <int D, int AT, int NW = 4, bool DUAL = false>
+__global__ __launch_bounds__(NW * kWave, DUAL ? 1 : 2)
 void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                  const __bf16* __restrict__ V, float* __restrict__ part,
                  float* __restrict__ dpart, View qw, View xw, int h, int n, int m, int chunks,
-                 int chunk_len, float c2, float* __restrict__ lse) {
+                 int chunk_len, float c2, float* __restrict__ lse,
+                 const __bf16* __restrict__ G = nullptr, View gw = View{0, 0, 0},
+                 float* __restrict__ partG = nullptr) {
   constexpr int J = AT / NW, KS = D / 32, DT = D / 16;
   constexpr int AS = 80;                     // A row stride (16J + padding, bank-spread)
   constexpr int VS = tr_stride<D>();
@@ -52,24 +56,27 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // anchor group
   const int c = lane & 15, g = lane >> 4;
   const size_t qb = view_base(qw, slice, h), xb = view_base(xw, slice, h);
+  const size_t gb = DUAL ? view_base(gw, slice, h) : 0;
   const int t_begin = chunk * chunk_len;
   const int t_end = min(n, t_begin + chunk_len);
 
+  __shared__ __attribute__((aligned(16))) __bf16 g_lds[DUAL ? NW * 32 * VS : 8];   // G rows
   __shared__ u32x4 q_lds[NW][2][KS][kWave];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds[NW * 32 * VS];   // V rows, this block
   __shared__ __attribute__((aligned(16))) __bf16 a_lds[NW][32 * AS];    // A rows, per wave
   __shared__ __attribute__((aligned(16))) float st_max[32 * NW][NW];    // per token, per group
   __shared__ __attribute__((aligned(16))) float st_sum[32 * NW][NW];
 
-  auto load_pair = [&](int blk, u32x4 (*qv)[KS], u32x4 (*vv)[KS]) {
+  auto load_pair = [&](int blk, u32x4 (*qv)[KS], u32x4 (*vv)[KS], u32x4 (*gv)[KS]) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       load_rows<D>(Q, qb, qw.st, blk + 32 * w + 16 * tt + c, n, g, qv[tt]);
       load_rows<D>(V, xb, xw.st, blk + 32 * w + 16 * tt + c, n, g, vv[tt]);
+      if constexpr (DUAL) load_rows<D>(G, gb, gw.st, blk + 32 * w + 16 * tt + c, n, g, gv[tt]);
     }
   };
-  u32x4 qv[2][KS], vv[2][KS];
-  load_pair(t_begin, qv, vv);
+  u32x4 qv[2][KS], vv[2][KS], gv[DUAL ? 2 : 1][KS];
+  load_pair(t_begin, qv, vv, gv);
 
   // This group's anchors as left operands of S^T = U Q^T: lane (c,g) of tile jl holds
   // anchor 16(wJ + jl) + c (zero rows past m).  mask[jl]: initial accumulators, -inf on
@@ -90,13 +97,17 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     for (int r = 0; r < 4; ++r) mask[jl][r] = (16 * (w * J + jl) + 4 * g + r < m) ? 0.f : -INFINITY;
   }
   const bf16x8 ones = splat_bf16(1.f);
-  f32x4 pacc[J][DT], dacc[J];
+  f32x4 pacc[J][DT], dacc[J], gacc[DUAL ? J : 1][DT];
 #pragma unroll
   for (int jl = 0; jl < J; ++jl) {
     dacc[jl] = zero4();
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) pacc[jl][dt] = zero4();
   }
+#pragma unroll
+  for (int jl = 0; jl < (DUAL ? J : 1); ++jl)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) gacc[jl][dt] = zero4();
 
   for (int blk = t_begin; blk < t_end; blk += 32 * NW) {
     {  // stage pair w of this block, then request the next block's rows
@@ -107,8 +118,13 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         __bf16* vrow = v_lds + (32 * w + 16 * tt + c) * VS + 8 * KS * g;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) *(u32x4*)(vrow + 8 * kk) = vv[tt][kk];
+        if constexpr (DUAL) {
+          __bf16* grow = g_lds + (32 * w + 16 * tt + c) * VS + 8 * KS * g;
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) *(u32x4*)(grow + 8 * kk) = gv[tt][kk];
+        }
       }
-      if (blk + 32 * NW < t_end) load_pair(blk + 32 * NW, qv, vv);
+      if (blk + 32 * NW < t_end) load_pair(blk + 32 * NW, qv, vv, gv);
     }
     __syncthreads();
 
@@ -195,6 +211,14 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         for (int dt = 0; dt < DT; ++dt) pacc[jl][dt] = mfma_bf16(xs[jl], ys[dt], pacc[jl][dt]);
         dacc[jl] = mfma_bf16(xs[jl], ones, dacc[jl]);
       }
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) ys[dt] = lds_operand_tr(g_lds + 32 * ps * VS, VS, 16 * dt, c, g);
+#pragma unroll
+        for (int jl = 0; jl < J; ++jl)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) gacc[jl][dt] = mfma_bf16(xs[jl], ys[dt], gacc[jl][dt]);
+      }
     }
     __syncthreads();   // q_lds / v_lds are restaged for the next block
   }
@@ -210,6 +234,11 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       float* dst = part + ((sc * AT + jt) * DT + dt) * 256;
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[r * 64 + lane] = pacc[jl][dt][r];
+      if constexpr (DUAL) {
+        float* dg = partG + ((sc * AT + jt) * DT + dt) * 256;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dg[r * 64 + lane] = gacc[jl][dt][r];
+      }
     }
     if (c == 0) {
 #pragma unroll
@@ -228,19 +257,24 @@ void pass1a_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 // contraction axis) from the row copies with the transposing LDS read.  Partials leave in
 // accumulator layout with dim tile dt holding dims 16dt .. 16dt + 15.
 //
+// DUAL (the backward): a second operand G ([token][dim], view gw) is accumulated beside V
+// from the same A, A^T G into partG (no Delta); Q is read and A formed once for both.
 // NYS (Nystrom attention, landmark pass): the anchors are the slice's landmark query rows,
 // gathered from U (the queries, view uw) through the landmark indices lidx ([B][m]); Q
 // holds the keys; and the weights are exp(c q.k - c M_a) with M_a landmark a's largest
 // logit over this chunk's tokens (a first sweep over the chunk finds it, and it is written
 // to cmax for the solve, which rescales the chunks to the overall maximum) instead of a
 // softmax over anchors; phase B then accumulates F3 V and the row sums of F3 unnormalised.
-template <int D, int MP, int NW, bool NYS = false>
-__global__ __launch_bounds__(NW * kWave, 2)
+template <int D, int MP, int NW, bool NYS = false, bool DUAL = false>
+__global__ __launch_bounds__(NW * kWave, DUAL ? 1 : 2)
 void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                  const __bf16* __restrict__ V, float* __restrict__ part,
                  float* __restrict__ dpart, View qw, View xw, int h, int n, int m, int chunks,
                  int chunk_len, float c2, float* __restrict__ cmax = nullptr,
-                 const int* __restrict__ lidx = nullptr, View uw = View{0, 0, 0}) {
+                 const int* __restrict__ lidx = nullptr, View uw = View{0, 0, 0},
+                 const __bf16* __restrict__ G = nullptr, View gw = View{0, 0, 0},
+                 float* __restrict__ partG = nullptr) {
+  static_assert(!(NYS && DUAL), "one mode at a time");
   constexpr int KS = D / 32, DT = D / 16, AT = 2 * MP;
   constexpr int TILES = AT * DT, TPW = (TILES + NW - 1) / NW;
   constexpr int NDA = (TPW + DT - 1) / DT;   // anchor tiles per wave needing a Delta
@@ -252,11 +286,13 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   const int c = lane & 15, g = lane >> 4;
   const size_t qb = view_base(qw, slice, h), xb = view_base(xw, slice, h);
+  const size_t gb = DUAL ? view_base(gw, slice, h) : 0;
   const int t_begin = chunk * chunk_len;
   const int t_end = min(n, t_begin + chunk_len);
   const int npairs = (t_end - t_begin + 31) >> 5;
 
   constexpr int AS = tr_stride<32 * MP>(), VS = tr_stride<D>();
+  __shared__ __attribute__((aligned(16))) __bf16 g_lds[DUAL ? NW * 32 * VS : 8];   // rows of G
   __shared__ u32x4 u_lds[AT][KS][kWave];
   __shared__ __attribute__((aligned(16))) __bf16 a_lds[NW * 32 * AS];   // rows of A, this round
   __shared__ __attribute__((aligned(16))) __bf16 v_lds[NW * 32 * VS];   // rows of V, this round
@@ -287,16 +323,18 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
   // weights are zeroed), so every load is unconditional and the waits are exact counts.
   // Two register sets alternate between rounds: the next round's rows are requested at
   // the start of a round and first waited for at the start of the next one.
-  auto load_pair = [&](int p, u32x4 (*qv)[KS], u32x4 (*vv)[KS]) {
+  auto load_pair = [&](int p, u32x4 (*qv)[KS], u32x4 (*vv)[KS], u32x4 (*gv)[KS]) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int row = min(t_begin + 32 * p + 16 * tt + c, t_end - 1);
       load_rows<D>(Q, qb, qw.st, row, n, g, qv[tt]);
       load_rows<D>(V, xb, xw.st, row, n, g, vv[tt]);
+      if constexpr (DUAL) load_rows<D>(G, gb, gw.st, row, n, g, gv[tt]);
     }
   };
-  u32x4 qa[2][KS], va[2][KS], qz[2][KS], vz[2][KS];
-  load_pair(w, qa, va);
+  constexpr int GR = DUAL ? 2 : 1;
+  u32x4 qa[2][KS], va[2][KS], qz[2][KS], vz[2][KS], ga[GR][KS], gz[GR][KS];
+  load_pair(w, qa, va, ga);
 #pragma unroll
   for (int i = 0; i < UPT; ++i) {
     const int idx = threadIdx.x + i * NW * kWave;
@@ -356,17 +394,20 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 
   // Wave w owns the contiguous tiles w*TPW .. w*TPW + TPW - 1 (tile t: anchor tile t / DT,
   // dim tile t % DT); the Delta of anchor tile ja is accumulated with its dim tile 0.
-  f32x4 pacc[TPW], dacc[NDA];
+  f32x4 pacc[TPW], dacc[NDA], gacc[DUAL ? TPW : 1];
 #pragma unroll
   for (int k = 0; k < TPW; ++k) pacc[k] = zero4();
 #pragma unroll
   for (int k = 0; k < NDA; ++k) dacc[k] = zero4();
+#pragma unroll
+  for (int k = 0; k < (DUAL ? TPW : 1); ++k) gacc[k] = zero4();
 
   const int rounds = (npairs + NW - 1) / NW;
-  auto round = [&](int r, u32x4 (*qc)[KS], u32x4 (*vc)[KS], u32x4 (*qn)[KS], u32x4 (*vn)[KS]) {
+  auto round = [&](int r, u32x4 (*qc)[KS], u32x4 (*vc)[KS], u32x4 (*gc)[KS], u32x4 (*qn)[KS],
+                   u32x4 (*vn)[KS], u32x4 (*gn)[KS]) {
     const int pairs_here = min(NW, npairs - r * NW);  // uniform over the workgroup
     const int p = r * NW + w;
-    load_pair(p + NW, qn, vn);
+    load_pair(p + NW, qn, vn, gn);
     // Phase A: rows 32w .. 32w + 31 of the round's LDS blocks hold this wave's pair.
     if (p < npairs) {
 #pragma unroll
@@ -388,15 +429,22 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         __bf16* vrow = v_lds + (32 * w + 16 * tt + c) * VS + 8 * KS * g;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) *(u32x4*)(vrow + 8 * kk) = vc[tt][kk];
+        if constexpr (DUAL) {
+          __bf16* grow = g_lds + (32 * w + 16 * tt + c) * VS + 8 * KS * g;
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) *(u32x4*)(grow + 8 * kk) = gc[tt][kk];
+        }
       }
     }
     __syncthreads();
     accumulate_tiles<TPW, DT, AS, VS>(a_lds, v_lds, w * TPW, pairs_here, c, g, ones, pacc, dacc);
+    if constexpr (DUAL)
+      accumulate_tiles<TPW, DT, AS, VS, false>(a_lds, g_lds, w * TPW, pairs_here, c, g, ones, gacc, dacc);
     __syncthreads();
   };
   for (int r = 0; r < rounds; r += 2) {
-    round(r, qa, va, qz, vz);
-    if (r + 1 < rounds) round(r + 1, qz, vz, qa, va);
+    round(r, qa, va, ga, qz, vz, gz);
+    if (r + 1 < rounds) round(r + 1, qz, vz, gz, qa, va, ga);
   }
 
   // Partials: [slice][chunk][jt][dt][r][lane] holds P[16jt + 4g + r][16dt + c];
@@ -409,6 +457,11 @@ void pass1x_bf16(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     float* dst = part + ((sc * AT + ja) * DT + dt) * 256;
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[r * 64 + lane] = pacc[k][r];
+    if constexpr (DUAL) {
+      float* dg = partG + ((sc * AT + ja) * DT + dt) * 256;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dg[r * 64 + lane] = gacc[k][r];
+    }
     if (dt == 0 && c == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) dpart[sc * (16 * AT) + 16 * ja + 4 * g + r] = dacc[k / DT][r];
@@ -739,6 +792,41 @@ hipError_t launch_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* 
   if (g.d == 64) return at(std::integral_constant<int, 64>{});
   if (g.d == 32) return at(std::integral_constant<int, 32>{});
   if (g.d == 128) return at(std::integral_constant<int, 128>{});
+  return hipErrorInvalidValue;
+}
+
+// The backward's pass 1 on V and on G in one launch (up to 256 anchors, d <= 64): A^T V
+// with Delta into part and dpart, A^T G into partG, partials as launch_pass1_bf16's.
+hipError_t launch_pass1_dual_bf16(const Geometry& g, const SplitPlan& p, const void* Q,
+                                  const void* U, const void* V, const View& vw, const void* G,
+                                  const View& gw, float* part, float* partG, float* dpart,
+                                  hipStream_t s) {
+  const long long g1 = g.slices * p.chunks1;
+  auto at = [&](auto D) -> hipError_t {
+    constexpr int d = decltype(D)::value;
+#define AA_DUAL(MP)                                                                          \
+  pass1x_bf16<d, MP, kPass1Waves, false, true><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, s>>>( \
+      (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, part, dpart, g.vw.q, vw, g.h, g.n, g.m, \
+      p.chunks1, p.chunk_len1, g.c2, nullptr, nullptr, View{0, 0, 0}, (const __bf16*)G, gw, partG)
+#define AA_DUALA(AT)                                                                         \
+  pass1a_bf16<d, AT, 4, true><<<dim3((unsigned)g1), dim3(4 * kWave), 0, s>>>(                  \
+      (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, part, dpart, g.vw.q, vw, g.h, g.n, g.m, \
+      p.chunks1, p.chunk_len1, g.c2, nullptr, (const __bf16*)G, gw, partG)
+    switch (g.at) {
+      case 2: AA_DUAL(1); break;
+      case 4: AA_DUAL(2); break;
+      case 6: AA_DUAL(3); break;
+      case 8: AA_DUAL(4); break;
+      case 12: AA_DUALA(12); break;
+      case 16: AA_DUALA(16); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef AA_DUAL
+#undef AA_DUALA
+    return hipGetLastError();
+  };
+  if (g.d == 64) return at(std::integral_constant<int, 64>{});
+  if (g.d == 32) return at(std::integral_constant<int, 32>{});
   return hipErrorInvalidValue;
 }
 

@@ -10,8 +10,9 @@
 
 namespace aa {
 
-// The split plan of one call (bf16 or fp32) on num_cus compute units.
-inline SplitPlan split_plan(const Geometry& g, bool bf16, int num_cus) {
+// The split plan of one call (bf16 or fp32) on num_cus compute units.  dual: the
+// backward's pass 1 on V and dH in one launch, which fits one workgroup per CU.
+inline SplitPlan split_plan(const Geometry& g, bool bf16, int num_cus, bool dual = false) {
   SplitPlan p{};
   const int n = g.n;
   // Pass 1: chunks a multiple of the 128-token block; about one workgroup per CU for the
@@ -19,7 +20,7 @@ inline SplitPlan split_plan(const Geometry& g, bool bf16, int num_cus) {
   // and measured faster) and for the eight-wave anchor-split one above 256 anchors (one
   // fits a CU), about two for the four-wave anchor-split one and for fp32 (one was slower
   // for both: long bf16 147.6 -> 165.9 us, long fp32 716 -> 755 us).
-  const bool one_per_cu = bf16 && (g.at <= 8 || g.at >= 24);
+  const bool one_per_cu = bf16 && (g.at <= 8 || g.at >= 24 || dual);
   const long long want1 = (one_per_cu ? 1LL : 2LL) * num_cus;
   int max_chunks1 = (n + kPass1Block - 1) / kPass1Block;
   int c1 = (int)std::min<long long>(max_chunks1, std::max<long long>(1, (want1 + g.slices - 1) / g.slices));

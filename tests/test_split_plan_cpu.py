@@ -1,5 +1,5 @@
 """Host logic of the split plan's chunking (csrc/split_plan.h), compiled with g++ and run on
-the CPU over a grid of shapes: every pass covers each slice's tokens with whole blocks and no
+the CPU over a grid of shapes (forward and the backward's dual pass 1): every pass covers each slice's tokens with whole blocks and no
 empty chunk, the backward's token pass never has more chunks than pass 1 (its dS^T Q
 partials live in a buffer sized for pass 1's), and the workspace sections hold what the
 kernels write."""
@@ -32,11 +32,11 @@ int main() {
   const int cuss[] = {1, 80, 256, 304};
   long long checked = 0;
   for (int n : ns) for (long long sl : slicess) for (int at : ats) for (int d : ds)
-  for (int bf16 = 0; bf16 < 2; ++bf16) for (int cus : cuss) {
+  for (int bf16 = 0; bf16 < 2; ++bf16) for (int cus : cuss) for (int dual = 0; dual < 2; ++dual) {
     Geometry g{};
     g.n = n; g.d = d; g.at = at; g.m_pad = 16 * at; g.m = g.m_pad; g.slices = sl;
     g.B = (int)sl; g.h = 1;
-    const SplitPlan p = split_plan(g, bf16 != 0, cus);
+    const SplitPlan p = split_plan(g, bf16 != 0, cus, dual != 0);
     if (!covers(n, p.chunks1, p.chunk_len1, kPass1Block)) return fail("pass 1 chunks", n, sl, at, d, bf16, cus);
     if (!covers(n, p.chunks2, p.chunk_len2, kPass2Block)) return fail("pass 2 chunks", n, sl, at, d, bf16, cus);
     if (sl * p.chunks1 > 0x7fffffffLL || sl * p.chunks2 > 0x7fffffffLL) return fail("grid", n, sl, at, d, bf16, cus);
