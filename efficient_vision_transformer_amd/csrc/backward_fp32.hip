@@ -371,9 +371,15 @@ static hipError_t go_bwd_fp32(const Geometry& g, const SplitPlan& p, const Backw
   gv.vw.q = gg.vw.q = bv.q;
   gv.vw.v = bv.v;
   gg.vw.v = bv.g;
-  hipError_t e = launch_pass1_fp32(gv, p, Q, U, V, wb.partP, wb.dpart, s);
-  if (e != hipSuccess) return e;
-  e = launch_pass1_fp32(gg, p, Q, U, G, wb.partG, wb.dpart, s);
+  hipError_t e;
+  if constexpr (D <= 64) {
+    // one pass 1 for both: Q read and A formed once (at d = 128 its LDS would not fit)
+    e = launch_pass1_dual_fp32(gv, p, Q, U, V, bv.v, G, bv.g, wb.partP, wb.partG, wb.dpart, s);
+  } else {
+    e = launch_pass1_fp32(gv, p, Q, U, V, wb.partP, wb.dpart, s);
+    if (e != hipSuccess) return e;
+    e = launch_pass1_fp32(gg, p, Q, U, G, wb.partG, wb.dpart, s);
+  }
   if (e != hipSuccess) return e;
   const long long grid = g.slices * p.chunks1;
   bwd_finalize_fp32<D><<<dim3((unsigned)(g.slices * AT)), dim3(256), 0, s>>>(

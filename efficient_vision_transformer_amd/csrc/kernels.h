@@ -46,6 +46,11 @@ hipError_t launch_backward_bf16(const Geometry& g, const SplitPlan& p, const Bac
 // fp32 split pass 1 alone on (Q, U, X), partials as launch_pass1_bf16's.
 hipError_t launch_pass1_fp32(const Geometry& g, const SplitPlan& p, const void* Q, const void* U,
                              const void* X, float* part, float* dpart, hipStream_t stream);
+// The fp32 backward's pass 1 on V and on G in one launch (d <= 64): A formed once.
+hipError_t launch_pass1_dual_fp32(const Geometry& g, const SplitPlan& p, const void* Q,
+                                  const void* U, const void* V, const View& vw, const void* G,
+                                  const View& gw, float* part, float* partG, float* dpart,
+                                  hipStream_t s);
 // Workspace sections of the fp32 backward (see backward_fp32.hip).
 struct BackwardBuffersF32 {
   float* partP;   // pass-1 partials of A^T V      [slice][chunk][AT][DT][256]

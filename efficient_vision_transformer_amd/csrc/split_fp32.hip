@@ -16,13 +16,15 @@ namespace aa {
 // Pass 1 (fp32).  Logits S = Q U^T with lanes = anchors, registers = tokens, so the
 // normalised A (one token per K step) feeds A^T V directly, and V's right operand
 // (one token row per K step, 16 consecutive dims across lanes) is read from a plain
-// row-major LDS copy.
-template <int D, int AT, int NA>
-__global__ __launch_bounds__(kPass1Waves * kWave, 2)
+// row-major LDS copy.  DUAL (the backward): a second operand G (view gw) is staged beside
+// V and A^T G accumulated into partG from the same A (no Delta).
+template <int D, int AT, int NA, bool DUAL = false>
+__global__ __launch_bounds__(kPass1Waves * kWave, DUAL ? 1 : 2)
 void pass1_fp32(const float* __restrict__ Q, const float* __restrict__ U,
                 const float* __restrict__ V, float* __restrict__ part,
                 float* __restrict__ dpart, View qw, View vw, int h, int n, int m, int chunks,
-                int chunk_len, float c2) {
+                int chunk_len, float c2, const float* __restrict__ G = nullptr,
+                View gw = View{0, 0, 0}, float* __restrict__ partG = nullptr) {
   constexpr int NW = kPass1Waves, ND = NW / NA, DT = D / 16, KQ = D / 16;
   constexpr int J = AT / NA, DTW = DT / ND, VS = D + 4;
   static_assert(AT % NA == 0 && DT % ND == 0, "wave split must tile the anchors and dims");
@@ -33,12 +35,14 @@ void pass1_fp32(const float* __restrict__ Q, const float* __restrict__ U,
   const int c = lane & 15, g = lane >> 4;
   const int ag = w % NA, dg = w / NA;
   const size_t qb = view_base(qw, slice, h), vb = view_base(vw, slice, h);
+  const size_t gb = DUAL ? view_base(gw, slice, h) : 0;
   const int t_begin = chunk * chunk_len;
   const int t_end = min(n, t_begin + chunk_len);
 
   // Q as left operands: lane (c,g) of tile tt holds token c, dims (D/4)g + 4kq + e.
   __shared__ f32x4 q_lds[NW][2][KQ][kWave];
   __shared__ __attribute__((aligned(16))) float v_lds[NW][32][VS];
+  __shared__ __attribute__((aligned(16))) float g_lds[DUAL ? NW : 1][DUAL ? 32 : 1][DUAL ? VS : 4];
   __shared__ float st_max[NA][32];
   __shared__ float st_sum[NA][32];
 
@@ -52,7 +56,7 @@ void pass1_fp32(const float* __restrict__ Q, const float* __restrict__ U,
     for (int kq = 0; kq < KQ; ++kq)
       uop[jl][kq] = (a < m) ? *(const f32x4*)(Uh + (size_t)a * D + (D / 4) * g + 4 * kq) : zero4();
   }
-  f32x4 pacc[J][DTW];
+  f32x4 pacc[J][DTW], gacc[DUAL ? J : 1][DTW];
   f32x4 dacc[J];
 #pragma unroll
   for (int jl = 0; jl < J; ++jl) {
@@ -60,6 +64,10 @@ void pass1_fp32(const float* __restrict__ Q, const float* __restrict__ U,
 #pragma unroll
     for (int dl = 0; dl < DTW; ++dl) pacc[jl][dl] = zero4();
   }
+#pragma unroll
+  for (int jl = 0; jl < (DUAL ? J : 1); ++jl)
+#pragma unroll
+    for (int dl = 0; dl < DTW; ++dl) gacc[jl][dl] = zero4();
 
   for (int blk = t_begin; blk < t_end; blk += 32 * NW) {
     {  // stage pair w
@@ -70,12 +78,17 @@ void pass1_fp32(const float* __restrict__ Q, const float* __restrict__ U,
         const bool ok = row < t_end;
         const size_t qo = qb + view_row(qw, ok ? row : 0) + (D / 4) * g;
         const size_t vo = vb + view_row(vw, ok ? row : 0) + (D / 4) * g;
+        const size_t go = DUAL ? gb + view_row(gw, ok ? row : 0) + (D / 4) * g : 0;
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq) {
           const f32x4 qv = ok ? *(const f32x4*)(Q + qo + 4 * kq) : zero4();
           const f32x4 vv = ok ? *(const f32x4*)(V + vo + 4 * kq) : zero4();
           q_lds[w][tt][kq][lane] = qv;
           *(f32x4*)&v_lds[w][16 * tt + c][(D / 4) * g + 4 * kq] = vv;
+          if constexpr (DUAL) {
+            const f32x4 gv = ok ? *(const f32x4*)(G + go + 4 * kq) : zero4();
+            *(f32x4*)&g_lds[w][16 * tt + c][(D / 4) * g + 4 * kq] = gv;
+          }
         }
       }
     }
@@ -174,6 +187,19 @@ void pass1_fp32(const float* __restrict__ Q, const float* __restrict__ U,
 #pragma unroll
             for (int r = 0; r < 4; ++r) dacc[jl] = mfma_f32(s[tt][jl][r], 1.f, dacc[jl]);
         }
+        if constexpr (DUAL) {
+#pragma unroll
+          for (int dl = 0; dl < DTW; ++dl) {
+            f32x4 acc = gacc[jl][dl];
+            const int col = 16 * (dg * DTW + dl) + c;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc = mfma_f32(s[tt][jl][r], g_lds[ps][16 * tt + 4 * g + r][col], acc);
+            gacc[jl][dl] = acc;
+          }
+        }
       }
     }
     __syncthreads();
@@ -190,6 +216,11 @@ void pass1_fp32(const float* __restrict__ Q, const float* __restrict__ U,
       float* dst = part + ((sc * AT + jt) * DT + dt) * 256;
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[r * 64 + lane] = pacc[jl][dl][r];
+      if constexpr (DUAL) {
+        float* dgp = partG + ((sc * AT + jt) * DT + dt) * 256;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dgp[r * 64 + lane] = gacc[jl][dl][r];
+      }
     }
     if (dg == 0 && c == 0) {
 #pragma unroll
@@ -411,6 +442,34 @@ hipError_t launch_split_fp32(const Geometry& g, const SplitPlan& p, const void* 
   if (g.d == 64) return dispatch_at<64>(g, p, Q, U, V, H, ws, stream);
   if (g.d == 32) return dispatch_at<32>(g, p, Q, U, V, H, ws, stream);
   if (g.d == 128) return dispatch_at<128>(g, p, Q, U, V, H, ws, stream);   // m <= 128
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_pass1_dual_fp32(const Geometry& g, const SplitPlan& p, const void* Q,
+                                  const void* U, const void* V, const View& vw, const void* G,
+                                  const View& gw, float* part, float* partG, float* dpart,
+                                  hipStream_t s) {
+  const long long g1 = g.slices * p.chunks1;
+  auto at = [&](auto D) -> hipError_t {
+    constexpr int d = decltype(D)::value;
+#define AA_P1FD(AT)                                                                          \
+  pass1_fp32<d, AT, (AT % 4 == 0) ? 4 : 2, true><<<dim3((unsigned)g1), dim3(kPass1Waves * kWave), 0, s>>>( \
+      (const float*)Q, (const float*)U, (const float*)V, part, dpart, g.vw.q, vw, g.h, g.n, \
+      g.m, p.chunks1, p.chunk_len1, g.c2, (const float*)G, gw, partG)
+    switch (g.at) {
+      case 2: AA_P1FD(2); break;
+      case 4: AA_P1FD(4); break;
+      case 6: AA_P1FD(6); break;
+      case 8: AA_P1FD(8); break;
+      case 12: AA_P1FD(12); break;
+      case 16: AA_P1FD(16); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef AA_P1FD
+    return hipGetLastError();
+  };
+  if (g.d == 64) return at(std::integral_constant<int, 64>{});
+  if (g.d == 32) return at(std::integral_constant<int, 32>{});
   return hipErrorInvalidValue;
 }
 
