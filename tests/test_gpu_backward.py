@@ -82,6 +82,10 @@ SHAPES = [
     (2, 2, 1000, 48, 64),
     (1, 1, 4096, 64, 64),
     (1, 2, 3000, 96, 32),
+    # the dual pass 1's chunking at its ends: more slices than CUs (one chunk per slice)
+    # and two slices cut into many chunks
+    (75, 4, 1500, 100, 64),
+    (1, 2, 12000, 200, 64),
 ]
 
 

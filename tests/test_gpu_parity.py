@@ -96,6 +96,9 @@ EDGE = [
     (1, 2, 300, 130, 64), (2, 1, 257, 200, 32), (1, 1, 77, 193, 64),
     # six anchor tiles: the token-split pass 1 takes its generic per-tile operand reads
     (1, 2, 200, 80, 64), (1, 1, 150, 70, 32),
+    # the split plan's chunking at its ends: more slices than CUs (one chunk per slice,
+    # twelve rounds in pass 1) and two slices cut into many chunks
+    (75, 4, 1500, 100, 64), (1, 2, 12000, 200, 64),
 ]
 
 
