@@ -778,7 +778,7 @@ static anchor_attn_status_t backward_strided_impl(
       wb.ds = (float*)w;
       e = aa::launch_backward_fp32(g, p, wb, bv, Q, U, V, dH, dQ, dU, dV, s);
     } else {
-      const SplitPlan p = aa::split_plan(g, true, ctx->num_cus, /*dual=*/g.d <= 64);
+      const SplitPlan p = aa::split_plan(g, true, ctx->num_cus, /*dual=*/g.d <= 64 || g.at <= 6);
       const size_t part = al((size_t)g.slices * p.chunks1 * g.m_pad * g.d * sizeof(float));
       const size_t dpart = al((size_t)g.slices * p.chunks1 * g.m_pad * sizeof(float));
       const size_t ops = al((size_t)g.slices * g.m_pad * g.d * es);

@@ -414,8 +414,9 @@ static hipError_t go_bwd(const Geometry& g, const SplitPlan& p, const BackwardBu
   gv.vw.v = bv.v;
   gg.vw.v = bv.g;
   hipError_t e;
-  if constexpr (D <= 64) {
-    // one pass 1 for both: Q read and A formed once (at d = 128 its registers would spill)
+  if constexpr (D <= 64 || AT <= 6) {
+    // one pass 1 for both: Q read and A formed once (at d = 128 with 128 anchors its
+    // registers would spill)
     e = launch_pass1_dual_bf16(gv, p, Q, U, V, bv.v, G, bv.g, wb.partP, wb.partG, wb.dpart, s);
   } else {
     e = launch_pass1_bf16(gv, p, Q, U, V, wb.partP, wb.dpart, s);

@@ -16,7 +16,8 @@ hipError_t launch_split_bf16(const Geometry& g, const SplitPlan& p, const void* 
 hipError_t launch_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* Q, const void* U,
                              const void* X, float* part, float* dpart, hipStream_t stream);
 // The backward's pass 1 on V (view vw) and on G (view gw) in one launch, up to 256 anchors
-// at d <= 64: A formed once, A^T V and Delta into part / dpart, A^T G into partG.
+// at d <= 64 and 96 at d = 128: A formed once, A^T V and Delta into part / dpart, A^T G
+// into partG.
 hipError_t launch_pass1_dual_bf16(const Geometry& g, const SplitPlan& p, const void* Q,
                                   const void* U, const void* V, const View& vw, const void* G,
                                   const View& gw, float* part, float* partG, float* dpart,

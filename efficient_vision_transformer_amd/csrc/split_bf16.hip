@@ -795,8 +795,9 @@ hipError_t launch_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* 
   return hipErrorInvalidValue;
 }
 
-// The backward's pass 1 on V and on G in one launch (up to 256 anchors, d <= 64): A^T V
-// with Delta into part and dpart, A^T G into partG, partials as launch_pass1_bf16's.
+// The backward's pass 1 on V and on G in one launch (up to 256 anchors at d <= 64, 96 at
+// d = 128): A^T V with Delta into part and dpart, A^T G into partG, partials as
+// launch_pass1_bf16's.
 hipError_t launch_pass1_dual_bf16(const Geometry& g, const SplitPlan& p, const void* Q,
                                   const void* U, const void* V, const View& vw, const void* G,
                                   const View& gw, float* part, float* partG, float* dpart,
@@ -816,9 +817,15 @@ hipError_t launch_pass1_dual_bf16(const Geometry& g, const SplitPlan& p, const v
       case 2: AA_DUAL(1); break;
       case 4: AA_DUAL(2); break;
       case 6: AA_DUAL(3); break;
-      case 8: AA_DUAL(4); break;
-      case 12: AA_DUALA(12); break;
-      case 16: AA_DUALA(16); break;
+      case 8:
+        if constexpr (d <= 64) { AA_DUAL(4); break; }
+        return hipErrorInvalidValue;
+      case 12:
+        if constexpr (d <= 64) { AA_DUALA(12); break; }
+        return hipErrorInvalidValue;
+      case 16:
+        if constexpr (d <= 64) { AA_DUALA(16); break; }
+        return hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
 #undef AA_DUAL
@@ -827,6 +834,7 @@ hipError_t launch_pass1_dual_bf16(const Geometry& g, const SplitPlan& p, const v
   };
   if (g.d == 64) return at(std::integral_constant<int, 64>{});
   if (g.d == 32) return at(std::integral_constant<int, 32>{});
+  if (g.d == 128 && g.at <= 6) return at(std::integral_constant<int, 128>{});
   return hipErrorInvalidValue;
 }
 
