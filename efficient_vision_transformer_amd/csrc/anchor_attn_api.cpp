@@ -783,7 +783,9 @@ static anchor_attn_status_t backward_strided_impl(
       const size_t dpart = al((size_t)g.slices * p.chunks1 * g.m_pad * sizeof(float));
       const size_t ops = al((size_t)g.slices * g.m_pad * g.d * es);
       const size_t ddb = al((size_t)g.slices * g.m_pad * sizeof(float));
-      st = ensure_workspace(ctx, 3 * part + dpart + 2 * ops + ddb);
+      // per-token log-sum-exp from pass 1 to the token pass above 128 anchors
+      const size_t lseb = g.at > 8 ? al((size_t)g.slices * g.n * sizeof(float)) : 0;
+      st = ensure_workspace(ctx, 3 * part + dpart + 2 * ops + ddb + lseb);
       if (st != ANCHOR_ATTN_SUCCESS) return st;
       char* w = (char*)ctx->workspace;
       aa::BackwardBuffers wb{};
@@ -793,7 +795,8 @@ static anchor_attn_status_t backward_strided_impl(
       wb.dpart = (float*)w; w += dpart;
       wb.wu = w; w += ops;
       wb.dprm = w; w += ops;
-      wb.dd = (float*)w;
+      wb.dd = (float*)w; w += ddb;
+      wb.lse = lseb ? (float*)w : nullptr;
       aa::token_pass_chunks(g, p, ctx->num_cus, &wb.chunks_t, &wb.chunk_len_t);
       e = aa::launch_backward_bf16(g, p, wb, bv, Q, U, V, dH, dQ, dU, dV, s);
     }

@@ -121,14 +121,16 @@ __device__ __forceinline__ bf16x8 rows_operand_out(const __bf16* blk, int stride
 // one 16-token tile per round, so a
 // round's rows of dS and Q for the dU tiles cover 64 tokens.  The next round's rows of Q,
 // V and dH are requested before the current round is computed.
-template <int D, int AT>
+// LSE: A comes from each token's base-2 log-sum-exp written by pass 1 ([slice][n]), one
+// FMA and one exponential per entry, instead of the softmax formed again.
+template <int D, int AT, bool LSE = false>
 __global__ __launch_bounds__(4 * kWave, 1)
 void bwd_tokens_rm(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
                    const __bf16* __restrict__ V, const __bf16* __restrict__ G,
                    const u32x4* __restrict__ wu, const __bf16* __restrict__ dprm,
                    const float* __restrict__ dd, __bf16* __restrict__ dQ, __bf16* __restrict__ dV,
                    float* __restrict__ partU, BwdViews bv, int h, int n, int m, int chunks,
-                   int chunk_len, float c2, float cs) {
+                   int chunk_len, float c2, float cs, const float* __restrict__ lse = nullptr) {
   constexpr int NW = 4, KS = D / 32, DT = D / 16, MP = AT / 2, NPAD = pad_tiles(AT);
   constexpr int TILES = AT * DT, TPW = TILES / NW;
   constexpr int RS = D + 16;                      // row stride of U, dP and Q rows
@@ -191,8 +193,11 @@ void bwd_tokens_rm(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
 
   const int rounds = (t_end - t_begin + TOK - 1) / TOK;
   u32x4 qv[KS], vv[KS], gv[KS];
+  const float* lse_s = LSE ? lse + (size_t)slice * n : nullptr;
+  float lv = 0.f;
   {
     const int row = min(t_begin + 16 * w + c, t_end - 1);
+    if constexpr (LSE) lv = lse_s[row];
     load_rows<D>(Q, qb, bv.q.st, row, n, g, qv);
     load_rows<D>(V, vb, bv.v.st, row, n, g, vv);
     load_rows<D>(G, gb, bv.g.st, row, n, g, gv);
@@ -206,6 +211,8 @@ void bwd_tokens_rm(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
     // next chunk's rows)
     u32x4 nq[KS], nv[KS], ng[KS];
     const int nrow = min(row + TOK, t_end - 1);
+    float nlv = 0.f;
+    if constexpr (LSE) nlv = lse_s[nrow];
     load_rows<D>(Q, qb, bv.q.st, nrow, n, g, nq);
     load_rows<D>(V, vb, bv.v.st, nrow, n, g, nv);
     load_rows<D>(G, gb, bv.g.st, nrow, n, g, ng);
@@ -225,24 +232,36 @@ void bwd_tokens_rm(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
         }
         sc[j] = acc;
       }
-      float mx = sc[0][0];
+      if constexpr (LSE) {
+        // already normalised; tokens past the end get exp2(-inf) = 0 (and so do padded
+        // anchors, whose logits start from -inf)
+        const float nl = ok ? -lv : -INFINITY;
 #pragma unroll
-      for (int j = 0; j < AT; ++j)
+        for (int j = 0; j < AT; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) mx = fmaxf(mx, sc[j][q]);
-      mx = xor32_max(xor16_max(mx));
-      const float mneg = -mx * c2;
-      f32x4 zt = zero4();
+          for (int q = 0; q < 4; ++q) sc[j][q] = exp2_fast(fmaf(sc[j][q], c2, nl));
 #pragma unroll
-      for (int j = 0; j < AT; ++j) {
+        for (int jj = 0; jj < MP; ++jj) ab[jj] = pack_bf16(sc[2 * jj], sc[2 * jj + 1]);
+      } else {
+        float mx = sc[0][0];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sc[j][q] = exp2_fast(fmaf(sc[j][q], c2, mneg));
-        zt += sc[j];
+        for (int j = 0; j < AT; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) mx = fmaxf(mx, sc[j][q]);
+        mx = xor32_max(xor16_max(mx));
+        const float mneg = -mx * c2;
+        f32x4 zt = zero4();
+#pragma unroll
+        for (int j = 0; j < AT; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sc[j][q] = exp2_fast(fmaf(sc[j][q], c2, mneg));
+          zt += sc[j];
+        }
+        const float z = xor32_sum(xor16_sum((zt[0] + zt[1]) + (zt[2] + zt[3])));
+        const float inv = ok ? 1.f / z : 0.f;
+#pragma unroll
+        for (int jj = 0; jj < MP; ++jj) ab[jj] = pack_bf16(sc[2 * jj] * inv, sc[2 * jj + 1] * inv);
       }
-      const float z = xor32_sum(xor16_sum((zt[0] + zt[1]) + (zt[2] + zt[3])));
-      const float inv = ok ? 1.f / z : 0.f;
-#pragma unroll
-      for (int jj = 0; jj < MP; ++jj) ab[jj] = pack_bf16(sc[2 * jj] * inv, sc[2 * jj + 1] * inv);
     }
     // this tile's rows of Q ([token][dim]) for the dU tiles
     {
@@ -321,6 +340,7 @@ void bwd_tokens_rm(const __bf16* __restrict__ Q, const __bf16* __restrict__ U,
       vv[kk] = nv[kk];
       gv[kk] = ng[kk];
     }
+    if constexpr (LSE) lv = nlv;
   }
 
   // dU partials: [slice][chunk][jt][dt][r][lane] holds the sum over the chunk's tokens of
@@ -417,7 +437,8 @@ static hipError_t go_bwd(const Geometry& g, const SplitPlan& p, const BackwardBu
   if constexpr (D <= 64 || AT <= 6) {
     // one pass 1 for both: Q read and A formed once (at d = 128 with 128 anchors its
     // registers would spill)
-    e = launch_pass1_dual_bf16(gv, p, Q, U, V, bv.v, G, bv.g, wb.partP, wb.partG, wb.dpart, s);
+    e = launch_pass1_dual_bf16(gv, p, Q, U, V, bv.v, G, bv.g, wb.partP, wb.partG, wb.dpart,
+                               AT > 8 ? wb.lse : nullptr, s);
   } else {
     e = launch_pass1_bf16(gv, p, Q, U, V, wb.partP, wb.dpart, s);
     if (e != hipSuccess) return e;
@@ -426,10 +447,13 @@ static hipError_t go_bwd(const Geometry& g, const SplitPlan& p, const BackwardBu
   if (e != hipSuccess) return e;
   bwd_finalize<D><<<dim3((unsigned)(g.slices * AT)), dim3(256), 0, s>>>(
       wb.partP, wb.partG, wb.dpart, (__bf16*)wb.wu, (__bf16*)wb.dprm, wb.dd, p.chunks1, AT);
-  bwd_tokens_rm<D, AT><<<dim3((unsigned)(g.slices * wb.chunks_t)), dim3(4 * kWave), 0, s>>>(
+  // above 128 anchors A comes from pass 1's log-sum-exp
+  constexpr bool kLse = (D <= 64 || AT <= 6) && AT > 8;
+  if (kLse && !wb.lse) return hipErrorInvalidValue;
+  bwd_tokens_rm<D, AT, kLse><<<dim3((unsigned)(g.slices * wb.chunks_t)), dim3(4 * kWave), 0, s>>>(
       (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, (const __bf16*)G,
       (const u32x4*)wb.wu, (const __bf16*)wb.dprm, wb.dd, (__bf16*)dQ, (__bf16*)dV, wb.partU,
-      bv, g.h, g.n, g.m, wb.chunks_t, wb.chunk_len_t, g.c2, cs);
+      bv, g.h, g.n, g.m, wb.chunks_t, wb.chunk_len_t, g.c2, cs, wb.lse);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_du_reduce_bf16(g, wb.partU, wb.chunks_t, dU, s);

@@ -21,7 +21,7 @@ hipError_t launch_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* 
 hipError_t launch_pass1_dual_bf16(const Geometry& g, const SplitPlan& p, const void* Q,
                                   const void* U, const void* V, const View& vw, const void* G,
                                   const View& gw, float* part, float* partG, float* dpart,
-                                  hipStream_t s);
+                                  float* lse, hipStream_t s);
 // Workspace sections of the backward (see bwd_finalize / bwd_tokens).
 struct BackwardBuffers {
   float* partP;   // pass-1 partials of A^T V      [slice][chunk][AT][DT][256]
@@ -31,6 +31,7 @@ struct BackwardBuffers {
   void* dprm;     // dP, row-major bf16            [slice][m_pad][d]
   float* dd;      // dDelta                        [slice][16 AT]
   float* partU;   // partials of dS^T Q            [slice][chunk_t][AT][DT][256]
+  float* lse;     // log-sum-exp (base 2) per token [slice][n], above 128 anchors
   int chunks_t, chunk_len_t;   // the token pass's chunks (at most pass 1's)
 };
 // Views of the backward's tensors: Q, V, dH (inputs) and dQ, dV (outputs).

@@ -797,11 +797,12 @@ hipError_t launch_pass1_bf16(const Geometry& g, const SplitPlan& p, const void* 
 
 // The backward's pass 1 on V and on G in one launch (up to 256 anchors at d <= 64, 96 at
 // d = 128): A^T V with Delta into part and dpart, A^T G into partG, partials as
-// launch_pass1_bf16's.
+// launch_pass1_bf16's.  Above 128 anchors each token's log-sum-exp (base 2) also goes to
+// lse ([slice][n]) when it is not null.
 hipError_t launch_pass1_dual_bf16(const Geometry& g, const SplitPlan& p, const void* Q,
                                   const void* U, const void* V, const View& vw, const void* G,
                                   const View& gw, float* part, float* partG, float* dpart,
-                                  hipStream_t s) {
+                                  float* lse, hipStream_t s) {
   const long long g1 = g.slices * p.chunks1;
   auto at = [&](auto D) -> hipError_t {
     constexpr int d = decltype(D)::value;
@@ -812,7 +813,7 @@ hipError_t launch_pass1_dual_bf16(const Geometry& g, const SplitPlan& p, const v
 #define AA_DUALA(AT)                                                                         \
   pass1a_bf16<d, AT, 4, true><<<dim3((unsigned)g1), dim3(4 * kWave), 0, s>>>(                  \
       (const __bf16*)Q, (const __bf16*)U, (const __bf16*)V, part, dpart, g.vw.q, vw, g.h, g.n, g.m, \
-      p.chunks1, p.chunk_len1, g.c2, nullptr, (const __bf16*)G, gw, partG)
+      p.chunks1, p.chunk_len1, g.c2, lse, (const __bf16*)G, gw, partG)
     switch (g.at) {
       case 2: AA_DUAL(1); break;
       case 4: AA_DUAL(2); break;
