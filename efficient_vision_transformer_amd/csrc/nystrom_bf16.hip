@@ -27,8 +27,10 @@
 
 namespace aa {
 
-// A double from lane `lane` of the wave (two 32-bit lane reads), and a double's halves
-// swapped between lanes l and l ^ 32.
+// A double from lane `lane` of the wave (two 32-bit lane reads), and the double of lane
+// l ^ 32.  permlane32_swap(v, v) hands each lane its own word and its partner's, in an
+// order that depends on the lane's half, so the partner's word is whichever of the two
+// is not the lane's own (when both are equal, either is).
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
   const long long b = __double_as_longlong(v);
   const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, lane);
@@ -37,9 +39,12 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
 }
 __device__ __forceinline__ double swap32_f64(double v) {
   const unsigned long long b = (unsigned long long)__double_as_longlong(v);
-  const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)b, (unsigned)b, false, false);
-  const auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(b >> 32), (unsigned)(b >> 32), false, false);
-  return __longlong_as_double((long long)(((unsigned long long)hi[0] << 32) | lo[0]));
+  const unsigned bl = (unsigned)b, bh = (unsigned)(b >> 32);
+  const auto lo = __builtin_amdgcn_permlane32_swap(bl, bl, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(bh, bh, false, false);
+  const unsigned pl = lo[0] == bl ? lo[1] : lo[0];
+  const unsigned ph = hi[0] == bh ? hi[1] : hi[0];
+  return __longlong_as_double((long long)(((unsigned long long)ph << 32) | pl));
 }
 
 // Landmark rows of Q and K for one slice into LDS (row stride RS, rows >= m zero), the
@@ -336,44 +341,58 @@ void nys_solve(const float* __restrict__ part, const float* __restrict__ dpart,
   }
 }
 
-// The same solve for up to 32 landmarks in one wave per slice, with no workgroup barrier:
-// the elimination's per-step exchange (pivot search, pivot row, multipliers) stays inside
-// the wave.  Lane l holds row l % MPAD of the augmented matrix [F2 | F3 V] and the CPL
-// consecutive columns of group l / MPAD (MPAD = 16 or 32: four or two groups).
-//   set-up: landmark rows of Q and K into LDS; F2's logits on the MFMA (fp32 sums of the
-//           bf16 products); F3 V from the chunk partials in chunk order; the row softmax
-//           of F2 one row per lane; the matrix into the lanes' registers;
-//   step k: the wave's largest |x[k]| among unused rows of the group holding column k
-//           (smallest row on ties), the pivot row published through LDS by its lanes and
-//           read back by every lane of the same group, the lane's own column-k value from
-//           the lane holding it, and x -= (x[k] / pivot) * pivot row on every row but the
-//           pivot's.  Unknown k is the pivot row's right-hand side over its pivot.
-template <int D, int AT>
-__global__ __launch_bounds__(kWave)
+// The same solve for up to 32 landmarks with F2's part of the elimination in one wave.
+// Wave 0 holds F2 (lane l: row l % MPAD; column group l / MPAD holds the interleaved
+// columns 2j + group, so that the columns already eliminated die in both groups at once
+// and are no longer updated), finds each step's pivot and the rows' multipliers, and
+// hands them to the other waves through LDS; wave 1 + r holds right-hand-side columns
+// 2RC r .. 2RC r + 2RC - 1 (RC per column group) and applies each step one barrier later.
+//   set-up: landmark rows of Q and K into LDS; F3 V from the chunk partials in chunk
+//           order (all waves); F2's logits on the MFMA (fp32 sums of the bf16 products)
+//           and its row softmax (wave 0); the matrix into the lanes' registers;
+//   step k: wave 0: the largest |x[k]| among unused rows (smallest row on ties), its
+//           pivot value by readlane, the multipliers x[k] / pivot (0 on the pivot row)
+//           and the pivot row published, and x -= multiplier * pivot row on its F2
+//           columns; the right-hand-side waves apply step k - 1 the same way, their own
+//           pivot row exchanged through LDS inside each wave.  Unknown k ends in the
+//           pivot row's right-hand side over its pivot.
+template <int D, int RC>
+constexpr int nys_solve1_waves() { return 1 + D / (2 * RC); }
+// right-hand-side columns per lane in the solve up to 32 landmarks
+constexpr int kNysRhsCols = 8;
+
+template <int D, int AT, int RC>
+__global__ __launch_bounds__((nys_solve1_waves<D, RC>() * kWave), 1)
 void nys_solve1(const float* __restrict__ part, const float* __restrict__ dpart,
                 const float* __restrict__ cmax, const __bf16* __restrict__ Q,
                 const __bf16* __restrict__ K, View vw, const int* __restrict__ idx,
                 __bf16* __restrict__ kt, __bf16* __restrict__ Wop, int h, int n, int m,
                 int chunks, float c2) {
-  constexpr int MPAD = 16 * AT, NC = MPAD + D, G = kWave / MPAD, CPL = NC / G;
+  constexpr int MPAD = 16 * AT, NC = MPAD + D, NW = nys_solve1_waves<D, RC>(), T = NW * kWave;
+  constexpr int G = 2, CPL = 16;   // two column groups of 16 registers in every wave
   constexpr int KS = D / 32, MP = AT / 2, LD = NC + 1, RS = D + 8;
-  static_assert(MPAD <= 32 && NC % G == 0 && CPL % 4 == 0, "one wave, whole column groups");
+  static_assert(MPAD == 32 && G * MPAD == kWave && G * CPL == MPAD, "32 rows, two groups");
+  static_assert(RC <= CPL && (NW - 1) * G * RC == D, "2 RC right-hand-side columns per wave");
   const int slice = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, w = tid / kWave, lane = tid % kWave;
   const int c = lane & 15, g = lane >> 4;
   const int row = lane % MPAD, grp = lane / MPAD;
   __shared__ float Mx[MPAD * LD];
   __shared__ __attribute__((aligned(16))) __bf16 ql[MPAD * RS], kl[MPAD * RS];
   __shared__ float zl[MPAD];
-  __shared__ __attribute__((aligned(16))) double prow[2][G][CPL];   // by step parity
+  __shared__ __attribute__((aligned(16))) double prow[NW][2][G][CPL];   // by step parity
+  __shared__ double fkl[2][MPAD];   // a step's multipliers, by step parity
+  __shared__ int pkl[2];            // a step's pivot row
+  __shared__ double pvl[MPAD];      // each row's pivot
+  __shared__ int varl[MPAD];        // the unknown each row ends with
   __shared__ float Ml[MPAD], facl[2][MPAD];
-  nys_landmark_rows<D, MPAD, kWave, RS>(Q, K, vw, idx, slice, h, n, m, lane, ql, kl, kt);
-  nys_rhs<D, AT, kWave, LD>(part, dpart, cmax, slice, chunks, m, c2, lane, Mx, zl, Ml, facl);
-  __syncthreads();   // one wave: orders the LDS writes above before the reads below
-  // F2 = rowsoftmax(q k^T c) in registers: logits q_a . k_l on the MFMA, tile (ti, tj),
-  // lane (c,g) ends with a = 16ti + 4g + r, l = 16tj + c; each row's maximum and sum over
-  // its m columns across the 16 lanes c (DPP); padded rows become identity rows
-  {
+  nys_landmark_rows<D, MPAD, T, RS>(Q, K, vw, idx, slice, h, n, m, tid, ql, kl, kt);
+  nys_rhs<D, AT, T, LD>(part, dpart, cmax, slice, chunks, m, c2, tid, Mx, zl, Ml, facl);
+  __syncthreads();
+  // F2 = rowsoftmax(q k^T c) (wave 0): logits q_a . k_l on the MFMA, tile (ti, tj), lane
+  // (c,g) ends with a = 16ti + 4g + r, l = 16tj + c; each row's maximum and sum over its m
+  // columns across the 16 lanes c (DPP); padded rows become identity rows
+  if (w == 0) {
     f32x4 f2[AT][AT];
 #pragma unroll
     for (int ti = 0; ti < AT; ++ti)
@@ -413,107 +432,146 @@ void nys_solve1(const float* __restrict__ part, const float* __restrict__ dpart,
   }
   __syncthreads();
 
-  // the elimination in fp64 (see nys_solve)
-  // the right-hand side is F3 V over F3's row sums (zero for padded landmark rows)
+  // the elimination in fp64 (see nys_solve); the right-hand side is F3 V over F3's row
+  // sums (zero for padded landmark rows)
   const float izl = (row < m) ? 1.f / zl[row] : 0.f;   // zl >= 1: each landmark's largest weight is exp(0)
+  // wave 0: register j holds F2 column 2j + grp; wave 1 + r: right-hand-side column
+  // 2RC r + RC grp + j (j < RC)
+  const int rhs0 = MPAD + 2 * RC * (w - 1) + RC * grp;
   double x[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
-    const int col = grp * CPL + j;
-    const float xv = Mx[row * LD + col];
-    x[j] = (double)(col >= MPAD ? xv * izl : xv);
+    if (w == 0) {
+      x[j] = (double)Mx[row * LD + G * j + grp];
+    } else if (j < RC) {
+      x[j] = (double)(Mx[row * LD + rhs0 + j] * izl);
+    }
   }
   bool used = false;
   int var = 0;
   double pvr = 1.0;
-  // Step k's elimination (multiplier f for this lane's row, pivot row pr) is applied at
-  // the start of step k + 1: first to column k + 1 alone, whose pivot-row value prk comes
-  // by readlane, so that step k + 1's pivot search can start at once; then to the other
-  // columns with the pivot row read back from LDS a whole step earlier.
+  // wave 0 applies step k's elimination at the start of step k + 1: first to column
+  // k + 1 alone, whose pivot-row value prk comes by readlane, so that step k + 1's pivot
+  // search can start at once; then to its other live columns with the pivot row read
+  // back from LDS a step earlier
   double fprev = 0.0, prk = 0.0;
   double pr[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) pr[j] = 0.0;
+  int lp = 0;
+  double f = 0.0;
+  // the right-hand-side waves apply step s (multipliers and pivot row published by wave
+  // 0 before the barrier that ends step s)
+  auto rhs_apply = [&](int s) {
+    const int b = s & 1;
+    const double fr = fkl[b][row];
+    const int p = pkl[b];
+    if (row == p) {
+#pragma unroll
+      for (int j = 0; j < RC; ++j) prow[w][b][grp][j] = x[j];
+    }
+    // one wave: its LDS writes are done before its reads (a wait and a compiler fence)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < RC; ++j) x[j] = fma(-fr, prow[w][b][grp][j], x[j]);
+  };
   // fully unrolled, so that column k is a fixed register in every step
 #pragma clang loop unroll(full)
   for (int k = 0; k < MPAD; ++k) {
-    const int gk = k / CPL, kr = k % CPL;   // column k: register kr of group gk
-    if (grp == gk) x[kr] = fma(-fprev, prk, x[kr]);
-    const bool cand = grp == gk && !used;
-    const float v = cand ? (float)fabs(x[kr]) : -1.f;
-    // maximum over the MPAD lanes of each group (other groups' lanes hold -1)
-    float best = row16_max(v);
-    if constexpr (MPAD >= 32) best = xor16_max(best);
-    // no candidate equals the maximum only when the column holds NaN: then the first
-    // unused row (the output is non-finite, and every unknown still gets its row)
-    const unsigned long long bal = __ballot(cand && v == best);
-    const unsigned long long any = __ballot(cand);
-    const int lp = (int)__builtin_ctzll(bal ? bal : any);
-    const int p = lp - gk * MPAD;
-    const double pv = readlane_f64(x[kr], lp);
-    // this lane's row in column k, from the lane of group gk that holds it
-    // (the exchange runs on every lane, outside any branch: a lane exchange under a
-    // divergent branch reads inactive lanes)
-    static_assert(G == 2, "two column groups");
-    const double other = swap32_f64(x[kr]);
-    const double xk = grp == gk ? x[kr] : other;
-    // 1 / pv: the hardware reciprocal refined by one Newton step
-    double ipv = __builtin_amdgcn_rcp(pv);
-    ipv = fma(ipv, fma(-pv, ipv, 1.0), ipv);
-    const bool piv = row == p;
-    const double f = piv ? 0.0 : xk * ipv;
-    if (piv) {   // every column group's copy of the pivot row
-      used = true;
-      var = k;
-      pvr = pv;
-    }
-    // step k - 1 on the remaining columns
-#pragma unroll
-    for (int j = 0; j < CPL; ++j)
-      if (j != kr) x[j] = fma(-fprev, pr[j], x[j]);
-    if (grp != gk) x[kr] = fma(-fprev, pr[kr], x[kr]);
-    // step k's pivot row (complete through step k - 1), one copy per column group; the
-    // barrier (one wave: a wait and a compiler fence) makes the pivot lanes' writes
-    // visible to the other lanes, and with the two buffers also orders the previous
-    // step's reads before the next writes (measured: as fast as fetching the row with
-    // ds_bpermute, and either exchange takes over half of the step)
+    const int gk = k % G, kr = k / G;   // column k: register kr of group gk
     const int b = k & 1;
-    if (piv) {
+    if (w == 0) {
+      if (grp == gk) x[kr] = fma(-fprev, prk, x[kr]);
+      const bool cand = grp == gk && !used;
+      const float v = cand ? (float)fabs(x[kr]) : -1.f;
+      // maximum over the MPAD lanes of each group (other groups' lanes hold -1)
+      float best = row16_max(v);
+      best = xor16_max(best);
+      // no candidate equals the maximum only when the column holds NaN: then the first
+      // unused row (the output is non-finite, and every unknown still gets its row)
+      const unsigned long long bal = __ballot(cand && v == best);
+      const unsigned long long any = __ballot(cand);
+      lp = (int)__builtin_ctzll(bal ? bal : any);
+      const int p = lp - gk * MPAD;
+      const double pv = readlane_f64(x[kr], lp);
+      // this lane's row in column k, from the lane of group gk that holds it (the
+      // exchange runs on every lane, outside any branch: a lane exchange under a
+      // divergent branch reads inactive lanes)
+      const double other = swap32_f64(x[kr]);
+      const double xk = grp == gk ? x[kr] : other;
+      // 1 / pv: the hardware reciprocal refined by one Newton step
+      double ipv = __builtin_amdgcn_rcp(pv);
+      ipv = fma(ipv, fma(-pv, ipv, 1.0), ipv);
+      const bool piv = row == p;
+      f = piv ? 0.0 : xk * ipv;
+      if (piv) {
+        used = true;
+        var = k;
+        pvr = pv;
+      }
+      if (grp == 0) fkl[b][row] = f;
+      if (lane == 0) pkl[b] = p;
+      // step k - 1 on the columns still live: registers above kr, and register kr of
+      // group 1 when it holds column k + 1
 #pragma unroll
-      for (int j = 0; j < CPL; ++j) prow[b][grp][j] = x[j];
+      for (int j = kr + 1; j < CPL; ++j) x[j] = fma(-fprev, pr[j], x[j]);
+      if (gk == 0 && grp == 1) x[kr] = fma(-fprev, pr[kr], x[kr]);
+      // step k's pivot row on the columns step k + 1 updates (complete through step k - 1)
+      if (piv) {
+#pragma unroll
+        for (int j = (k + 1) / G; j < CPL; ++j) prow[0][b][grp][j] = x[j];
+      }
+    } else if (k > 0) {
+      rhs_apply(k - 1);
     }
+    // publishes step k to every wave, and with the two buffers orders the previous
+    // step's reads before the next writes
     __syncthreads();
+    if (w == 0) {
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) pr[j] = prow[b][grp][j];
-    if (k + 1 < MPAD) {
-      const int gk1 = (k + 1) / CPL, kr1 = (k + 1) % CPL;
-      prk = readlane_f64(x[kr1], lp + (gk1 - gk) * MPAD);
+      for (int j = (k + 1) / G; j < CPL; ++j) pr[j] = prow[0][b][grp][j];
+      if (k + 1 < MPAD) {
+        const int gk1 = (k + 1) % G, kr1 = (k + 1) / G;
+        prk = readlane_f64(x[kr1], lp + (gk1 - gk) * MPAD);
+      }
+      fprev = f;
     }
-    fprev = f;
   }
-  // the last step on every column
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) x[j] = fma(-fprev, pr[j], x[j]);
+  if (w == 0) {
+    if (grp == 0) {
+      varl[row] = var;
+      pvl[row] = pvr;
+    }
+  } else {
+    rhs_apply(MPAD - 1);
+  }
+  __syncthreads();
   // Z[var][k] = right-hand side over the pivot: through LDS (row var of Mx), then out as
   // pass 2's W operands in 16-byte pieces
-  const double ipr = (var < m) ? 1.0 / pvr : 0.0;
+  if (w > 0) {
+    const int vr = varl[row];
+    const double ipr = (vr < m) ? 1.0 / pvl[row] : 0.0;
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int col = grp * CPL + j;
-    if (col >= MPAD) Mx[var * LD + col] = (float)(x[j] * ipr);
+    for (int j = 0; j < RC; ++j) Mx[vr * LD + rhs0 + j] = (float)(x[j] * ipr);
   }
   __syncthreads();
   u32x4* dst = (u32x4*)(Wop + (size_t)slice * MPAD * D);
+  constexpr int PIECES = MPAD * D / 8;
 #pragma unroll
-  for (int i = 0; i < MPAD * D / (8 * kWave); ++i) {
-    // piece q = lane + 64 i of [dt2][jj][lane'][8]: lane' (c', g') holds dim
+  for (int i = 0; i < (PIECES + T - 1) / T; ++i) {
+    // piece q = tid + T i of [dt2][jj][lane'][8]: lane' (c', g') holds dim
     // out_dim_c(dt2, c') and anchors 32jj + 4g' + s (s < 4), 32jj + 16 + 4g' + s - 4
-    const int q = lane + kWave * i, lq = q & 63, jj = (q >> 6) % MP, dt2 = (q >> 6) / MP;
-    const int k = out_dim_c(dt2, lq & 15), a0 = 32 * jj + 4 * (lq >> 4);
-    float v[8];
+    const int q = tid + T * i;
+    if (PIECES % T == 0 || q < PIECES) {
+      const int lq = q & 63, jj = (q >> 6) % MP, dt2 = (q >> 6) / MP;
+      const int k = out_dim_c(dt2, lq & 15), a0 = 32 * jj + 4 * (lq >> 4);
+      float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = Mx[(a0 + (e < 4 ? e : 12 + e)) * LD + MPAD + k];
-    dst[q] = as_u32x4(pack_bf16(f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]}));
+      for (int e = 0; e < 8; ++e) v[e] = Mx[(a0 + (e < 4 ? e : 12 + e)) * LD + MPAD + k];
+      dst[q] = as_u32x4(pack_bf16(f32x4{v[0], v[1], v[2], v[3]}, f32x4{v[4], v[5], v[6], v[7]}));
+    }
   }
 }
 
@@ -522,9 +580,10 @@ template <int D, int AT>
 static void launch_nys_solve_t(const Geometry& g, const SplitPlan& p, const NystromBuffers& nb,
                                const void* Q, const void* K, const int* idx, hipStream_t s) {
   if constexpr (16 * AT <= 32 && D <= 64) {
-    // one wave per slice up to 32 landmarks (at 64, with 64 dependent steps over 128
-    // columns per lane, the ViT-B/16-shape step took 153 us with it against 122 us)
-    nys_solve1<D, AT><<<dim3((unsigned)g.slices), dim3(kWave), 0, s>>>(
+    // F2's elimination in one wave up to 32 landmarks (at 64, a one-wave solve over all
+    // 128 columns made the ViT-B/16-shape step 153 us against 122 us with the multi-wave one)
+    constexpr int RC = kNysRhsCols;
+    nys_solve1<D, AT, RC><<<dim3((unsigned)g.slices), dim3(nys_solve1_waves<D, RC>() * kWave), 0, s>>>(
         nb.part, nb.dpart, nb.cmax, (const __bf16*)Q, (const __bf16*)K, g.vw.q, idx, nb.kt,
         nb.wop, g.h, g.n, g.m, p.chunks1, g.c2);
   } else {
